@@ -1,0 +1,239 @@
+"""CPU oracle for the ANS-resident 4D-STEM query path.
+
+TEST INFRASTRUCTURE ONLY: the library never imports this package. Tests, the
+smoke check and the benchmark's CPU-baseline leg use it to produce expected
+values. It wraps ``oracle.c`` (a plain scalar encoder/decoder written from
+FORMAT.md, plus the dense product definitions) and adds NumPy brute-force
+versions of the products for tiny inputs.
+
+Pins (see tests/test_oracle.py): round-trip identity on every generator and on
+adversarial streams; NumPy brute force and closed forms for the sums and CoM;
+numpy.rint for ties-to-even codes; NumPy float64 reconstruction; table and
+model invariants; hand-built streams decoded against hand-computed values.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK, ERR_ARG, ERR_MALFORMED, ERR_UNSUPPORTED, ERR_OOM = 0, -1, -2, -3, -4
+BLOCK = 512
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in
+                ("scan_rows", "scan_cols", "det_rows", "det_cols", "dtype", "layout", "scaled")]
+
+
+class OracleError(ValueError):
+    def __init__(self, code, msg=""):
+        super().__init__(f"oracle error {code} {msg}")
+        self.code = code
+
+
+def build(force=False):
+    """Compile liboracle.so with gcc (plain C)."""
+    src = os.path.join(_HERE, "oracle.c")
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        cmd = f"gcc -O2 -fPIC -shared -o {_LIB_PATH}.tmp {src} -lm && mv {_LIB_PATH}.tmp {_LIB_PATH}"
+        if os.system(cmd) != 0:
+            raise RuntimeError("failed to build liboracle.so")
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, u64, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
+        lib.orc_encode.argtypes = [ctypes.POINTER(_Geom), vp, ctypes.POINTER(ctypes.POINTER(ctypes.c_uint8))]
+        lib.orc_encode.restype = ctypes.c_int64
+        lib.orc_free.argtypes = [vp]
+        lib.orc_decode.argtypes = [vp, u64, vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+        lib.orc_calibration.argtypes = [vp, u64, vp]
+        lib.orc_masked_sum.argtypes = [vp, u32, u64, u64, vp, vp, u32, vp]
+        lib.orc_com.argtypes = [vp, u32, u64, u32, u32, vp, vp, vp, vp, vp]
+        lib.orc_calibrate.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), vp]
+        lib.orc_reconstruct.argtypes = [vp, u64, ctypes.c_double, ctypes.c_double, vp]
+        lib.orc_reconstruct.restype = None
+        lib.orc_pair_models.argtypes = [vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def encode(counts, scan_rows, scan_cols, det_rows, det_cols, layout=0, scaled=False):
+    """Encode dense counts (S x P, uint8/uint16) or float32 (scaled) into a container blob (bytes)."""
+    arr = np.ascontiguousarray(counts)
+    if scaled:
+        assert arr.dtype == np.float32
+        dtype = 2
+    else:
+        dtype = {np.dtype(np.uint8): 1, np.dtype(np.uint16): 2}[arr.dtype]
+    g = _Geom(scan_rows, scan_cols, det_rows, det_cols, dtype, layout, 1 if scaled else 0)
+    out = ctypes.POINTER(ctypes.c_uint8)()
+    n = _load().orc_encode(ctypes.byref(g), arr.ctypes.data, ctypes.byref(out))
+    if n < 0:
+        raise OracleError(n, "encode")
+    blob = ctypes.string_at(out, n)
+    _lib.orc_free(out)
+    return blob
+
+
+def header(blob):
+    """Geometry fields of a container header."""
+    h = np.frombuffer(blob[:256], dtype=np.uint8)
+    u32 = h[40:80].view(np.uint32)
+    u64 = h[80:144].view(np.uint64)
+    return dict(version=int(u32[0]), layout=int(u32[1]), scan_rows=int(u32[2]), scan_cols=int(u32[3]),
+                det_rows=int(u32[4]), det_cols=int(u32[5]), dtype=int(u32[6]), block_scans=int(u32[7]),
+                n_blocks=int(u32[8]), flags=int(u32[9]), dir_off=int(u64[0]), table_off=int(u64[1]),
+                gbase_off=int(u64[2]), rel_off=int(u64[3]), payload_off=int(u64[4]),
+                payload_bytes=int(u64[5]), calib_off=int(u64[6]), total_bytes=int(u64[7]))
+
+
+def decode(blob):
+    """Dense native counts (S x P) of a blob; raises OracleError(MALFORMED) with the first bad stream."""
+    h = header(blob)
+    S, P = h["scan_rows"] * h["scan_cols"], h["det_rows"] * h["det_cols"]
+    out = np.empty((S, P), dtype=np.uint8 if h["dtype"] == 1 else np.uint16)
+    bb, bp = ctypes.c_int64(), ctypes.c_int64()
+    buf = np.frombuffer(blob, dtype=np.uint8)
+    rc = _load().orc_decode(buf.ctypes.data, len(blob), out.ctypes.data, ctypes.byref(bb), ctypes.byref(bp))
+    if rc:
+        raise OracleError(rc, f"decode block {bb.value} pixel {bp.value}")
+    return out
+
+
+def calibration(blob):
+    """(n_blocks, 2) array of per-block (scale, offset) of a scaled blob."""
+    h = header(blob)
+    out = np.empty((h["n_blocks"], 2), dtype=np.float64)
+    buf = np.frombuffer(blob, dtype=np.uint8)
+    rc = _load().orc_calibration(buf.ctypes.data, len(blob), out.ctypes.data)
+    if rc:
+        raise OracleError(rc, "calibration")
+    return out
+
+
+def sum_bits(P, dtype):
+    """64 when a full-detector sum could exceed 2^32 - 1, else 32."""
+    maxv = 255 if dtype == 1 else 65535
+    return 64 if P * maxv > 2**32 - 1 else 32
+
+
+def masked_sum(counts, mask, valid=None, stride=1):
+    """Exact per-scan sums over mask & valid (uint64); scans of skipped blocks are 0."""
+    c = np.ascontiguousarray(counts)
+    S, P = c.shape
+    dtype = 1 if c.dtype == np.uint8 else 2
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    v = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    out = np.empty(S, dtype=np.uint64)
+    rc = _load().orc_masked_sum(c.ctypes.data, dtype, S, P, m.ctypes.data, _ptr(v), stride, out.ctypes.data)
+    if rc:
+        raise OracleError(rc, "masked_sum")
+    return out
+
+
+def dense_df(counts, mask, valid=None):
+    """Cached-total form of dense DF: total over valid minus the sum over valid & ~mask."""
+    P = counts.shape[1]
+    allm = np.ones(P, dtype=np.uint8)
+    total = masked_sum(counts, allm, valid)
+    comp = masked_sum(counts, (1 - np.asarray(mask, dtype=np.uint8)).astype(np.uint8), valid)
+    return total - comp
+
+
+def com(counts, det_rows, det_cols, mask=None, valid=None):
+    """Exact-moment CoM: (row, col) float32 per scan, plus M0."""
+    c = np.ascontiguousarray(counts)
+    S = c.shape[0]
+    dtype = 1 if c.dtype == np.uint8 else 2
+    m = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    v = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    row = np.empty(S, dtype=np.float32)
+    col = np.empty(S, dtype=np.float32)
+    m0 = np.empty(S, dtype=np.uint64)
+    rc = _load().orc_com(c.ctypes.data, dtype, S, det_rows, det_cols, _ptr(m), _ptr(v), row.ctypes.data,
+                         col.ctypes.data, m0.ctypes.data)
+    if rc:
+        raise OracleError(rc, "com")
+    return row, col, m0
+
+
+def region(counts, scan_cols, r0, r1, c0, c1, valid=None):
+    """counts of the half-open scan rectangle, (h*w, P), invalid pixels zeroed."""
+    rows = []
+    for r in range(r0, r1):
+        rows.append(counts[r * scan_cols + c0: r * scan_cols + c1])
+    out = np.concatenate(rows, axis=0).copy()
+    if valid is not None:
+        out[:, np.asarray(valid) == 0] = 0
+    return out
+
+
+def calibrate(x):
+    """(scale, offset, codes) of one region of float32 values."""
+    a = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    sc, off = ctypes.c_double(), ctypes.c_double()
+    codes = np.empty(a.size, dtype=np.uint16)
+    rc = _load().orc_calibrate(a.ctypes.data, a.size, ctypes.byref(sc), ctypes.byref(off), codes.ctypes.data)
+    if rc:
+        raise OracleError(rc, "calibrate")
+    return sc.value, off.value, codes
+
+
+def reconstruct(codes, scale, offset):
+    """float32 of code*scale + offset, product and sum each rounded in float64."""
+    c = np.ascontiguousarray(codes, dtype=np.uint16).ravel()
+    out = np.empty(c.size, dtype=np.float32)
+    _load().orc_reconstruct(c.ctypes.data, c.size, scale, offset, out.ctypes.data)
+    return out
+
+
+def pair_models():
+    """(32, 256) uint16 pair counts, (32,) window bases and (32,) in-use bit masks of the paired layout."""
+    n = np.empty((32, 256), dtype=np.uint16)
+    a0 = np.empty(32, dtype=np.uint32)
+    use = np.empty(32, dtype=np.uint32)
+    _load().orc_pair_models(n.ctypes.data, a0.ctypes.data, use.ctypes.data)
+    return n, a0, use
+
+
+# ---------------------------------------------------------------------------
+# NumPy brute force for tiny inputs (independent of oracle.c)
+# ---------------------------------------------------------------------------
+
+def brute_masked_sum(counts, mask, valid=None, stride=1):
+    sel = np.asarray(mask).astype(bool)
+    if valid is not None:
+        sel &= np.asarray(valid).astype(bool)
+    out = counts.astype(np.uint64)[:, sel].sum(axis=1, dtype=np.uint64)
+    blocks = np.arange(counts.shape[0]) // BLOCK
+    out[blocks % stride != 0] = 0
+    return out
+
+
+def brute_com(counts, det_rows, det_cols, mask=None, valid=None):
+    sel = np.ones(det_rows * det_cols, dtype=bool) if mask is None else np.asarray(mask).astype(bool)
+    if valid is not None:
+        sel &= np.asarray(valid).astype(bool)
+    kr = (np.arange(det_rows * det_cols) // det_cols).astype(np.uint64)
+    kc = (np.arange(det_rows * det_cols) % det_cols).astype(np.uint64)
+    c = counts.astype(np.uint64)[:, sel]
+    m0 = c.sum(axis=1)
+    mr = (c * kr[sel]).sum(axis=1)
+    mc = (c * kc[sel]).sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        row = np.where(m0 > 0, mr.astype(np.float64) / np.maximum(m0, 1).astype(np.float64), 0.0).astype(np.float32)
+        col = np.where(m0 > 0, mc.astype(np.float64) / np.maximum(m0, 1).astype(np.float64), 0.0).astype(np.float32)
+    return row, col, m0
