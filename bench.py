@@ -1,0 +1,204 @@
+"""Throughput of the fused ANS decode + virtual-detector queries on one MI355X.
+
+Workload: 128 x 128 scans x 192 x 192 uint16 Poisson counts (bright-field
+disk r = 30, mean 5 inside / 0.1 outside, smoothly drifting centre), byte-rANS
+resident in HBM. One step runs every query of the hot path once on it:
+masked_sum (BF disk, block stride 1 and 4), dense DF (warm total cache), CoM
+over the full detector and over the BF disk, and an 8 x 8-scan region read.
+
+Prints one JSON line: value = decoded counts per second over the step (the
+logical counts each query reads, summed), plus encoded-byte GB/s, a roofline
+entry for the dominant kernel and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=16)
+    return ap.parse_args()
+
+
+def step_counts(n_scans, scan_cols, stride_scans, bf, df_mask, valid, P):
+    """Logical counts the step's queries read over the first n_scans scans."""
+    v = np.ones(P, bool) if valid is None else valid.astype(bool)
+    nbf = int((bf.astype(bool) & v).sum())
+    ncomp = int((~df_mask.astype(bool) & v).sum())
+    nvalid = int(v.sum())
+    blocks = sorted({(r * scan_cols + c) // 512 for r in range(8) for c in range(8)})
+    region = sum(min(512, n_scans - b * 512) for b in blocks) * nvalid
+    return n_scans * nbf + stride_scans * nbf + n_scans * ncomp + n_scans * nvalid + n_scans * nbf + region
+
+
+def visited_scans(n_scans, stride):
+    return sum(min(512, n_scans - b * 512) for b in range(0, (n_scans + 511) // 512, stride))
+
+
+def cpu_baseline(w, masks, df_mask, sample_blocks):
+    """The oracle (single-threaded C, as it stands) on the first blocks of the same workload."""
+    import oracle
+    import stem_compressed_count_amd as qsc
+    import synth
+
+    n = min(w.S, 512 * sample_blocks)
+    rows = n // w.scan_cols
+    n = rows * w.scan_cols
+    counts = synth.counts(w, 0, n)
+    blob = qsc.encode(counts, rows, w.scan_cols, w.det_rows, w.det_cols, layout=w.layout).tobytes()
+    valid = synth.valid_pixels(w)
+    bf = masks["bf"]
+    t0 = time.perf_counter()
+    dec = oracle.decode(blob)
+    oracle.masked_sum(dec, bf, valid)
+    oracle.masked_sum(dec, bf, valid, stride=4)
+    oracle.dense_df(dec, df_mask, valid)
+    oracle.com(dec, w.det_rows, w.det_cols, None, valid)
+    oracle.com(dec, w.det_rows, w.det_cols, bf, valid)
+    oracle.region(dec, w.scan_cols, 0, 8, 0, 8, valid)
+    dt = time.perf_counter() - t0
+    done = step_counts(n, w.scan_cols, visited_scans(n, 4), bf, df_mask, valid, w.P)
+    return {"value": round(done / dt, 1), "unit": "counts/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} scans ({(n + 511) // 512} blocks) of the same workload: one oracle decode, "
+                      f"then the step's queries on the decoded counts; {dt:.2f} s single-threaded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: every query runs on a single device's resident "
+              "(the sharded design is described, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import stem_compressed_count_amd as qsc
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    enc = qsc.Encoder(w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, dtype=w.dtype, layout=w.layout)
+    chunk = 512 * 16
+    for s0 in range(0, w.S, chunk):
+        enc.add(synth.counts(w, s0, min(chunk, w.S - s0)))
+    blob = enc.blob()
+    enc.close()
+    t_setup = time.perf_counter() - t0
+    valid = synth.valid_pixels(w)
+    masks = synth.query_masks(w)
+    bf = masks["bf"]
+    df_mask = masks.get("df", (1 - bf).astype(np.uint8))
+    res = qsc.Resident(blob, valid=valid)
+    stream = torch.cuda.current_stream()
+    d_bf = torch.as_tensor(bf, device=dev)
+    d_df = torch.as_tensor(df_mask, device=dev)
+    out = torch.empty(w.S, dtype=res.sum_dtype, device=dev)
+    out4 = torch.empty_like(out)
+    outdf = torch.empty_like(out)
+    row = torch.empty(w.S, dtype=torch.float32, device=dev)
+    col = torch.empty_like(row)
+    rowb = torch.empty_like(row)
+    colb = torch.empty_like(row)
+    reg = torch.empty(64 * w.P, dtype=torch.int16 if w.dtype == 2 else torch.uint8, device=dev)
+
+    # cold: the first dense DF builds the full-detector total cache
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    res.dense_df(d_df, out=outdf, wait=True)
+    cold_ms = (time.perf_counter() - c0) * 1e3
+
+    ev = {}
+
+    def step(timed):
+        res.masked_sum(d_bf, 1, out=out, wait=False)
+        res.masked_sum(d_bf, 4, out=out4, wait=False)
+        res.dense_df(d_df, out=outdf, wait=False)
+        if timed:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        res.com(None, out_row=row, out_col=col, wait=False)
+        if timed:
+            b.record(stream)
+            ev.setdefault("com_full", []).append((a, b))
+        res.com(d_bf, out_row=rowb, out_col=colb, wait=False)
+        res.decode_region(0, 8, 0, 8, out=reg, wait=False)
+
+    for _ in range(args.warmup):
+        step(False)
+    res.finish()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    res.finish()
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / args.steps
+
+    # logical counts and encoded bytes each query of the step reads
+    P = w.P
+    full = np.ones(P, np.uint8) if valid is None else valid
+    by_bf, _ = res.query_bytes(bf, 1)
+    by_bf4, _ = res.query_bytes(bf, 4)
+    by_df, _ = res.query_bytes((1 - df_mask).astype(np.uint8), 1)
+    by_full, cn_full = res.query_bytes(full, 1)
+    n_reg_blocks = len({(r * w.scan_cols + c) // 512 for r in range(8) for c in range(8)})
+    step_cnt = step_counts(w.S, w.scan_cols, visited_scans(w.S, 4), bf, df_mask, valid, P)
+    step_bytes = by_bf + by_bf4 + by_df + by_full + by_bf + by_full * n_reg_blocks / res.info.n_blocks
+    value = step_cnt / (ms_per_step * 1e-3)
+    gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    com_ms = np.mean([a.elapsed_time(b) for a, b in ev["com_full"]])
+    com_gbps = by_full / (com_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(com_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(com_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "k_reduce_rans<uint16, moments> (full-detector CoM query: plan + reduce + finalize)",
+                "launch_ms": round(float(com_ms), 4), "counts_per_launch": cn_full,
+                "encoded_bytes_per_launch": by_full,
+                "counts_per_s": round(cn_full / (com_ms * 1e-3), 1)}
+
+    line = {
+        "metric": "decode+masked_sum counts/s and encoded-byte GB/s (fraction of HBM peak)",
+        "value": round(value, 1), "unit": "counts/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u16" if w.dtype == 2 else "u8", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.scan_rows}x{w.scan_cols} scans x {w.det_rows}x{w.det_cols} "
+                               f"{'uint16' if w.dtype == 2 else 'uint8'} Poisson, "
+                               f"{'byte-rANS' if w.layout == 0 else 'paired tANS'} resident",
+                   "step": "masked_sum BF (stride 1, 4) + dense_df (warm) + com full + com BF + 8x8 region",
+                   "resident_bytes": int(res.info.resident_bytes), "payload_bytes": int(res.info.payload_bytes)},
+        "encoded_GBps": round(gbps, 2), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "step_counts": int(step_cnt), "step_encoded_bytes": int(step_bytes),
+        "host_ms_per_step": round(host_s * 1e3 / args.steps, 4), "cold_dense_df_ms": round(cold_ms, 3),
+        "setup_s": round(t_setup, 2),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, masks, df_mask, args.cpu_sample_blocks)
+    res.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * qsc — ANS-resident 4D-STEM detector counts with fused decode + virtual
+ * detector reductions on AMD Instinct MI355X (gfx950).
+ *
+ * Counts I[s, p] (scan s in row-major order, detector pixel p = kr*det_cols +
+ * kc, native uint8 or uint16) stay entropy coded in device memory as the
+ * container defined in FORMAT.md (byte-rANS or paired tANS layout, 512-scan
+ * blocks, per-pixel streams, grouped offsets). Queries decode and reduce in one
+ * pass on the GPU.
+ *
+ * Conventions for every entry point:
+ *  - Return value: QSC_OK (0) or a negative qsc_status.
+ *  - "host" pointers are CPU memory, "device" pointers are HIP device memory
+ *    of the resident's GPU. The caller owns every buffer it passes in; the
+ *    library owns the resident and everything it allocates for it.
+ *  - hip_stream is a hipStream_t (NULL = the default stream). Queries are
+ *    enqueued on it. With wait = 0 a query only enqueues and its decode status
+ *    is reported by qsc_finish; with wait = 1 it synchronises the stream and
+ *    returns QSC_ERR_MALFORMED if any stream it decoded was malformed, in
+ *    which case the output buffer holds no result (paired-resident page,
+ *    "Contract": a malformed stream fails the query and no result is
+ *    returned).
+ *  - Argument errors are detected on the host before anything is enqueued and
+ *    leave outputs untouched.
+ *  - Calls that enqueue work on the same resident must not run concurrently
+ *    from several host threads (they share the resident's scratch buffers).
+ */
+#ifndef QSC_H
+#define QSC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qsc_status;
+#define QSC_OK 0
+#define QSC_ERR_INVALID_ARG -1 /* bad pointer, size, rectangle or geometry */
+#define QSC_ERR_MALFORMED -2   /* a container or stream breaks FORMAT.md */
+#define QSC_ERR_UNSUPPORTED -3 /* another ABI tag or format version */
+#define QSC_ERR_OOM -4         /* host or device allocation failed */
+#define QSC_ERR_HIP -5         /* a HIP runtime call failed */
+
+typedef struct qsc_resident qsc_resident;
+typedef struct qsc_encoder qsc_encoder;
+
+/* Geometry of an acquisition; dtype 1 = uint8, 2 = uint16; layout 0 =
+ * byte-rANS, 1 = paired tANS; scaled = 1: float32 input stored as per-block
+ * calibrated uint16 codes (layout 0, dtype 2 only). */
+typedef struct {
+    uint32_t scan_rows, scan_cols, det_rows, det_cols;
+    uint32_t dtype, layout, scaled;
+} qsc_geometry;
+
+typedef struct {
+    qsc_geometry geom;
+    uint32_t n_blocks;      /* ceil(scans / 512) */
+    uint32_t sum_bits;      /* 32 or 64: width of masked_sum / dense_df outputs */
+    uint64_t resident_bytes; /* device bytes held by the resident */
+    uint64_t payload_bytes; /* encoded stream bytes */
+    uint64_t mode_counts[8]; /* streams per mode number (FORMAT 2.4 / 3.4) */
+} qsc_info;
+
+/* ABI strings of the stream layouts this build reads:
+ * "qsc-byte-rans-v1;qsc-paired-v1". A container carrying another tag is
+ * refused (paired-resident page, "Contract": reopen refuses another ABI). */
+const char *qsc_abi(void);
+
+/* Human-readable text of a status code. */
+const char *qsc_status_string(qsc_status s);
+
+/* ---------------------------------------------------------------- encoder
+ * Host encoder (FORMAT.md), multithreaded over 512-scan blocks. Its output is
+ * byte-identical to the format's reference encoder. The paired-resident page
+ * ("Operation pipeline" items 1-2) has counts arrive as complete 512-scan
+ * blocks and be coded per detector-pixel stream; the scaled-uint16 page has
+ * float32 regions calibrated to uint16 codes before ANS coding.
+ *
+ * qsc_encoder_create: validates the geometry (INVALID_ARG otherwise).
+ * qsc_encoder_add: host_data holds n_scans x P values, scan-major, native
+ *   dtype (float32 when scaled). Scans are appended in order; every call but
+ *   the last must carry a multiple of 512 scans. threads <= 0 picks the host
+ *   core count. NaN/Inf in scaled input or too many scans -> INVALID_ARG.
+ * qsc_encoder_size / qsc_encoder_write: once all scans are added, the blob
+ *   size and a copy into caller memory of at least that many bytes.
+ */
+qsc_status qsc_encoder_create(const qsc_geometry *geom, qsc_encoder **out);
+qsc_status qsc_encoder_add(qsc_encoder *enc, const void *host_data, uint64_t n_scans, int threads);
+qsc_status qsc_encoder_size(const qsc_encoder *enc, uint64_t *nbytes);
+qsc_status qsc_encoder_write(const qsc_encoder *enc, void *host_out, uint64_t capacity);
+qsc_status qsc_encoder_destroy(qsc_encoder *enc);
+
+/* ---------------------------------------------------------------- resident
+ * qsc_resident_create: validates a host blob (header, ABI tag, block
+ *   directory, grouped offsets, table sums, every stream header: reserved
+ *   bits, mode, model) and copies it to device memory on the current HIP
+ *   device. host_valid (nullable) is P bytes, nonzero = valid detector pixel;
+ *   NULL means every pixel is valid. Validity never changes the stored counts
+ *   (quantem.widget ANS page: valid_pixels does not overwrite raw sentinels).
+ *   Errors: INVALID_ARG, MALFORMED (structure), UNSUPPORTED (ABI), OOM, HIP.
+ * qsc_resident_destroy: synchronises and frees everything the resident owns.
+ *   The caller must destroy every resident it creates (scaled-uint16 page:
+ *   the caller closes loaded residents).
+ * qsc_resident_info: geometry and sizes (see qsc_info).
+ */
+qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uint8_t *host_valid,
+                               void *hip_stream, qsc_resident **out);
+qsc_status qsc_resident_destroy(qsc_resident *res);
+qsc_status qsc_resident_info(const qsc_resident *res, qsc_info *info);
+
+/* ---------------------------------------------------------------- queries
+ * qsc_masked_sum: virtual image out[s] = sum over p with mask[p] != 0 and
+ *   valid[p] of I[s, p], exact, as uint32, or uint64 when
+ *   P * maxval(dtype) > 2^32 - 1 (qsc_info.sum_bits; paired-resident page,
+ *   "Contract", row "virtual image"). d_mask: device, P bytes. d_out: device,
+ *   scans x (sum_bits/8) bytes. block_stride k >= 1 decodes only blocks b
+ *   with b mod k == 0 (paired-resident page, "Operation pipeline" item 4);
+ *   scans of the other blocks read 0.
+ * qsc_dense_df: dark field out[s] = total[s] - sum over valid p with
+ *   mask[p] == 0 of I[s, p], where total is the full-detector sum over valid
+ *   pixels, built by a full decode on the first call and cached in the
+ *   resident (optimization matrix page, "Product Coverage", row "Dense DF").
+ *   Equals qsc_masked_sum with the same mask.
+ * qsc_com: centre of mass in detector pixel-index units (optimization matrix
+ *   page, "Product Coverage", row "CoM/DPC"): exact integer moments
+ *   M0 = sum I, Mr = sum I*kr, Mc = sum I*kc over mask & valid (all valid
+ *   pixels when d_mask is NULL), then row = (float)((double)Mr / M0), col
+ *   likewise, 0 where M0 = 0. d_row, d_col: device float32[scans].
+ * qsc_decode_region: counts of the half-open scan rectangle r0 <= r < r1,
+ *   c0 <= c < c1 (scaled-uint16 page: read(scan_region=...)), written as
+ *   out[((r-r0)*(c1-c0) + (c-c0)) * P + p]; invalid pixels read 0
+ *   (paired-resident page, "Contract", row "diffraction pattern"). out_kind
+ *   0: native dtype; 1: float32 calibrated intensity code*scale+offset of the
+ *   scan's region (scaled residents only). Empty or out-of-range rectangle,
+ *   or out_kind 1 on an unscaled resident -> INVALID_ARG.
+ * qsc_finish: synchronises hip_stream and reports (then clears) the first
+ *   malformed stream found by queries enqueued since the last check.
+ * qsc_last_error: message of the resident's last failure, naming the first
+ *   bad (block, pixel) for MALFORMED; valid until the next call on it.
+ */
+qsc_status qsc_masked_sum(qsc_resident *res, const uint8_t *d_mask, uint32_t block_stride, void *d_out,
+                          void *hip_stream, int wait);
+qsc_status qsc_dense_df(qsc_resident *res, const uint8_t *d_mask, void *d_out, void *hip_stream, int wait);
+qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float *d_col, void *hip_stream,
+                   int wait);
+qsc_status qsc_decode_region(qsc_resident *res, uint32_t r0, uint32_t r1, uint32_t c0, uint32_t c1, int out_kind,
+                             void *d_out, void *hip_stream, int wait);
+qsc_status qsc_finish(qsc_resident *res, void *hip_stream);
+const char *qsc_last_error(const qsc_resident *res);
+
+/* Exact encoded bytes and logical counts a masked_sum with this host mask
+ * (P bytes) and stride touches: stream bytes of every selected (block, pixel)
+ * plus its offset entries, and n_visited_scans x n_selected counts. This is
+ * the numerator of the encoded-byte GB/s a query sustains. */
+qsc_status qsc_query_bytes(const qsc_resident *res, const uint8_t *host_mask, uint32_t block_stride,
+                           uint64_t *bytes, uint64_t *counts);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,267 @@
+"""Python binding of libqsc: ANS-resident 4D-STEM counts with fused GPU queries.
+
+Argument marshalling only: every step of a query runs in the library's HIP
+kernels. PyTorch supplies device memory and streams (tensor data pointers and
+``torch.cuda.current_stream().cuda_stream``). Importing works without a GPU
+(the encoder is host code); queries need a gfx950 device. There is no CPU
+fallback: if libqsc.so is missing the import fails.
+
+Entry points mirror include/qsc.h:
+    encode(data, geometry) -> bytes          qsc_encoder_*
+    Resident(blob, valid=None)               qsc_resident_create / destroy / info
+    Resident.masked_sum(mask, block_stride)  qsc_masked_sum
+    Resident.dense_df(mask)                  qsc_dense_df
+    Resident.com(mask=None)                  qsc_com
+    Resident.decode_region(r0, r1, c0, c1)   qsc_decode_region
+    Resident.finish()                        qsc_finish
+    Resident.query_bytes(mask, stride)       qsc_query_bytes
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsc.so")
+
+OK, ERR_INVALID_ARG, ERR_MALFORMED, ERR_UNSUPPORTED, ERR_OOM, ERR_HIP = 0, -1, -2, -3, -4, -5
+
+
+class QscError(RuntimeError):
+    """A failed library call; ``code`` is the qsc_status."""
+
+    def __init__(self, code, msg):
+        super().__init__(msg)
+        self.code = code
+
+
+class QscValueError(QscError, ValueError):
+    """Malformed container/stream or invalid argument (the pages' ValueError)."""
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in
+                ("scan_rows", "scan_cols", "det_rows", "det_cols", "dtype", "layout", "scaled")]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("geom", Geometry), ("n_blocks", ctypes.c_uint32), ("sum_bits", ctypes.c_uint32),
+                ("resident_bytes", ctypes.c_uint64), ("payload_bytes", ctypes.c_uint64),
+                ("mode_counts", ctypes.c_uint64 * 8)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(python -m stem_compressed_count_amd.build); there is no fallback path")
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _u32, _u64, _i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32
+_SIGS = {
+    "qsc_abi": ([], ctypes.c_char_p),
+    "qsc_status_string": ([_i32], ctypes.c_char_p),
+    "qsc_encoder_create": ([ctypes.POINTER(Geometry), ctypes.POINTER(_vp)], _i32),
+    "qsc_encoder_add": ([_vp, _vp, _u64, ctypes.c_int], _i32),
+    "qsc_encoder_size": ([_vp, ctypes.POINTER(_u64)], _i32),
+    "qsc_encoder_write": ([_vp, _vp, _u64], _i32),
+    "qsc_encoder_destroy": ([_vp], _i32),
+    "qsc_resident_create": ([_vp, _u64, _vp, _vp, ctypes.POINTER(_vp)], _i32),
+    "qsc_resident_destroy": ([_vp], _i32),
+    "qsc_resident_info": ([_vp, ctypes.POINTER(Info)], _i32),
+    "qsc_masked_sum": ([_vp, _vp, _u32, _vp, _vp, ctypes.c_int], _i32),
+    "qsc_dense_df": ([_vp, _vp, _vp, _vp, ctypes.c_int], _i32),
+    "qsc_com": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int], _i32),
+    "qsc_decode_region": ([_vp, _u32, _u32, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
+    "qsc_finish": ([_vp, _vp], _i32),
+    "qsc_last_error": ([_vp], ctypes.c_char_p),
+    "qsc_query_bytes": ([_vp, _vp, _u32, ctypes.POINTER(_u64), ctypes.POINTER(_u64)], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTS = tuple(_SIGS)
+
+
+def abi():
+    return lib.qsc_abi().decode()
+
+
+def _raise(code, msg):
+    text = f"{lib.qsc_status_string(code).decode()}: {msg}"
+    if code in (ERR_MALFORMED, ERR_INVALID_ARG, ERR_UNSUPPORTED):
+        raise QscValueError(code, text)
+    raise QscError(code, text)
+
+
+def encode(data, scan_rows, scan_cols, det_rows, det_cols, layout=0, scaled=False, threads=0):
+    """Encode (S x P) uint8/uint16 counts, or float32 when scaled, into a container blob (numpy uint8)."""
+    enc = Encoder(scan_rows, scan_cols, det_rows, det_cols,
+                  dtype=2 if scaled else (1 if np.asarray(data).dtype == np.uint8 else 2),
+                  layout=layout, scaled=scaled)
+    try:
+        enc.add(data, threads)
+        return enc.blob()
+    finally:
+        enc.close()
+
+
+class Encoder:
+    """Streaming host encoder: add scans in order (multiples of 512 but the last), then blob()."""
+
+    def __init__(self, scan_rows, scan_cols, det_rows, det_cols, dtype, layout=0, scaled=False):
+        self.geom = Geometry(scan_rows, scan_cols, det_rows, det_cols, dtype, layout, 1 if scaled else 0)
+        self.P = det_rows * det_cols
+        self.scaled = scaled
+        self._h = _vp()
+        rc = lib.qsc_encoder_create(ctypes.byref(self.geom), ctypes.byref(self._h))
+        if rc:
+            _raise(rc, "encoder geometry")
+
+    def add(self, data, threads=0):
+        want = np.float32 if self.scaled else (np.uint8 if self.geom.dtype == 1 else np.uint16)
+        a = np.ascontiguousarray(data)
+        if a.dtype != want or a.size % self.P:
+            raise ValueError(f"expected {np.dtype(want).name} data with {self.P} values per scan")
+        rc = lib.qsc_encoder_add(self._h, a.ctypes.data, a.size // self.P, threads)
+        if rc:
+            _raise(rc, "encoder add")
+
+    def blob(self):
+        n = _u64()
+        rc = lib.qsc_encoder_size(self._h, ctypes.byref(n))
+        if rc:
+            _raise(rc, "encoder size (were all scans added?)")
+        out = np.empty(n.value, dtype=np.uint8)
+        rc = lib.qsc_encoder_write(self._h, out.ctypes.data, n.value)
+        if rc:
+            _raise(rc, "encoder write")
+        return out
+
+    def close(self):
+        if self._h:
+            lib.qsc_encoder_destroy(self._h)
+            self._h = _vp()
+
+    def __del__(self):
+        self.close()
+
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Resident:
+    """An encoded acquisition resident in device memory (qsc_resident)."""
+
+    def __init__(self, blob, valid=None, stream=None):
+        import torch
+        b = np.ascontiguousarray(np.frombuffer(blob, dtype=np.uint8) if isinstance(blob, (bytes, bytearray))
+                                 else blob, dtype=np.uint8)
+        v = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+        self._h = _vp()
+        rc = lib.qsc_resident_create(b.ctypes.data, b.size, None if v is None else v.ctypes.data,
+                                     _stream_handle(stream), ctypes.byref(self._h))
+        if rc:
+            _raise(rc, "resident_create")
+        info = Info()
+        lib.qsc_resident_info(self._h, ctypes.byref(info))
+        self.info = info
+        g = info.geom
+        self.scan_rows, self.scan_cols, self.det_rows, self.det_cols = g.scan_rows, g.scan_cols, g.det_rows, g.det_cols
+        self.S, self.P = g.scan_rows * g.scan_cols, g.det_rows * g.det_cols
+        self.dtype = g.dtype
+        self.scaled = bool(g.scaled)
+        self.sum_dtype = torch.int64 if info.sum_bits == 64 else torch.int32
+        self.device = torch.device("cuda", torch.cuda.current_device())
+
+    # -- helpers
+    def _check(self, rc, what):
+        if rc:
+            _raise(rc, f"{what}: {lib.qsc_last_error(self._h).decode()}")
+
+    def _mask(self, mask):
+        import torch
+        m = torch.as_tensor(mask, dtype=torch.uint8, device=self.device).contiguous()
+        if m.numel() != self.P:
+            raise ValueError(f"mask must have {self.P} entries")
+        return m
+
+    def _out(self, out, dtype, n):
+        import torch
+        if out is None:
+            return torch.empty(n, dtype=dtype, device=self.device)
+        if out.dtype != dtype or out.numel() != n or not out.is_contiguous() or out.device != self.device:
+            raise ValueError(f"out must be a contiguous {dtype} tensor of {n} elements on {self.device}")
+        return out
+
+    # -- queries
+    def masked_sum(self, mask, block_stride=1, out=None, stream=None, wait=True):
+        """Exact per-scan sums over mask & valid (int32 storage of uint32, or int64 of uint64)."""
+        m = self._mask(mask)
+        o = self._out(out, self.sum_dtype, self.S)
+        self._check(lib.qsc_masked_sum(self._h, m.data_ptr(), block_stride, o.data_ptr(), _stream_handle(stream),
+                                       int(wait)), "masked_sum")
+        return o
+
+    def dense_df(self, mask, out=None, stream=None, wait=True):
+        m = self._mask(mask)
+        o = self._out(out, self.sum_dtype, self.S)
+        self._check(lib.qsc_dense_df(self._h, m.data_ptr(), o.data_ptr(), _stream_handle(stream), int(wait)),
+                    "dense_df")
+        return o
+
+    def com(self, mask=None, out_row=None, out_col=None, stream=None, wait=True):
+        import torch
+        m = None if mask is None else self._mask(mask)
+        row = self._out(out_row, torch.float32, self.S)
+        col = self._out(out_col, torch.float32, self.S)
+        self._check(lib.qsc_com(self._h, None if m is None else m.data_ptr(), row.data_ptr(), col.data_ptr(),
+                                _stream_handle(stream), int(wait)), "com")
+        return row, col
+
+    def decode_region(self, r0, r1, c0, c1, calibrated=False, out=None, stream=None, wait=True):
+        """(h*w, P) counts of the scan rectangle; float32 intensities when calibrated (scaled residents)."""
+        import torch
+        if not (0 <= r0 < r1 <= self.scan_rows and 0 <= c0 < c1 <= self.scan_cols):
+            raise ValueError("scan_region out of range or empty")
+        n = (r1 - r0) * (c1 - c0) * self.P
+        dt = torch.float32 if calibrated else (torch.uint8 if self.dtype == 1 else torch.int16)
+        o = self._out(out, dt, n)
+        self._check(lib.qsc_decode_region(self._h, r0, r1, c0, c1, 1 if calibrated else 0, o.data_ptr(),
+                                          _stream_handle(stream), int(wait)), "decode_region")
+        return o.view((r1 - r0) * (c1 - c0), self.P)
+
+    def finish(self, stream=None):
+        self._check(lib.qsc_finish(self._h, _stream_handle(stream)), "finish")
+
+    def query_bytes(self, mask, block_stride=1):
+        """(encoded bytes, logical counts) a masked_sum with this mask reads."""
+        m = np.ascontiguousarray(mask, dtype=np.uint8)
+        by, cn = _u64(), _u64()
+        self._check(lib.qsc_query_bytes(self._h, m.ctypes.data, block_stride, ctypes.byref(by), ctypes.byref(cn)),
+                    "query_bytes")
+        return by.value, cn.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib.qsc_resident_destroy(self._h)
+            self._h = _vp()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        self.close()
+
+
+def as_unsigned(t):
+    """numpy view of a sum tensor as uint32/uint64 (the library's result type)."""
+    a = t.cpu().numpy()
+    return a.view(np.uint32 if a.dtype == np.int32 else np.uint64 if a.dtype == np.int64 else
+                  np.uint16 if a.dtype == np.int16 else a.dtype)

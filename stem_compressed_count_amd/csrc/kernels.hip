@@ -1,0 +1,1014 @@
+// Fused ANS decode + virtual-detector reduction kernels for gfx950 (CDNA4).
+//
+// Hot path of the paired-resident page ("Operation pipeline" item 4): a mask
+// becomes a list of selected detector pixels (plan), then every selected
+// stream of every visited 512-scan block is decoded by one lane, with a 64-bit
+// bit reservoir refilled 32 bits at a time from a prefetched dword, decode
+// tables in LDS, and a wavefront transpose-reduce of per-scan partial sums
+// (the page's warp-wide packed reduction per 32 scans, done here on wave64
+// lanes). Streams stored in exact non-entropy forms (constant, sparse) are
+// folded into LDS partials directly instead of stepping through the scans.
+// Outputs are exact integers; the reduction order never matters.
+//
+// The products follow the optimization-matrix page, "Product Coverage": sparse
+// BF/ADF masks as selected-pixel sums, dense DF as a cached full-detector total
+// minus the complement, and CoM from fused moment sums.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace qsc {
+
+namespace {
+
+constexpr uint32_t kBlk = 512;
+constexpr uint32_t kRansWG = 256;   // threads per byte-rANS workgroup
+constexpr uint32_t kPairWG = 1024;  // threads per paired workgroup (one per CU: all 32 tables in LDS)
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
+
+__device__ __forceinline__ void report(const DevResident &r, uint32_t b, uint32_t p) {
+    atomicCAS(r.err, 0ull, ((unsigned long long)(b + 1) << 32) | p);
+}
+
+struct Extent {
+    uint64_t start, end;
+};
+
+__device__ __forceinline__ Extent locate(const DevResident &r, uint32_t b, uint32_t p, uint64_t base,
+                                         uint32_t nbytes) {
+    const uint64_t gi = (uint64_t)b * r.G + (p >> 5);
+    Extent e;
+    e.start = base + r.gbase[gi] + r.rel[gi * 32 + (p & 31)];
+    if (p + 1 < r.P) {
+        const uint64_t gj = (uint64_t)b * r.G + ((p + 1) >> 5);
+        e.end = base + r.gbase[gj] + r.rel[gj * 32 + ((p + 1) & 31)];
+    } else {
+        e.end = base + nbytes;
+    }
+    return e;
+}
+
+__device__ __forceinline__ uint32_t ld16(const uint8_t *pay, uint64_t off) {
+    return *reinterpret_cast<const uint16_t *>(pay + off);
+}
+
+// ------------------------------------------------------------------ bit reservoir
+// Next bits of the stream sit at the bottom of r; n bits are valid. The dword
+// after them is already loaded into pf, so a refill never waits on a fresh load.
+struct Bits {
+    uint64_t r;
+    uint32_t n;
+    uint32_t q;  // dword index of pf in the payload
+    uint32_t pf;
+};
+
+__device__ __forceinline__ void bits_init(Bits &s, const uint32_t *pay32, uint64_t start) {
+    const uint32_t qd = (uint32_t)(start >> 2);
+    const uint32_t d0 = pay32[qd], d1 = pay32[qd + 1];
+    s.r = ((uint64_t)d1 << 32) | d0;
+    s.n = 64;
+    if (start & 2) {
+        s.r >>= 16;
+        s.n = 48;
+    }
+    s.q = qd + 2;
+    s.pf = pay32[s.q];
+}
+
+__device__ __forceinline__ void bits_refill(Bits &s, const uint32_t *pay32) {
+    if (s.n <= 32) {
+        s.r |= (uint64_t)s.pf << s.n;
+        s.n += 32;
+        s.q++;
+        s.pf = pay32[s.q];
+    }
+}
+
+// bits consumed since the stream start; org = (start >> 2) << 1 | (start >> 1 & 1)
+__device__ __forceinline__ uint32_t bits_used(const Bits &s, uint32_t org) {
+    return 32u * (s.q - (org >> 1)) - s.n - ((org & 1) ? 16u : 0u);
+}
+
+__device__ __forceinline__ uint32_t origin(uint64_t start) {
+    return (uint32_t)((start >> 2) << 1) | (uint32_t)((start >> 1) & 1);
+}
+
+__device__ __forceinline__ uint32_t pop16(Bits &s) {
+    const uint32_t w = (uint32_t)s.r & 0xFFFFu;
+    s.r >>= 16;
+    s.n -= 16;
+    return w;
+}
+
+__device__ __forceinline__ uint32_t popn(Bits &s, uint32_t nb) {
+    const uint32_t v = (uint32_t)s.r & ((1u << nb) - 1u);
+    s.r >>= nb;
+    s.n -= nb;
+    return v;
+}
+
+// byte-rANS decode of one value (FORMAT 2.3). Table entry: sym | (f-1) << 8 | (slot - c) << 20.
+template <bool WIDE>
+__device__ __forceinline__ uint32_t rans_step(uint32_t &x, Bits &s, const uint32_t *tbl, uint32_t &bad) {
+    const uint32_t e = tbl[x & 4095u];
+    const uint32_t q = x >> 12;
+    const uint32_t xn = __umul24((e >> 8) & 0xFFFu, q) + q + (e >> 20);
+    const uint32_t w = (uint32_t)s.r & 0xFFFFu;
+    const bool need = xn < 65536u;
+    x = need ? ((xn << 16) | w) : xn;
+    const uint32_t sh = need ? 16u : 0u;
+    s.r >>= sh;
+    s.n -= sh;
+    uint32_t v = e & 0xFFu;
+    if (WIDE && v == 255u) {
+        const uint32_t lit = pop16(s);
+        bad |= lit < 255u;
+        v = lit;
+    }
+    return v;
+}
+
+// ------------------------------------------------------------------ wave reductions
+// Transpose-reduce of CH per-lane accumulators over the 64 lanes of a wave:
+// every level pairs two registers and halves their count, so no value is ever
+// moved twice. Cross-row levels use the gfx950 lane-swap instructions
+// (v_permlane32_swap: lanes l and l+32; v_permlane16_swap: rows of 16), in-row
+// levels a DPP-sourced add. Afterwards each lane holds the wave total of one
+// scan of the chunk; which one is lane_scan() (found by reducing an index
+// probe once, so the result does not depend on the swap direction).
+__device__ __forceinline__ uint32_t bf32(uint32_t a, uint32_t b) {
+    const auto s = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return s[0] + s[1];
+}
+__device__ __forceinline__ uint32_t bf16(uint32_t a, uint32_t b) {
+    const auto s = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return s[0] + s[1];
+}
+// DPP level: lanes with (lane & BIT) == 0 keep a, the others keep b; CTRL
+// pairs each lane with one of the opposite half.
+template <int CTRL, int BIT>
+__device__ __forceinline__ uint32_t bfdpp(uint32_t a, uint32_t b) {
+    const bool up = lane_id() & BIT;
+    const uint32_t keep = up ? b : a, send = up ? a : b;
+    return keep + (uint32_t)__builtin_amdgcn_mov_dpp((int)send, CTRL, 0xF, 0xF, false);
+}
+constexpr int kRowRor8 = 0x128;     // lane i <- i^8 within a row of 16
+constexpr int kHalfMirror = 0x141;  // lane i <- 7-i within each 8 lanes (pairs bit 2)
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+
+template <int CH>
+__device__ __forceinline__ uint32_t wave_transpose_sum(uint32_t (&a)[CH]) {
+    static_assert(CH == 32 || CH == 16 || CH == 8, "chunk of 8, 16 or 32 scans");
+    uint32_t v;
+    if (CH == 32) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) a[i] = bf32(a[i], a[i + 16]);
+#pragma unroll
+        for (int i = 0; i < 8; i++) a[i] = bf16(a[i], a[i + 8]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) a[i] = bfdpp<kRowRor8, 8>(a[i], a[i + 4]);
+#pragma unroll
+        for (int i = 0; i < 2; i++) a[i] = bfdpp<kHalfMirror, 4>(a[i], a[i + 2]);
+        v = bfdpp<kQuadXor2, 2>(a[0], a[1]);
+        v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, false);
+    } else if (CH == 16) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) a[i] = bf32(a[i], a[i + 8]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) a[i] = bf16(a[i], a[i + 4]);
+#pragma unroll
+        for (int i = 0; i < 2; i++) a[i] = bfdpp<kRowRor8, 8>(a[i], a[i + 2]);
+        v = bfdpp<kHalfMirror, 4>(a[0], a[1]);
+        v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, false);
+        v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, false);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) a[i] = bf32(a[i], a[i + 4]);
+#pragma unroll
+        for (int i = 0; i < 2; i++) a[i] = bf16(a[i], a[i + 2]);
+        v = bfdpp<kRowRor8, 8>(a[0], a[1]);
+        v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kHalfMirror, 0xF, 0xF, false);
+        v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, false);
+        v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, false);
+    }
+    return v;
+}
+
+// Scan (within the chunk) whose total lane_id() holds after wave_transpose_sum,
+// and whether this lane is the one that writes it.
+template <int CH>
+__device__ __forceinline__ uint32_t lane_scan() {
+    uint32_t probe[CH];
+#pragma unroll
+    for (int i = 0; i < CH; i++) probe[i] = lane_id() == 0 ? (uint32_t)i : 0u;
+    return wave_transpose_sum<CH>(probe) & (CH - 1);
+}
+template <int CH>
+__device__ __forceinline__ bool lane_writes() {
+    return (lane_id() & (64 / CH - 1)) == 0;
+}
+
+// Adds the wave totals of one chunk to the LDS partials. Moment terms can pass
+// 2^32 over a wave, so they are split into 16-bit halves that reduce without
+// overflow (64 lanes x 2^16 < 2^32) and are recombined in 64 bits.
+template <int CH, Op OP>
+__device__ __forceinline__ void chunk_to_lds(uint32_t (&a0)[CH], uint32_t (&ar)[OP == Op::Moments ? CH : 1],
+                                             uint32_t (&ac)[OP == Op::Moments ? CH : 1], uint32_t my, bool writer,
+                                             uint32_t *m0, unsigned long long *mr, unsigned long long *mc) {
+    const uint32_t t0 = wave_transpose_sum<CH>(a0);
+    if (writer && t0) atomicAdd(&m0[my], t0);
+    if constexpr (OP == Op::Moments) {
+        uint32_t lo[CH];
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            lo[i] = ar[i] & 0xFFFFu;
+            ar[i] >>= 16;
+        }
+        const unsigned long long tr =
+            ((unsigned long long)wave_transpose_sum<CH>(ar) << 16) + wave_transpose_sum<CH>(lo);
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            lo[i] = ac[i] & 0xFFFFu;
+            ac[i] >>= 16;
+        }
+        const unsigned long long tc =
+            ((unsigned long long)wave_transpose_sum<CH>(ac) << 16) + wave_transpose_sum<CH>(lo);
+        if (writer && tr) atomicAdd(&mr[my], tr);
+        if (writer && tc) atomicAdd(&mc[my], tc);
+    }
+}
+// ------------------------------------------------------------------ LDS partials of one work item
+template <Op OP>
+struct Partials {
+    uint32_t *m0;            // [512]
+    unsigned long long *mr;  // [512] (moments only)
+    unsigned long long *mc;
+    uint32_t *c0;            // constant per scan (constant streams)
+    unsigned long long *cr, *cc;
+};
+
+template <Op OP>
+__device__ __forceinline__ void add_event(const Partials<OP> &pt, int pos, uint32_t v, uint32_t kr, uint32_t kc) {
+    if (pos < 0) {
+        atomicAdd(pt.c0, v);
+        if (OP == Op::Moments) {
+            atomicAdd(pt.cr, (unsigned long long)v * kr);
+            atomicAdd(pt.cc, (unsigned long long)v * kc);
+        }
+    } else {
+        atomicAdd(&pt.m0[pos], v);
+        if (OP == Op::Moments) {
+            atomicAdd(&pt.mr[pos], (unsigned long long)v * kr);
+            atomicAdd(&pt.mc[pos], (unsigned long long)v * kc);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ byte-rANS tile
+// Per-slot state kept in registers across the 512 steps (kept small: the tile
+// holds up to four slots per lane).
+struct RSlot {
+    uint32_t x;     // rANS state
+    uint32_t meta;  // mode (1 RANS, 2 RAW, 3 idle) | held byte of a RAW uint8 word << 8
+    uint32_t p;     // detector pixel
+    uint32_t org;   // stream origin (see bits_used)
+    uint32_t len;   // stream bytes
+    Bits s;
+};
+
+template <int K, bool WIDE, Op OP>
+__device__ __forceinline__ void rans_tile(const DevResident &r, const uint32_t *sel, uint32_t n_sel, uint32_t first, uint32_t b,
+                          uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt) {
+    const uint32_t *pay32 = reinterpret_cast<const uint32_t *>(r.payload);
+    const uint32_t lane = lane_id();
+    const uint32_t maxv = WIDE ? 65535u : 255u;
+    RSlot sl[K];
+    uint32_t bad = 0;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        RSlot &z = sl[k];
+        z.meta = 3;
+        z.x = 0;
+        z.p = 0;
+        const uint32_t i = first + k * 64 + lane;
+        if (i >= n_sel) continue;
+        z.p = sel[i];
+        const Extent e = locate(r, b, z.p, base, nbytes);
+        z.org = origin(e.start);
+        z.len = (uint32_t)(e.end - e.start);
+        const uint32_t hdr = ld16(r.payload, e.start);
+        const uint32_t mode = hdr & 7u;
+        if (mode == 0) {  // CONST
+            const uint32_t v = ld16(r.payload, e.start + 2);
+            if (z.len != 4 || v > maxv) {
+                report(r, b, z.p);
+                continue;
+            }
+            const uint32_t kr = z.p / r.det_cols;
+            if (v) add_event<OP>(pt, -1, v, kr, z.p - kr * r.det_cols);
+            continue;
+        }
+        z.meta = mode;
+        bits_init(z.s, pay32, e.start);
+        pop16(z.s);  // header
+        if (mode == 1) {
+            z.x = pop16(z.s);
+            z.x |= pop16(z.s) << 16;
+        }
+        bits_refill(z.s, pay32);
+    }
+    uint32_t kr[OP == Op::Moments ? K : 1], kc[OP == Op::Moments ? K : 1];
+    if (OP == Op::Moments) {
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            kr[k] = sl[k].p / r.det_cols;
+            kc[k] = sl[k].p - kr[k] * r.det_cols;
+        }
+    }
+
+    constexpr int CH = OP == Op::Sum ? 32 : 16;
+    const uint32_t my = lane_scan<CH>();
+    const bool writer = lane_writes<CH>();
+    const uint32_t nch = (n + CH - 1) / CH;
+    for (uint32_t c = 0; c < nch; c++) {
+        uint32_t a0[CH];
+        uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            a0[i] = 0;
+            if (OP == Op::Moments) {
+                ar[i] = 0;
+                ac[i] = 0;
+            }
+        }
+        const uint32_t jn = min((uint32_t)CH, n - c * CH);
+#pragma unroll
+        for (int jj = 0; jj < CH; jj++) {
+            if ((uint32_t)jj < jn) {
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+                    RSlot &z = sl[k];
+                    const uint32_t mode = z.meta & 0xFFu;
+                    uint32_t v = 0;
+                    if (mode == 1) {
+                        v = rans_step<WIDE>(z.x, z.s, tbl, bad);
+                        bits_refill(z.s, pay32);
+                    } else if (mode == 2) {
+                        if (WIDE) {
+                            v = pop16(z.s);
+                        } else if ((jj & 1) == 0) {  // chunks start at even scans
+                            const uint32_t w = pop16(z.s);
+                            v = w & 0xFFu;
+                            z.meta = 2u | ((w >> 8) << 8);
+                        } else {
+                            v = z.meta >> 8;
+                        }
+                        bits_refill(z.s, pay32);
+                    }
+                    a0[jj] += v;
+                    if (OP == Op::Moments) {
+                        ar[jj] += v * kr[k];
+                        ac[jj] += v * kc[k];
+                    }
+                }
+            }
+        }
+        chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
+    }
+    // end checks (FORMAT 2.3-2.4)
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        const RSlot &z = sl[k];
+        const uint32_t mode = z.meta & 0xFFu;
+        if (mode > 2) continue;
+        bool ok = bits_used(z.s, z.org) == 8u * z.len;
+        if (mode == 1) ok = ok && z.x == 65536u;
+        if (mode == 2 && !WIDE && (n & 1)) ok = ok && (z.meta >> 8) == 0;
+        if (!ok || bad) report(r, b, z.p);
+    }
+}
+
+// ------------------------------------------------------------------ paired tile
+struct PSlot {
+    uint32_t X;     // tANS state
+    uint32_t meta;  // mode (3 PAIRED, 4 RAW, 7 idle) | model << 3
+    uint32_t p;
+    uint32_t org;
+    uint32_t len;
+    Bits s;
+};
+
+__device__ __forceinline__ uint32_t window_sym(uint32_t v, uint32_t a0, uint32_t use) {
+    const uint32_t d = v - a0;
+    return (v >= a0 && d < 15u && ((use >> d) & 1u)) ? d : 15u;
+}
+
+// An escaped count: its literal, returned relative to the model's window base.
+template <bool WIDE>
+__device__ __forceinline__ uint32_t pair_literal(Bits &s, const uint32_t *pay32, uint32_t info,
+                                                           uint32_t &bad) {
+    bits_refill(s, pay32);
+    const uint32_t lit = popn(s, WIDE ? 16u : 8u);
+    const uint32_t a0 = info & 0xFFFFu;
+    bad |= window_sym(lit, a0, info >> 16) != 15u;
+    return lit - a0;
+}
+
+template <int K, bool WIDE, Op OP>
+__device__ __forceinline__ void paired_tile(const DevResident &r, const uint32_t *sel, uint32_t n_sel, uint32_t first, uint32_t b,
+                            uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt) {
+    const uint32_t *pay32 = reinterpret_cast<const uint32_t *>(r.payload);
+    const uint32_t lane = lane_id();
+    const uint32_t maxv = WIDE ? 65535u : 255u;
+    PSlot sl[K];
+    uint32_t bad = 0;
+    // window-base contributions, added once per chunk instead of once per value
+    uint32_t base0 = 0, baseR = 0, baseC = 0;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        PSlot &z = sl[k];
+        z.meta = 7;
+        z.X = 0;
+        z.p = 0;
+        const uint32_t i = first + k * 64 + lane;
+        if (i >= n_sel) continue;
+        z.p = sel[i];
+        const uint32_t kr = z.p / r.det_cols, kc = z.p - kr * r.det_cols;
+        const Extent e = locate(r, b, z.p, base, nbytes);
+        z.org = origin(e.start);
+        z.len = (uint32_t)(e.end - e.start);
+        const uint32_t hdr = ld16(r.payload, e.start);
+        const uint32_t mode = hdr & 7u;
+        if (mode == 0) {  // EMPTY
+            if (z.len != 2) report(r, b, z.p);
+            continue;
+        }
+        if (mode == 1) {  // CONST
+            const uint32_t v = ld16(r.payload, e.start + 2);
+            if (z.len != 4 || v == 0 || v > maxv)
+                report(r, b, z.p);
+            else
+                add_event<OP>(pt, -1, v, kr, kc);
+            continue;
+        }
+        if (mode == 2) {  // SPARSE: add the nonzeros straight into the LDS partials
+            const uint32_t nnz = z.len >= 4 ? ld16(r.payload, e.start + 2) : 0;
+            const uint32_t need = 4u + 2u * nnz + (WIDE ? 2u * nnz : nnz + (nnz & 1u));
+            if (nnz == 0 || nnz > kBlk || need != z.len) {
+                report(r, b, z.p);
+                continue;
+            }
+            int prev = -1;
+            bool ok = true;
+            for (uint32_t t = 0; t < nnz; t++) {
+                const int pos = (int)ld16(r.payload, e.start + 4 + 2 * t);
+                const uint32_t v = WIDE ? ld16(r.payload, e.start + 4 + 2 * nnz + 2 * t)
+                                        : r.payload[e.start + 4 + 2 * nnz + t];
+                if (pos <= prev || pos >= (int)kBlk || v == 0) {
+                    ok = false;
+                    break;
+                }
+                add_event<OP>(pt, pos, v, kr, kc);
+                prev = pos;
+            }
+            if (ok && !WIDE && (nnz & 1)) ok = r.payload[e.start + 4 + 3 * nnz] == 0;
+            if (!ok) report(r, b, z.p);
+            continue;
+        }
+        z.meta = hdr & 0xFFu;  // mode and model
+        bits_init(z.s, pay32, e.start);
+        pop16(z.s);  // header
+        if (mode == 3) {
+            const uint32_t a0 = r.model_info[(hdr >> 3) & 31u] & 0xFFFFu;
+            z.X = popn(z.s, 10);
+            base0 += a0;
+            baseR += a0 * kr;
+            baseC += a0 * kc;
+        }
+        bits_refill(z.s, pay32);
+    }
+    uint32_t kr[OP == Op::Moments ? K : 1], kc[OP == Op::Moments ? K : 1];
+    if (OP == Op::Moments) {
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            kr[k] = sl[k].p / r.det_cols;
+            kc[k] = sl[k].p - kr[k] * r.det_cols;
+        }
+    }
+
+    constexpr int CH = 16;  // paired workgroups have 128 VGPRs per lane
+    const uint32_t my = lane_scan<CH>();
+    const bool writer = lane_writes<CH>();
+    for (uint32_t c = 0; c < kBlk / CH; c++) {
+        uint32_t a0[CH];
+        uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            a0[i] = base0;
+            if (OP == Op::Moments) {
+                ar[i] = baseR;
+                ac[i] = baseC;
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < CH / 2; tt++) {
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                PSlot &z = sl[k];
+                const uint32_t mode = z.meta & 7u;
+                uint32_t v0 = 0, v1 = 0;
+                if (mode == 3) {
+                    const uint32_t e = tbl[((z.meta >> 3) << 10) + z.X];
+                    z.X = (e >> 12) + popn(z.s, (e >> 8) & 15u);
+                    v0 = e & 15u;
+                    v1 = (e >> 4) & 15u;
+                    if (v0 == 15u || v1 == 15u) {
+                        const uint32_t info = r.model_info[z.meta >> 3];
+                        if (v0 == 15u) v0 = pair_literal<WIDE>(z.s, pay32, info, bad);
+                        if (v1 == 15u) v1 = pair_literal<WIDE>(z.s, pay32, info, bad);
+                    }
+                    bits_refill(z.s, pay32);
+                } else if (mode == 4) {
+                    if (WIDE) {
+                        v0 = pop16(z.s);
+                        bits_refill(z.s, pay32);
+                        v1 = pop16(z.s);
+                    } else {
+                        const uint32_t w = pop16(z.s);
+                        v0 = w & 0xFFu;
+                        v1 = w >> 8;
+                    }
+                    bits_refill(z.s, pay32);
+                }
+                a0[2 * tt] += v0;
+                a0[2 * tt + 1] += v1;
+                if (OP == Op::Moments) {
+                    ar[2 * tt] += v0 * kr[k];
+                    ar[2 * tt + 1] += v1 * kr[k];
+                    ac[2 * tt] += v0 * kc[k];
+                    ac[2 * tt + 1] += v1 * kc[k];
+                }
+            }
+        }
+        chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
+    }
+    // end checks (FORMAT 3.3-3.4)
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        PSlot &z = sl[k];
+        const uint32_t mode = z.meta & 7u;
+        if (mode != 3 && mode != 4) continue;
+        const uint32_t used = bits_used(z.s, z.org), total = 8u * z.len;
+        bool ok;
+        if (mode == 4) {
+            ok = used == total;
+        } else {
+            ok = z.X == 0 && used <= total && total - used < 16;
+            if (ok && total > used) {
+                bits_refill(z.s, pay32);
+                ok = popn(z.s, total - used) == 0;
+            }
+        }
+        if (!ok || bad) report(r, b, z.p);
+    }
+}
+
+// ------------------------------------------------------------------ reduce kernels
+template <Op OP>
+struct SharedPartials {
+    uint32_t m0[kBlk];
+    unsigned long long mr[OP == Op::Moments ? kBlk : 1];
+    unsigned long long mc[OP == Op::Moments ? kBlk : 1];
+    uint32_t c0;
+    unsigned long long cr, cc;
+};
+
+template <Op OP>
+__device__ __forceinline__ void zero_partials(SharedPartials<OP> &sp, uint32_t n) {
+    for (uint32_t j = threadIdx.x; j < n; j += blockDim.x) {
+        sp.m0[j] = 0;
+        if (OP == Op::Moments) {
+            sp.mr[j] = 0;
+            sp.mc[j] = 0;
+        }
+    }
+    if (threadIdx.x == 0) {
+        sp.c0 = 0;
+        sp.cr = 0;
+        sp.cc = 0;
+    }
+}
+
+template <Op OP>
+__device__ __forceinline__ void flush_partials(SharedPartials<OP> &sp, uint32_t n, uint64_t s0, uint64_t S, void *out,
+                                               int out64, int negate) {
+    for (uint32_t j = threadIdx.x; j < n; j += blockDim.x) {
+        const uint64_t s = s0 + j;
+        if (OP == Op::Sum) {
+            uint64_t v = (uint64_t)sp.m0[j] + sp.c0;
+            if (!v) continue;
+            if (out64)
+                atomicAdd(reinterpret_cast<unsigned long long *>(out) + s,
+                          (unsigned long long)(negate ? (0ull - v) : v));
+            else
+                atomicAdd(reinterpret_cast<uint32_t *>(out) + s, (uint32_t)(negate ? (0u - (uint32_t)v) : (uint32_t)v));
+        } else {
+            unsigned long long *m = reinterpret_cast<unsigned long long *>(out);
+            const unsigned long long v0 = (unsigned long long)sp.m0[j] + sp.c0;
+            const unsigned long long vr = sp.mr[j] + sp.cr, vc = sp.mc[j] + sp.cc;
+            if (v0) atomicAdd(m + s, v0);
+            if (vr) atomicAdd(m + S + s, vr);
+            if (vc) atomicAdd(m + 2 * S + s, vc);
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t slots_per_lane(uint64_t streams, uint32_t target_lanes) {
+    if (streams > 2ull * target_lanes) return 4;
+    if (streams > (uint64_t)target_lanes) return 2;
+    return 1;
+}
+
+template <bool WIDE, Op OP>
+__global__ __launch_bounds__(kRansWG) void k_reduce_rans(DevResident r, Plan plan, uint32_t stride, uint32_t n_visited,
+                                                         uint32_t target_lanes, void *out, int out64, int negate) {
+    __shared__ uint32_t tbl[4096];
+    __shared__ SharedPartials<OP> sp;
+    const uint32_t n_sel = *plan.n_sel;
+    if (n_sel == 0) return;
+    const uint32_t K = slots_per_lane((uint64_t)n_sel * n_visited, target_lanes);
+    const uint32_t tile = kRansWG * K;
+    const uint32_t n_tiles = (n_sel + tile - 1) / tile;
+    const uint64_t n_work = (uint64_t)n_tiles * n_visited;
+    const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
+    uint32_t loaded = 0xFFFFFFFFu;
+    for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
+        const uint32_t vb = (uint32_t)(w / n_tiles), t = (uint32_t)(w % n_tiles);
+        const uint32_t b = vb * stride;
+        const uint8_t *d = r.dir + 16ull * b;
+        const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
+        const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
+        const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
+        __syncthreads();
+        if (b != loaded) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(r.tables + 4096ull * b);
+            uint4 *dst = reinterpret_cast<uint4 *>(tbl);
+            for (uint32_t i = threadIdx.x; i < 1024; i += kRansWG) dst[i] = src[i];
+            loaded = b;
+        }
+        zero_partials<OP>(sp, n);
+        __syncthreads();
+        const uint32_t first = t * tile + (threadIdx.x >> 6) * 64 * K;
+        if (K == 4)
+            rans_tile<4, WIDE, OP>(r, plan.sel, n_sel, first, b, n, base, nbytes, tbl, pt);
+        else if (K == 2)
+            rans_tile<2, WIDE, OP>(r, plan.sel, n_sel, first, b, n, base, nbytes, tbl, pt);
+        else
+            rans_tile<1, WIDE, OP>(r, plan.sel, n_sel, first, b, n, base, nbytes, tbl, pt);
+        __syncthreads();
+        flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate);
+    }
+}
+
+template <bool WIDE, Op OP>
+__global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, Plan plan, uint32_t stride,
+                                                           uint32_t n_visited, uint32_t target_lanes, void *out,
+                                                           int out64, int negate) {
+    __shared__ uint32_t tbl[32 * 1024];
+    __shared__ SharedPartials<OP> sp;
+    const uint32_t n_sel = *plan.n_sel;
+    if (n_sel == 0) return;
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(r.tables);
+        uint4 *dst = reinterpret_cast<uint4 *>(tbl);
+        for (uint32_t i = threadIdx.x; i < 32 * 1024 / 4; i += kPairWG) dst[i] = src[i];
+    }
+    // at most two slots per lane: 1024-thread workgroups have 128 VGPRs per lane
+    const uint32_t K = min(2u, slots_per_lane((uint64_t)n_sel * n_visited, target_lanes));
+    const uint32_t tile = kPairWG * K;
+    const uint32_t n_tiles = (n_sel + tile - 1) / tile;
+    const uint64_t n_work = (uint64_t)n_tiles * n_visited;
+    const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
+    for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
+        const uint32_t vb = (uint32_t)(w / n_tiles), t = (uint32_t)(w % n_tiles);
+        const uint32_t b = vb * stride;
+        const uint8_t *d = r.dir + 16ull * b;
+        const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
+        const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
+        __syncthreads();
+        zero_partials<OP>(sp, kBlk);
+        __syncthreads();
+        const uint32_t first = t * tile + (threadIdx.x >> 6) * 64 * K;
+        if (K == 2)
+            paired_tile<2, WIDE, OP>(r, plan.sel, n_sel, first, b, base, nbytes, tbl, pt);
+        else
+            paired_tile<1, WIDE, OP>(r, plan.sel, n_sel, first, b, base, nbytes, tbl, pt);
+        __syncthreads();
+        flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate);
+    }
+}
+
+// ------------------------------------------------------------------ plan
+// Block 0 compacts (mask xor complement) & valid into a sorted pixel list; the
+// other blocks initialise the output.
+constexpr uint32_t kPlanWG = 1024;
+
+__global__ __launch_bounds__(kPlanWG) void k_plan(const uint8_t *mask, const uint8_t *valid, uint32_t P,
+                                                  int complement, uint32_t *sel, uint32_t *n_sel, void *out,
+                                                  int out64, const void *init, uint64_t n_out) {
+    if (blockIdx.x == 0) {
+        __shared__ uint32_t scan[kPlanWG];
+        const uint32_t per = (P + kPlanWG - 1) / kPlanWG;
+        const uint32_t p0 = threadIdx.x * per, p1 = min(P, p0 + per);
+        uint32_t cnt = 0;
+        for (uint32_t p = p0; p < p1; p++) cnt += (mask ? ((mask[p] != 0) != (complement != 0)) : 1) && valid[p];
+        scan[threadIdx.x] = cnt;
+        __syncthreads();
+        for (uint32_t off = 1; off < kPlanWG; off <<= 1) {  // inclusive scan
+            const uint32_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+            __syncthreads();
+            scan[threadIdx.x] += v;
+            __syncthreads();
+        }
+        uint32_t o = scan[threadIdx.x] - cnt;
+        for (uint32_t p = p0; p < p1; p++)
+            if ((mask ? ((mask[p] != 0) != (complement != 0)) : 1) && valid[p]) sel[o++] = p;
+        if (threadIdx.x == kPlanWG - 1) *n_sel = scan[kPlanWG - 1];
+        return;
+    }
+    const uint64_t stride = (uint64_t)(gridDim.x - 1) * blockDim.x;
+    for (uint64_t i = (uint64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < n_out; i += stride) {
+        if (out64)
+            reinterpret_cast<uint64_t *>(out)[i] = init ? reinterpret_cast<const uint64_t *>(init)[i] : 0;
+        else
+            reinterpret_cast<uint32_t *>(out)[i] = init ? reinterpret_cast<const uint32_t *>(init)[i] : 0;
+    }
+}
+
+__global__ void k_com_finalize(const uint64_t *m, uint64_t S, float *row, float *col) {
+    for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < S; s += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t m0 = m[s];
+        if (m0 == 0) {
+            row[s] = 0.0f;
+            col[s] = 0.0f;
+        } else {
+            row[s] = (float)((double)m[S + s] / (double)m0);
+            col[s] = (float)((double)m[2 * S + s] / (double)m0);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ region decode
+// One lane per (touched block, pixel): the whole stream is decoded (so its end
+// checks run) and values of scans inside the rectangle are written out.
+template <bool WIDE>
+__device__ __forceinline__ void region_put(void *out, int out_kind, uint64_t idx, uint32_t v, double scale,
+                                           double offset) {
+    if (out_kind == 1)
+        reinterpret_cast<float *>(out)[idx] = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
+    else if (WIDE)
+        reinterpret_cast<uint16_t *>(out)[idx] = (uint16_t)v;
+    else
+        reinterpret_cast<uint8_t *>(out)[idx] = (uint8_t)v;
+}
+
+template <bool WIDE>
+__global__ __launch_bounds__(256) void k_region(DevResident r, RegionBlocks blocks, uint32_t r0, uint32_t r1,
+                                                uint32_t c0, uint32_t c1, int out_kind, void *out) {
+    const uint32_t b = blocks.b[blockIdx.y];
+    const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= r.P) return;
+    const uint8_t *d = r.dir + 16ull * b;
+    const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
+    const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
+    const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
+    const uint32_t w = c1 - c0;
+    const uint64_t s0 = (uint64_t)b * kBlk;
+    double scale = 1.0, offset = 0.0;
+    if (out_kind == 1) {
+        scale = r.calib[2 * b];
+        offset = r.calib[2 * b + 1];
+    }
+    const bool valid = r.valid[p] != 0;
+    // walk the scans of the block with their (row, col)
+    uint32_t row = (uint32_t)(s0 / r.scan_cols), col = (uint32_t)(s0 % r.scan_cols);
+    if (!valid) {
+        for (uint32_t j = 0; j < n; j++) {
+            if (row >= r0 && row < r1 && col >= c0 && col < c1)
+                region_put<WIDE>(out, out_kind, ((uint64_t)(row - r0) * w + (col - c0)) * r.P + p, 0, 1.0, 0.0);
+            if (++col == r.scan_cols) {
+                col = 0;
+                row++;
+            }
+        }
+        return;
+    }
+    const uint32_t *pay32 = reinterpret_cast<const uint32_t *>(r.payload);
+    const Extent e = locate(r, b, p, base, nbytes);
+    const uint32_t len = (uint32_t)(e.end - e.start);
+    const uint32_t hdr = ld16(r.payload, e.start);
+    const uint32_t mode = hdr & 7u;
+    const uint32_t maxv = WIDE ? 65535u : 255u;
+    uint32_t bad = 0;
+    Bits s;
+    bits_init(s, pay32, e.start);
+    pop16(s);
+    bits_refill(s, pay32);
+    uint32_t x = 0, hold = 0, cval = 0, X = 0, a0 = 0, use = 0, tb = 0;
+    uint32_t nnz = 0, k = 0, next_pos = 0xFFFFFFFFu, pend = 0;
+    int prev = -1;
+    // kind: 0 constant value cval, 1 rANS, 2 raw, 3 paired, 4 sparse
+    uint32_t kind = 0;
+    const uint32_t *tbl = r.tables;
+    if (r.layout == 0) {
+        if (mode == 0) {
+            cval = ld16(r.payload, e.start + 2);
+            if (len != 4 || cval > maxv) bad = 1;
+        } else if (mode == 1) {
+            kind = 1;
+            tbl = r.tables + 4096ull * b;
+            x = pop16(s);
+            x |= pop16(s) << 16;
+            bits_refill(s, pay32);
+        } else {
+            kind = 2;
+        }
+    } else {
+        if (mode == 0) {
+            if (len != 2) bad = 1;
+        } else if (mode == 1) {
+            cval = ld16(r.payload, e.start + 2);
+            if (len != 4 || cval == 0 || cval > maxv) bad = 1;
+        } else if (mode == 2) {
+            kind = 4;
+            nnz = len >= 4 ? ld16(r.payload, e.start + 2) : 0;
+            const uint64_t need = 4ull + 2ull * nnz + (WIDE ? 2ull * nnz : nnz + (nnz & 1));
+            if (nnz == 0 || nnz > kBlk || need != len) {
+                bad = 1;
+                kind = 0;
+            } else {
+                next_pos = ld16(r.payload, e.start + 4);
+            }
+        } else if (mode == 3) {
+            kind = 3;
+            const uint32_t m = (hdr >> 3) & 31u;
+            tb = m * 1024u;
+            a0 = r.model_info[m] & 0xFFFFu;
+            use = r.model_info[m] >> 16;
+            X = popn(s, 10);
+            bits_refill(s, pay32);
+        } else {
+            kind = 2;
+        }
+    }
+    for (uint32_t j = 0; j < n; j++) {
+        uint32_t v = cval;
+        if (kind == 1) {
+            v = rans_step<WIDE>(x, s, tbl, bad);
+            bits_refill(s, pay32);
+        } else if (kind == 2) {
+            if (WIDE) {
+                v = pop16(s);
+            } else if ((j & 1) == 0) {
+                const uint32_t wd = pop16(s);
+                v = wd & 0xFFu;
+                hold = wd >> 8;
+            } else {
+                v = hold;
+            }
+            bits_refill(s, pay32);
+        } else if (kind == 3) {
+            if ((j & 1) == 0) {
+                const uint32_t en = tbl[tb + X];
+                X = (en >> 12) + popn(s, (en >> 8) & 15u);
+                uint32_t v0 = en & 15u, v1 = (en >> 4) & 15u;
+                const uint32_t info = a0 | (use << 16);
+                v0 = a0 + (v0 == 15u ? pair_literal<WIDE>(s, pay32, info, bad) : v0);
+                v1 = a0 + (v1 == 15u ? pair_literal<WIDE>(s, pay32, info, bad) : v1);
+                bits_refill(s, pay32);
+                v = v0;
+                pend = v1;
+            } else {
+                v = pend;
+            }
+        } else if (kind == 4) {
+            v = 0;
+            if (j == next_pos) {
+                v = WIDE ? ld16(r.payload, e.start + 4 + 2 * nnz + 2 * k) : r.payload[e.start + 4 + 2 * nnz + k];
+                if ((int)next_pos <= prev || v == 0) bad = 1;
+                prev = (int)next_pos;
+                k++;
+                next_pos = k < nnz ? ld16(r.payload, e.start + 4 + 2 * k) : 0xFFFFFFFFu;
+                if (k < nnz && (next_pos >= kBlk || (int)next_pos <= prev)) bad = 1;
+            }
+        }
+        if (row >= r0 && row < r1 && col >= c0 && col < c1)
+            region_put<WIDE>(out, out_kind, ((uint64_t)(row - r0) * w + (col - c0)) * r.P + p, v, scale, offset);
+        if (++col == r.scan_cols) {
+            col = 0;
+            row++;
+        }
+    }
+    // end checks
+    if (kind == 1 || kind == 2 || kind == 3) {
+        const uint32_t used = bits_used(s, origin(e.start)), total = 8u * len;
+        if (kind == 1) bad |= x != 65536u || used != total;
+        if (kind == 2) {
+            bad |= used != total;
+            if (!WIDE && (n & 1)) bad |= hold != 0;
+        }
+        if (kind == 3) {
+            bad |= X != 0 || used > total || total - used >= 16;
+            if (!bad && total > used) bad |= popn(s, total - used) != 0;
+        }
+    }
+    if (kind == 4) {
+        bad |= k != nnz;
+        if (!WIDE && (nnz & 1)) bad |= r.payload[e.start + 4 + 3 * nnz] != 0;
+    }
+    if (bad) report(r, b, p);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+int device_cu_count() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+            cus = prop.multiProcessorCount;
+        if (cus <= 0) cus = 256;
+    }
+    return cus;
+}
+
+hipError_t launch_plan(const DevResident &r, const uint8_t *mask, int complement, Plan plan, void *out, int out64,
+                       const void *init_total, hipStream_t st) {
+    const uint32_t init_blocks = (uint32_t)std::min<uint64_t>(1024, (r.S + 1023) / 1024);
+    hipLaunchKernelGGL(k_plan, dim3(1 + init_blocks), dim3(kPlanWG), 0, st, mask, r.valid, r.P, complement, plan.sel,
+                       plan.n_sel, out, out64, init_total, r.S);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_moments(const DevResident &r, const uint8_t *mask, Plan plan, uint64_t *moments,
+                               hipStream_t st) {
+    const uint64_t n = 3 * r.S;
+    const uint32_t init_blocks = (uint32_t)std::min<uint64_t>(1024, (n + 1023) / 1024);
+    hipLaunchKernelGGL(k_plan, dim3(1 + init_blocks), dim3(kPlanWG), 0, st, mask, r.valid, r.P, 0, plan.sel,
+                       plan.n_sel, (void *)moments, 1, (const void *)nullptr, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const DevResident &r, Plan plan, uint32_t stride, Op op, void *out, int out64, int negate,
+                         hipStream_t st) {
+    const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
+    const uint32_t cus = (uint32_t)device_cu_count();
+    const uint32_t target = cus * 4 * 64 * 4;  // lanes that keep four waves per SIMD busy
+    const bool wide = r.dtype == 2;
+    if (r.layout == 0) {
+        const uint64_t max_work = (uint64_t)((r.P + kRansWG - 1) / kRansWG) * n_visited;
+        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(max_work, 8ull * cus));
+#define QSC_RANS(W, O) hipLaunchKernelGGL((k_reduce_rans<W, O>), dim3(grid), dim3(kRansWG), 0, st, r, plan, stride, \
+                                          n_visited, target, out, out64, negate)
+        if (op == Op::Sum) {
+            if (wide) QSC_RANS(true, Op::Sum); else QSC_RANS(false, Op::Sum);
+        } else {
+            if (wide) QSC_RANS(true, Op::Moments); else QSC_RANS(false, Op::Moments);
+        }
+#undef QSC_RANS
+    } else {
+        const uint64_t max_work = (uint64_t)((r.P + kPairWG - 1) / kPairWG) * n_visited;
+        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(max_work, cus));
+#define QSC_PAIR(W, O) hipLaunchKernelGGL((k_reduce_paired<W, O>), dim3(grid), dim3(kPairWG), 0, st, r, plan, \
+                                          stride, n_visited, target, out, out64, negate)
+        if (op == Op::Sum) {
+            if (wide) QSC_PAIR(true, Op::Sum); else QSC_PAIR(false, Op::Sum);
+        } else {
+            if (wide) QSC_PAIR(true, Op::Moments); else QSC_PAIR(false, Op::Moments);
+        }
+#undef QSC_PAIR
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, float *col, hipStream_t st) {
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(4096, (S + 255) / 256);
+    hipLaunchKernelGGL(k_com_finalize, dim3(std::max(1u, grid)), dim3(256), 0, st, moments, S, row, col);
+    return hipGetLastError();
+}
+
+hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, uint32_t r0, uint32_t r1, uint32_t c0,
+                         uint32_t c1, int out_kind, void *out, hipStream_t st) {
+    const dim3 grid((r.P + 255) / 256, blocks.n);
+    if (r.dtype == 2)
+        hipLaunchKernelGGL(k_region<true>, grid, dim3(256), 0, st, r, blocks, r0, r1, c0, c1, out_kind, out);
+    else
+        hipLaunchKernelGGL(k_region<false>, grid, dim3(256), 0, st, r, blocks, r0, r1, c0, c1, out_kind, out);
+    return hipGetLastError();
+}
+
+}  // namespace qsc

@@ -1,0 +1,78 @@
+// Internal host-side definitions shared by the library's translation units.
+#pragma once
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/qsc.h"
+
+namespace qsc {
+
+constexpr uint32_t kBlock = 512;      // scans per block
+constexpr uint32_t kRansM = 4096;     // byte-rANS table size (12-bit precision)
+constexpr uint32_t kRansL = 1u << 16; // byte-rANS state lower bound
+constexpr uint32_t kTansL = 1024;     // paired tANS states
+constexpr uint32_t kModels = 32;      // paired pair models
+constexpr uint64_t kHeaderBytes = 256;
+constexpr uint64_t kDevicePad = 16384; // zero bytes after the payload on the device (decoder read-ahead)
+
+// stream modes (FORMAT 2.4, 3.4)
+enum : uint32_t { R_CONST = 0, R_RANS = 1, R_RAW = 2 };
+enum : uint32_t { P_EMPTY = 0, P_CONST = 1, P_SPARSE = 2, P_PAIRED = 3, P_RAW = 4 };
+
+struct Geometry {
+    uint32_t scan_rows = 0, scan_cols = 0, det_rows = 0, det_cols = 0;
+    uint32_t dtype = 0, layout = 0, scaled = 0;
+    uint64_t S() const { return uint64_t(scan_rows) * scan_cols; }
+    uint32_t P() const { return det_rows * det_cols; }
+    uint32_t G() const { return (P() + 31) / 32; }
+    uint32_t n_blocks() const { return uint32_t((S() + kBlock - 1) / kBlock); }
+    uint32_t maxval() const { return dtype == 1 ? 255u : 65535u; }
+    uint32_t sum_bits() const { return uint64_t(P()) * maxval() > 0xFFFFFFFFull ? 64 : 32; }
+};
+
+// Validates a geometry; returns an empty string or the reason it is refused.
+std::string check_geometry(const Geometry &g);
+
+// Section offsets of a blob (FORMAT 1.1).
+struct Sections {
+    uint64_t dir = 0, table = 0, gbase = 0, rel = 0, payload = 0, payload_bytes = 0, calib = 0, total = 0;
+};
+
+// Section layout the encoder writes for a geometry and payload size.
+Sections layout_sections(const Geometry &g, uint64_t payload_bytes);
+
+// A parsed and structurally validated blob.
+struct Parsed {
+    Geometry g;
+    Sections sec;
+    const uint8_t *blob = nullptr;
+    uint64_t nbytes = 0;
+    uint64_t mode_counts[8] = {0};
+};
+
+// Full host validation (FORMAT 1.x headers, offsets, tables, stream headers).
+// Returns QSC_OK or an error with a message.
+qsc_status parse_and_validate(const uint8_t *blob, uint64_t nbytes, Parsed *out, std::string *msg);
+
+// Paired pair models (FORMAT 3.1): counts[32][256], window bases, in-use masks.
+struct PairModels {
+    uint16_t n[kModels][256];
+    uint32_t a0[kModels];
+    uint32_t in_use[kModels];
+};
+const PairModels &pair_models();
+
+// Device decode-table entries.
+//  byte-rANS (per block, 4096 entries): symbol | (f-1) << 8 | (slot - c) << 20
+//  paired (per model, 1024 entries): a | b << 4 | nbits << 8 | newX << 12
+void build_rans_table(const uint16_t *freq, uint32_t *out4096);
+void build_pair_tables(uint32_t *out /* 32 x 1024 */);
+
+// little-endian access
+inline uint16_t ld16(const uint8_t *p) { return uint16_t(p[0] | (p[1] << 8)); }
+inline uint32_t ld32(const uint8_t *p) { return uint32_t(ld16(p)) | (uint32_t(ld16(p + 2)) << 16); }
+inline uint64_t ld64(const uint8_t *p) { return uint64_t(ld32(p)) | (uint64_t(ld32(p + 4)) << 32); }
+
+} // namespace qsc

@@ -1,0 +1,356 @@
+// C-ABI of the library: resident creation and the query entry points.
+//
+// The shape follows the pages' interface: a loaded acquisition stays ANS
+// encoded on the GPU (quantem.widget ANS page; scaled-uint16 page), queries
+// are enqueued and may be waited for later (paired-resident page, "Contract",
+// row "queued queries"), a malformed stream fails the query with no result,
+// and masked sums are exact uint32, or uint64 when a full-detector sum could
+// pass 2^32 ("Contract", row "virtual image").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <memory>
+#include <new>
+
+#include "kernels.hpp"
+#include "qsc_internal.hpp"
+
+using namespace qsc;
+
+struct qsc_resident {
+    int device = 0;
+    Geometry g;
+    Sections sec;
+    uint64_t mode_counts[8] = {0};
+    // host copies of the directory and offsets (query byte accounting)
+    std::vector<uint8_t> dir;
+    std::vector<uint32_t> gbase;
+    std::vector<uint16_t> rel;
+    // device memory owned by the resident
+    uint8_t *d_blob = nullptr;
+    uint32_t *d_tables = nullptr;
+    uint32_t *d_model_info = nullptr;
+    uint8_t *d_valid = nullptr;
+    uint32_t *d_sel = nullptr;
+    uint32_t *d_nsel = nullptr;
+    unsigned long long *d_err = nullptr;
+    void *d_total = nullptr;
+    bool total_ready = false;
+    uint64_t *d_moments = nullptr;
+    uint64_t device_bytes = 0;
+    DevResident dev{};
+    std::string last_error;
+};
+
+namespace {
+
+qsc_status fail(qsc_resident *res, qsc_status st, const std::string &msg) {
+    if (res) res->last_error = msg;
+    return st;
+}
+
+qsc_status hip_fail(qsc_resident *res, hipError_t e, const char *what) {
+    return fail(res, e == hipErrorOutOfMemory ? QSC_ERR_OOM : QSC_ERR_HIP,
+                std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <typename T>
+hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
+    void *q = nullptr;
+    hipError_t e = hipMalloc(&q, bytes ? bytes : 1);
+    if (e == hipSuccess) {
+        *p = static_cast<T *>(q);
+        res->device_bytes += bytes;
+    }
+    return e;
+}
+
+void free_all(qsc_resident *res) {
+    for (void *p : {(void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
+                    (void *)res->d_sel, (void *)res->d_nsel, (void *)res->d_err, res->d_total,
+                    (void *)res->d_moments})
+        if (p) (void)hipFree(p);
+}
+
+// Current device must be the resident's; returns false if it cannot be set.
+bool on_device(const qsc_resident *res) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return false;
+    return cur == res->device || hipSetDevice(res->device) == hipSuccess;
+}
+
+qsc_status check_done(qsc_resident *res, hipStream_t st) {
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(res, e, "stream synchronize");
+    unsigned long long err = 0;
+    e = hipMemcpy(&err, res->d_err, sizeof(err), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(res, e, "error word readback");
+    if (!err) return QSC_OK;
+    (void)hipMemset(res->d_err, 0, sizeof(err));
+    res->total_ready = false;  // a cache built by a failed decode is not kept
+    const uint64_t b = (err >> 32) - 1, p = err & 0xFFFFFFFFull;
+    return fail(res, QSC_ERR_MALFORMED,
+                "malformed stream at block " + std::to_string(b) + ", pixel " + std::to_string(p));
+}
+
+qsc_status finish_query(qsc_resident *res, hipError_t launch, hipStream_t st, int wait) {
+    if (launch != hipSuccess) return hip_fail(res, launch, "kernel launch");
+    return wait ? check_done(res, st) : QSC_OK;
+}
+
+Plan plan_of(qsc_resident *res) { return Plan{res->d_sel, res->d_nsel}; }
+
+}  // namespace
+
+extern "C" {
+
+const char *qsc_abi(void) { return "qsc-byte-rans-v1;qsc-paired-v1"; }
+
+const char *qsc_status_string(qsc_status s) {
+    switch (s) {
+    case QSC_OK: return "ok";
+    case QSC_ERR_INVALID_ARG: return "invalid argument";
+    case QSC_ERR_MALFORMED: return "malformed container or stream";
+    case QSC_ERR_UNSUPPORTED: return "unsupported ABI or format version";
+    case QSC_ERR_OOM: return "out of memory";
+    case QSC_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uint8_t *host_valid, void *hip_stream,
+                               qsc_resident **out) {
+    if (!host_blob || !out) return QSC_ERR_INVALID_ARG;
+    *out = nullptr;
+    Parsed ps;
+    std::string msg;
+    std::unique_ptr<qsc_resident> res(new (std::nothrow) qsc_resident);
+    if (!res) return QSC_ERR_OOM;
+    qsc_status st = parse_and_validate(static_cast<const uint8_t *>(host_blob), nbytes, &ps, &msg);
+    if (st != QSC_OK) return st;  // no resident exists to carry the message
+    const Geometry &g = ps.g;
+    const Sections &s = ps.sec;
+    res->g = g;
+    res->sec = s;
+    std::copy(ps.mode_counts, ps.mode_counts + 8, res->mode_counts);
+    const uint8_t *blob = static_cast<const uint8_t *>(host_blob);
+    const uint64_t nb = g.n_blocks(), G = g.G();
+    res->dir.assign(blob + s.dir, blob + s.dir + 16 * nb);
+    res->gbase.resize(nb * G);
+    std::memcpy(res->gbase.data(), blob + s.gbase, 4 * nb * G);
+    res->rel.resize(nb * G * 32);
+    std::memcpy(res->rel.data(), blob + s.rel, 64 * nb * G);
+    if (hipGetDevice(&res->device) != hipSuccess) return QSC_ERR_HIP;
+    hipStream_t strm = static_cast<hipStream_t>(hip_stream);
+    hipError_t e;
+    auto bail = [&](hipError_t err, const char *) {
+        free_all(res.get());
+        return err == hipErrorOutOfMemory ? QSC_ERR_OOM : QSC_ERR_HIP;
+    };
+    // the whole blob, plus zero padding that the decoders may read ahead into
+    if ((e = dalloc(res.get(), &res->d_blob, nbytes + kDevicePad)) != hipSuccess) return bail(e, "blob");
+    if ((e = hipMemcpy(res->d_blob, blob, nbytes, hipMemcpyHostToDevice)) != hipSuccess) return bail(e, "upload");
+    if ((e = hipMemset(res->d_blob + nbytes, 0, kDevicePad)) != hipSuccess) return bail(e, "pad");
+    // decode tables
+    std::vector<uint32_t> tables;
+    std::vector<uint32_t> info(kModels, 0);
+    if (g.layout == 0) {
+        tables.resize(nb * kRansM);
+        for (uint64_t b = 0; b < nb; b++) {
+            uint16_t f[256];
+            std::memcpy(f, blob + s.table + 512 * b, 512);
+            build_rans_table(f, tables.data() + kRansM * b);
+        }
+    } else {
+        tables.resize(kModels * kTansL);
+        build_pair_tables(tables.data());
+        const PairModels &pm = pair_models();
+        for (uint32_t m = 0; m < kModels; m++) info[m] = pm.a0[m] | (pm.in_use[m] << 16);
+    }
+    if ((e = dalloc(res.get(), &res->d_tables, 4 * tables.size())) != hipSuccess) return bail(e, "tables");
+    if ((e = hipMemcpy(res->d_tables, tables.data(), 4 * tables.size(), hipMemcpyHostToDevice)) != hipSuccess)
+        return bail(e, "tables upload");
+    if ((e = dalloc(res.get(), &res->d_model_info, 4 * kModels)) != hipSuccess) return bail(e, "model info");
+    if ((e = hipMemcpy(res->d_model_info, info.data(), 4 * kModels, hipMemcpyHostToDevice)) != hipSuccess)
+        return bail(e, "model info upload");
+    std::vector<uint8_t> valid(g.P(), 1);
+    if (host_valid)
+        for (uint32_t p = 0; p < g.P(); p++) valid[p] = host_valid[p] ? 1 : 0;
+    if ((e = dalloc(res.get(), &res->d_valid, g.P())) != hipSuccess) return bail(e, "valid");
+    if ((e = hipMemcpy(res->d_valid, valid.data(), g.P(), hipMemcpyHostToDevice)) != hipSuccess)
+        return bail(e, "valid upload");
+    if ((e = dalloc(res.get(), &res->d_sel, 4ull * g.P())) != hipSuccess) return bail(e, "selection");
+    if ((e = dalloc(res.get(), &res->d_nsel, 256)) != hipSuccess) return bail(e, "selection count");
+    if ((e = dalloc(res.get(), &res->d_err, 256)) != hipSuccess) return bail(e, "error word");
+    if ((e = hipMemset(res->d_err, 0, 256)) != hipSuccess) return bail(e, "error word");
+    if ((e = hipStreamSynchronize(strm)) != hipSuccess) return bail(e, "synchronize");
+
+    DevResident &d = res->dev;
+    d.payload = res->d_blob + s.payload;
+    d.dir = res->d_blob + s.dir;
+    d.gbase = reinterpret_cast<const uint32_t *>(res->d_blob + s.gbase);
+    d.rel = reinterpret_cast<const uint16_t *>(res->d_blob + s.rel);
+    d.tables = res->d_tables;
+    d.model_info = res->d_model_info;
+    d.valid = res->d_valid;
+    d.calib = g.scaled ? reinterpret_cast<const double *>(res->d_blob + s.calib) : nullptr;
+    d.err = res->d_err;
+    d.S = g.S();
+    d.P = g.P();
+    d.G = g.G();
+    d.det_cols = g.det_cols;
+    d.scan_cols = g.scan_cols;
+    d.n_blocks = g.n_blocks();
+    d.dtype = g.dtype;
+    d.layout = g.layout;
+    *out = res.release();
+    return QSC_OK;
+}
+
+qsc_status qsc_resident_destroy(qsc_resident *res) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    on_device(res);
+    (void)hipDeviceSynchronize();
+    free_all(res);
+    delete res;
+    return QSC_OK;
+}
+
+qsc_status qsc_resident_info(const qsc_resident *res, qsc_info *info) {
+    if (!res || !info) return QSC_ERR_INVALID_ARG;
+    const Geometry &g = res->g;
+    info->geom = qsc_geometry{g.scan_rows, g.scan_cols, g.det_rows, g.det_cols, g.dtype, g.layout, g.scaled};
+    info->n_blocks = g.n_blocks();
+    info->sum_bits = g.sum_bits();
+    info->resident_bytes = res->device_bytes;
+    info->payload_bytes = res->sec.payload_bytes;
+    std::copy(res->mode_counts, res->mode_counts + 8, info->mode_counts);
+    return QSC_OK;
+}
+
+qsc_status qsc_masked_sum(qsc_resident *res, const uint8_t *d_mask, uint32_t block_stride, void *d_out,
+                          void *hip_stream, int wait) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    if (!d_mask || !d_out || block_stride < 1) return fail(res, QSC_ERR_INVALID_ARG, "masked_sum: bad argument");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const int out64 = res->g.sum_bits() == 64;
+    hipError_t e = launch_plan(res->dev, d_mask, 0, plan_of(res), d_out, out64, nullptr, st);
+    if (e == hipSuccess) e = launch_reduce(res->dev, plan_of(res), block_stride, Op::Sum, d_out, out64, 0, st);
+    return finish_query(res, e, st, wait);
+}
+
+qsc_status qsc_dense_df(qsc_resident *res, const uint8_t *d_mask, void *d_out, void *hip_stream, int wait) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    if (!d_mask || !d_out) return fail(res, QSC_ERR_INVALID_ARG, "dense_df: bad argument");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const int out64 = res->g.sum_bits() == 64;
+    const uint64_t width = out64 ? 8 : 4;
+    hipError_t e = hipSuccess;
+    if (!res->d_total && (e = dalloc(res, &res->d_total, width * res->g.S())) != hipSuccess)
+        return hip_fail(res, e, "total cache");
+    if (!res->total_ready) {
+        // cold: full-detector total over the valid pixels, decoded once and kept
+        e = launch_plan(res->dev, nullptr, 0, plan_of(res), res->d_total, out64, nullptr, st);
+        if (e == hipSuccess) e = launch_reduce(res->dev, plan_of(res), 1, Op::Sum, res->d_total, out64, 0, st);
+        if (e != hipSuccess) return hip_fail(res, e, "total cache build");
+        res->total_ready = true;
+    }
+    // warm: out = total - sum over valid & ~mask
+    e = launch_plan(res->dev, d_mask, 1, plan_of(res), d_out, out64, res->d_total, st);
+    if (e == hipSuccess) e = launch_reduce(res->dev, plan_of(res), 1, Op::Sum, d_out, out64, 1, st);
+    return finish_query(res, e, st, wait);
+}
+
+qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float *d_col, void *hip_stream, int wait) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    if (!d_row || !d_col) return fail(res, QSC_ERR_INVALID_ARG, "com: bad argument");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipSuccess;
+    if (!res->d_moments && (e = dalloc(res, &res->d_moments, 3 * 8 * res->g.S())) != hipSuccess)
+        return hip_fail(res, e, "moment buffer");
+    e = launch_plan_moments(res->dev, d_mask, plan_of(res), res->d_moments, st);
+    if (e == hipSuccess) e = launch_reduce(res->dev, plan_of(res), 1, Op::Moments, res->d_moments, 1, 0, st);
+    if (e == hipSuccess) e = launch_com_finalize(res->d_moments, res->g.S(), d_row, d_col, st);
+    return finish_query(res, e, st, wait);
+}
+
+qsc_status qsc_decode_region(qsc_resident *res, uint32_t r0, uint32_t r1, uint32_t c0, uint32_t c1, int out_kind,
+                             void *d_out, void *hip_stream, int wait) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    const Geometry &g = res->g;
+    if (!d_out || r0 >= r1 || c0 >= c1 || r1 > g.scan_rows || c1 > g.scan_cols || out_kind < 0 || out_kind > 1 ||
+        (out_kind == 1 && !g.scaled))
+        return fail(res, QSC_ERR_INVALID_ARG, "decode_region: bad rectangle or output kind");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    // blocks holding a scan of the rectangle
+    std::vector<uint32_t> blocks;
+    for (uint32_t r = r0; r < r1; r++) {
+        const uint64_t sa = uint64_t(r) * g.scan_cols + c0, sb = uint64_t(r) * g.scan_cols + c1 - 1;
+        for (uint64_t b = sa / kBlock; b <= sb / kBlock; b++)
+            if (blocks.empty() || blocks.back() < b) blocks.push_back(uint32_t(b));
+    }
+    // the touched-block list travels as kernel launches of up to 64 blocks each (no device staging buffer)
+    hipError_t e = hipSuccess;
+    for (size_t i = 0; i < blocks.size() && e == hipSuccess; i += 64) {
+        RegionBlocks rb{};
+        rb.n = uint32_t(std::min<size_t>(64, blocks.size() - i));
+        for (uint32_t k = 0; k < rb.n; k++) rb.b[k] = blocks[i + k];
+        e = launch_region(res->dev, rb, r0, r1, c0, c1, out_kind, d_out, st);
+    }
+    return finish_query(res, e, st, wait);
+}
+
+qsc_status qsc_finish(qsc_resident *res, void *hip_stream) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    return check_done(res, static_cast<hipStream_t>(hip_stream));
+}
+
+const char *qsc_last_error(const qsc_resident *res) { return res ? res->last_error.c_str() : "no resident"; }
+
+qsc_status qsc_query_bytes(const qsc_resident *res, const uint8_t *host_mask, uint32_t block_stride, uint64_t *bytes,
+                           uint64_t *counts) {
+    if (!res || !host_mask || !bytes || !counts || block_stride < 1) return QSC_ERR_INVALID_ARG;
+    const Geometry &g = res->g;
+    const uint32_t P = g.P(), G = g.G(), nb = g.n_blocks();
+    std::vector<uint32_t> sel;
+    std::vector<uint8_t> valid(P, 1);
+    // the resident keeps validity on the device only; fetch it once
+    if (hipMemcpy(valid.data(), res->d_valid, P, hipMemcpyDeviceToHost) != hipSuccess) return QSC_ERR_HIP;
+    for (uint32_t p = 0; p < P; p++)
+        if (host_mask[p] && valid[p]) sel.push_back(p);
+    uint64_t by = 0, cn = 0;
+    for (uint32_t b = 0; b < nb; b += block_stride) {
+        const uint8_t *d = res->dir.data() + 16ull * b;
+        const uint32_t n = ld32(d + 8), nbytes = ld32(d + 12);
+        by += 16 + (g.layout == 0 ? 512 : 0);  // directory entry and frequency table
+        uint32_t last_group = 0xFFFFFFFFu;
+        for (uint32_t p : sel) {
+            const uint64_t gi = uint64_t(b) * G + (p >> 5);
+            const uint64_t st = res->gbase[gi] + res->rel[gi * 32 + (p & 31)];
+            uint64_t en;
+            if (p + 1 < P) {
+                const uint64_t gj = uint64_t(b) * G + ((p + 1) >> 5);
+                en = res->gbase[gj] + res->rel[gj * 32 + ((p + 1) & 31)];
+            } else {
+                en = nbytes;
+            }
+            by += en - st + 2;  // stream bytes and its relative offset
+            if ((p >> 5) != last_group) {
+                by += 4;  // group base
+                last_group = p >> 5;
+            }
+        }
+        cn += uint64_t(n) * sel.size();
+    }
+    if (g.layout == 1) by += 2ull * kModels * 256;
+    *bytes = by;
+    *counts = cn;
+    return QSC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,273 @@
+"""GPU parity: every query of the HIP path against the CPU oracle.
+
+Integer products (masked sums, dense DF, region reads, exact moments) must be
+bit-exact. CoM must be within 1e-5 relative (the optimization matrix page's
+real-crop agreement gate); it is also checked bit for bit, because both sides
+divide the same exact moments once in float64. Inputs are the seeded synthetic
+workloads; reduced scan counts keep the oracle fast while still spanning many
+workgroup tiles, several 512-scan blocks and a ragged final block.
+"""
+import functools
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def q():
+    import stem_compressed_count_amd as m
+    return m
+
+
+@functools.lru_cache(maxsize=8)
+def case(name, sr=None, sc=None, layout=None):
+    w = synth.WORKLOADS[name]
+    if sr is not None:
+        w = w.with_scans(sr, sc)
+    lay = w.layout if layout is None else layout
+    counts = synth.counts(w)
+    blob = q().encode(counts, w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, layout=lay)
+    return w, counts, synth.valid_pixels(w), blob
+
+
+def u(t):
+    return q().as_unsigned(t).astype(np.uint64)
+
+
+def check_com(res, counts, w, mask, valid):
+    row, col = res.com(mask)
+    orow, ocol, m0 = oracle.com(counts, w.det_rows, w.det_cols, mask=mask, valid=valid)
+    grow, gcol = row.cpu().numpy(), col.cpu().numpy()
+    for g, o in ((grow, orow), (gcol, ocol)):
+        rel = np.abs(g.astype(np.float64) - o) / np.maximum(np.abs(o).astype(np.float64), 1.0)
+        assert rel.max() <= 1e-5
+        assert np.array_equal(g, o)
+
+
+def check_all_products(w, counts, valid, blob, masks, df_mask, rects, strides=(1,)):
+    with q().Resident(blob, valid=valid) as res:
+        for name, m in masks.items():
+            for k in strides:
+                got = u(res.masked_sum(m, block_stride=k))
+                assert np.array_equal(got, oracle.masked_sum(counts, m, valid, stride=k)), (name, k)
+        if df_mask is not None:
+            for _ in range(2):  # cold (builds the total cache), then warm
+                got = u(res.dense_df(df_mask))
+                assert np.array_equal(got, oracle.dense_df(counts, df_mask, valid))
+        check_com(res, counts, w, None, valid)
+        for m in masks.values():
+            check_com(res, counts, w, m, valid)
+        for (r0, r1, c0, c1) in rects:
+            got = q().as_unsigned(res.decode_region(r0, r1, c0, c1))
+            assert np.array_equal(got, oracle.region(counts, w.scan_cols, r0, r1, c0, c1, valid)), (r0, r1, c0, c1)
+        res.finish()
+
+
+def random_rects(w, n, seed, size=8):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        h = int(rng.integers(1, size + 1))
+        wd = int(rng.integers(1, size + 1))
+        r0 = int(rng.integers(0, w.scan_rows - h + 1))
+        c0 = int(rng.integers(0, w.scan_cols - wd + 1))
+        out.append((r0, r0 + h, c0, c0 + wd))
+    return out
+
+
+def test_tiny_full_size():
+    w, counts, valid, blob = case("tiny")
+    masks = synth.query_masks(w)
+    check_all_products(w, counts, valid, blob, masks, masks["adf"],
+                       [(0, 16, 0, 16), (0, 1, 0, 1), (15, 16, 15, 16), (3, 11, 2, 10)] + random_rects(w, 4, 1))
+
+
+def test_c2_full_size():
+    w, counts, valid, blob = case("c2")
+    masks = synth.query_masks(w)
+    check_all_products(w, counts, valid, blob, {"bf": masks["bf"]}, masks["df"],
+                       [(0, 8, 0, 8), (60, 68, 124, 128)], strides=(1, 3, 4))
+
+
+def test_c3_sentinels_and_valid_pixels():
+    w, counts, valid, blob = case("c3", 40, 256)  # 10240 scans: 20 blocks
+    assert valid is not None and valid.sum() < w.P
+    masks = synth.query_masks(w)
+    check_all_products(w, counts, valid, blob, {"bf": masks["bf"], "full": np.ones(w.P, np.uint8)}, masks["df"],
+                       [(0, 8, 0, 8), (1, 9, 124, 132), (32, 40, 248, 256)] + random_rects(w, 6, 3))
+
+
+def test_c3_scaled_region_reads():
+    w = synth.WORKLOADS["c3"].with_scans(10, 256)  # 2560 scans: 5 regions
+    x = synth.scaled(w)
+    blob = q().encode(x, w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, scaled=True)
+    codes = oracle.decode(blob.tobytes())
+    cal = oracle.calibration(blob.tobytes())
+    with q().Resident(blob) as res:
+        for (r0, r1, c0, c1) in [(0, 8, 0, 8), (1, 9, 124, 132), (0, 10, 250, 256)] + random_rects(w, 4, 5):
+            got = res.decode_region(r0, r1, c0, c1, calibrated=True).cpu().numpy()
+            want = []
+            for r in range(r0, r1):
+                for c in range(c0, c1):
+                    s = r * w.scan_cols + c
+                    sc, off = cal[s // 512]
+                    want.append(oracle.reconstruct(codes[s], sc, off))
+            assert np.array_equal(got, np.stack(want)), (r0, r1, c0, c1)
+            raw = q().as_unsigned(res.decode_region(r0, r1, c0, c1))
+            assert np.array_equal(raw, oracle.region(codes, w.scan_cols, r0, r1, c0, c1))
+        # integer products of a scaled resident are exact sums of the codes
+        bf = synth.query_masks(w)["bf"]
+        assert np.array_equal(u(res.masked_sum(bf)), oracle.masked_sum(codes, bf))
+
+
+def test_c4_u8_low_dose():
+    w, counts, valid, blob = case("c4", 48, 512)  # 24576 scans: 48 blocks
+    masks = synth.query_masks(w)
+    check_all_products(w, counts, valid, blob, masks, masks["bf"], [(0, 8, 0, 8), (47, 48, 500, 512)],
+                       strides=(1, 4))
+
+
+def test_c4_moving_mask_sweep():
+    w, counts, valid, blob = case("c4", 16, 512)
+    sweep = synth.sweep_masks(w)
+    with q().Resident(blob) as res:
+        for i, m in enumerate(sweep[::5]):
+            assert np.array_equal(u(res.masked_sum(m)), oracle.masked_sum(counts, m)), i
+
+
+def test_c5_paired_layout():
+    w, counts, valid, blob = case("c5", 24, 1024)  # 24576 scans: 48 blocks
+    masks = synth.query_masks(w)
+    check_all_products(w, counts, valid, blob, {"bf": masks["bf"]}, masks["df"],
+                       [(0, 8, 0, 8), (23, 24, 1016, 1024)] + random_rects(w, 3, 7), strides=(1, 4))
+
+
+def test_c5_generator_byte_rans_too():
+    w, counts, valid, blob = case("c5", 8, 1024, 0)
+    masks = synth.query_masks(w)
+    check_all_products(w, counts, valid, blob, {"bf": masks["bf"]}, masks["df"], [(0, 8, 0, 8)], strides=(1, 4))
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_uint64_sums_257_detector(layout):
+    # 257 x 257 uint16: a full-detector sum can pass 2^32, so outputs are uint64
+    P = 257 * 257
+    rng = np.random.default_rng(21)
+    S = 1024
+    c = rng.poisson(0.2, size=(S, P)).astype(np.uint16)
+    c[:, :257] = 65535                       # saturated detector row
+    c[:, 257:514] = rng.integers(255, 65536, size=(S, 257))  # wide literals
+    c[5] = 65535                             # one saturated frame: full sum 4,328,521,215
+    valid = np.ones(P, np.uint8)
+    valid[1000] = 0                          # one invalid pixel
+    blob = q().encode(c, 2, 512, 257, 257, layout=layout)
+    with q().Resident(blob, valid=valid) as res:
+        assert res.info.sum_bits == 64
+        full = np.ones(P, np.uint8)
+        got = u(res.masked_sum(full))
+        want = oracle.masked_sum(c, full, valid)
+        assert np.array_equal(got, want)
+        assert int(want[5]) == 4328521215 - 65535 and want.max() > 2**32
+        assert np.array_equal(u(res.dense_df(full)), want)
+        check_com(res, c, synth.Workload("x", 2, 512, 257, 257, 2, 0, 0, 0, 0, 0, 0, 0, 0, layout), None, valid)
+        got = q().as_unsigned(res.decode_region(0, 1, 3, 8))
+        assert np.array_equal(got, oracle.region(c, 512, 0, 1, 3, 8, valid))
+
+
+@pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("det", [(17, 17), (19, 19)])
+def test_adversarial_streams(dtype, layout, det):
+    from test_oracle import adversarial
+    rng = np.random.default_rng(13)
+    sr, sc = (2, 512) if layout == 1 else (3, 301)
+    P = det[0] * det[1]
+    c = adversarial(sr * sc, P, dtype, rng)
+    valid = np.ones(P, np.uint8)
+    valid[P // 2] = 0
+    blob = q().encode(c, sr, sc, det[0], det[1], layout=layout)
+    w = synth.Workload("adv", sr, sc, det[0], det[1], 1 if dtype == np.uint8 else 2, 0, 0, 0, 0, 0, 0, 0, 0, layout)
+    masks = {"all": np.ones(P, np.uint8), "half": (np.arange(P) % 2).astype(np.uint8)}
+    check_all_products(w, c, valid, blob, masks, masks["half"], [(0, sr, 0, sc), (1, 2, 5, 40)],
+                       strides=(1, 2))
+
+
+def test_empty_mask_and_determinism():
+    w, counts, valid, blob = case("tiny")
+    with q().Resident(blob) as res:
+        z = u(res.masked_sum(np.zeros(w.P, np.uint8)))
+        assert (z == 0).all()
+        bf = synth.query_masks(w)["bf"]
+        a = u(res.masked_sum(bf))
+        for _ in range(3):
+            assert np.array_equal(u(res.masked_sum(bf)), a)
+
+
+def corrupt_rans_word(blob):
+    """Flip a bit in the state word of the first RANS stream."""
+    b = bytearray(blob.tobytes())
+    h = oracle.header(bytes(b))
+    P = h["det_rows"] * h["det_cols"]
+    G = (P + 31) // 32
+    for p in range(P):
+        g, i = divmod(p, 32)
+        gb, = struct.unpack_from("<I", b, h["gbase_off"] + 4 * g)
+        rel, = struct.unpack_from("<H", b, h["rel_off"] + 2 * (32 * g + i))
+        off = h["payload_off"] + gb + rel
+        if struct.unpack_from("<H", b, off)[0] == 1:
+            b[off + 2] ^= 0x10
+            return bytes(b), p
+    raise AssertionError("no RANS stream")
+
+
+def test_malformed_stream_fails_the_query():
+    w, counts, valid, blob = case("tiny")
+    bad, p = corrupt_rans_word(blob)
+    with pytest.raises(oracle.OracleError):
+        oracle.decode(bad)
+    qq = q()
+    with qq.Resident(bad) as res:
+        all_px = np.ones(w.P, np.uint8)
+        with pytest.raises(qq.QscValueError) as e:
+            res.masked_sum(all_px)
+        assert e.value.code == qq.ERR_MALFORMED and f"pixel {p}" in str(e.value)
+        # queued form: the error surfaces at finish(), then the resident is usable again
+        res.masked_sum(all_px, wait=False)
+        with pytest.raises(qq.QscValueError):
+            res.finish()
+        other = np.zeros(w.P, np.uint8)
+        other[(p + 1) % w.P] = 1
+        got = u(res.masked_sum(other))
+        assert np.array_equal(got, oracle.masked_sum(counts, other))
+        with pytest.raises(qq.QscValueError):
+            res.decode_region(0, 16, 0, 16)
+        with pytest.raises(qq.QscValueError):
+            res.com()
+
+
+def test_argument_errors():
+    w, counts, valid, blob = case("tiny")
+    qq = q()
+    with qq.Resident(blob) as res:
+        with pytest.raises(ValueError):
+            res.decode_region(0, 0, 0, 4)
+        with pytest.raises(ValueError):
+            res.decode_region(0, 17, 0, 4)
+        with pytest.raises(ValueError):
+            res.decode_region(0, 2, 0, 2, calibrated=True)  # not a scaled resident
+        with pytest.raises(ValueError):
+            res.masked_sum(np.ones(5, np.uint8))
+        assert qq.lib.qsc_masked_sum(res._h, None, 1, None, None, 1) == qq.ERR_INVALID_ARG

@@ -1,0 +1,156 @@
+"""Library checks that need no GPU: the C-ABI loads and exports every declared
+symbol, the host encoder is byte-identical to the oracle encoder, and
+resident_create rejects malformed containers before touching the device."""
+import ctypes
+import os
+import re
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def qsc():
+    import stem_compressed_count_amd as q
+    return q
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "qsc.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qsc_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    q = qsc()
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(q.lib, n), n
+    assert set(names) == set(q.EXPORTS)
+    assert q.abi() == "qsc-byte-rans-v1;qsc-paired-v1"
+
+
+def test_library_is_gfx950_code():
+    # the shared object carries an offload bundle for gfx950
+    blob = open(qsc().LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+CASES = [
+    ("tiny", 16, 16, 0), ("c2", 4, 128, 0), ("c3", 4, 128, 0), ("c4", 2, 256, 0), ("c4", 3, 301, 0),
+]
+
+
+@pytest.mark.parametrize("name,sr,sc,layout", CASES)
+def test_encoder_matches_oracle_bytes(name, sr, sc, layout):
+    w = synth.WORKLOADS[name].with_scans(sr, sc)
+    c = synth.counts(w)
+    a = qsc().encode(c, sr, sc, w.det_rows, w.det_cols, layout=layout).tobytes()
+    assert a == oracle.encode(c, sr, sc, w.det_rows, w.det_cols, layout=layout)
+
+
+def test_encoder_matches_oracle_paired_and_scaled():
+    w = synth.Workload("p", 16, 64, 64, 64, 2, 5.0, 0.1, 32, 32, 20, 2, 0, 77, 1)
+    c = synth.counts(w)
+    assert qsc().encode(c, 16, 64, 64, 64, layout=1).tobytes() == oracle.encode(c, 16, 64, 64, 64, layout=1)
+    x = synth.scaled(synth.WORKLOADS["c3"].with_scans(2, 300))
+    assert qsc().encode(x, 2, 300, 192, 192, scaled=True).tobytes() == oracle.encode(x, 2, 300, 192, 192, scaled=True)
+
+
+@pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_encoder_matches_oracle_adversarial(dtype, layout):
+    from test_oracle import adversarial
+    rng = np.random.default_rng(11)
+    sr, sc = (2, 512) if layout == 1 else (3, 301)
+    for det in [(17, 17), (19, 19)]:
+        c = adversarial(sr * sc, det[0] * det[1], dtype, rng)
+        a = qsc().encode(c, sr, sc, det[0], det[1], layout=layout).tobytes()
+        assert a == oracle.encode(c, sr, sc, det[0], det[1], layout=layout)
+        assert np.array_equal(oracle.decode(a), c)
+
+
+def test_encoder_streams_in_several_calls():
+    w = synth.WORKLOADS["c2"].with_scans(6, 200)  # 1200 scans: blocks of 512, 512, 176
+    c = synth.counts(w)
+    q = qsc()
+    enc = q.Encoder(6, 200, 192, 192, dtype=2)
+    enc.add(c[:512])
+    enc.add(c[512:])
+    blob = enc.blob().tobytes()
+    enc.close()
+    assert blob == oracle.encode(c, 6, 200, 192, 192)
+    enc = q.Encoder(6, 200, 192, 192, dtype=2)
+    with pytest.raises(ValueError):
+        enc.add(c[:100].astype(np.uint8))  # wrong dtype
+    enc.add(c[:300])
+    with pytest.raises(q.QscError):
+        enc.add(c[300:])  # a partial block was already added
+    enc.close()
+
+
+def test_encoder_rejects_nan_and_bad_geometry():
+    q = qsc()
+    x = np.ones((512, 4), dtype=np.float32)
+    x[3, 1] = np.nan
+    with pytest.raises(q.QscValueError):
+        q.encode(x, 1, 512, 2, 2, scaled=True)
+    with pytest.raises(q.QscValueError):
+        q.Encoder(3, 100, 2, 2, dtype=2, layout=1)  # paired needs complete 512-scan blocks
+    with pytest.raises(q.QscValueError):
+        q.Encoder(1, 10, 2000, 2, dtype=2)  # detector dimension above 1024
+
+
+def create_status(blob):
+    q = qsc()
+    b = np.frombuffer(blob, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    return q.lib.qsc_resident_create(b.ctypes.data, b.size, None, None, ctypes.byref(h))
+
+
+def test_resident_create_rejects_malformed_before_the_device():
+    w = synth.WORKLOADS["tiny"]
+    c = synth.counts(w)
+    blob = bytearray(oracle.encode(c, 16, 16, 64, 64))
+    h = oracle.header(bytes(blob))
+    q = qsc()
+    # reserved stream header bit (paired-resident page, "Verification")
+    bad = bytearray(blob)
+    bad[h["payload_off"] + 1] |= 0x80
+    assert create_status(bytes(bad)) == q.ERR_MALFORMED
+    # invalid mode
+    bad = bytearray(blob)
+    bad[h["payload_off"]] = (bad[h["payload_off"]] & ~7) | 5
+    assert create_status(bytes(bad)) == q.ERR_MALFORMED
+    # shortened extent: the last stream's end moves before its start
+    bad = bytearray(blob)
+    struct.pack_into("<I", bad, h["dir_off"] + 12, 1)
+    assert create_status(bytes(bad)) == q.ERR_MALFORMED
+    # a relative offset that breaks monotonic order
+    bad = bytearray(blob)
+    struct.pack_into("<H", bad, h["rel_off"] + 2, 0xFFFF)
+    assert create_status(bytes(bad)) == q.ERR_MALFORMED
+    # frequency table not summing to 4096
+    bad = bytearray(blob)
+    bad[h["table_off"]] ^= 1
+    assert create_status(bytes(bad)) == q.ERR_MALFORMED
+    # another ABI is refused
+    bad = bytearray(blob)
+    bad[8:24] = b"qsc-byte-rans-v7"
+    assert create_status(bytes(bad)) == q.ERR_UNSUPPORTED
+    # truncated blob
+    assert create_status(bytes(blob[:-2])) == q.ERR_MALFORMED
+
+
+def test_paired_model_tables_are_validated():
+    w = synth.Workload("p", 1, 512, 8, 8, 2, 5.0, 0.1, 4, 4, 2, 0, 0, 3, 1)
+    c = synth.counts(w)
+    blob = bytearray(oracle.encode(c, 1, 512, 8, 8, layout=1))
+    h = oracle.header(bytes(blob))
+    blob[h["table_off"] + 2] ^= 1  # one count of model 0 changed
+    assert create_status(bytes(blob)) == qsc().ERR_MALFORMED
