@@ -15,6 +15,9 @@
 // minus the complement, and CoM from fused moment sums.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "kernels.hpp"
 
 namespace qsc {
@@ -85,6 +88,74 @@ __device__ __forceinline__ void bits_refill(Bits &s, const uint32_t *pay32) {
     }
 }
 
+// The same reservoir fed through a buffer resource over one block's payload:
+// 32-bit offsets, one add per refill, and reads past the block return zero.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Block base and size are the same in every lane; readfirstlane keeps the
+// descriptor in scalar registers (a per-lane descriptor would serialise loads).
+__device__ __forceinline__ Rsrc block_rsrc(const uint8_t *block, uint32_t nbytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(block);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    // the range check is per dword and a block may end on a 2-byte boundary: cover
+    // its last partial dword (the next block or the device padding follows it)
+    const uint32_t nb = __builtin_amdgcn_readfirstlane(nbytes + 16u);
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)nb, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t bload(Rsrc rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0);
+}
+
+struct BBits {
+    uint64_t r;
+    uint32_t n;
+    uint32_t off;  // block offset of the prefetched dword pf
+    uint32_t pf;
+};
+
+__device__ __forceinline__ void bbits_init(BBits &s, Rsrc rs, uint32_t start) {
+    const uint32_t a = start & ~3u;
+    const uint32_t d0 = bload(rs, a), d1 = bload(rs, a + 4);
+    s.r = ((uint64_t)d1 << 32) | d0;
+    s.n = 64;
+    if (start & 2) {
+        s.r >>= 16;
+        s.n = 48;
+    }
+    s.off = a + 8;
+    s.pf = bload(rs, s.off);
+}
+
+__device__ __forceinline__ void bbits_refill(BBits &s, Rsrc rs) {
+    if (s.n <= 32) {
+        s.r |= (uint64_t)s.pf << s.n;
+        s.n += 32;
+        s.off += 4;
+        s.pf = bload(rs, s.off);
+    }
+}
+
+// bits consumed since the stream start (block offset start)
+__device__ __forceinline__ uint32_t bbits_used(const BBits &s, uint32_t start) {
+    return 8u * (s.off - (start & ~3u)) - s.n - ((start & 2) ? 16u : 0u);
+}
+
+// Loads one dword of every 128-byte line of a stream so the whole stream is in
+// flight towards the caches at once: the decode then waits for one memory
+// latency per tile instead of one per line. The values only feed a dummy sum.
+__device__ __forceinline__ uint32_t touch_stream(Rsrc rs, uint32_t start, uint32_t len) {
+    uint32_t t[9];
+#pragma unroll
+    for (int i = 0; i < 9; i++) t[i] = (uint32_t)i * 128u < len ? bload(rs, (start & ~3u) + 128u * i) : 0u;
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 9; i++) s += t[i];
+    return s;
+}
+
 // bits consumed since the stream start; org = (start >> 2) << 1 | (start >> 1 & 1)
 __device__ __forceinline__ uint32_t bits_used(const Bits &s, uint32_t org) {
     return 32u * (s.q - (org >> 1)) - s.n - ((org & 1) ? 16u : 0u);
@@ -94,39 +165,53 @@ __device__ __forceinline__ uint32_t origin(uint64_t start) {
     return (uint32_t)((start >> 2) << 1) | (uint32_t)((start >> 1) & 1);
 }
 
-__device__ __forceinline__ uint32_t pop16(Bits &s) {
+template <typename B>
+__device__ __forceinline__ uint32_t pop16(B &s) {
     const uint32_t w = (uint32_t)s.r & 0xFFFFu;
     s.r >>= 16;
     s.n -= 16;
     return w;
 }
 
-__device__ __forceinline__ uint32_t popn(Bits &s, uint32_t nb) {
+template <typename B>
+__device__ __forceinline__ uint32_t popn(B &s, uint32_t nb) {
     const uint32_t v = (uint32_t)s.r & ((1u << nb) - 1u);
     s.r >>= nb;
     s.n -= nb;
     return v;
 }
 
-// byte-rANS decode of one value (FORMAT 2.3). Table entry: sym | (f-1) << 8 | (slot - c) << 20.
-template <bool WIDE>
-__device__ __forceinline__ uint32_t rans_step(uint32_t &x, Bits &s, const uint32_t *tbl, uint32_t &bad) {
-    const uint32_t e = tbl[x & 4095u];
-    const uint32_t q = x >> 12;
-    const uint32_t xn = __umul24((e >> 8) & 0xFFFu, q) + q + (e >> 20);
-    const uint32_t w = (uint32_t)s.r & 0xFFFFu;
+// byte-rANS decode of one value (FORMAT 2.3). The table has two planes of
+// 4096 entries: f | symbol << 24 (v_mad_u32_u24 reads only the low 24 bits, so
+// the symbol rides along) and slot - c[symbol]. Consumes at most one 16-bit
+// renormalisation word; an escape (symbol 255 of a uint16 stream) is resolved
+// by rans_escape.
+template <typename B>
+__device__ __forceinline__ uint32_t rans_step(uint32_t &x, B &s, const uint32_t *tbl) {
+    const uint32_t slot = x & 4095u;
+    const uint32_t e = tbl[slot], bias = tbl[slot + 4096];
+    const uint32_t xn = __umul24(e, x >> 12) + bias;
     const bool need = xn < 65536u;
-    x = need ? ((xn << 16) | w) : xn;
+    // (xn << 16) | low word of the reservoir, as one byte permute
+    x = need ? __builtin_amdgcn_perm(xn, (uint32_t)s.r, 0x05040100u) : xn;
     const uint32_t sh = need ? 16u : 0u;
     s.r >>= sh;
     s.n -= sh;
-    uint32_t v = e & 0xFFu;
-    if (WIDE && v == 255u) {
-        const uint32_t lit = pop16(s);
-        bad |= lit < 255u;
-        v = lit;
-    }
-    return v;
+    return e >> 24;
+}
+
+// The 16-bit literal after an escape symbol; refills first so it is always there.
+__device__ __forceinline__ uint32_t rans_escape(Bits &s, const uint32_t *pay32, uint32_t &bad) {
+    bits_refill(s, pay32);
+    const uint32_t lit = pop16(s);
+    bad |= lit < 255u;
+    return lit;
+}
+__device__ __forceinline__ uint32_t rans_escape(BBits &s, Rsrc rs, uint32_t &bad) {
+    bbits_refill(s, rs);
+    const uint32_t lit = pop16(s);
+    bad |= lit < 255u;
+    return lit;
 }
 
 // ------------------------------------------------------------------ wave reductions
@@ -271,32 +356,45 @@ __device__ __forceinline__ void add_event(const Partials<OP> &pt, int pos, uint3
 // holds up to four slots per lane).
 struct RSlot {
     uint32_t x;     // rANS state
-    uint32_t meta;  // mode (1 RANS, 2 RAW, 3 idle) | held byte of a RAW uint8 word << 8
+    uint32_t hold;  // second byte of a RAW uint8 word
     uint32_t p;     // detector pixel
-    uint32_t org;   // stream origin (see bits_used)
+    uint32_t org;   // stream start within the block payload
     uint32_t len;   // stream bytes
-    Bits s;
+    BBits s;
+    bool raw;       // RAW stream, or an idle slot (raw over an empty range: every read is 0)
+    bool live;      // a RANS or RAW stream is decoded in this slot
 };
 
+// Every slot steps through the same instructions whatever its mode: a RAW
+// stream is a renormalisation that always takes a word, and an idle slot is a
+// RAW stream whose reads fall outside the buffer range and return zero. With
+// no per-slot branches the K table reads of a step issue together.
 template <int K, bool WIDE, Op OP>
-__device__ __forceinline__ void rans_tile(const DevResident &r, const uint32_t *sel, uint32_t n_sel, uint32_t first, uint32_t b,
+__device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
                           uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt) {
-    const uint32_t *pay32 = reinterpret_cast<const uint32_t *>(r.payload);
+    const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
     RSlot sl[K];
-    uint32_t bad = 0;
+    uint32_t bad = 0, touched = 0;
 #pragma unroll
     for (int k = 0; k < K; k++) {
         RSlot &z = sl[k];
-        z.meta = 3;
         z.x = 0;
+        z.hold = 0;
         z.p = 0;
+        z.raw = true;
+        z.live = false;
+        z.s.r = 0;
+        z.s.n = 64;
+        // outside the range (a block is far below 2 GB) and it cannot wrap back in: loads return 0
+        z.s.off = 0x80000000u;
+        z.s.pf = 0;
         const uint32_t i = first + k * 64 + lane;
         if (i >= n_sel) continue;
-        z.p = sel[i];
+        z.p = p0 + sel[i];
         const Extent e = locate(r, b, z.p, base, nbytes);
-        z.org = origin(e.start);
+        z.org = (uint32_t)(e.start - base);
         z.len = (uint32_t)(e.end - e.start);
         const uint32_t hdr = ld16(r.payload, e.start);
         const uint32_t mode = hdr & 7u;
@@ -310,14 +408,16 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint32_t *
             if (v) add_event<OP>(pt, -1, v, kr, z.p - kr * r.det_cols);
             continue;
         }
-        z.meta = mode;
-        bits_init(z.s, pay32, e.start);
+        z.live = true;
+        z.raw = mode == 2;
+        touched += touch_stream(rs, z.org, z.len);
+        bbits_init(z.s, rs, z.org);
         pop16(z.s);  // header
         if (mode == 1) {
             z.x = pop16(z.s);
             z.x |= pop16(z.s) << 16;
         }
-        bits_refill(z.s, pay32);
+        bbits_refill(z.s, rs);
     }
     uint32_t kr[OP == Op::Moments ? K : 1], kc[OP == Op::Moments ? K : 1];
     if (OP == Op::Moments) {
@@ -328,11 +428,62 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint32_t *
         }
     }
 
-    constexpr int CH = OP == Op::Sum ? 32 : 16;
+    // one step of every slot: values in v[], escapes resolved
+    auto step = [&](bool even, uint32_t (&v)[K]) {
+        uint32_t e[K], bias[K];
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            const uint32_t slot = sl[k].x & 4095u;
+            e[k] = tbl[slot];
+            bias[k] = tbl[slot + 4096];
+        }
+        bool esc_any = false;
+        bool esc[K];
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            RSlot &z = sl[k];
+            const uint32_t xn = __umul24(e[k], z.x >> 12) + bias[k];
+            const uint32_t sym = e[k] >> 24;
+            const uint32_t w = (uint32_t)z.s.r;
+            // a RAW uint8 word covers an even scan and the odd scan after it
+            const bool raw_take = WIDE || even;
+            const bool need = z.raw ? raw_take : xn < 65536u;
+            z.x = need ? __builtin_amdgcn_perm(xn, w, 0x05040100u) : xn;
+            const uint32_t sh = need ? 16u : 0u;
+            z.s.r >>= sh;
+            z.s.n -= sh;
+            uint32_t rv;
+            if (WIDE) {
+                rv = w & 0xFFFFu;
+            } else if (even) {
+                rv = w & 0xFFu;
+                z.hold = z.raw ? (w >> 8) & 0xFFu : z.hold;
+            } else {
+                rv = z.hold;
+            }
+            v[k] = z.raw ? rv : sym;
+            esc[k] = WIDE && !z.raw && sym == 255u;
+            esc_any |= esc[k];
+        }
+        if (WIDE && __builtin_amdgcn_ballot_w64(esc_any)) {  // rare: escapes of uint16 streams
+#pragma unroll
+            for (int k = 0; k < K; k++)
+                if (esc[k]) v[k] = rans_escape(sl[k].s, rs, bad);
+        }
+    };
+    // Refill on a wave-uniform cadence: two steps use at most 32 bits (an escape
+    // refills on its own), so the dword prefetched at the previous cadence point
+    // has a full period to arrive.
+    auto refill = [&]() {
+#pragma unroll
+        for (int k = 0; k < K; k++) bbits_refill(sl[k].s, rs);
+    };
+
+    constexpr int CH = 16;
     const uint32_t my = lane_scan<CH>();
     const bool writer = lane_writes<CH>();
-    const uint32_t nch = (n + CH - 1) / CH;
-    for (uint32_t c = 0; c < nch; c++) {
+    const uint32_t nfull = n / CH;
+    for (uint32_t c = 0; c < nfull; c++) {
         uint32_t a0[CH];
         uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
 #pragma unroll
@@ -343,49 +494,53 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint32_t *
                 ac[i] = 0;
             }
         }
-        const uint32_t jn = min((uint32_t)CH, n - c * CH);
 #pragma unroll
         for (int jj = 0; jj < CH; jj++) {
-            if ((uint32_t)jj < jn) {
+            uint32_t v[K];
+            step((jj & 1) == 0, v);  // chunks start at even scans
 #pragma unroll
-                for (int k = 0; k < K; k++) {
-                    RSlot &z = sl[k];
-                    const uint32_t mode = z.meta & 0xFFu;
-                    uint32_t v = 0;
-                    if (mode == 1) {
-                        v = rans_step<WIDE>(z.x, z.s, tbl, bad);
-                        bits_refill(z.s, pay32);
-                    } else if (mode == 2) {
-                        if (WIDE) {
-                            v = pop16(z.s);
-                        } else if ((jj & 1) == 0) {  // chunks start at even scans
-                            const uint32_t w = pop16(z.s);
-                            v = w & 0xFFu;
-                            z.meta = 2u | ((w >> 8) << 8);
-                        } else {
-                            v = z.meta >> 8;
-                        }
-                        bits_refill(z.s, pay32);
-                    }
-                    a0[jj] += v;
-                    if (OP == Op::Moments) {
-                        ar[jj] += v * kr[k];
-                        ac[jj] += v * kc[k];
-                    }
+            for (int k = 0; k < K; k++) {
+                a0[jj] += v[k];
+                if (OP == Op::Moments) {
+                    ar[jj] += v[k] * kr[k];
+                    ac[jj] += v[k] * kc[k];
                 }
             }
+            if (jj & 1) refill();
+            // keep the scheduler's interleaving to the K independent slots of one step
+            __builtin_amdgcn_sched_barrier(0);
         }
         chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
     }
+    // ragged end of a final partial block: one scan at a time, reduced per scan
+    for (uint32_t j = nfull * CH; j < n; j++) {
+        uint32_t v[K];
+        step((j & 1) == 0, v);
+        uint32_t t0 = 0, tr = 0, tc = 0;
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            t0 += v[k];
+            if (OP == Op::Moments) {
+                tr += v[k] * kr[k];
+                tc += v[k] * kc[k];
+            }
+        }
+        if (t0) atomicAdd(&pt.m0[j], t0);
+        if (OP == Op::Moments) {
+            if (tr) atomicAdd(&pt.mr[j], (unsigned long long)tr);
+            if (tc) atomicAdd(&pt.mc[j], (unsigned long long)tc);
+        }
+        if ((j & 1) || j + 1 == n) refill();
+    }
+    asm volatile("" ::"v"(touched));
     // end checks (FORMAT 2.3-2.4)
 #pragma unroll
     for (int k = 0; k < K; k++) {
         const RSlot &z = sl[k];
-        const uint32_t mode = z.meta & 0xFFu;
-        if (mode > 2) continue;
-        bool ok = bits_used(z.s, z.org) == 8u * z.len;
-        if (mode == 1) ok = ok && z.x == 65536u;
-        if (mode == 2 && !WIDE && (n & 1)) ok = ok && (z.meta >> 8) == 0;
+        if (!z.live) continue;
+        bool ok = bbits_used(z.s, z.org) == 8u * z.len;
+        if (!z.raw) ok = ok && z.x == 65536u;
+        if (z.raw && !WIDE && (n & 1)) ok = ok && z.hold == 0;
         if (!ok || bad) report(r, b, z.p);
     }
 }
@@ -395,9 +550,9 @@ struct PSlot {
     uint32_t X;     // tANS state
     uint32_t meta;  // mode (3 PAIRED, 4 RAW, 7 idle) | model << 3
     uint32_t p;
-    uint32_t org;
+    uint32_t org;  // stream start within the block payload
     uint32_t len;
-    Bits s;
+    BBits s;
 };
 
 __device__ __forceinline__ uint32_t window_sym(uint32_t v, uint32_t a0, uint32_t use) {
@@ -407,9 +562,16 @@ __device__ __forceinline__ uint32_t window_sym(uint32_t v, uint32_t a0, uint32_t
 
 // An escaped count: its literal, returned relative to the model's window base.
 template <bool WIDE>
-__device__ __forceinline__ uint32_t pair_literal(Bits &s, const uint32_t *pay32, uint32_t info,
-                                                           uint32_t &bad) {
+__device__ __forceinline__ uint32_t pair_literal(Bits &s, const uint32_t *pay32, uint32_t info, uint32_t &bad) {
     bits_refill(s, pay32);
+    const uint32_t lit = popn(s, WIDE ? 16u : 8u);
+    const uint32_t a0 = info & 0xFFFFu;
+    bad |= window_sym(lit, a0, info >> 16) != 15u;
+    return lit - a0;
+}
+template <bool WIDE>
+__device__ __forceinline__ uint32_t pair_literal(BBits &s, Rsrc rs, uint32_t info, uint32_t &bad) {
+    bbits_refill(s, rs);
     const uint32_t lit = popn(s, WIDE ? 16u : 8u);
     const uint32_t a0 = info & 0xFFFFu;
     bad |= window_sym(lit, a0, info >> 16) != 15u;
@@ -417,13 +579,13 @@ __device__ __forceinline__ uint32_t pair_literal(Bits &s, const uint32_t *pay32,
 }
 
 template <int K, bool WIDE, Op OP>
-__device__ __forceinline__ void paired_tile(const DevResident &r, const uint32_t *sel, uint32_t n_sel, uint32_t first, uint32_t b,
+__device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
                             uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt) {
-    const uint32_t *pay32 = reinterpret_cast<const uint32_t *>(r.payload);
+    const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
     PSlot sl[K];
-    uint32_t bad = 0;
+    uint32_t bad = 0, touched = 0;
     // window-base contributions, added once per chunk instead of once per value
     uint32_t base0 = 0, baseR = 0, baseC = 0;
 #pragma unroll
@@ -434,13 +596,14 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint32_t
         z.p = 0;
         const uint32_t i = first + k * 64 + lane;
         if (i >= n_sel) continue;
-        z.p = sel[i];
+        z.p = p0 + sel[i];
         const uint32_t kr = z.p / r.det_cols, kc = z.p - kr * r.det_cols;
         const Extent e = locate(r, b, z.p, base, nbytes);
-        z.org = origin(e.start);
+        z.org = (uint32_t)(e.start - base);
         z.len = (uint32_t)(e.end - e.start);
         const uint32_t hdr = ld16(r.payload, e.start);
         const uint32_t mode = hdr & 7u;
+        if (mode >= 3) touched += touch_stream(rs, z.org, z.len);
         if (mode == 0) {  // EMPTY
             if (z.len != 2) report(r, b, z.p);
             continue;
@@ -478,7 +641,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint32_t
             continue;
         }
         z.meta = hdr & 0xFFu;  // mode and model
-        bits_init(z.s, pay32, e.start);
+        bbits_init(z.s, rs, z.org);
         pop16(z.s);  // header
         if (mode == 3) {
             const uint32_t a0 = r.model_info[(hdr >> 3) & 31u] & 0xFFFFu;
@@ -487,7 +650,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint32_t
             baseR += a0 * kr;
             baseC += a0 * kc;
         }
-        bits_refill(z.s, pay32);
+        bbits_refill(z.s, rs);
     }
     uint32_t kr[OP == Op::Moments ? K : 1], kc[OP == Op::Moments ? K : 1];
     if (OP == Op::Moments) {
@@ -514,6 +677,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint32_t
         }
 #pragma unroll
         for (int tt = 0; tt < CH / 2; tt++) {
+            const uint32_t t = c * (CH / 2) + tt;  // pair index within the block
 #pragma unroll
             for (int k = 0; k < K; k++) {
                 PSlot &z = sl[k];
@@ -524,23 +688,29 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint32_t
                     z.X = (e >> 12) + popn(z.s, (e >> 8) & 15u);
                     v0 = e & 15u;
                     v1 = (e >> 4) & 15u;
-                    if (v0 == 15u || v1 == 15u) {
-                        const uint32_t info = r.model_info[z.meta >> 3];
-                        if (v0 == 15u) v0 = pair_literal<WIDE>(z.s, pay32, info, bad);
-                        if (v1 == 15u) v1 = pair_literal<WIDE>(z.s, pay32, info, bad);
+                    const bool esc = v0 == 15u || v1 == 15u;
+                    if (__builtin_amdgcn_ballot_w64(esc)) {
+                        if (esc) {
+                            const uint32_t info = r.model_info[z.meta >> 3];
+                            if (v0 == 15u) v0 = pair_literal<WIDE>(z.s, rs, info, bad);
+                            if (v1 == 15u) v1 = pair_literal<WIDE>(z.s, rs, info, bad);
+                            bbits_refill(z.s, rs);  // keep 32+ bits until the next cadence point
+                        }
                     }
-                    bits_refill(z.s, pay32);
+                    // codes are at most 10 bits: one 32-bit refill per three pairs, on a
+                    // wave-uniform cadence (the paired-resident page's refill rhythm)
+                    if (t % 3 == 2) bbits_refill(z.s, rs);
                 } else if (mode == 4) {
                     if (WIDE) {
                         v0 = pop16(z.s);
-                        bits_refill(z.s, pay32);
+                        bbits_refill(z.s, rs);
                         v1 = pop16(z.s);
                     } else {
                         const uint32_t w = pop16(z.s);
                         v0 = w & 0xFFu;
                         v1 = w >> 8;
                     }
-                    bits_refill(z.s, pay32);
+                    bbits_refill(z.s, rs);
                 }
                 a0[2 * tt] += v0;
                 a0[2 * tt + 1] += v1;
@@ -554,20 +724,21 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint32_t
         }
         chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
     }
+    asm volatile("" ::"v"(touched));
     // end checks (FORMAT 3.3-3.4)
 #pragma unroll
     for (int k = 0; k < K; k++) {
         PSlot &z = sl[k];
         const uint32_t mode = z.meta & 7u;
         if (mode != 3 && mode != 4) continue;
-        const uint32_t used = bits_used(z.s, z.org), total = 8u * z.len;
+        const uint32_t used = bbits_used(z.s, z.org), total = 8u * z.len;
         bool ok;
         if (mode == 4) {
             ok = used == total;
         } else {
             ok = z.X == 0 && used <= total && total - used < 16;
             if (ok && total > used) {
-                bits_refill(z.s, pay32);
+                bbits_refill(z.s, rs);
                 ok = popn(z.s, total - used) == 0;
             }
         }
@@ -625,121 +796,130 @@ __device__ __forceinline__ void flush_partials(SharedPartials<OP> &sp, uint32_t 
     }
 }
 
-__device__ __forceinline__ uint32_t slots_per_lane(uint64_t streams, uint32_t target_lanes) {
-    if (streams > 2ull * target_lanes) return 4;
-    if (streams > (uint64_t)target_lanes) return 2;
-    return 1;
+// Selection of one pixel tile: writes the tile-local offsets of the pixels with
+// (mask[p] != 0) != complement (every pixel when mask is null) and valid[p],
+// in increasing order, to sel (LDS) and returns their number. Wave ballots
+// give each selected pixel its slot; nothing outside the workgroup is needed.
+template <int WG>
+__device__ __forceinline__ uint32_t select_tile(const DevResident &r, const uint8_t *mask, int complement, uint32_t p0,
+                                                uint32_t cnt, uint16_t *sel, uint32_t *wtot) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    uint32_t total = 0;
+    for (uint32_t base = 0; base < cnt; base += WG) {
+        const uint32_t off = base + tid;
+        bool f = false;
+        if (off < cnt) {
+            const uint32_t p = p0 + off;
+            f = r.valid[p] != 0 && (mask ? ((mask[p] != 0) != (complement != 0)) : true);
+        }
+        const unsigned long long bal = __ballot(f);
+        if (lane == 0) wtot[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t before = total, all = total;
+#pragma unroll
+        for (uint32_t w = 0; w < WG / 64; w++) {
+            const uint32_t c = wtot[w];
+            before += w < wave ? c : 0u;
+            all += c;
+        }
+        if (f) sel[before + (uint32_t)__popcll(bal & below)] = (uint16_t)off;
+        __syncthreads();
+        total = all;
+    }
+    return total;
 }
 
 template <bool WIDE, Op OP>
-__global__ __launch_bounds__(kRansWG) void k_reduce_rans(DevResident r, Plan plan, uint32_t stride, uint32_t n_visited,
-                                                         uint32_t target_lanes, void *out, int out64, int negate) {
-    __shared__ uint32_t tbl[4096];
+__global__ __launch_bounds__(kRansWG, 3) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
+                                                         uint32_t stride, uint32_t n_visited, uint32_t tile_px,
+                                                         void *out, int out64, int negate) {
+    __shared__ uint32_t tbl[2 * 4096];
     __shared__ SharedPartials<OP> sp;
-    const uint32_t n_sel = *plan.n_sel;
-    if (n_sel == 0) return;
-    const uint32_t K = slots_per_lane((uint64_t)n_sel * n_visited, target_lanes);
-    const uint32_t tile = kRansWG * K;
-    const uint32_t n_tiles = (n_sel + tile - 1) / tile;
+    __shared__ uint16_t sel[4 * kRansWG];
+    __shared__ uint32_t wtot[kRansWG / 64];
+    const uint32_t n_tiles = (r.P + tile_px - 1) / tile_px;
     const uint64_t n_work = (uint64_t)n_tiles * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     uint32_t loaded = 0xFFFFFFFFu;
     for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = (uint32_t)(w / n_tiles), t = (uint32_t)(w % n_tiles);
-        const uint32_t b = vb * stride;
+        const uint32_t b = vb * stride, p0 = t * tile_px;
+        __syncthreads();
+        const uint32_t n_sel = select_tile<kRansWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
+        if (n_sel == 0) continue;
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
-        __syncthreads();
         if (b != loaded) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(r.tables + 4096ull * b);
+            const uint4 *src = reinterpret_cast<const uint4 *>(r.tables + 8192ull * b);
             uint4 *dst = reinterpret_cast<uint4 *>(tbl);
-            for (uint32_t i = threadIdx.x; i < 1024; i += kRansWG) dst[i] = src[i];
+            for (uint32_t i = threadIdx.x; i < 2048; i += kRansWG) dst[i] = src[i];
             loaded = b;
         }
         zero_partials<OP>(sp, n);
         __syncthreads();
-        const uint32_t first = t * tile + (threadIdx.x >> 6) * 64 * K;
-        if (K == 4)
-            rans_tile<4, WIDE, OP>(r, plan.sel, n_sel, first, b, n, base, nbytes, tbl, pt);
-        else if (K == 2)
-            rans_tile<2, WIDE, OP>(r, plan.sel, n_sel, first, b, n, base, nbytes, tbl, pt);
-        else
-            rans_tile<1, WIDE, OP>(r, plan.sel, n_sel, first, b, n, base, nbytes, tbl, pt);
+        // uint8 tiles hold at most 512 pixels: four uint8 slots per lane do not fit 3 waves per SIMD
+        const uint32_t K = n_sel <= kRansWG ? 1 : n_sel <= 2 * kRansWG ? 2 : 4;
+        const uint32_t first = (threadIdx.x >> 6) * 64 * K;
+        if (first < n_sel) {  // whole waves without a stream skip the decode
+            if (WIDE && K == 4)
+                rans_tile<4, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt);
+            else if (K == 2)
+                rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt);
+            else
+                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt);
+        }
         __syncthreads();
         flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate);
     }
 }
 
 template <bool WIDE, Op OP>
-__global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, Plan plan, uint32_t stride,
-                                                           uint32_t n_visited, uint32_t target_lanes, void *out,
-                                                           int out64, int negate) {
+__global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const uint8_t *mask, int complement,
+                                                           uint32_t stride, uint32_t n_visited, uint32_t tile_px,
+                                                           void *out, int out64, int negate) {
     __shared__ uint32_t tbl[32 * 1024];
     __shared__ SharedPartials<OP> sp;
-    const uint32_t n_sel = *plan.n_sel;
-    if (n_sel == 0) return;
+    __shared__ uint16_t sel[2 * kPairWG];
+    __shared__ uint32_t wtot[kPairWG / 64];
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(r.tables);
         uint4 *dst = reinterpret_cast<uint4 *>(tbl);
         for (uint32_t i = threadIdx.x; i < 32 * 1024 / 4; i += kPairWG) dst[i] = src[i];
     }
-    // at most two slots per lane: 1024-thread workgroups have 128 VGPRs per lane
-    const uint32_t K = min(2u, slots_per_lane((uint64_t)n_sel * n_visited, target_lanes));
-    const uint32_t tile = kPairWG * K;
-    const uint32_t n_tiles = (n_sel + tile - 1) / tile;
+    const uint32_t n_tiles = (r.P + tile_px - 1) / tile_px;
     const uint64_t n_work = (uint64_t)n_tiles * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = (uint32_t)(w / n_tiles), t = (uint32_t)(w % n_tiles);
-        const uint32_t b = vb * stride;
+        const uint32_t b = vb * stride, p0 = t * tile_px;
+        __syncthreads();
+        const uint32_t n_sel = select_tile<kPairWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
+        if (n_sel == 0) continue;
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
-        __syncthreads();
         zero_partials<OP>(sp, kBlk);
         __syncthreads();
-        const uint32_t first = t * tile + (threadIdx.x >> 6) * 64 * K;
-        if (K == 2)
-            paired_tile<2, WIDE, OP>(r, plan.sel, n_sel, first, b, base, nbytes, tbl, pt);
-        else
-            paired_tile<1, WIDE, OP>(r, plan.sel, n_sel, first, b, base, nbytes, tbl, pt);
+        // at most two slots per lane: 1024-thread workgroups have 128 VGPRs per lane
+        const uint32_t K = n_sel <= kPairWG ? 1 : 2;
+        const uint32_t first = (threadIdx.x >> 6) * 64 * K;
+        if (first < n_sel) {
+            if (K == 2)
+                paired_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt);
+            else
+                paired_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt);
+        }
         __syncthreads();
         flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate);
     }
 }
 
-// ------------------------------------------------------------------ plan
-// Block 0 compacts (mask xor complement) & valid into a sorted pixel list; the
-// other blocks initialise the output.
-constexpr uint32_t kPlanWG = 1024;
-
-__global__ __launch_bounds__(kPlanWG) void k_plan(const uint8_t *mask, const uint8_t *valid, uint32_t P,
-                                                  int complement, uint32_t *sel, uint32_t *n_sel, void *out,
-                                                  int out64, const void *init, uint64_t n_out) {
-    if (blockIdx.x == 0) {
-        __shared__ uint32_t scan[kPlanWG];
-        const uint32_t per = (P + kPlanWG - 1) / kPlanWG;
-        const uint32_t p0 = threadIdx.x * per, p1 = min(P, p0 + per);
-        uint32_t cnt = 0;
-        for (uint32_t p = p0; p < p1; p++) cnt += (mask ? ((mask[p] != 0) != (complement != 0)) : 1) && valid[p];
-        scan[threadIdx.x] = cnt;
-        __syncthreads();
-        for (uint32_t off = 1; off < kPlanWG; off <<= 1) {  // inclusive scan
-            const uint32_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
-            __syncthreads();
-            scan[threadIdx.x] += v;
-            __syncthreads();
-        }
-        uint32_t o = scan[threadIdx.x] - cnt;
-        for (uint32_t p = p0; p < p1; p++)
-            if ((mask ? ((mask[p] != 0) != (complement != 0)) : 1) && valid[p]) sel[o++] = p;
-        if (threadIdx.x == kPlanWG - 1) *n_sel = scan[kPlanWG - 1];
-        return;
-    }
-    const uint64_t stride = (uint64_t)(gridDim.x - 1) * blockDim.x;
-    for (uint64_t i = (uint64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < n_out; i += stride) {
+// out[i] = init[i], or 0 without init (u32 or u64 elements)
+__global__ void k_init(void *out, int out64, const void *init, uint64_t n) {
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
         if (out64)
             reinterpret_cast<uint64_t *>(out)[i] = init ? reinterpret_cast<const uint64_t *>(init)[i] : 0;
         else
@@ -828,7 +1008,7 @@ __global__ __launch_bounds__(256) void k_region(DevResident r, RegionBlocks bloc
             if (len != 4 || cval > maxv) bad = 1;
         } else if (mode == 1) {
             kind = 1;
-            tbl = r.tables + 4096ull * b;
+            tbl = r.tables + 8192ull * b;
             x = pop16(s);
             x |= pop16(s) << 16;
             bits_refill(s, pay32);
@@ -866,7 +1046,8 @@ __global__ __launch_bounds__(256) void k_region(DevResident r, RegionBlocks bloc
     for (uint32_t j = 0; j < n; j++) {
         uint32_t v = cval;
         if (kind == 1) {
-            v = rans_step<WIDE>(x, s, tbl, bad);
+            v = rans_step(x, s, tbl);
+            if (WIDE && v == 255u) v = rans_escape(s, pay32, bad);
             bits_refill(s, pay32);
         } else if (kind == 2) {
             if (WIDE) {
@@ -946,34 +1127,44 @@ int device_cu_count() {
     return cus;
 }
 
-hipError_t launch_plan(const DevResident &r, const uint8_t *mask, int complement, Plan plan, void *out, int out64,
-                       const void *init_total, hipStream_t st) {
-    const uint32_t init_blocks = (uint32_t)std::min<uint64_t>(1024, (r.S + 1023) / 1024);
-    hipLaunchKernelGGL(k_plan, dim3(1 + init_blocks), dim3(kPlanWG), 0, st, mask, r.valid, r.P, complement, plan.sel,
-                       plan.n_sel, out, out64, init_total, r.S);
+hipError_t launch_init(void *out, int out64, const void *init, uint64_t n, hipStream_t st) {
+    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(2048, (n + 255) / 256));
+    hipLaunchKernelGGL(k_init, dim3(grid), dim3(256), 0, st, out, out64, init, n);
     return hipGetLastError();
 }
 
-hipError_t launch_plan_moments(const DevResident &r, const uint8_t *mask, Plan plan, uint64_t *moments,
-                               hipStream_t st) {
-    const uint64_t n = 3 * r.S;
-    const uint32_t init_blocks = (uint32_t)std::min<uint64_t>(1024, (n + 1023) / 1024);
-    hipLaunchKernelGGL(k_plan, dim3(1 + init_blocks), dim3(kPlanWG), 0, st, mask, r.valid, r.P, 0, plan.sel,
-                       plan.n_sel, (void *)moments, 1, (const void *)nullptr, n);
-    return hipGetLastError();
+// Pixel-tile size: the largest tile whose count of (block, tile) items fills
+// the resident workgroup slots in whole rounds.
+static uint32_t pick_tile(uint32_t P, uint32_t n_visited, uint32_t slots, const uint32_t *cands, int ncand) {
+    uint32_t best = cands[ncand - 1];
+    double best_eff = -1.0;
+    for (int i = 0; i < ncand; i++) {
+        const double items = (double)((P + cands[i] - 1) / cands[i]) * n_visited;
+        const double rounds = items / slots;
+        const double eff = rounds / std::ceil(rounds);
+        if (eff >= 0.85) return cands[i];
+        if (eff > best_eff) {
+            best_eff = eff;
+            best = cands[i];
+        }
+    }
+    return best;
 }
 
-hipError_t launch_reduce(const DevResident &r, Plan plan, uint32_t stride, Op op, void *out, int out64, int negate,
-                         hipStream_t st) {
+hipError_t launch_reduce(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
+                         int out64, int negate, hipStream_t st) {
     const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
     const uint32_t cus = (uint32_t)device_cu_count();
-    const uint32_t target = cus * 4 * 64 * 4;  // lanes that keep four waves per SIMD busy
     const bool wide = r.dtype == 2;
     if (r.layout == 0) {
-        const uint64_t max_work = (uint64_t)((r.P + kRansWG - 1) / kRansWG) * n_visited;
-        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(max_work, 8ull * cus));
-#define QSC_RANS(W, O) hipLaunchKernelGGL((k_reduce_rans<W, O>), dim3(grid), dim3(kRansWG), 0, st, r, plan, stride, \
-                                          n_visited, target, out, out64, negate)
+        const uint32_t cands[3] = {4 * kRansWG, 2 * kRansWG, kRansWG};
+        // uint8 decodes with at most two slots per lane (register budget), so its tiles stop at 512
+        const uint32_t tile = wide ? pick_tile(r.P, n_visited, 3 * cus, cands, 3)
+                                   : pick_tile(r.P, n_visited, 3 * cus, cands + 1, 2);
+        const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * n_visited;
+        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, 8ull * cus));
+#define QSC_RANS(W, O) hipLaunchKernelGGL((k_reduce_rans<W, O>), dim3(grid), dim3(kRansWG), 0, st, r, mask, \
+                                          complement, stride, n_visited, tile, out, out64, negate)
         if (op == Op::Sum) {
             if (wide) QSC_RANS(true, Op::Sum); else QSC_RANS(false, Op::Sum);
         } else {
@@ -981,10 +1172,12 @@ hipError_t launch_reduce(const DevResident &r, Plan plan, uint32_t stride, Op op
         }
 #undef QSC_RANS
     } else {
-        const uint64_t max_work = (uint64_t)((r.P + kPairWG - 1) / kPairWG) * n_visited;
-        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(max_work, cus));
-#define QSC_PAIR(W, O) hipLaunchKernelGGL((k_reduce_paired<W, O>), dim3(grid), dim3(kPairWG), 0, st, r, plan, \
-                                          stride, n_visited, target, out, out64, negate)
+        const uint32_t cands[2] = {2 * kPairWG, kPairWG};
+        const uint32_t tile = pick_tile(r.P, n_visited, cus, cands, 2);
+        const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * n_visited;
+        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, cus));
+#define QSC_PAIR(W, O) hipLaunchKernelGGL((k_reduce_paired<W, O>), dim3(grid), dim3(kPairWG), 0, st, r, mask, \
+                                          complement, stride, n_visited, tile, out, out64, negate)
         if (op == Op::Sum) {
             if (wide) QSC_PAIR(true, Op::Sum); else QSC_PAIR(false, Op::Sum);
         } else {

@@ -12,7 +12,7 @@ struct DevResident {
     const uint8_t *dir;      // n_blocks x {u64 base, u32 n_scans, u32 nbytes}
     const uint32_t *gbase;   // n_blocks x G
     const uint16_t *rel;     // n_blocks x G x 32
-    const uint32_t *tables;  // byte-rANS: n_blocks x 4096 entries; paired: 32 x 1024 entries
+    const uint32_t *tables;  // byte-rANS: n_blocks x 2 x 4096 entries; paired: 32 x 1024 entries
     const uint32_t *model_info; // paired: per model a0 | in_use << 16
     const uint8_t *valid;    // P bytes, nonzero = valid
     const double *calib;     // scaled: n_blocks x {scale, offset}
@@ -23,12 +23,6 @@ struct DevResident {
 
 enum class Op : int { Sum = 0, Moments = 1 };
 
-// Selection plan: sel[0..n_sel) sorted pixel indices of (mask or ~mask) & valid.
-struct Plan {
-    uint32_t *sel;
-    uint32_t *n_sel; // device counter
-};
-
 // Blocks touched by a region read, passed by value to one launch.
 struct RegionBlocks {
     uint32_t n;
@@ -36,16 +30,13 @@ struct RegionBlocks {
 };
 
 // Launch wrappers (enqueue only; return hipSuccess or the launch error).
-//  plan: builds the selection and initialises the output of a sum query:
-//  out[s] = 0, or total[s] when init_total is not null.
-hipError_t launch_plan(const DevResident &r, const uint8_t *mask, int complement, Plan plan, void *out, int out64,
-                       const void *init_total, hipStream_t st);
-//  plan for moment queries: zeroes the three moment arrays (u64 [3][S]).
-hipError_t launch_plan_moments(const DevResident &r, const uint8_t *mask, Plan plan, uint64_t *moments,
-                               hipStream_t st);
-//  fused decode + reduce over the visited blocks (b % stride == 0).
-hipError_t launch_reduce(const DevResident &r, Plan plan, uint32_t stride, Op op, void *out, int out64, int negate,
-                         hipStream_t st);
+//  out[i] = init[i] (or 0 when init is null), n elements of 4 or 8 bytes.
+hipError_t launch_init(void *out, int out64, const void *init, uint64_t n, hipStream_t st);
+//  fused selection + decode + reduce over the visited blocks (b % stride == 0):
+//  adds (negate: subtracts) the sums over pixels with (mask[p] != 0) != complement
+//  (all pixels when mask is null) and valid[p]. Sum: out[s]; Moments: u64 [3][S].
+hipError_t launch_reduce(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
+                         int out64, int negate, hipStream_t st);
 //  CoM from exact moments.
 hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, float *col, hipStream_t st);
 //  decode of a scan rectangle over the listed touched blocks.

@@ -65,9 +65,9 @@ struct PairModels {
 const PairModels &pair_models();
 
 // Device decode-table entries.
-//  byte-rANS (per block, 4096 entries): symbol | (f-1) << 8 | (slot - c) << 20
+//  byte-rANS (per block, two planes of 4096 entries): f | symbol << 24, then slot - c
 //  paired (per model, 1024 entries): a | b << 4 | nbits << 8 | newX << 12
-void build_rans_table(const uint16_t *freq, uint32_t *out4096);
+void build_rans_table(const uint16_t *freq, uint32_t *out8192);
 void build_pair_tables(uint32_t *out /* 32 x 1024 */);
 
 // little-endian access

@@ -31,8 +31,6 @@ struct qsc_resident {
     uint32_t *d_tables = nullptr;
     uint32_t *d_model_info = nullptr;
     uint8_t *d_valid = nullptr;
-    uint32_t *d_sel = nullptr;
-    uint32_t *d_nsel = nullptr;
     unsigned long long *d_err = nullptr;
     void *d_total = nullptr;
     bool total_ready = false;
@@ -67,8 +65,7 @@ hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
 
 void free_all(qsc_resident *res) {
     for (void *p : {(void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
-                    (void *)res->d_sel, (void *)res->d_nsel, (void *)res->d_err, res->d_total,
-                    (void *)res->d_moments})
+                    (void *)res->d_err, res->d_total, (void *)res->d_moments})
         if (p) (void)hipFree(p);
 }
 
@@ -97,8 +94,6 @@ qsc_status finish_query(qsc_resident *res, hipError_t launch, hipStream_t st, in
     if (launch != hipSuccess) return hip_fail(res, launch, "kernel launch");
     return wait ? check_done(res, st) : QSC_OK;
 }
-
-Plan plan_of(qsc_resident *res) { return Plan{res->d_sel, res->d_nsel}; }
 
 }  // namespace
 
@@ -155,11 +150,11 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     std::vector<uint32_t> tables;
     std::vector<uint32_t> info(kModels, 0);
     if (g.layout == 0) {
-        tables.resize(nb * kRansM);
+        tables.resize(nb * 2 * kRansM);
         for (uint64_t b = 0; b < nb; b++) {
             uint16_t f[256];
             std::memcpy(f, blob + s.table + 512 * b, 512);
-            build_rans_table(f, tables.data() + kRansM * b);
+            build_rans_table(f, tables.data() + 2 * kRansM * b);
         }
     } else {
         tables.resize(kModels * kTansL);
@@ -179,8 +174,6 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     if ((e = dalloc(res.get(), &res->d_valid, g.P())) != hipSuccess) return bail(e, "valid");
     if ((e = hipMemcpy(res->d_valid, valid.data(), g.P(), hipMemcpyHostToDevice)) != hipSuccess)
         return bail(e, "valid upload");
-    if ((e = dalloc(res.get(), &res->d_sel, 4ull * g.P())) != hipSuccess) return bail(e, "selection");
-    if ((e = dalloc(res.get(), &res->d_nsel, 256)) != hipSuccess) return bail(e, "selection count");
     if ((e = dalloc(res.get(), &res->d_err, 256)) != hipSuccess) return bail(e, "error word");
     if ((e = hipMemset(res->d_err, 0, 256)) != hipSuccess) return bail(e, "error word");
     if ((e = hipStreamSynchronize(strm)) != hipSuccess) return bail(e, "synchronize");
@@ -235,8 +228,8 @@ qsc_status qsc_masked_sum(qsc_resident *res, const uint8_t *d_mask, uint32_t blo
     if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const int out64 = res->g.sum_bits() == 64;
-    hipError_t e = launch_plan(res->dev, d_mask, 0, plan_of(res), d_out, out64, nullptr, st);
-    if (e == hipSuccess) e = launch_reduce(res->dev, plan_of(res), block_stride, Op::Sum, d_out, out64, 0, st);
+    hipError_t e = launch_init(d_out, out64, nullptr, res->g.S(), st);
+    if (e == hipSuccess) e = launch_reduce(res->dev, d_mask, 0, block_stride, Op::Sum, d_out, out64, 0, st);
     return finish_query(res, e, st, wait);
 }
 
@@ -252,14 +245,14 @@ qsc_status qsc_dense_df(qsc_resident *res, const uint8_t *d_mask, void *d_out, v
         return hip_fail(res, e, "total cache");
     if (!res->total_ready) {
         // cold: full-detector total over the valid pixels, decoded once and kept
-        e = launch_plan(res->dev, nullptr, 0, plan_of(res), res->d_total, out64, nullptr, st);
-        if (e == hipSuccess) e = launch_reduce(res->dev, plan_of(res), 1, Op::Sum, res->d_total, out64, 0, st);
+        e = launch_init(res->d_total, out64, nullptr, res->g.S(), st);
+        if (e == hipSuccess) e = launch_reduce(res->dev, nullptr, 0, 1, Op::Sum, res->d_total, out64, 0, st);
         if (e != hipSuccess) return hip_fail(res, e, "total cache build");
         res->total_ready = true;
     }
     // warm: out = total - sum over valid & ~mask
-    e = launch_plan(res->dev, d_mask, 1, plan_of(res), d_out, out64, res->d_total, st);
-    if (e == hipSuccess) e = launch_reduce(res->dev, plan_of(res), 1, Op::Sum, d_out, out64, 1, st);
+    e = launch_init(d_out, out64, res->d_total, res->g.S(), st);
+    if (e == hipSuccess) e = launch_reduce(res->dev, d_mask, 1, 1, Op::Sum, d_out, out64, 1, st);
     return finish_query(res, e, st, wait);
 }
 
@@ -271,8 +264,8 @@ qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float
     hipError_t e = hipSuccess;
     if (!res->d_moments && (e = dalloc(res, &res->d_moments, 3 * 8 * res->g.S())) != hipSuccess)
         return hip_fail(res, e, "moment buffer");
-    e = launch_plan_moments(res->dev, d_mask, plan_of(res), res->d_moments, st);
-    if (e == hipSuccess) e = launch_reduce(res->dev, plan_of(res), 1, Op::Moments, res->d_moments, 1, 0, st);
+    e = launch_init(res->d_moments, 1, nullptr, 3 * res->g.S(), st);
+    if (e == hipSuccess) e = launch_reduce(res->dev, d_mask, 0, 1, Op::Moments, res->d_moments, 1, 0, st);
     if (e == hipSuccess) e = launch_com_finalize(res->d_moments, res->g.S(), d_row, d_col, st);
     return finish_query(res, e, st, wait);
 }
