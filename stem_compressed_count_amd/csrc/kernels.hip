@@ -295,31 +295,38 @@ __device__ __forceinline__ bool lane_writes() {
     return (lane_id() & (64 / CH - 1)) == 0;
 }
 
-// Adds the wave totals of one chunk to the LDS partials. Moment terms can pass
-// 2^32 over a wave, so they are split into 16-bit halves that reduce without
-// overflow (64 lanes x 2^16 < 2^32) and are recombined in 64 bits.
+// Adds the wave totals of one chunk to the LDS partials. A lane's moment term
+// is at most 4 slots x 65535 x (dim - 1); over 64 lanes that stays below 2^32
+// while both detector dimensions are at most 256 (split = false). Larger
+// detectors split the terms into 16-bit halves that reduce without overflow
+// (64 lanes x 2^16 < 2^32) and recombine in 64 bits.
 template <int CH, Op OP>
 __device__ __forceinline__ void chunk_to_lds(uint32_t (&a0)[CH], uint32_t (&ar)[OP == Op::Moments ? CH : 1],
                                              uint32_t (&ac)[OP == Op::Moments ? CH : 1], uint32_t my, bool writer,
-                                             uint32_t *m0, unsigned long long *mr, unsigned long long *mc) {
+                                             bool split, uint32_t *m0, unsigned long long *mr,
+                                             unsigned long long *mc) {
     const uint32_t t0 = wave_transpose_sum<CH>(a0);
     if (writer && t0) atomicAdd(&m0[my], t0);
     if constexpr (OP == Op::Moments) {
-        uint32_t lo[CH];
+        unsigned long long tr, tc;
+        if (!split) {
+            tr = wave_transpose_sum<CH>(ar);
+            tc = wave_transpose_sum<CH>(ac);
+        } else {
+            uint32_t lo[CH];
 #pragma unroll
-        for (int i = 0; i < CH; i++) {
-            lo[i] = ar[i] & 0xFFFFu;
-            ar[i] >>= 16;
-        }
-        const unsigned long long tr =
-            ((unsigned long long)wave_transpose_sum<CH>(ar) << 16) + wave_transpose_sum<CH>(lo);
+            for (int i = 0; i < CH; i++) {
+                lo[i] = ar[i] & 0xFFFFu;
+                ar[i] >>= 16;
+            }
+            tr = ((unsigned long long)wave_transpose_sum<CH>(ar) << 16) + wave_transpose_sum<CH>(lo);
 #pragma unroll
-        for (int i = 0; i < CH; i++) {
-            lo[i] = ac[i] & 0xFFFFu;
-            ac[i] >>= 16;
+            for (int i = 0; i < CH; i++) {
+                lo[i] = ac[i] & 0xFFFFu;
+                ac[i] >>= 16;
+            }
+            tc = ((unsigned long long)wave_transpose_sum<CH>(ac) << 16) + wave_transpose_sum<CH>(lo);
         }
-        const unsigned long long tc =
-            ((unsigned long long)wave_transpose_sum<CH>(ac) << 16) + wave_transpose_sum<CH>(lo);
         if (writer && tr) atomicAdd(&mr[my], tr);
         if (writer && tc) atomicAdd(&mc[my], tc);
     }
@@ -351,6 +358,64 @@ __device__ __forceinline__ void add_event(const Partials<OP> &pt, int pos, uint3
     }
 }
 
+// ------------------------------------------------------------------ region output
+template <bool WIDE>
+__device__ __forceinline__ void region_put(void *out, int out_kind, uint64_t idx, uint32_t v, double scale,
+                                           double offset) {
+    if (out_kind == 1)
+        reinterpret_cast<float *>(out)[idx] = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
+    else if (WIDE)
+        reinterpret_cast<uint16_t *>(out)[idx] = (uint16_t)v;
+    else
+        reinterpret_cast<uint8_t *>(out)[idx] = (uint8_t)v;
+}
+
+// Scan walk of one block for a region read: (row, col) of scan s0 + j, the
+// output index of an in-rectangle scan, and the calibration of the block.
+struct RegionWalk {
+    uint32_t row, col;
+    uint32_t scan_cols;
+    const RegionArgs *ra;
+    double scale, offset;
+    __device__ __forceinline__ bool inside() const {
+        return row >= ra->r0 && row < ra->r1 && col >= ra->c0 && col < ra->c1;
+    }
+    __device__ __forceinline__ uint64_t index(uint32_t P) const {
+        return ((uint64_t)(row - ra->r0) * (ra->c1 - ra->c0) + (col - ra->c0)) * P;
+    }
+    __device__ __forceinline__ void next() {
+        if (++col == scan_cols) {
+            col = 0;
+            row++;
+        }
+    }
+};
+
+__device__ __forceinline__ RegionWalk region_walk(const DevResident &r, uint32_t b, const RegionArgs &ra) {
+    RegionWalk rw;
+    const uint64_t s0 = (uint64_t)b * kBlk;
+    rw.row = (uint32_t)(s0 / r.scan_cols);
+    rw.col = (uint32_t)(s0 % r.scan_cols);
+    rw.scan_cols = r.scan_cols;
+    rw.ra = &ra;
+    rw.scale = 1.0;
+    rw.offset = 0.0;
+    if (ra.out_kind == 1) {
+        rw.scale = r.calib[2 * b];
+        rw.offset = r.calib[2 * b + 1];
+    }
+    return rw;
+}
+
+// A stream whose scans hold one value (constant, or zero): written directly.
+template <bool WIDE>
+__device__ __forceinline__ void region_fill(const DevResident &r, uint32_t b, uint32_t n, uint32_t p, uint32_t v,
+                                            const RegionArgs &ra) {
+    RegionWalk rw = region_walk(r, b, ra);
+    for (uint32_t j = 0; j < n; j++, rw.next())
+        if (rw.inside()) region_put<WIDE>(ra.out, ra.out_kind, rw.index(r.P) + p, v, rw.scale, rw.offset);
+}
+
 // ------------------------------------------------------------------ byte-rANS tile
 // Per-slot state kept in registers across the 512 steps (kept small: the tile
 // holds up to four slots per lane).
@@ -371,7 +436,8 @@ struct RSlot {
 // no per-slot branches the K table reads of a step issue together.
 template <int K, bool WIDE, Op OP>
 __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
-                          uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt) {
+                          uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt,
+                          const RegionArgs &ra) {
     const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
@@ -404,8 +470,12 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 report(r, b, z.p);
                 continue;
             }
-            const uint32_t kr = z.p / r.det_cols;
-            if (v) add_event<OP>(pt, -1, v, kr, z.p - kr * r.det_cols);
+            if constexpr (OP == Op::Region) {
+                region_fill<WIDE>(r, b, n, z.p, v, ra);
+            } else {
+                const uint32_t kr = z.p / r.det_cols;
+                if (v) add_event<OP>(pt, -1, v, kr, z.p - kr * r.det_cols);
+            }
             continue;
         }
         z.live = true;
@@ -479,58 +549,91 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         for (int k = 0; k < K; k++) bbits_refill(sl[k].s, rs);
     };
 
-    constexpr int CH = 16;
-    const uint32_t my = lane_scan<CH>();
-    const bool writer = lane_writes<CH>();
-    const uint32_t nfull = n / CH;
-    for (uint32_t c = 0; c < nfull; c++) {
-        uint32_t a0[CH];
-        uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+    if constexpr (OP == Op::Region) {
+        // values of scans inside the rectangle go straight to the output
+        constexpr int CH = 16;
+        RegionWalk rw = region_walk(r, b, ra);
+        auto put = [&](const uint32_t (&v)[K]) {
+            if (rw.inside()) {
+                const uint64_t idx = rw.index(r.P);
 #pragma unroll
-        for (int i = 0; i < CH; i++) {
-            a0[i] = 0;
-            if (OP == Op::Moments) {
-                ar[i] = 0;
-                ac[i] = 0;
+                for (int k = 0; k < K; k++)
+                    if (sl[k].live) region_put<WIDE>(ra.out, ra.out_kind, idx + sl[k].p, v[k], rw.scale, rw.offset);
+            }
+            rw.next();
+        };
+        const uint32_t nfull = n / CH;
+        for (uint32_t c = 0; c < nfull; c++) {
+#pragma unroll
+            for (int jj = 0; jj < CH; jj++) {
+                uint32_t v[K];
+                step((jj & 1) == 0, v);
+                put(v);
+                if (jj & 1) refill();
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-#pragma unroll
-        for (int jj = 0; jj < CH; jj++) {
+        for (uint32_t j = nfull * CH; j < n; j++) {
             uint32_t v[K];
-            step((jj & 1) == 0, v);  // chunks start at even scans
-#pragma unroll
-            for (int k = 0; k < K; k++) {
-                a0[jj] += v[k];
+            step((j & 1) == 0, v);
+            put(v);
+            if ((j & 1) || j + 1 == n) refill();
+        }
+    } else {
+        constexpr int CH = 16;
+        const uint32_t my = lane_scan<CH>();
+        const bool writer = lane_writes<CH>();
+        const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
+        const uint32_t nfull = n / CH;
+        for (uint32_t c = 0; c < nfull; c++) {
+            uint32_t a0[CH];
+            uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+    #pragma unroll
+            for (int i = 0; i < CH; i++) {
+                a0[i] = 0;
                 if (OP == Op::Moments) {
-                    ar[jj] += v[k] * kr[k];
-                    ac[jj] += v[k] * kc[k];
+                    ar[i] = 0;
+                    ac[i] = 0;
                 }
             }
-            if (jj & 1) refill();
-            // keep the scheduler's interleaving to the K independent slots of one step
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
-    }
-    // ragged end of a final partial block: one scan at a time, reduced per scan
-    for (uint32_t j = nfull * CH; j < n; j++) {
-        uint32_t v[K];
-        step((j & 1) == 0, v);
-        uint32_t t0 = 0, tr = 0, tc = 0;
-#pragma unroll
-        for (int k = 0; k < K; k++) {
-            t0 += v[k];
-            if (OP == Op::Moments) {
-                tr += v[k] * kr[k];
-                tc += v[k] * kc[k];
+    #pragma unroll
+            for (int jj = 0; jj < CH; jj++) {
+                uint32_t v[K];
+                step((jj & 1) == 0, v);  // chunks start at even scans
+    #pragma unroll
+                for (int k = 0; k < K; k++) {
+                    a0[jj] += v[k];
+                    if (OP == Op::Moments) {
+                        ar[jj] += v[k] * kr[k];
+                        ac[jj] += v[k] * kc[k];
+                    }
+                }
+                if (jj & 1) refill();
+                // keep the scheduler's interleaving to the K independent slots of one step
+                __builtin_amdgcn_sched_barrier(0);
             }
+            chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
         }
-        if (t0) atomicAdd(&pt.m0[j], t0);
-        if (OP == Op::Moments) {
-            if (tr) atomicAdd(&pt.mr[j], (unsigned long long)tr);
-            if (tc) atomicAdd(&pt.mc[j], (unsigned long long)tc);
+        // ragged end of a final partial block: one scan at a time, reduced per scan
+        for (uint32_t j = nfull * CH; j < n; j++) {
+            uint32_t v[K];
+            step((j & 1) == 0, v);
+            uint32_t t0 = 0, tr = 0, tc = 0;
+    #pragma unroll
+            for (int k = 0; k < K; k++) {
+                t0 += v[k];
+                if (OP == Op::Moments) {
+                    tr += v[k] * kr[k];
+                    tc += v[k] * kc[k];
+                }
+            }
+            if (t0) atomicAdd(&pt.m0[j], t0);
+            if (OP == Op::Moments) {
+                if (tr) atomicAdd(&pt.mr[j], (unsigned long long)tr);
+                if (tc) atomicAdd(&pt.mc[j], (unsigned long long)tc);
+            }
+            if ((j & 1) || j + 1 == n) refill();
         }
-        if ((j & 1) || j + 1 == n) refill();
     }
     asm volatile("" ::"v"(touched));
     // end checks (FORMAT 2.3-2.4)
@@ -580,7 +683,8 @@ __device__ __forceinline__ uint32_t pair_literal(BBits &s, Rsrc rs, uint32_t inf
 
 template <int K, bool WIDE, Op OP>
 __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
-                            uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt) {
+                            uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt,
+                            const RegionArgs &ra) {
     const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
@@ -606,12 +710,15 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         if (mode >= 3) touched += touch_stream(rs, z.org, z.len);
         if (mode == 0) {  // EMPTY
             if (z.len != 2) report(r, b, z.p);
+            if constexpr (OP == Op::Region) region_fill<WIDE>(r, b, kBlk, z.p, 0, ra);
             continue;
         }
         if (mode == 1) {  // CONST
             const uint32_t v = ld16(r.payload, e.start + 2);
             if (z.len != 4 || v == 0 || v > maxv)
                 report(r, b, z.p);
+            else if constexpr (OP == Op::Region)
+                region_fill<WIDE>(r, b, kBlk, z.p, v, ra);
             else
                 add_event<OP>(pt, -1, v, kr, kc);
             continue;
@@ -625,6 +732,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             }
             int prev = -1;
             bool ok = true;
+            if constexpr (OP == Op::Region) region_fill<WIDE>(r, b, kBlk, z.p, 0, ra);
             for (uint32_t t = 0; t < nnz; t++) {
                 const int pos = (int)ld16(r.payload, e.start + 4 + 2 * t);
                 const uint32_t v = WIDE ? ld16(r.payload, e.start + 4 + 2 * nnz + 2 * t)
@@ -633,7 +741,15 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     ok = false;
                     break;
                 }
-                add_event<OP>(pt, pos, v, kr, kc);
+                if constexpr (OP == Op::Region) {
+                    RegionWalk rw = region_walk(r, b, ra);
+                    const uint64_t s = (uint64_t)b * kBlk + (uint32_t)pos;
+                    rw.row = (uint32_t)(s / r.scan_cols);
+                    rw.col = (uint32_t)(s % r.scan_cols);
+                    if (rw.inside()) region_put<WIDE>(ra.out, ra.out_kind, rw.index(r.P) + z.p, v, rw.scale, rw.offset);
+                } else {
+                    add_event<OP>(pt, pos, v, kr, kc);
+                }
                 prev = pos;
             }
             if (ok && !WIDE && (nnz & 1)) ok = r.payload[e.start + 4 + 3 * nnz] == 0;
@@ -661,68 +777,120 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         }
     }
 
-    constexpr int CH = 16;  // paired workgroups have 128 VGPRs per lane
-    const uint32_t my = lane_scan<CH>();
-    const bool writer = lane_writes<CH>();
-    for (uint32_t c = 0; c < kBlk / CH; c++) {
-        uint32_t a0[CH];
-        uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
-#pragma unroll
-        for (int i = 0; i < CH; i++) {
-            a0[i] = base0;
-            if (OP == Op::Moments) {
-                ar[i] = baseR;
-                ac[i] = baseC;
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < CH / 2; tt++) {
-            const uint32_t t = c * (CH / 2) + tt;  // pair index within the block
+    if constexpr (OP == Op::Region) {
+        RegionWalk rw = region_walk(r, b, ra);
+        for (uint32_t t = 0; t < kBlk / 2; t++) {
+            uint32_t v0[K], v1[K];
 #pragma unroll
             for (int k = 0; k < K; k++) {
                 PSlot &z = sl[k];
                 const uint32_t mode = z.meta & 7u;
-                uint32_t v0 = 0, v1 = 0;
+                v0[k] = 0;
+                v1[k] = 0;
                 if (mode == 3) {
                     const uint32_t e = tbl[((z.meta >> 3) << 10) + z.X];
                     z.X = (e >> 12) + popn(z.s, (e >> 8) & 15u);
-                    v0 = e & 15u;
-                    v1 = (e >> 4) & 15u;
-                    const bool esc = v0 == 15u || v1 == 15u;
-                    if (__builtin_amdgcn_ballot_w64(esc)) {
-                        if (esc) {
-                            const uint32_t info = r.model_info[z.meta >> 3];
-                            if (v0 == 15u) v0 = pair_literal<WIDE>(z.s, rs, info, bad);
-                            if (v1 == 15u) v1 = pair_literal<WIDE>(z.s, rs, info, bad);
-                            bbits_refill(z.s, rs);  // keep 32+ bits until the next cadence point
-                        }
-                    }
-                    // codes are at most 10 bits: one 32-bit refill per three pairs, on a
-                    // wave-uniform cadence (the paired-resident page's refill rhythm)
-                    if (t % 3 == 2) bbits_refill(z.s, rs);
+                    const uint32_t info = r.model_info[z.meta >> 3];
+                    const uint32_t a0 = info & 0xFFFFu;
+                    uint32_t w0 = e & 15u, w1 = (e >> 4) & 15u;
+                    if (w0 == 15u) w0 = pair_literal<WIDE>(z.s, rs, info, bad);
+                    if (w1 == 15u) w1 = pair_literal<WIDE>(z.s, rs, info, bad);
+                    v0[k] = a0 + w0;
+                    v1[k] = a0 + w1;
+                    bbits_refill(z.s, rs);
                 } else if (mode == 4) {
                     if (WIDE) {
-                        v0 = pop16(z.s);
+                        v0[k] = pop16(z.s);
                         bbits_refill(z.s, rs);
-                        v1 = pop16(z.s);
+                        v1[k] = pop16(z.s);
                     } else {
                         const uint32_t w = pop16(z.s);
-                        v0 = w & 0xFFu;
-                        v1 = w >> 8;
+                        v0[k] = w & 0xFFu;
+                        v1[k] = w >> 8;
                     }
                     bbits_refill(z.s, rs);
                 }
-                a0[2 * tt] += v0;
-                a0[2 * tt + 1] += v1;
-                if (OP == Op::Moments) {
-                    ar[2 * tt] += v0 * kr[k];
-                    ar[2 * tt + 1] += v1 * kr[k];
-                    ac[2 * tt] += v0 * kc[k];
-                    ac[2 * tt + 1] += v1 * kc[k];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                if (rw.inside()) {
+                    const uint64_t idx = rw.index(r.P);
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        const uint32_t mode = sl[k].meta & 7u;
+                        if (mode == 3 || mode == 4)
+                            region_put<WIDE>(ra.out, ra.out_kind, idx + sl[k].p, h ? v1[k] : v0[k], rw.scale,
+                                             rw.offset);
+                    }
                 }
+                rw.next();
             }
         }
-        chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
+    } else {
+        constexpr int CH = 16;  // paired workgroups have 128 VGPRs per lane
+        const uint32_t my = lane_scan<CH>();
+        const bool writer = lane_writes<CH>();
+        const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
+        for (uint32_t c = 0; c < kBlk / CH; c++) {
+            uint32_t a0[CH];
+            uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+    #pragma unroll
+            for (int i = 0; i < CH; i++) {
+                a0[i] = base0;
+                if (OP == Op::Moments) {
+                    ar[i] = baseR;
+                    ac[i] = baseC;
+                }
+            }
+    #pragma unroll
+            for (int tt = 0; tt < CH / 2; tt++) {
+                const uint32_t t = c * (CH / 2) + tt;  // pair index within the block
+    #pragma unroll
+                for (int k = 0; k < K; k++) {
+                    PSlot &z = sl[k];
+                    const uint32_t mode = z.meta & 7u;
+                    uint32_t v0 = 0, v1 = 0;
+                    if (mode == 3) {
+                        const uint32_t e = tbl[((z.meta >> 3) << 10) + z.X];
+                        z.X = (e >> 12) + popn(z.s, (e >> 8) & 15u);
+                        v0 = e & 15u;
+                        v1 = (e >> 4) & 15u;
+                        const bool esc = v0 == 15u || v1 == 15u;
+                        if (__builtin_amdgcn_ballot_w64(esc)) {
+                            if (esc) {
+                                const uint32_t info = r.model_info[z.meta >> 3];
+                                if (v0 == 15u) v0 = pair_literal<WIDE>(z.s, rs, info, bad);
+                                if (v1 == 15u) v1 = pair_literal<WIDE>(z.s, rs, info, bad);
+                                bbits_refill(z.s, rs);  // keep 32+ bits until the next cadence point
+                            }
+                        }
+                        // codes are at most 10 bits: one 32-bit refill per three pairs, on a
+                        // wave-uniform cadence (the paired-resident page's refill rhythm)
+                        if (t % 3 == 2) bbits_refill(z.s, rs);
+                    } else if (mode == 4) {
+                        if (WIDE) {
+                            v0 = pop16(z.s);
+                            bbits_refill(z.s, rs);
+                            v1 = pop16(z.s);
+                        } else {
+                            const uint32_t w = pop16(z.s);
+                            v0 = w & 0xFFu;
+                            v1 = w >> 8;
+                        }
+                        bbits_refill(z.s, rs);
+                    }
+                    a0[2 * tt] += v0;
+                    a0[2 * tt + 1] += v1;
+                    if (OP == Op::Moments) {
+                        ar[2 * tt] += v0 * kr[k];
+                        ar[2 * tt + 1] += v1 * kr[k];
+                        ac[2 * tt] += v0 * kc[k];
+                        ac[2 * tt + 1] += v1 * kc[k];
+                    }
+                }
+            }
+            chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
+        }
     }
     asm volatile("" ::"v"(touched));
     // end checks (FORMAT 3.3-3.4)
@@ -833,7 +1001,8 @@ __device__ __forceinline__ uint32_t select_tile(const DevResident &r, const uint
 template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kRansWG, 3) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
-                                                         void *out, int out64, int negate) {
+                                                         void *out, int out64, int negate, RegionBlocks rb,
+                                                         RegionArgs ra) {
     __shared__ uint32_t tbl[2 * 4096];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[4 * kRansWG];
@@ -844,7 +1013,7 @@ __global__ __launch_bounds__(kRansWG, 3) void k_reduce_rans(DevResident r, const
     uint32_t loaded = 0xFFFFFFFFu;
     for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = (uint32_t)(w / n_tiles), t = (uint32_t)(w % n_tiles);
-        const uint32_t b = vb * stride, p0 = t * tile_px;
+        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = t * tile_px;
         __syncthreads();
         const uint32_t n_sel = select_tile<kRansWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
         if (n_sel == 0) continue;
@@ -858,28 +1027,29 @@ __global__ __launch_bounds__(kRansWG, 3) void k_reduce_rans(DevResident r, const
             for (uint32_t i = threadIdx.x; i < 2048; i += kRansWG) dst[i] = src[i];
             loaded = b;
         }
-        zero_partials<OP>(sp, n);
+        if (OP != Op::Region) zero_partials<OP>(sp, n);
         __syncthreads();
         // uint8 tiles hold at most 512 pixels: four uint8 slots per lane do not fit 3 waves per SIMD
         const uint32_t K = n_sel <= kRansWG ? 1 : n_sel <= 2 * kRansWG ? 2 : 4;
         const uint32_t first = (threadIdx.x >> 6) * 64 * K;
         if (first < n_sel) {  // whole waves without a stream skip the decode
             if (WIDE && K == 4)
-                rans_tile<4, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt);
+                rans_tile<4, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra);
             else if (K == 2)
-                rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt);
+                rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra);
             else
-                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt);
+                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra);
         }
         __syncthreads();
-        flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate);
+        if (OP != Op::Region) flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate);
     }
 }
 
 template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const uint8_t *mask, int complement,
                                                            uint32_t stride, uint32_t n_visited, uint32_t tile_px,
-                                                           void *out, int out64, int negate) {
+                                                           void *out, int out64, int negate, RegionBlocks rb,
+                                                           RegionArgs ra) {
     __shared__ uint32_t tbl[32 * 1024];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kPairWG];
@@ -894,26 +1064,26 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = (uint32_t)(w / n_tiles), t = (uint32_t)(w % n_tiles);
-        const uint32_t b = vb * stride, p0 = t * tile_px;
+        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = t * tile_px;
         __syncthreads();
         const uint32_t n_sel = select_tile<kPairWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
         if (n_sel == 0) continue;
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
-        zero_partials<OP>(sp, kBlk);
+        if (OP != Op::Region) zero_partials<OP>(sp, kBlk);
         __syncthreads();
         // at most two slots per lane: 1024-thread workgroups have 128 VGPRs per lane
         const uint32_t K = n_sel <= kPairWG ? 1 : 2;
         const uint32_t first = (threadIdx.x >> 6) * 64 * K;
         if (first < n_sel) {
             if (K == 2)
-                paired_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt);
+                paired_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt, ra);
             else
-                paired_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt);
+                paired_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt, ra);
         }
         __syncthreads();
-        flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate);
+        if (OP != Op::Region) flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate);
     }
 }
 
@@ -927,6 +1097,20 @@ __global__ void k_init(void *out, int out64, const void *init, uint64_t n) {
     }
 }
 
+__global__ void k_zero_bytes(uint8_t *out, uint64_t n) {
+    const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x, step = (uint64_t)gridDim.x * blockDim.x;
+    const uint64_t head = (16 - (reinterpret_cast<uint64_t>(out) & 15)) & 15;
+    if (n <= head + 16) {
+        for (uint64_t i = i0; i < n; i += step) out[i] = 0;
+        return;
+    }
+    for (uint64_t i = i0; i < head; i += step) out[i] = 0;
+    uint4 *body = reinterpret_cast<uint4 *>(out + head);
+    const uint64_t nv = (n - head) / 16;
+    for (uint64_t i = i0; i < nv; i += step) body[i] = make_uint4(0, 0, 0, 0);
+    for (uint64_t i = head + 16 * nv + i0; i < n; i += step) out[i] = 0;
+}
+
 __global__ void k_com_finalize(const uint64_t *m, uint64_t S, float *row, float *col) {
     for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < S; s += (uint64_t)gridDim.x * blockDim.x) {
         const uint64_t m0 = m[s];
@@ -938,178 +1122,6 @@ __global__ void k_com_finalize(const uint64_t *m, uint64_t S, float *row, float 
             col[s] = (float)((double)m[2 * S + s] / (double)m0);
         }
     }
-}
-
-// ------------------------------------------------------------------ region decode
-// One lane per (touched block, pixel): the whole stream is decoded (so its end
-// checks run) and values of scans inside the rectangle are written out.
-template <bool WIDE>
-__device__ __forceinline__ void region_put(void *out, int out_kind, uint64_t idx, uint32_t v, double scale,
-                                           double offset) {
-    if (out_kind == 1)
-        reinterpret_cast<float *>(out)[idx] = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
-    else if (WIDE)
-        reinterpret_cast<uint16_t *>(out)[idx] = (uint16_t)v;
-    else
-        reinterpret_cast<uint8_t *>(out)[idx] = (uint8_t)v;
-}
-
-template <bool WIDE>
-__global__ __launch_bounds__(256) void k_region(DevResident r, RegionBlocks blocks, uint32_t r0, uint32_t r1,
-                                                uint32_t c0, uint32_t c1, int out_kind, void *out) {
-    const uint32_t b = blocks.b[blockIdx.y];
-    const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= r.P) return;
-    const uint8_t *d = r.dir + 16ull * b;
-    const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
-    const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
-    const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
-    const uint32_t w = c1 - c0;
-    const uint64_t s0 = (uint64_t)b * kBlk;
-    double scale = 1.0, offset = 0.0;
-    if (out_kind == 1) {
-        scale = r.calib[2 * b];
-        offset = r.calib[2 * b + 1];
-    }
-    const bool valid = r.valid[p] != 0;
-    // walk the scans of the block with their (row, col)
-    uint32_t row = (uint32_t)(s0 / r.scan_cols), col = (uint32_t)(s0 % r.scan_cols);
-    if (!valid) {
-        for (uint32_t j = 0; j < n; j++) {
-            if (row >= r0 && row < r1 && col >= c0 && col < c1)
-                region_put<WIDE>(out, out_kind, ((uint64_t)(row - r0) * w + (col - c0)) * r.P + p, 0, 1.0, 0.0);
-            if (++col == r.scan_cols) {
-                col = 0;
-                row++;
-            }
-        }
-        return;
-    }
-    const uint32_t *pay32 = reinterpret_cast<const uint32_t *>(r.payload);
-    const Extent e = locate(r, b, p, base, nbytes);
-    const uint32_t len = (uint32_t)(e.end - e.start);
-    const uint32_t hdr = ld16(r.payload, e.start);
-    const uint32_t mode = hdr & 7u;
-    const uint32_t maxv = WIDE ? 65535u : 255u;
-    uint32_t bad = 0;
-    Bits s;
-    bits_init(s, pay32, e.start);
-    pop16(s);
-    bits_refill(s, pay32);
-    uint32_t x = 0, hold = 0, cval = 0, X = 0, a0 = 0, use = 0, tb = 0;
-    uint32_t nnz = 0, k = 0, next_pos = 0xFFFFFFFFu, pend = 0;
-    int prev = -1;
-    // kind: 0 constant value cval, 1 rANS, 2 raw, 3 paired, 4 sparse
-    uint32_t kind = 0;
-    const uint32_t *tbl = r.tables;
-    if (r.layout == 0) {
-        if (mode == 0) {
-            cval = ld16(r.payload, e.start + 2);
-            if (len != 4 || cval > maxv) bad = 1;
-        } else if (mode == 1) {
-            kind = 1;
-            tbl = r.tables + 8192ull * b;
-            x = pop16(s);
-            x |= pop16(s) << 16;
-            bits_refill(s, pay32);
-        } else {
-            kind = 2;
-        }
-    } else {
-        if (mode == 0) {
-            if (len != 2) bad = 1;
-        } else if (mode == 1) {
-            cval = ld16(r.payload, e.start + 2);
-            if (len != 4 || cval == 0 || cval > maxv) bad = 1;
-        } else if (mode == 2) {
-            kind = 4;
-            nnz = len >= 4 ? ld16(r.payload, e.start + 2) : 0;
-            const uint64_t need = 4ull + 2ull * nnz + (WIDE ? 2ull * nnz : nnz + (nnz & 1));
-            if (nnz == 0 || nnz > kBlk || need != len) {
-                bad = 1;
-                kind = 0;
-            } else {
-                next_pos = ld16(r.payload, e.start + 4);
-            }
-        } else if (mode == 3) {
-            kind = 3;
-            const uint32_t m = (hdr >> 3) & 31u;
-            tb = m * 1024u;
-            a0 = r.model_info[m] & 0xFFFFu;
-            use = r.model_info[m] >> 16;
-            X = popn(s, 10);
-            bits_refill(s, pay32);
-        } else {
-            kind = 2;
-        }
-    }
-    for (uint32_t j = 0; j < n; j++) {
-        uint32_t v = cval;
-        if (kind == 1) {
-            v = rans_step(x, s, tbl);
-            if (WIDE && v == 255u) v = rans_escape(s, pay32, bad);
-            bits_refill(s, pay32);
-        } else if (kind == 2) {
-            if (WIDE) {
-                v = pop16(s);
-            } else if ((j & 1) == 0) {
-                const uint32_t wd = pop16(s);
-                v = wd & 0xFFu;
-                hold = wd >> 8;
-            } else {
-                v = hold;
-            }
-            bits_refill(s, pay32);
-        } else if (kind == 3) {
-            if ((j & 1) == 0) {
-                const uint32_t en = tbl[tb + X];
-                X = (en >> 12) + popn(s, (en >> 8) & 15u);
-                uint32_t v0 = en & 15u, v1 = (en >> 4) & 15u;
-                const uint32_t info = a0 | (use << 16);
-                v0 = a0 + (v0 == 15u ? pair_literal<WIDE>(s, pay32, info, bad) : v0);
-                v1 = a0 + (v1 == 15u ? pair_literal<WIDE>(s, pay32, info, bad) : v1);
-                bits_refill(s, pay32);
-                v = v0;
-                pend = v1;
-            } else {
-                v = pend;
-            }
-        } else if (kind == 4) {
-            v = 0;
-            if (j == next_pos) {
-                v = WIDE ? ld16(r.payload, e.start + 4 + 2 * nnz + 2 * k) : r.payload[e.start + 4 + 2 * nnz + k];
-                if ((int)next_pos <= prev || v == 0) bad = 1;
-                prev = (int)next_pos;
-                k++;
-                next_pos = k < nnz ? ld16(r.payload, e.start + 4 + 2 * k) : 0xFFFFFFFFu;
-                if (k < nnz && (next_pos >= kBlk || (int)next_pos <= prev)) bad = 1;
-            }
-        }
-        if (row >= r0 && row < r1 && col >= c0 && col < c1)
-            region_put<WIDE>(out, out_kind, ((uint64_t)(row - r0) * w + (col - c0)) * r.P + p, v, scale, offset);
-        if (++col == r.scan_cols) {
-            col = 0;
-            row++;
-        }
-    }
-    // end checks
-    if (kind == 1 || kind == 2 || kind == 3) {
-        const uint32_t used = bits_used(s, origin(e.start)), total = 8u * len;
-        if (kind == 1) bad |= x != 65536u || used != total;
-        if (kind == 2) {
-            bad |= used != total;
-            if (!WIDE && (n & 1)) bad |= hold != 0;
-        }
-        if (kind == 3) {
-            bad |= X != 0 || used > total || total - used >= 16;
-            if (!bad && total > used) bad |= popn(s, total - used) != 0;
-        }
-    }
-    if (kind == 4) {
-        bad |= k != nnz;
-        if (!WIDE && (nnz & 1)) bad |= r.payload[e.start + 4 + 3 * nnz] != 0;
-    }
-    if (bad) report(r, b, p);
 }
 
 }  // namespace
@@ -1164,7 +1176,8 @@ hipError_t launch_reduce(const DevResident &r, const uint8_t *mask, int compleme
         const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * n_visited;
         const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, 8ull * cus));
 #define QSC_RANS(W, O) hipLaunchKernelGGL((k_reduce_rans<W, O>), dim3(grid), dim3(kRansWG), 0, st, r, mask, \
-                                          complement, stride, n_visited, tile, out, out64, negate)
+                                          complement, stride, n_visited, tile, out, out64, negate, RegionBlocks{}, \
+                                          RegionArgs{})
         if (op == Op::Sum) {
             if (wide) QSC_RANS(true, Op::Sum); else QSC_RANS(false, Op::Sum);
         } else {
@@ -1177,7 +1190,8 @@ hipError_t launch_reduce(const DevResident &r, const uint8_t *mask, int compleme
         const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * n_visited;
         const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, cus));
 #define QSC_PAIR(W, O) hipLaunchKernelGGL((k_reduce_paired<W, O>), dim3(grid), dim3(kPairWG), 0, st, r, mask, \
-                                          complement, stride, n_visited, tile, out, out64, negate)
+                                          complement, stride, n_visited, tile, out, out64, negate, RegionBlocks{}, \
+                                          RegionArgs{})
         if (op == Op::Sum) {
             if (wide) QSC_PAIR(true, Op::Sum); else QSC_PAIR(false, Op::Sum);
         } else {
@@ -1194,13 +1208,39 @@ hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, 
     return hipGetLastError();
 }
 
-hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, uint32_t r0, uint32_t r1, uint32_t c0,
-                         uint32_t c1, int out_kind, void *out, hipStream_t st) {
-    const dim3 grid((r.P + 255) / 256, blocks.n);
-    if (r.dtype == 2)
-        hipLaunchKernelGGL(k_region<true>, grid, dim3(256), 0, st, r, blocks, r0, r1, c0, c1, out_kind, out);
-    else
-        hipLaunchKernelGGL(k_region<false>, grid, dim3(256), 0, st, r, blocks, r0, r1, c0, c1, out_kind, out);
+hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const RegionArgs &ra, hipStream_t st) {
+    const uint32_t cus = (uint32_t)device_cu_count();
+    const bool wide = r.dtype == 2;
+    if (r.layout == 0) {
+        const uint32_t cands[3] = {4 * kRansWG, 2 * kRansWG, kRansWG};
+        const uint32_t tile = wide ? pick_tile(r.P, blocks.n, 3 * cus, cands, 3)
+                                   : pick_tile(r.P, blocks.n, 3 * cus, cands + 1, 2);
+        const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * blocks.n;
+        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, 8ull * cus));
+        if (wide)
+            hipLaunchKernelGGL((k_reduce_rans<true, Op::Region>), dim3(grid), dim3(kRansWG), 0, st, r, nullptr, 0, 1,
+                               blocks.n, tile, nullptr, 0, 0, blocks, ra);
+        else
+            hipLaunchKernelGGL((k_reduce_rans<false, Op::Region>), dim3(grid), dim3(kRansWG), 0, st, r, nullptr, 0, 1,
+                               blocks.n, tile, nullptr, 0, 0, blocks, ra);
+    } else {
+        const uint32_t cands[2] = {2 * kPairWG, kPairWG};
+        const uint32_t tile = pick_tile(r.P, blocks.n, cus, cands, 2);
+        const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * blocks.n;
+        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, cus));
+        if (wide)
+            hipLaunchKernelGGL((k_reduce_paired<true, Op::Region>), dim3(grid), dim3(kPairWG), 0, st, r, nullptr, 0, 1,
+                               blocks.n, tile, nullptr, 0, 0, blocks, ra);
+        else
+            hipLaunchKernelGGL((k_reduce_paired<false, Op::Region>), dim3(grid), dim3(kPairWG), 0, st, r, nullptr, 0,
+                               1, blocks.n, tile, nullptr, 0, 0, blocks, ra);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_bytes(void *out, uint64_t n, hipStream_t st) {
+    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(2048, (n / 16 + 255) / 256));
+    hipLaunchKernelGGL(k_zero_bytes, dim3(grid), dim3(256), 0, st, reinterpret_cast<uint8_t *>(out), n);
     return hipGetLastError();
 }
 

@@ -21,7 +21,15 @@ struct DevResident {
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };
 
-enum class Op : int { Sum = 0, Moments = 1 };
+enum class Op : int { Sum = 0, Moments = 1, Region = 2 };
+
+// A region read: half-open scan rectangle, output buffer and kind
+// (0 native dtype, 1 float32 code*scale+offset of the scan's region).
+struct RegionArgs {
+    uint32_t r0, r1, c0, c1;
+    int out_kind;
+    void *out;
+};
 
 // Blocks touched by a region read, passed by value to one launch.
 struct RegionBlocks {
@@ -40,8 +48,9 @@ hipError_t launch_reduce(const DevResident &r, const uint8_t *mask, int compleme
 //  CoM from exact moments.
 hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, float *col, hipStream_t st);
 //  decode of a scan rectangle over the listed touched blocks.
-hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, uint32_t r0, uint32_t r1, uint32_t c0,
-                         uint32_t c1, int out_kind, void *out, hipStream_t st);
+hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const RegionArgs &ra, hipStream_t st);
+//  zero n bytes (region outputs of residents with invalid pixels)
+hipError_t launch_zero_bytes(void *out, uint64_t n, hipStream_t st);
 
 int device_cu_count();
 

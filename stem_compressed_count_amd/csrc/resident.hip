@@ -36,6 +36,7 @@ struct qsc_resident {
     bool total_ready = false;
     uint64_t *d_moments = nullptr;
     uint64_t device_bytes = 0;
+    uint32_t n_valid = 0;
     DevResident dev{};
     std::string last_error;
 };
@@ -171,6 +172,7 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     std::vector<uint8_t> valid(g.P(), 1);
     if (host_valid)
         for (uint32_t p = 0; p < g.P(); p++) valid[p] = host_valid[p] ? 1 : 0;
+    for (uint8_t v : valid) res->n_valid += v;
     if ((e = dalloc(res.get(), &res->d_valid, g.P())) != hipSuccess) return bail(e, "valid");
     if ((e = hipMemcpy(res->d_valid, valid.data(), g.P(), hipMemcpyHostToDevice)) != hipSuccess)
         return bail(e, "valid upload");
@@ -286,13 +288,19 @@ qsc_status qsc_decode_region(qsc_resident *res, uint32_t r0, uint32_t r1, uint32
         for (uint64_t b = sa / kBlock; b <= sb / kBlock; b++)
             if (blocks.empty() || blocks.back() < b) blocks.push_back(uint32_t(b));
     }
-    // the touched-block list travels as kernel launches of up to 64 blocks each (no device staging buffer)
+    // invalid pixels read 0: the decode skips them, so clear the output first
     hipError_t e = hipSuccess;
+    if (res->n_valid < g.P()) {
+        const uint64_t elem = out_kind == 1 ? 4 : g.dtype;
+        e = launch_zero_bytes(d_out, uint64_t(r1 - r0) * (c1 - c0) * g.P() * elem, st);
+    }
+    // the touched-block list travels as kernel launches of up to 64 blocks each (no device staging buffer)
+    const RegionArgs ra{r0, r1, c0, c1, out_kind, d_out};
     for (size_t i = 0; i < blocks.size() && e == hipSuccess; i += 64) {
         RegionBlocks rb{};
         rb.n = uint32_t(std::min<size_t>(64, blocks.size() - i));
         for (uint32_t k = 0; k < rb.n; k++) rb.b[k] = blocks[i + k];
-        e = launch_region(res->dev, rb, r0, r1, c0, c1, out_kind, d_out, st);
+        e = launch_region(res->dev, rb, ra, st);
     }
     return finish_query(res, e, st, wait);
 }
