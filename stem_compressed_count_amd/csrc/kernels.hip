@@ -1,22 +1,27 @@
 // Fused ANS decode + virtual-detector reduction kernels for gfx950 (CDNA4).
 //
-// Hot path of the paired-resident page ("Operation pipeline" item 4): a mask
-// becomes a list of selected detector pixels (plan), then every selected
-// stream of every visited 512-scan block is decoded by one lane, with a 64-bit
-// bit reservoir refilled 32 bits at a time from a prefetched dword, decode
-// tables in LDS, and a wavefront transpose-reduce of per-scan partial sums
-// (the page's warp-wide packed reduction per 32 scans, done here on wave64
-// lanes). Streams stored in exact non-entropy forms (constant, sparse) are
-// folded into LDS partials directly instead of stepping through the scans.
-// Outputs are exact integers; the reduction order never matters.
+// Hot path of the paired-resident page ("Operation pipeline", steps 3-4): each
+// workgroup takes one (visited 512-scan block, detector-pixel tile) work item,
+// selects the tile's pixels that the mask and valid_pixels keep (wave ballots
+// into an LDS list), stages the block's decode table in LDS and decodes every
+// selected stream with one lane per stream. A lane keeps a 64-bit bit
+// reservoir refilled 32 bits at a time from a prefetched dword on a
+// wave-uniform cadence, and per-scan partial sums are reduced across the wave
+// by a transpose-reduce (the page's warp-wide packed reduction per 32 scans,
+// done here on 64-lane waves with the gfx950 lane-swap instructions and DPP).
+// Streams stored in exact non-entropy forms (constant, sparse) are folded into
+// LDS partials directly instead of stepping through the scans. Outputs are
+// exact integers; the reduction order never matters.
 //
 // The products follow the optimization-matrix page, "Product Coverage": sparse
 // BF/ADF masks as selected-pixel sums, dense DF as a cached full-detector total
-// minus the complement, and CoM from fused moment sums.
+// minus the complement, CoM from fused moment sums, and region reads that
+// write the decoded values of the requested scans.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -57,39 +62,9 @@ __device__ __forceinline__ uint32_t ld16(const uint8_t *pay, uint64_t off) {
 }
 
 // ------------------------------------------------------------------ bit reservoir
-// Next bits of the stream sit at the bottom of r; n bits are valid. The dword
-// after them is already loaded into pf, so a refill never waits on a fresh load.
-struct Bits {
-    uint64_t r;
-    uint32_t n;
-    uint32_t q;  // dword index of pf in the payload
-    uint32_t pf;
-};
-
-__device__ __forceinline__ void bits_init(Bits &s, const uint32_t *pay32, uint64_t start) {
-    const uint32_t qd = (uint32_t)(start >> 2);
-    const uint32_t d0 = pay32[qd], d1 = pay32[qd + 1];
-    s.r = ((uint64_t)d1 << 32) | d0;
-    s.n = 64;
-    if (start & 2) {
-        s.r >>= 16;
-        s.n = 48;
-    }
-    s.q = qd + 2;
-    s.pf = pay32[s.q];
-}
-
-__device__ __forceinline__ void bits_refill(Bits &s, const uint32_t *pay32) {
-    if (s.n <= 32) {
-        s.r |= (uint64_t)s.pf << s.n;
-        s.n += 32;
-        s.q++;
-        s.pf = pay32[s.q];
-    }
-}
-
-// The same reservoir fed through a buffer resource over one block's payload:
-// 32-bit offsets, one add per refill, and reads past the block return zero.
+// Next bits of the stream sit at the bottom of r; n bits are valid. The stream
+// is read through a buffer resource over one block's payload: 32-bit offsets,
+// one add per refill, and reads past the block return zero.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 // Block base and size are the same in every lane; readfirstlane keeps the
@@ -156,15 +131,6 @@ __device__ __forceinline__ uint32_t touch_stream(Rsrc rs, uint32_t start, uint32
     return s;
 }
 
-// bits consumed since the stream start; org = (start >> 2) << 1 | (start >> 1 & 1)
-__device__ __forceinline__ uint32_t bits_used(const Bits &s, uint32_t org) {
-    return 32u * (s.q - (org >> 1)) - s.n - ((org & 1) ? 16u : 0u);
-}
-
-__device__ __forceinline__ uint32_t origin(uint64_t start) {
-    return (uint32_t)((start >> 2) << 1) | (uint32_t)((start >> 1) & 1);
-}
-
 template <typename B>
 __device__ __forceinline__ uint32_t pop16(B &s) {
     const uint32_t w = (uint32_t)s.r & 0xFFFFu;
@@ -201,12 +167,6 @@ __device__ __forceinline__ uint32_t rans_step(uint32_t &x, B &s, const uint32_t 
 }
 
 // The 16-bit literal after an escape symbol; refills first so it is always there.
-__device__ __forceinline__ uint32_t rans_escape(Bits &s, const uint32_t *pay32, uint32_t &bad) {
-    bits_refill(s, pay32);
-    const uint32_t lit = pop16(s);
-    bad |= lit < 255u;
-    return lit;
-}
 __device__ __forceinline__ uint32_t rans_escape(BBits &s, Rsrc rs, uint32_t &bad) {
     bbits_refill(s, rs);
     const uint32_t lit = pop16(s);
@@ -418,7 +378,7 @@ __device__ __forceinline__ void region_fill(const DevResident &r, uint32_t b, ui
 
 // ------------------------------------------------------------------ byte-rANS tile
 // Per-slot state kept in registers across the 512 steps (kept small: the tile
-// holds up to four slots per lane).
+// holds up to two slots per lane).
 struct RSlot {
     uint32_t x;     // rANS state
     uint32_t hold;  // second byte of a RAW uint8 word
@@ -498,8 +458,14 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         }
     }
 
-    // one step of every slot: values in v[], escapes resolved
-    auto step = [&](bool even, uint32_t (&v)[K]) {
+    // One step of every slot: values in v[], escapes resolved. Three forms of
+    // the same step, chosen once per wave:
+    //  kMixed   some slot is RAW or idle: every slot runs the unified step;
+    //  kEscape  all slots are rANS and the block's table codes symbol 255;
+    //  kPlain   all slots are rANS and no escape can occur.
+    constexpr int kMixed = 0, kEscape = 1, kPlain = 2;
+    auto step = [&](auto form, bool even, uint32_t (&v)[K]) {
+        constexpr int F = decltype(form)::value;
         uint32_t e[K], bias[K];
 #pragma unroll
         for (int k = 0; k < K; k++) {
@@ -515,27 +481,37 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             const uint32_t xn = __umul24(e[k], z.x >> 12) + bias[k];
             const uint32_t sym = e[k] >> 24;
             const uint32_t w = (uint32_t)z.s.r;
-            // a RAW uint8 word covers an even scan and the odd scan after it
-            const bool raw_take = WIDE || even;
-            const bool need = z.raw ? raw_take : xn < 65536u;
+            bool need;
+            if constexpr (F == kMixed) {
+                // a RAW uint8 word covers an even scan and the odd scan after it
+                const bool raw_take = WIDE || even;
+                need = z.raw ? raw_take : xn < 65536u;
+            } else {
+                need = xn < 65536u;
+            }
             z.x = need ? __builtin_amdgcn_perm(xn, w, 0x05040100u) : xn;
             const uint32_t sh = need ? 16u : 0u;
             z.s.r >>= sh;
             z.s.n -= sh;
-            uint32_t rv;
-            if (WIDE) {
-                rv = w & 0xFFFFu;
-            } else if (even) {
-                rv = w & 0xFFu;
-                z.hold = z.raw ? (w >> 8) & 0xFFu : z.hold;
+            if constexpr (F == kMixed) {
+                uint32_t rv;
+                if (WIDE) {
+                    rv = w & 0xFFFFu;
+                } else if (even) {
+                    rv = w & 0xFFu;
+                    z.hold = z.raw ? (w >> 8) & 0xFFu : z.hold;
+                } else {
+                    rv = z.hold;
+                }
+                v[k] = z.raw ? rv : sym;
+                esc[k] = WIDE && !z.raw && sym == 255u;
             } else {
-                rv = z.hold;
+                v[k] = sym;
+                esc[k] = F == kEscape && sym == 255u;
             }
-            v[k] = z.raw ? rv : sym;
-            esc[k] = WIDE && !z.raw && sym == 255u;
             esc_any |= esc[k];
         }
-        if (WIDE && __builtin_amdgcn_ballot_w64(esc_any)) {  // rare: escapes of uint16 streams
+        if (WIDE && F != kPlain && __builtin_amdgcn_ballot_w64(esc_any)) {  // rare: escapes of uint16 streams
 #pragma unroll
             for (int k = 0; k < K; k++)
                 if (esc[k]) v[k] = rans_escape(sl[k].s, rs, bad);
@@ -549,91 +525,113 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         for (int k = 0; k < K; k++) bbits_refill(sl[k].s, rs);
     };
 
-    if constexpr (OP == Op::Region) {
-        // values of scans inside the rectangle go straight to the output
-        constexpr int CH = 16;
-        RegionWalk rw = region_walk(r, b, ra);
-        auto put = [&](const uint32_t (&v)[K]) {
-            if (rw.inside()) {
-                const uint64_t idx = rw.index(r.P);
+    auto run = [&](auto form) {
+        if constexpr (OP == Op::Region) {
+            // values of scans inside the rectangle go straight to the output
+            constexpr int CH = 16;
+            RegionWalk rw = region_walk(r, b, ra);
+            auto put = [&](const uint32_t (&v)[K]) {
+                if (rw.inside()) {
+                    const uint64_t idx = rw.index(r.P);
 #pragma unroll
-                for (int k = 0; k < K; k++)
-                    if (sl[k].live) region_put<WIDE>(ra.out, ra.out_kind, idx + sl[k].p, v[k], rw.scale, rw.offset);
-            }
-            rw.next();
-        };
-        const uint32_t nfull = n / CH;
-        for (uint32_t c = 0; c < nfull; c++) {
+                    for (int k = 0; k < K; k++)
+                        if (sl[k].live) region_put<WIDE>(ra.out, ra.out_kind, idx + sl[k].p, v[k], rw.scale, rw.offset);
+                }
+                rw.next();
+            };
+            const uint32_t nfull = n / CH;
+            for (uint32_t c = 0; c < nfull; c++) {
 #pragma unroll
-            for (int jj = 0; jj < CH; jj++) {
-                uint32_t v[K];
-                step((jj & 1) == 0, v);
-                put(v);
-                if (jj & 1) refill();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        for (uint32_t j = nfull * CH; j < n; j++) {
-            uint32_t v[K];
-            step((j & 1) == 0, v);
-            put(v);
-            if ((j & 1) || j + 1 == n) refill();
-        }
-    } else {
-        constexpr int CH = 16;
-        const uint32_t my = lane_scan<CH>();
-        const bool writer = lane_writes<CH>();
-        const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
-        const uint32_t nfull = n / CH;
-        for (uint32_t c = 0; c < nfull; c++) {
-            uint32_t a0[CH];
-            uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
-    #pragma unroll
-            for (int i = 0; i < CH; i++) {
-                a0[i] = 0;
-                if (OP == Op::Moments) {
-                    ar[i] = 0;
-                    ac[i] = 0;
+                for (int jj = 0; jj < CH; jj++) {
+                    uint32_t v[K];
+                    step(form, (jj & 1) == 0, v);
+                    put(v);
+                    if (jj & 1) refill();
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-    #pragma unroll
-            for (int jj = 0; jj < CH; jj++) {
+            for (uint32_t j = nfull * CH; j < n; j++) {
                 uint32_t v[K];
-                step((jj & 1) == 0, v);  // chunks start at even scans
-    #pragma unroll
-                for (int k = 0; k < K; k++) {
-                    a0[jj] += v[k];
+                step(form, (j & 1) == 0, v);
+                put(v);
+                if ((j & 1) || j + 1 == n) refill();
+            }
+        } else {
+            constexpr int CH = 16;
+            const uint32_t my = lane_scan<CH>();
+            const bool writer = lane_writes<CH>();
+            const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
+            const uint32_t nfull = n / CH;
+            for (uint32_t c = 0; c < nfull; c++) {
+                uint32_t a0[CH];
+                uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+#pragma unroll
+                for (int i = 0; i < CH; i++) {
+                    a0[i] = 0;
                     if (OP == Op::Moments) {
-                        ar[jj] += v[k] * kr[k];
-                        ac[jj] += v[k] * kc[k];
+                        ar[i] = 0;
+                        ac[i] = 0;
                     }
                 }
-                if (jj & 1) refill();
-                // keep the scheduler's interleaving to the K independent slots of one step
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
-        }
-        // ragged end of a final partial block: one scan at a time, reduced per scan
-        for (uint32_t j = nfull * CH; j < n; j++) {
-            uint32_t v[K];
-            step((j & 1) == 0, v);
-            uint32_t t0 = 0, tr = 0, tc = 0;
-    #pragma unroll
-            for (int k = 0; k < K; k++) {
-                t0 += v[k];
-                if (OP == Op::Moments) {
-                    tr += v[k] * kr[k];
-                    tc += v[k] * kc[k];
+#pragma unroll
+                for (int jj = 0; jj < CH; jj++) {
+                    uint32_t v[K];
+                    step(form, (jj & 1) == 0, v);  // chunks start at even scans
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        a0[jj] += v[k];
+                        if (OP == Op::Moments) {
+                            ar[jj] += v[k] * kr[k];
+                            ac[jj] += v[k] * kc[k];
+                        }
+                    }
+                    if (jj & 1) refill();
+                    // keep the scheduler's interleaving to the K independent slots of one step
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+                chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
             }
-            if (t0) atomicAdd(&pt.m0[j], t0);
-            if (OP == Op::Moments) {
-                if (tr) atomicAdd(&pt.mr[j], (unsigned long long)tr);
-                if (tc) atomicAdd(&pt.mc[j], (unsigned long long)tc);
+            // ragged end of a final partial block: one scan at a time, reduced per scan
+            for (uint32_t j = nfull * CH; j < n; j++) {
+                uint32_t v[K];
+                step(form, (j & 1) == 0, v);
+                uint32_t t0 = 0, tr = 0, tc = 0;
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+                    t0 += v[k];
+                    if (OP == Op::Moments) {
+                        tr += v[k] * kr[k];
+                        tc += v[k] * kc[k];
+                    }
+                }
+                if (t0) atomicAdd(&pt.m0[j], t0);
+                if (OP == Op::Moments) {
+                    if (tr) atomicAdd(&pt.mr[j], (unsigned long long)tr);
+                    if (tc) atomicAdd(&pt.mc[j], (unsigned long long)tc);
+                }
+                if ((j & 1) || j + 1 == n) refill();
             }
-            if ((j & 1) || j + 1 == n) refill();
         }
+    };
+
+    // The form is uniform over the wave. An idle slot (x = 0, reads outside the
+    // buffer) decodes the symbol of table slot 0 forever, so the rANS-only forms
+    // can carry it when that symbol is 0 (the smallest coded value is 0).
+    bool raw = false, idle = false;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        raw |= sl[k].live && sl[k].raw;
+        idle |= !sl[k].live;
+    }
+    const bool idle_ok = (tbl[0] >> 24) == 0u;
+    if (__builtin_amdgcn_ballot_w64(raw || (idle && !idle_ok))) {
+        run(std::integral_constant<int, kMixed>{});
+    } else if (WIDE && (tbl[4095] >> 24) == 255u) {
+        // symbols are laid out in increasing order, so the last slot holds the
+        // largest coded symbol: 255 there means escapes can occur
+        run(std::integral_constant<int, kEscape>{});
+    } else {
+        run(std::integral_constant<int, kPlain>{});
     }
     asm volatile("" ::"v"(touched));
     // end checks (FORMAT 2.3-2.4)
@@ -664,14 +662,6 @@ __device__ __forceinline__ uint32_t window_sym(uint32_t v, uint32_t a0, uint32_t
 }
 
 // An escaped count: its literal, returned relative to the model's window base.
-template <bool WIDE>
-__device__ __forceinline__ uint32_t pair_literal(Bits &s, const uint32_t *pay32, uint32_t info, uint32_t &bad) {
-    bits_refill(s, pay32);
-    const uint32_t lit = popn(s, WIDE ? 16u : 8u);
-    const uint32_t a0 = info & 0xFFFFu;
-    bad |= window_sym(lit, a0, info >> 16) != 15u;
-    return lit - a0;
-}
 template <bool WIDE>
 __device__ __forceinline__ uint32_t pair_literal(BBits &s, Rsrc rs, uint32_t info, uint32_t &bad) {
     bbits_refill(s, rs);
@@ -998,14 +988,17 @@ __device__ __forceinline__ uint32_t select_tile(const DevResident &r, const uint
     return total;
 }
 
+// uint16 sums fit four workgroups per CU (36 KB of LDS, 128 VGPRs); moment
+// partials and the uint8 RAW pair logic need three. The extra waves hide
+// latency when few streams are selected.
 template <bool WIDE, Op OP>
-__global__ __launch_bounds__(kRansWG, 3) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
+__global__ __launch_bounds__(kRansWG, (OP == Op::Moments || !WIDE) ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                          void *out, int out64, int negate, RegionBlocks rb,
                                                          RegionArgs ra) {
     __shared__ uint32_t tbl[2 * 4096];
     __shared__ SharedPartials<OP> sp;
-    __shared__ uint16_t sel[4 * kRansWG];
+    __shared__ uint16_t sel[2 * kRansWG];
     __shared__ uint32_t wtot[kRansWG / 64];
     const uint32_t n_tiles = (r.P + tile_px - 1) / tile_px;
     const uint64_t n_work = (uint64_t)n_tiles * n_visited;
@@ -1029,13 +1022,11 @@ __global__ __launch_bounds__(kRansWG, 3) void k_reduce_rans(DevResident r, const
         }
         if (OP != Op::Region) zero_partials<OP>(sp, n);
         __syncthreads();
-        // uint8 tiles hold at most 512 pixels: four uint8 slots per lane do not fit 3 waves per SIMD
-        const uint32_t K = n_sel <= kRansWG ? 1 : n_sel <= 2 * kRansWG ? 2 : 4;
+        // at most two slots per lane: with three decode forms, more do not fit 3 waves per SIMD
+        const uint32_t K = n_sel <= kRansWG ? 1 : 2;
         const uint32_t first = (threadIdx.x >> 6) * 64 * K;
         if (first < n_sel) {  // whole waves without a stream skip the decode
-            if (WIDE && K == 4)
-                rans_tile<4, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra);
-            else if (K == 2)
+            if (K == 2)
                 rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra);
             else
                 rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra);
@@ -1169,10 +1160,10 @@ hipError_t launch_reduce(const DevResident &r, const uint8_t *mask, int compleme
     const uint32_t cus = (uint32_t)device_cu_count();
     const bool wide = r.dtype == 2;
     if (r.layout == 0) {
-        const uint32_t cands[3] = {4 * kRansWG, 2 * kRansWG, kRansWG};
-        // uint8 decodes with at most two slots per lane (register budget), so its tiles stop at 512
-        const uint32_t tile = wide ? pick_tile(r.P, n_visited, 3 * cus, cands, 3)
-                                   : pick_tile(r.P, n_visited, 3 * cus, cands + 1, 2);
+        // balanced for three workgroups per CU: a sparse mask leaves most tiles
+        // of a block empty, and the larger tiles keep more streams per item
+        const uint32_t cands[2] = {2 * kRansWG, kRansWG};
+        const uint32_t tile = pick_tile(r.P, n_visited, 3 * cus, cands, 2);
         const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * n_visited;
         const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, 8ull * cus));
 #define QSC_RANS(W, O) hipLaunchKernelGGL((k_reduce_rans<W, O>), dim3(grid), dim3(kRansWG), 0, st, r, mask, \
@@ -1212,9 +1203,8 @@ hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const
     const uint32_t cus = (uint32_t)device_cu_count();
     const bool wide = r.dtype == 2;
     if (r.layout == 0) {
-        const uint32_t cands[3] = {4 * kRansWG, 2 * kRansWG, kRansWG};
-        const uint32_t tile = wide ? pick_tile(r.P, blocks.n, 3 * cus, cands, 3)
-                                   : pick_tile(r.P, blocks.n, 3 * cus, cands + 1, 2);
+        const uint32_t cands[2] = {2 * kRansWG, kRansWG};
+        const uint32_t tile = pick_tile(r.P, blocks.n, 3 * cus, cands, 2);
         const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * blocks.n;
         const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, 8ull * cus));
         if (wide)
