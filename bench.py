@@ -47,9 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default="scan128_u16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=16)
+    ap.add_argument("--cpu-sample-blocks", type=int, default=32)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (the FETCH_SIZE/WRITE_SIZE calibration kernel)")
     return ap.parse_args()

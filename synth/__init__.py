@@ -1,6 +1,6 @@
 """Seeded synthetic 4D-STEM workloads (input generation only).
 
-The five workloads follow the configurations the method is benchmarked on:
+The five workloads mirror the acquisitions the method is benchmarked on:
 Poisson counts, bright inside a disk that drifts per scan and dim outside it,
 with optional sentinel pixels. This module draws inputs and builds query
 masks; it holds none of the coding or reduction arithmetic, and it is the only
@@ -95,11 +95,11 @@ class Workload:
 
 # The five benchmark workloads (seed = 1000 + index).
 WORKLOADS = {
-    "tiny": Workload("tiny", 16, 16, 64, 64, 1, 2.0, 0.05, 32, 32, 10, 1, 0, 1001, 0),
-    "c2": Workload("c2", 128, 128, 192, 192, 2, 5.0, 0.1, 96, 96, 30, 2, 0, 1002, 0),
-    "c3": Workload("c3", 256, 256, 192, 192, 2, 5.0, 0.1, 96, 96, 30, 2, 1, 1003, 0),
-    "c4": Workload("c4", 512, 512, 192, 192, 1, 0.8, 0.02, 96, 96, 30, 2, 0, 1004, 0),
-    "c5": Workload("c5", 1024, 1024, 192, 192, 2, 5.0, 0.1, 96, 96, 30, 2, 0, 1005, 1),
+    "tiny_u8": Workload("tiny_u8", 16, 16, 64, 64, 1, 2.0, 0.05, 32, 32, 10, 1, 0, 1001, 0),
+    "scan128_u16": Workload("scan128_u16", 128, 128, 192, 192, 2, 5.0, 0.1, 96, 96, 30, 2, 0, 1002, 0),
+    "scan256_u16_sentinel": Workload("scan256_u16_sentinel", 256, 256, 192, 192, 2, 5.0, 0.1, 96, 96, 30, 2, 1, 1003, 0),
+    "scan512_u8_lowdose": Workload("scan512_u8_lowdose", 512, 512, 192, 192, 1, 0.8, 0.02, 96, 96, 30, 2, 0, 1004, 0),
+    "scan1024_u16_paired": Workload("scan1024_u16_paired", 1024, 1024, 192, 192, 2, 5.0, 0.1, 96, 96, 30, 2, 0, 1005, 1),
 }
 
 
@@ -162,9 +162,9 @@ def annulus_mask(det_rows, det_cols, cr, cc, r_in, r_out):
 
 def query_masks(w: Workload):
     """The named masks each workload is queried with."""
-    if w.name == "tiny":
+    if w.name == "tiny_u8":
         return {"bf": disk_mask(64, 64, 32, 32, 8), "adf": annulus_mask(64, 64, 32, 32, 14, 30)}
-    if w.name == "c4":
+    if w.name == "scan512_u8_lowdose":
         return {"bf": disk_mask(192, 192, 96, 96, 53), "adf": annulus_mask(192, 192, 96, 96, 60, 90)}
     bf = disk_mask(w.det_rows, w.det_cols, 96, 96, 30)
     return {"bf": bf, "df": (1 - bf).astype(np.uint8)}

@@ -89,29 +89,29 @@ def random_rects(w, n, seed, size=8):
 
 
 def test_tiny_full_size():
-    w, counts, valid, blob = case("tiny")
+    w, counts, valid, blob = case("tiny_u8")
     masks = synth.query_masks(w)
     check_all_products(w, counts, valid, blob, masks, masks["adf"],
                        [(0, 16, 0, 16), (0, 1, 0, 1), (15, 16, 15, 16), (3, 11, 2, 10)] + random_rects(w, 4, 1))
 
 
-def test_c2_full_size():
-    w, counts, valid, blob = case("c2")
+def test_u16_128x128_full_size():
+    w, counts, valid, blob = case("scan128_u16")
     masks = synth.query_masks(w)
     check_all_products(w, counts, valid, blob, {"bf": masks["bf"]}, masks["df"],
                        [(0, 8, 0, 8), (60, 68, 124, 128)], strides=(1, 3, 4))
 
 
-def test_c3_sentinels_and_valid_pixels():
-    w, counts, valid, blob = case("c3", 40, 256)  # 10240 scans: 20 blocks
+def test_u16_sentinels_and_valid_pixels():
+    w, counts, valid, blob = case("scan256_u16_sentinel", 40, 256)  # 10240 scans: 20 blocks
     assert valid is not None and valid.sum() < w.P
     masks = synth.query_masks(w)
     check_all_products(w, counts, valid, blob, {"bf": masks["bf"], "full": np.ones(w.P, np.uint8)}, masks["df"],
                        [(0, 8, 0, 8), (1, 9, 124, 132), (32, 40, 248, 256)] + random_rects(w, 6, 3))
 
 
-def test_c3_scaled_region_reads():
-    w = synth.WORKLOADS["c3"].with_scans(10, 256)  # 2560 scans: 5 regions
+def test_scaled_region_reads():
+    w = synth.WORKLOADS["scan256_u16_sentinel"].with_scans(10, 256)  # 2560 scans: 5 regions
     x = synth.scaled(w)
     blob = q().encode(x, w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, scaled=True)
     codes = oracle.decode(blob.tobytes())
@@ -133,30 +133,30 @@ def test_c3_scaled_region_reads():
         assert np.array_equal(u(res.masked_sum(bf)), oracle.masked_sum(codes, bf))
 
 
-def test_c4_u8_low_dose():
-    w, counts, valid, blob = case("c4", 48, 512)  # 24576 scans: 48 blocks
+def test_u8_low_dose():
+    w, counts, valid, blob = case("scan512_u8_lowdose", 48, 512)  # 24576 scans: 48 blocks
     masks = synth.query_masks(w)
     check_all_products(w, counts, valid, blob, masks, masks["bf"], [(0, 8, 0, 8), (47, 48, 500, 512)],
                        strides=(1, 4))
 
 
-def test_c4_moving_mask_sweep():
-    w, counts, valid, blob = case("c4", 16, 512)
+def test_u8_moving_mask_sweep():
+    w, counts, valid, blob = case("scan512_u8_lowdose", 16, 512)
     sweep = synth.sweep_masks(w)
     with q().Resident(blob) as res:
         for i, m in enumerate(sweep[::5]):
             assert np.array_equal(u(res.masked_sum(m)), oracle.masked_sum(counts, m)), i
 
 
-def test_c5_paired_layout():
-    w, counts, valid, blob = case("c5", 24, 1024)  # 24576 scans: 48 blocks
+def test_paired_layout():
+    w, counts, valid, blob = case("scan1024_u16_paired", 24, 1024)  # 24576 scans: 48 blocks
     masks = synth.query_masks(w)
     check_all_products(w, counts, valid, blob, {"bf": masks["bf"]}, masks["df"],
                        [(0, 8, 0, 8), (23, 24, 1016, 1024)] + random_rects(w, 3, 7), strides=(1, 4))
 
 
-def test_c5_generator_byte_rans_too():
-    w, counts, valid, blob = case("c5", 8, 1024, 0)
+def test_paired_generator_byte_rans_too():
+    w, counts, valid, blob = case("scan1024_u16_paired", 8, 1024, 0)
     masks = synth.query_masks(w)
     check_all_products(w, counts, valid, blob, {"bf": masks["bf"]}, masks["df"], [(0, 8, 0, 8)], strides=(1, 4))
 
@@ -206,7 +206,7 @@ def test_adversarial_streams(dtype, layout, det):
 
 
 def test_empty_mask_and_determinism():
-    w, counts, valid, blob = case("tiny")
+    w, counts, valid, blob = case("tiny_u8")
     with q().Resident(blob) as res:
         z = u(res.masked_sum(np.zeros(w.P, np.uint8)))
         assert (z == 0).all()
@@ -234,7 +234,7 @@ def corrupt_rans_word(blob):
 
 
 def test_malformed_stream_fails_the_query():
-    w, counts, valid, blob = case("tiny")
+    w, counts, valid, blob = case("tiny_u8")
     bad, p = corrupt_rans_word(blob)
     with pytest.raises(oracle.OracleError):
         oracle.decode(bad)
@@ -259,7 +259,7 @@ def test_malformed_stream_fails_the_query():
 
 
 def test_argument_errors():
-    w, counts, valid, blob = case("tiny")
+    w, counts, valid, blob = case("tiny_u8")
     qq = q()
     with qq.Resident(blob) as res:
         with pytest.raises(ValueError):

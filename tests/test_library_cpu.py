@@ -42,7 +42,7 @@ def test_library_is_gfx950_code():
 
 
 CASES = [
-    ("tiny", 16, 16, 0), ("c2", 4, 128, 0), ("c3", 4, 128, 0), ("c4", 2, 256, 0), ("c4", 3, 301, 0),
+    ("tiny_u8", 16, 16, 0), ("scan128_u16", 4, 128, 0), ("scan256_u16_sentinel", 4, 128, 0), ("scan512_u8_lowdose", 2, 256, 0), ("scan512_u8_lowdose", 3, 301, 0),
 ]
 
 
@@ -58,7 +58,7 @@ def test_encoder_matches_oracle_paired_and_scaled():
     w = synth.Workload("p", 16, 64, 64, 64, 2, 5.0, 0.1, 32, 32, 20, 2, 0, 77, 1)
     c = synth.counts(w)
     assert qsc().encode(c, 16, 64, 64, 64, layout=1).tobytes() == oracle.encode(c, 16, 64, 64, 64, layout=1)
-    x = synth.scaled(synth.WORKLOADS["c3"].with_scans(2, 300))
+    x = synth.scaled(synth.WORKLOADS["scan256_u16_sentinel"].with_scans(2, 300))
     assert qsc().encode(x, 2, 300, 192, 192, scaled=True).tobytes() == oracle.encode(x, 2, 300, 192, 192, scaled=True)
 
 
@@ -76,7 +76,7 @@ def test_encoder_matches_oracle_adversarial(dtype, layout):
 
 
 def test_encoder_streams_in_several_calls():
-    w = synth.WORKLOADS["c2"].with_scans(6, 200)  # 1200 scans: blocks of 512, 512, 176
+    w = synth.WORKLOADS["scan128_u16"].with_scans(6, 200)  # 1200 scans: blocks of 512, 512, 176
     c = synth.counts(w)
     q = qsc()
     enc = q.Encoder(6, 200, 192, 192, dtype=2)
@@ -114,7 +114,7 @@ def create_status(blob):
 
 
 def test_resident_create_rejects_malformed_before_the_device():
-    w = synth.WORKLOADS["tiny"]
+    w = synth.WORKLOADS["tiny_u8"]
     c = synth.counts(w)
     blob = bytearray(oracle.encode(c, 16, 16, 64, 64))
     h = oracle.header(bytes(blob))

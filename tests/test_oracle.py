@@ -125,7 +125,7 @@ def test_pair_model_invariants():
 
 
 def test_rans_table_quantization_invariants():
-    w = synth.WORKLOADS["tiny"]
+    w = synth.WORKLOADS["tiny_u8"]
     c = synth.counts(w)
     blob = oracle.encode(c, 16, 16, 64, 64)
     h = oracle.header(blob)
@@ -139,10 +139,10 @@ def test_rans_table_quantization_invariants():
 
 
 ROUNDTRIP = [
-    ("tiny", 16, 16, 0),
-    ("c2", 8, 64, 0),
-    ("c3", 8, 64, 0),
-    ("c4", 4, 128, 0),
+    ("tiny_u8", 16, 16, 0),
+    ("scan128_u16", 8, 64, 0),
+    ("scan256_u16_sentinel", 8, 64, 0),
+    ("scan512_u8_lowdose", 4, 128, 0),
 ]
 
 
@@ -155,8 +155,8 @@ def test_roundtrip_generators(name, sr, sc, layout):
 
 
 def test_roundtrip_paired_generator():
-    # the C5 generator on a 64 x 64 detector crop keeps the test fast
-    w = synth.WORKLOADS["c5"]
+    # the 1024x1024-scan paired generator on a 64 x 64 detector crop keeps the test fast
+    w = synth.WORKLOADS["scan1024_u16_paired"]
     w = synth.Workload("p", 16, 64, 64, 64, 2, 5.0, 0.1, 32, 32, 20, 2, 0, 77, 1)
     c = synth.counts(w)
     blob = oracle.encode(c, 16, 64, 64, 64, layout=1)
@@ -241,7 +241,7 @@ def test_mode_choice_rans():
 
 
 def test_malformed_streams_are_rejected():
-    w = synth.WORKLOADS["tiny"]
+    w = synth.WORKLOADS["tiny_u8"]
     c = synth.counts(w)
     blob = bytearray(oracle.encode(c, 16, 16, 64, 64))
     h = oracle.header(bytes(blob))
@@ -270,7 +270,7 @@ def test_malformed_streams_are_rejected():
 # ---------------------------------------------------------------------------
 
 def test_masked_sum_matches_brute_force():
-    w = synth.WORKLOADS["tiny"]
+    w = synth.WORKLOADS["tiny_u8"]
     c = synth.counts(w)
     for name, m in synth.query_masks(w).items():
         assert np.array_equal(oracle.masked_sum(c, m), oracle.brute_masked_sum(c, m)), name
@@ -302,7 +302,7 @@ def test_uint64_closed_form():
 
 
 def test_dense_df_invariants():
-    w = synth.WORKLOADS["c3"].with_scans(2, 256)
+    w = synth.WORKLOADS["scan256_u16_sentinel"].with_scans(2, 256)
     c = synth.counts(w)
     valid = synth.valid_pixels(w)
     bf = synth.query_masks(w)["bf"]
@@ -340,7 +340,7 @@ def test_com_closed_forms():
 
 
 def test_com_matches_brute_force():
-    w = synth.WORKLOADS["tiny"]
+    w = synth.WORKLOADS["tiny_u8"]
     c = synth.counts(w)
     bf = synth.query_masks(w)["bf"]
     for m in (None, bf):
@@ -350,7 +350,7 @@ def test_com_matches_brute_force():
 
 
 def test_region_definition():
-    w = synth.WORKLOADS["c3"].with_scans(4, 16)
+    w = synth.WORKLOADS["scan256_u16_sentinel"].with_scans(4, 16)
     c = synth.counts(w)
     valid = synth.valid_pixels(w)
     out = oracle.region(c, 16, 1, 3, 5, 9, valid)
@@ -397,7 +397,7 @@ def test_reconstruction_matches_numpy_float64():
 
 
 def test_scaled_roundtrip_and_error_bound():
-    w = synth.WORKLOADS["c3"].with_scans(4, 200)  # 800 scans: one full and one partial region
+    w = synth.WORKLOADS["scan256_u16_sentinel"].with_scans(4, 200)  # 800 scans: one full and one partial region
     x = synth.scaled(w)
     blob = oracle.encode(x, 4, 200, w.det_rows, w.det_cols, scaled=True)
     codes = oracle.decode(blob)
@@ -421,4 +421,4 @@ def test_workload_masks_match_the_pages():
     assert synth.disk_mask(64, 64, 32, 32, 8).sum() == 197
     assert synth.annulus_mask(64, 64, 32, 32, 14, 30).sum() == 2212
     assert synth.annulus_mask(192, 192, 96, 96, 60, 90).sum() == 14168
-    assert len(synth.sweep_masks(synth.WORKLOADS["c4"])) == 64
+    assert len(synth.sweep_masks(synth.WORKLOADS["scan512_u8_lowdose"])) == 64
