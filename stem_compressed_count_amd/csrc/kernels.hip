@@ -585,6 +585,9 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                             ac[jj] += v[k] * kc[k];
                         }
                     }
+                    // materialise the sums here: deferring them to the chunk end keeps every step's table entry live
+                    asm volatile("" : "+v"(a0[jj]));
+                    if constexpr (OP == Op::Moments) asm volatile("" : "+v"(ar[jj]), "+v"(ac[jj]));
                     if (jj & 1) refill();
                     // keep the scheduler's interleaving to the K independent slots of one step
                     __builtin_amdgcn_sched_barrier(0);
@@ -988,11 +991,11 @@ __device__ __forceinline__ uint32_t select_tile(const DevResident &r, const uint
     return total;
 }
 
-// uint16 sums fit four workgroups per CU (36 KB of LDS, 128 VGPRs); moment
-// partials and the uint8 RAW pair logic need three. The extra waves hide
-// latency when few streams are selected.
+// Sums fit four workgroups per CU (36 KB of LDS, at most 128 VGPRs); the
+// moment partials (44 KB of LDS) fit three. The extra waves hide latency when
+// few streams are selected.
 template <bool WIDE, Op OP>
-__global__ __launch_bounds__(kRansWG, (OP == Op::Moments || !WIDE) ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
+__global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                          void *out, int out64, int negate, RegionBlocks rb,
                                                          RegionArgs ra) {
