@@ -152,7 +152,8 @@ void build_pair_tables(uint32_t *out) {
             const uint32_t y = next[i]++;
             const uint32_t nb = 10 - (31 - __builtin_clz(y));
             const uint32_t newX = (y << nb) - kTansL;
-            out[m * kTansL + X] = (i >> 4) | ((i & 15) << 4) | (nb << 8) | (newX << 12);
+            const uint32_t a = i >> 4, b = i & 15;
+            out[m * kTansL + X] = a | (b << 8) | (nb << 16) | (newX << 20) | ((a == 15 || b == 15) ? 1u << 31 : 0u);
         }
     }
 }

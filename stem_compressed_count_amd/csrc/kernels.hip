@@ -147,25 +147,6 @@ __device__ __forceinline__ uint32_t popn(B &s, uint32_t nb) {
     return v;
 }
 
-// byte-rANS decode of one value (FORMAT 2.3). The table has two planes of
-// 4096 entries: f | symbol << 24 (v_mad_u32_u24 reads only the low 24 bits, so
-// the symbol rides along) and slot - c[symbol]. Consumes at most one 16-bit
-// renormalisation word; an escape (symbol 255 of a uint16 stream) is resolved
-// by rans_escape.
-template <typename B>
-__device__ __forceinline__ uint32_t rans_step(uint32_t &x, B &s, const uint32_t *tbl) {
-    const uint32_t slot = x & 4095u;
-    const uint32_t e = tbl[slot], bias = tbl[slot + 4096];
-    const uint32_t xn = __umul24(e, x >> 12) + bias;
-    const bool need = xn < 65536u;
-    // (xn << 16) | low word of the reservoir, as one byte permute
-    x = need ? __builtin_amdgcn_perm(xn, (uint32_t)s.r, 0x05040100u) : xn;
-    const uint32_t sh = need ? 16u : 0u;
-    s.r >>= sh;
-    s.n -= sh;
-    return e >> 24;
-}
-
 // The 16-bit literal after an escape symbol; refills first so it is always there.
 __device__ __forceinline__ uint32_t rans_escape(BBits &s, Rsrc rs, uint32_t &bad) {
     bbits_refill(s, rs);
@@ -458,6 +439,12 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         }
     }
 
+    // byte-rANS decode step (FORMAT 2.3). The block table has two planes of 4096
+    // entries, read together by one ds_read2st64: f | symbol << 24
+    // (v_mad_u32_u24 reads only the low 24 bits, so the symbol rides along) and
+    // slot - c[symbol]. A renormalisation appends the next 16-bit word with one
+    // byte permute; an escape (symbol 255 of a uint16 stream) reads its literal.
+    //
     // One step of every slot: values in v[], escapes resolved. Three forms of
     // the same step, chosen once per wave:
     //  kMixed   some slot is RAW or idle: every slot runs the unified step;
@@ -653,11 +640,29 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
 struct PSlot {
     uint32_t X;     // tANS state
     uint32_t meta;  // mode (3 PAIRED, 4 RAW, 7 idle) | model << 3
+    uint32_t tb;    // LDS index of the slot's decode table (the idle entry unless PAIRED)
+    uint32_t a0;    // window base of the slot's model (0 unless PAIRED)
     uint32_t p;
     uint32_t org;  // stream start within the block payload
     uint32_t len;
     BBits s;
 };
+
+// Paired decode-table entry: window values a, b (15 = escape) in bytes 0 and 1,
+// code length in bits 16-19, next-state base in bits 20-29, bit 31 set when
+// either value escapes.
+__device__ __forceinline__ uint32_t pe_a(uint32_t e) { return e & 0xFFu; }
+__device__ __forceinline__ uint32_t pe_b(uint32_t e) { return __builtin_amdgcn_ubfe(e, 8, 8); }
+__device__ __forceinline__ uint32_t pe_nbits(uint32_t e) { return __builtin_amdgcn_ubfe(e, 16, 4); }
+__device__ __forceinline__ uint32_t pe_next(uint32_t e) { return __builtin_amdgcn_ubfe(e, 20, 10); }
+
+// Reads nb (< 32) bits from the reservoir.
+__device__ __forceinline__ uint32_t take_bits(BBits &s, uint32_t nb) {
+    const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)s.r, 0, nb);
+    s.r >>= nb;
+    s.n -= nb;
+    return v;
+}
 
 __device__ __forceinline__ uint32_t window_sym(uint32_t v, uint32_t a0, uint32_t use) {
     const uint32_t d = v - a0;
@@ -691,6 +696,13 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         z.meta = 7;
         z.X = 0;
         z.p = 0;
+        z.tb = 32u << 10;  // the idle entry after the 32 model tables
+        z.a0 = 0;
+        // an idle slot reads outside the buffer range (zeros) and consumes no bits
+        z.s.r = 0;
+        z.s.n = 64;
+        z.s.off = 0x80000000u;
+        z.s.pf = 0;
         const uint32_t i = first + k * 64 + lane;
         if (i >= n_sel) continue;
         z.p = p0 + sel[i];
@@ -755,6 +767,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         if (mode == 3) {
             const uint32_t a0 = r.model_info[(hdr >> 3) & 31u] & 0xFFFFu;
             z.X = popn(z.s, 10);
+            z.tb = ((hdr >> 3) & 31u) << 10;
+            z.a0 = a0;
             base0 += a0;
             baseR += a0 * kr;
             baseC += a0 * kc;
@@ -770,10 +784,45 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         }
     }
 
-    if constexpr (OP == Op::Region) {
-        RegionWalk rw = region_walk(r, b, ra);
-        for (uint32_t t = 0; t < kBlk / 2; t++) {
-            uint32_t v0[K], v1[K];
+    // One pair step of every slot: window-relative values for PAIRED slots,
+    // absolute values for RAW slots, zeros for idle ones. Two forms, chosen
+    // once per wave: kPMixed when some slot is RAW (per-slot branches), kPPlain
+    // otherwise (every slot, idle ones included, runs the same table step).
+    constexpr int kPMixed = 0, kPPlain = 1;
+    auto step = [&](auto form, uint32_t t, uint32_t (&v0)[K], uint32_t (&v1)[K]) {
+        constexpr int F = decltype(form)::value;
+        if constexpr (F == kPPlain) {
+            uint32_t e[K];
+#pragma unroll
+            for (int k = 0; k < K; k++) e[k] = tbl[sl[k].tb + sl[k].X];
+            bool esc_any = false;
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                PSlot &z = sl[k];
+                z.X = pe_next(e[k]) + take_bits(z.s, pe_nbits(e[k]));
+                v0[k] = pe_a(e[k]);
+                v1[k] = pe_b(e[k]);
+                esc_any |= (int32_t)e[k] < 0;
+            }
+            if (__builtin_amdgcn_ballot_w64(esc_any)) {  // values outside the model window
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+                    if ((int32_t)e[k] < 0) {
+                        PSlot &z = sl[k];
+                        const uint32_t info = r.model_info[z.meta >> 3];
+                        if (v0[k] == 15u) v0[k] = pair_literal<WIDE>(z.s, rs, info, bad);
+                        if (v1[k] == 15u) v1[k] = pair_literal<WIDE>(z.s, rs, info, bad);
+                        bbits_refill(z.s, rs);  // keep 32+ bits until the next cadence point
+                    }
+                }
+            }
+            // codes are at most 10 bits: one 32-bit refill per three pairs, on a
+            // wave-uniform cadence (the paired-resident page's refill rhythm)
+            if (t % 3 == 2) {
+#pragma unroll
+                for (int k = 0; k < K; k++) bbits_refill(sl[k].s, rs);
+            }
+        } else {
 #pragma unroll
             for (int k = 0; k < K; k++) {
                 PSlot &z = sl[k];
@@ -781,16 +830,17 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 v0[k] = 0;
                 v1[k] = 0;
                 if (mode == 3) {
-                    const uint32_t e = tbl[((z.meta >> 3) << 10) + z.X];
-                    z.X = (e >> 12) + popn(z.s, (e >> 8) & 15u);
-                    const uint32_t info = r.model_info[z.meta >> 3];
-                    const uint32_t a0 = info & 0xFFFFu;
-                    uint32_t w0 = e & 15u, w1 = (e >> 4) & 15u;
-                    if (w0 == 15u) w0 = pair_literal<WIDE>(z.s, rs, info, bad);
-                    if (w1 == 15u) w1 = pair_literal<WIDE>(z.s, rs, info, bad);
-                    v0[k] = a0 + w0;
-                    v1[k] = a0 + w1;
-                    bbits_refill(z.s, rs);
+                    const uint32_t e = tbl[z.tb + z.X];
+                    z.X = pe_next(e) + take_bits(z.s, pe_nbits(e));
+                    v0[k] = pe_a(e);
+                    v1[k] = pe_b(e);
+                    if ((int32_t)e < 0) {
+                        const uint32_t info = r.model_info[z.meta >> 3];
+                        if (v0[k] == 15u) v0[k] = pair_literal<WIDE>(z.s, rs, info, bad);
+                        if (v1[k] == 15u) v1[k] = pair_literal<WIDE>(z.s, rs, info, bad);
+                        bbits_refill(z.s, rs);
+                    }
+                    if (t % 3 == 2) bbits_refill(z.s, rs);
                 } else if (mode == 4) {
                     if (WIDE) {
                         v0[k] = pop16(z.s);
@@ -804,87 +854,80 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     bbits_refill(z.s, rs);
                 }
             }
+        }
+    };
+
+    auto run = [&](auto form) {
+        if constexpr (OP == Op::Region) {
+            RegionWalk rw = region_walk(r, b, ra);
+            for (uint32_t t = 0; t < kBlk / 2; t++) {
+                uint32_t v0[K], v1[K];
+                step(form, t, v0, v1);
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
-                if (rw.inside()) {
-                    const uint64_t idx = rw.index(r.P);
+                for (int h = 0; h < 2; h++) {
+                    if (rw.inside()) {
+                        const uint64_t idx = rw.index(r.P);
+#pragma unroll
+                        for (int k = 0; k < K; k++) {
+                            const uint32_t mode = sl[k].meta & 7u;
+                            if (mode == 3 || mode == 4)
+                                region_put<WIDE>(ra.out, ra.out_kind, idx + sl[k].p, sl[k].a0 + (h ? v1[k] : v0[k]),
+                                                 rw.scale, rw.offset);
+                        }
+                    }
+                    rw.next();
+                }
+            }
+        } else {
+            // paired workgroups have 128 VGPRs per lane: moments reduce every 8 scans
+            constexpr int CH = OP == Op::Moments ? 8 : 16;
+            const uint32_t my = lane_scan<CH>();
+            const bool writer = lane_writes<CH>();
+            const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
+            for (uint32_t c = 0; c < kBlk / CH; c++) {
+                uint32_t a0[CH];
+                uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+#pragma unroll
+                for (int i = 0; i < CH; i++) {
+                    a0[i] = base0;
+                    if (OP == Op::Moments) {
+                        ar[i] = baseR;
+                        ac[i] = baseC;
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < CH / 2; tt++) {
+                    uint32_t v0[K], v1[K];
+                    step(form, c * (CH / 2) + tt, v0, v1);
 #pragma unroll
                     for (int k = 0; k < K; k++) {
-                        const uint32_t mode = sl[k].meta & 7u;
-                        if (mode == 3 || mode == 4)
-                            region_put<WIDE>(ra.out, ra.out_kind, idx + sl[k].p, h ? v1[k] : v0[k], rw.scale,
-                                             rw.offset);
+                        a0[2 * tt] += v0[k];
+                        a0[2 * tt + 1] += v1[k];
+                        if (OP == Op::Moments) {
+                            ar[2 * tt] += v0[k] * kr[k];
+                            ar[2 * tt + 1] += v1[k] * kr[k];
+                            ac[2 * tt] += v0[k] * kc[k];
+                            ac[2 * tt + 1] += v1[k] * kc[k];
+                        }
                     }
+                    // materialise the sums here (see the byte-rANS tile)
+                    asm volatile("" : "+v"(a0[2 * tt]), "+v"(a0[2 * tt + 1]));
+                    if constexpr (OP == Op::Moments)
+                        asm volatile("" : "+v"(ar[2 * tt]), "+v"(ar[2 * tt + 1]), "+v"(ac[2 * tt]), "+v"(ac[2 * tt + 1]));
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                rw.next();
+                chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
             }
         }
-    } else {
-        constexpr int CH = 16;  // paired workgroups have 128 VGPRs per lane
-        const uint32_t my = lane_scan<CH>();
-        const bool writer = lane_writes<CH>();
-        const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
-        for (uint32_t c = 0; c < kBlk / CH; c++) {
-            uint32_t a0[CH];
-            uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
-    #pragma unroll
-            for (int i = 0; i < CH; i++) {
-                a0[i] = base0;
-                if (OP == Op::Moments) {
-                    ar[i] = baseR;
-                    ac[i] = baseC;
-                }
-            }
-    #pragma unroll
-            for (int tt = 0; tt < CH / 2; tt++) {
-                const uint32_t t = c * (CH / 2) + tt;  // pair index within the block
-    #pragma unroll
-                for (int k = 0; k < K; k++) {
-                    PSlot &z = sl[k];
-                    const uint32_t mode = z.meta & 7u;
-                    uint32_t v0 = 0, v1 = 0;
-                    if (mode == 3) {
-                        const uint32_t e = tbl[((z.meta >> 3) << 10) + z.X];
-                        z.X = (e >> 12) + popn(z.s, (e >> 8) & 15u);
-                        v0 = e & 15u;
-                        v1 = (e >> 4) & 15u;
-                        const bool esc = v0 == 15u || v1 == 15u;
-                        if (__builtin_amdgcn_ballot_w64(esc)) {
-                            if (esc) {
-                                const uint32_t info = r.model_info[z.meta >> 3];
-                                if (v0 == 15u) v0 = pair_literal<WIDE>(z.s, rs, info, bad);
-                                if (v1 == 15u) v1 = pair_literal<WIDE>(z.s, rs, info, bad);
-                                bbits_refill(z.s, rs);  // keep 32+ bits until the next cadence point
-                            }
-                        }
-                        // codes are at most 10 bits: one 32-bit refill per three pairs, on a
-                        // wave-uniform cadence (the paired-resident page's refill rhythm)
-                        if (t % 3 == 2) bbits_refill(z.s, rs);
-                    } else if (mode == 4) {
-                        if (WIDE) {
-                            v0 = pop16(z.s);
-                            bbits_refill(z.s, rs);
-                            v1 = pop16(z.s);
-                        } else {
-                            const uint32_t w = pop16(z.s);
-                            v0 = w & 0xFFu;
-                            v1 = w >> 8;
-                        }
-                        bbits_refill(z.s, rs);
-                    }
-                    a0[2 * tt] += v0;
-                    a0[2 * tt + 1] += v1;
-                    if (OP == Op::Moments) {
-                        ar[2 * tt] += v0 * kr[k];
-                        ar[2 * tt + 1] += v1 * kr[k];
-                        ac[2 * tt] += v0 * kc[k];
-                        ac[2 * tt + 1] += v1 * kc[k];
-                    }
-                }
-            }
-            chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
-        }
-    }
+    };
+
+    bool raw = false;
+#pragma unroll
+    for (int k = 0; k < K; k++) raw |= (sl[k].meta & 7u) == 4u;
+    if (__builtin_amdgcn_ballot_w64(raw))
+        run(std::integral_constant<int, kPMixed>{});
+    else
+        run(std::integral_constant<int, kPPlain>{});
     asm volatile("" ::"v"(touched));
     // end checks (FORMAT 3.3-3.4)
 #pragma unroll
@@ -1044,14 +1087,14 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
                                                            uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                            void *out, int out64, int negate, RegionBlocks rb,
                                                            RegionArgs ra) {
-    __shared__ uint32_t tbl[32 * 1024];
+    __shared__ uint32_t tbl[kPairTable];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kPairWG];
     __shared__ uint32_t wtot[kPairWG / 64];
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(r.tables);
         uint4 *dst = reinterpret_cast<uint4 *>(tbl);
-        for (uint32_t i = threadIdx.x; i < 32 * 1024 / 4; i += kPairWG) dst[i] = src[i];
+        for (uint32_t i = threadIdx.x; i < kPairTable / 4; i += kPairWG) dst[i] = src[i];
     }
     const uint32_t n_tiles = (r.P + tile_px - 1) / tile_px;
     const uint64_t n_work = (uint64_t)n_tiles * n_visited;

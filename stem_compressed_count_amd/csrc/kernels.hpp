@@ -6,13 +6,17 @@
 
 namespace qsc {
 
+// Paired decode tables on the device: 32 models x 1024 states, then one idle
+// entry (values 0, no bits, next state 0) padded to 16 bytes.
+constexpr uint32_t kPairTable = 32 * 1024 + 4;
+
 // Device view of a resident (all pointers are device memory).
 struct DevResident {
     const uint8_t *payload;  // stream bytes, followed by zero padding
     const uint8_t *dir;      // n_blocks x {u64 base, u32 n_scans, u32 nbytes}
     const uint32_t *gbase;   // n_blocks x G
     const uint16_t *rel;     // n_blocks x G x 32
-    const uint32_t *tables;  // byte-rANS: n_blocks x 2 x 4096 entries; paired: 32 x 1024 entries
+    const uint32_t *tables;  // byte-rANS: n_blocks x 2 x 4096 entries; paired: kPairTable entries
     const uint32_t *model_info; // paired: per model a0 | in_use << 16
     const uint8_t *valid;    // P bytes, nonzero = valid
     const double *calib;     // scaled: n_blocks x {scale, offset}

@@ -66,7 +66,7 @@ const PairModels &pair_models();
 
 // Device decode-table entries.
 //  byte-rANS (per block, two planes of 4096 entries): f | symbol << 24, then slot - c
-//  paired (per model, 1024 entries): a | b << 4 | nbits << 8 | newX << 12
+//  paired (per model, 1024 entries): a | b << 8 | nbits << 16 | newX << 20 | escape << 31
 void build_rans_table(const uint16_t *freq, uint32_t *out8192);
 void build_pair_tables(uint32_t *out /* 32 x 1024 */);
 

@@ -158,7 +158,7 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
             build_rans_table(f, tables.data() + 2 * kRansM * b);
         }
     } else {
-        tables.resize(kModels * kTansL);
+        tables.assign(kPairTable, 0);  // the idle entry stays 0
         build_pair_tables(tables.data());
         const PairModels &pm = pair_models();
         for (uint32_t m = 0; m < kModels; m++) info[m] = pm.a0[m] | (pm.in_use[m] << 16);
