@@ -23,7 +23,9 @@
  *  - Argument errors are detected on the host before anything is enqueued and
  *    leave outputs untouched.
  *  - Calls that enqueue work on the same resident must not run concurrently
- *    from several host threads (they share the resident's scratch buffers).
+ *    from several host threads, and the queries of one resident must run in
+ *    order on the device: issue them on one stream, or order the streams. They
+ *    share the resident's total and moment caches and its work-claim counter.
  */
 #ifndef QSC_H
 #define QSC_H

@@ -21,7 +21,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #include "kernels.hpp"
 
@@ -950,6 +952,91 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     }
 }
 
+// ------------------------------------------------------------------ query plan
+// The init kernel counts the selected pixels of every fine pixel tile. Each
+// reduce workgroup then reads the counts, picks the work-item size (one or two
+// fine tiles), and lists the non-empty items in LDS by ballot compaction, so
+// no work item is spent on pixels the mask misses.
+//
+// Item size: a sparse mask leaves items latency-bound (their streams decode
+// side by side, whatever their number), a dense one makes them throughput-bound
+// (cost grows with the streams per item). The estimate is rounds of the
+// resident workgroups times max(1, selected per item / fine tile).
+struct Plan {
+    uint32_t n_items;  // non-empty items per visited block
+    uint32_t mult;     // fine tiles per item
+};
+
+template <int WG>
+__device__ __forceinline__ Plan plan_items(const uint32_t *counts, uint32_t n_fine, uint32_t fine_px, uint32_t n_visited,
+                                           uint16_t *list, uint32_t *wtot) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    // totals: selected pixels, non-empty single and paired fine tiles
+    uint32_t sel = 0, live1 = 0, live2 = 0;
+    for (uint32_t t = tid; t < n_fine; t += WG) {
+        const uint32_t c = counts[t];
+        sel += c;
+        live1 += c != 0;
+        if ((t & 1u) == 0) live2 += (c + (t + 1 < n_fine ? counts[t + 1] : 0u)) != 0;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        sel += __shfl_xor(sel, off);
+        live1 += __shfl_xor(live1, off);
+        live2 += __shfl_xor(live2, off);
+    }
+    __shared__ uint32_t part[3][WG / 64];
+    if (lane == 0) {
+        part[0][wave] = sel;
+        part[1][wave] = live1;
+        part[2][wave] = live2;
+    }
+    __syncthreads();
+    sel = live1 = live2 = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < WG / 64; w++) {
+        sel += part[0][w];
+        live1 += part[1][w];
+        live2 += part[2][w];
+    }
+    const double slots = gridDim.x;
+    auto cost = [&](uint32_t live, uint32_t mult) {
+        if (!live) return 0.0;
+        const double rounds = ceil((double)live * n_visited / slots);
+        return rounds * fmax(1.0, (double)sel / live / fine_px);
+    };
+    // on a tie, dense items prefer two slots per lane (more independent work per
+    // wave), sparse ones more workgroups
+    const double c1 = cost(live1, 1), c2 = cost(live2, 2);
+    const bool dense = live1 && (double)sel / live1 > 0.5 * fine_px;
+    const uint32_t mult = (c2 < c1 || (c2 == c1 && dense)) ? 2u : 1u;
+    const uint32_t n_items = (n_fine + mult - 1) / mult;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    uint32_t total = 0;
+    for (uint32_t base = 0; base < n_items; base += WG) {
+        const uint32_t it = base + tid;
+        bool f = false;
+        if (it < n_items) {
+            const uint32_t t = it * mult;
+            f = counts[t] != 0 || (mult == 2 && t + 1 < n_fine && counts[t + 1] != 0);
+        }
+        const unsigned long long bal = __ballot(f);
+        if (lane == 0) wtot[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t before = total, all = total;
+#pragma unroll
+        for (uint32_t w = 0; w < WG / 64; w++) {
+            const uint32_t c = wtot[w];
+            before += w < wave ? c : 0u;
+            all += c;
+        }
+        if (f) list[before + (uint32_t)__popcll(bal & below)] = (uint16_t)it;
+        __syncthreads();
+        total = all;
+    }
+    return Plan{total, mult};
+}
+
 // ------------------------------------------------------------------ reduce kernels
 template <Op OP>
 struct SharedPartials {
@@ -1040,18 +1127,25 @@ __device__ __forceinline__ uint32_t select_tile(const DevResident &r, const uint
 template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
-                                                         void *out, int out64, int negate, RegionBlocks rb,
-                                                         RegionArgs ra) {
+                                                         const uint32_t *plan, void *out, int out64, int negate,
+                                                         RegionBlocks rb, RegionArgs ra) {
     __shared__ uint32_t tbl[2 * 4096];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kRansWG];
     __shared__ uint32_t wtot[kRansWG / 64];
-    const uint32_t n_tiles = (r.P + tile_px - 1) / tile_px;
-    const uint64_t n_work = (uint64_t)n_tiles * n_visited;
+    __shared__ uint16_t tiles[kMaxPlanTiles];
+    // with a plan, tile_px is the fine tile the counts were taken over
+    uint32_t n_live = (r.P + tile_px - 1) / tile_px;
+    if (plan) {
+        const Plan pl = plan_items<kRansWG>(plan, n_live, tile_px, n_visited, tiles, wtot);
+        n_live = pl.n_items;
+        tile_px *= pl.mult;
+    }
+    const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     uint32_t loaded = 0xFFFFFFFFu;
-    for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-        const uint32_t vb = (uint32_t)(w / n_tiles), t = (uint32_t)(w % n_tiles);
+    for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
+        const uint32_t vb = w / n_live, t = plan ? tiles[w % n_live] : w % n_live;
         const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = t * tile_px;
         __syncthreads();
         const uint32_t n_sel = select_tile<kRansWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
@@ -1085,8 +1179,8 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
 template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const uint8_t *mask, int complement,
                                                            uint32_t stride, uint32_t n_visited, uint32_t tile_px,
-                                                           void *out, int out64, int negate, RegionBlocks rb,
-                                                           RegionArgs ra) {
+                                                           const uint32_t *plan, void *out, int out64, int negate,
+                                                           RegionBlocks rb, RegionArgs ra) {
     __shared__ uint32_t tbl[kPairTable];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kPairWG];
@@ -1096,11 +1190,18 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
         uint4 *dst = reinterpret_cast<uint4 *>(tbl);
         for (uint32_t i = threadIdx.x; i < kPairTable / 4; i += kPairWG) dst[i] = src[i];
     }
-    const uint32_t n_tiles = (r.P + tile_px - 1) / tile_px;
-    const uint64_t n_work = (uint64_t)n_tiles * n_visited;
+    __shared__ uint16_t tiles[kMaxPlanTiles];
+    // with a plan, tile_px is the fine tile the counts were taken over
+    uint32_t n_live = (r.P + tile_px - 1) / tile_px;
+    if (plan) {
+        const Plan pl = plan_items<kPairWG>(plan, n_live, tile_px, n_visited, tiles, wtot);
+        n_live = pl.n_items;
+        tile_px *= pl.mult;
+    }
+    const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
-    for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-        const uint32_t vb = (uint32_t)(w / n_tiles), t = (uint32_t)(w % n_tiles);
+    for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
+        const uint32_t vb = w / n_live, t = plan ? tiles[w % n_live] : w % n_live;
         const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = t * tile_px;
         __syncthreads();
         const uint32_t n_sel = select_tile<kPairWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
@@ -1124,13 +1225,37 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     }
 }
 
-// out[i] = init[i], or 0 without init (u32 or u64 elements)
-__global__ void k_init(void *out, int out64, const void *init, uint64_t n) {
+// out[i] = init[i], or 0 without init (u32 or u64 elements); with a plan,
+// workgroup t also counts the selected pixels of pixel tile t.
+struct PlanArgs {
+    const uint8_t *mask;
+    const uint8_t *valid;
+    int complement;
+    uint32_t P, tile_px, n_tiles;
+    uint32_t *counts;  // null: no plan
+};
+
+__global__ void __launch_bounds__(256) k_init(void *out, int out64, const void *init, uint64_t n, PlanArgs pa) {
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
         if (out64)
             reinterpret_cast<uint64_t *>(out)[i] = init ? reinterpret_cast<const uint64_t *>(init)[i] : 0;
         else
             reinterpret_cast<uint32_t *>(out)[i] = init ? reinterpret_cast<const uint32_t *>(init)[i] : 0;
+    }
+    if (!pa.counts) return;
+    __shared__ uint32_t wsum[4];
+    for (uint32_t t = blockIdx.x; t < pa.n_tiles; t += gridDim.x) {
+        const uint32_t p0 = t * pa.tile_px, p1 = min(p0 + pa.tile_px, pa.P);
+        uint32_t c = 0;
+        for (uint32_t p = p0 + threadIdx.x; p < p1; p += blockDim.x)
+            c += pa.valid[p] != 0 && (pa.mask ? ((pa.mask[p] != 0) != (pa.complement != 0)) : true);
+        // the tile's count: a wave sum, then the four waves
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+        if ((threadIdx.x & 63u) == 0) wsum[threadIdx.x >> 6] = c;
+        __syncthreads();
+        if (threadIdx.x == 0) pa.counts[t] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
     }
 }
 
@@ -1176,12 +1301,6 @@ int device_cu_count() {
     return cus;
 }
 
-hipError_t launch_init(void *out, int out64, const void *init, uint64_t n, hipStream_t st) {
-    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(2048, (n + 255) / 256));
-    hipLaunchKernelGGL(k_init, dim3(grid), dim3(256), 0, st, out, out64, init, n);
-    return hipGetLastError();
-}
-
 // Pixel-tile size: the largest tile whose count of (block, tile) items fills
 // the resident workgroup slots in whole rounds.
 static uint32_t pick_tile(uint32_t P, uint32_t n_visited, uint32_t slots, const uint32_t *cands, int ncand) {
@@ -1200,42 +1319,79 @@ static uint32_t pick_tile(uint32_t P, uint32_t n_visited, uint32_t slots, const 
     return best;
 }
 
-hipError_t launch_reduce(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
-                         int out64, int negate, hipStream_t st) {
-    const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
-    const uint32_t cus = (uint32_t)device_cu_count();
-    const bool wide = r.dtype == 2;
+// Workgroups of a kernel that the device holds at once (occupancy x CUs),
+// computed once per kernel.
+template <typename F>
+static uint32_t resident_wgs(F kern, int threads) {
+    static std::mutex mu;
+    static std::unordered_map<const void *, uint32_t> cache;
+    const void *key = reinterpret_cast<const void *>(kern);
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess || per < 1) per = 1;
+    const uint32_t n = (uint32_t)per * (uint32_t)device_cu_count();
+    cache.emplace(key, n);
+    return n;
+}
+
+// One query: the init kernel (outputs + plan), then the reduce. The tile size
+// is chosen for whole rounds of the resident workgroups and the grid never
+// exceeds them.
+template <typename F>
+static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, hipStream_t st, const DevResident &r,
+                         const uint8_t *mask, int complement, uint32_t stride, uint32_t n_visited, void *out, int out64,
+                         int negate, const void *init, uint64_t n_init, const RegionBlocks &rb, const RegionArgs &ra) {
+    const uint32_t slots = resident_wgs(kern, threads);
+    // a planned query counts the finest tiles and lets the reduce pick the
+    // item size; without a plan (region reads, or too many tiles) the host picks
+    const uint32_t fine = cands[ncand - 1], n_fine = (r.P + fine - 1) / fine;
+    const bool planned = n_init && n_fine <= kMaxPlanTiles;
+    const uint32_t tile = planned ? fine : pick_tile(r.P, n_visited, slots, cands, ncand);
+    const uint32_t n_tiles = (r.P + tile - 1) / tile;
+    uint32_t *plan = planned ? r.tile_counts : nullptr;
+    if (n_init) {
+        const PlanArgs pa{mask, r.valid, complement, r.P, tile, n_tiles, plan};
+        const uint32_t grid = (uint32_t)std::max<uint64_t>(
+            planned ? n_tiles : 1, std::max<uint64_t>(1, std::min<uint64_t>(2048, (n_init + 255) / 256)));
+        hipLaunchKernelGGL(k_init, dim3(grid), dim3(256), 0, st, out, out64, init, n_init, pa);
+    }
+    const uint64_t items = (uint64_t)n_tiles * n_visited;
+    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, slots));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, r, mask, complement, stride, n_visited, tile, plan, out,
+                       out64, negate, rb, ra);
+}
+
+template <bool W, Op O>
+static void launch_layout(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride,
+                          uint32_t n_visited, void *out, int out64, int negate, const void *init, uint64_t n_init,
+                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st) {
     if (r.layout == 0) {
-        // balanced for three workgroups per CU: a sparse mask leaves most tiles
-        // of a block empty, and the larger tiles keep more streams per item
         const uint32_t cands[2] = {2 * kRansWG, kRansWG};
-        const uint32_t tile = pick_tile(r.P, n_visited, 3 * cus, cands, 2);
-        const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * n_visited;
-        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, 8ull * cus));
-#define QSC_RANS(W, O) hipLaunchKernelGGL((k_reduce_rans<W, O>), dim3(grid), dim3(kRansWG), 0, st, r, mask, \
-                                          complement, stride, n_visited, tile, out, out64, negate, RegionBlocks{}, \
-                                          RegionArgs{})
-        if (op == Op::Sum) {
-            if (wide) QSC_RANS(true, Op::Sum); else QSC_RANS(false, Op::Sum);
-        } else {
-            if (wide) QSC_RANS(true, Op::Moments); else QSC_RANS(false, Op::Moments);
-        }
-#undef QSC_RANS
+        launch_items(k_reduce_rans<W, O>, kRansWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
+                     negate, init, n_init, rb, ra);
     } else {
         const uint32_t cands[2] = {2 * kPairWG, kPairWG};
-        const uint32_t tile = pick_tile(r.P, n_visited, cus, cands, 2);
-        const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * n_visited;
-        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, cus));
-#define QSC_PAIR(W, O) hipLaunchKernelGGL((k_reduce_paired<W, O>), dim3(grid), dim3(kPairWG), 0, st, r, mask, \
-                                          complement, stride, n_visited, tile, out, out64, negate, RegionBlocks{}, \
-                                          RegionArgs{})
-        if (op == Op::Sum) {
-            if (wide) QSC_PAIR(true, Op::Sum); else QSC_PAIR(false, Op::Sum);
-        } else {
-            if (wide) QSC_PAIR(true, Op::Moments); else QSC_PAIR(false, Op::Moments);
-        }
-#undef QSC_PAIR
+        launch_items(k_reduce_paired<W, O>, kPairWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
+                     negate, init, n_init, rb, ra);
     }
+}
+
+hipError_t launch_query(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
+                        int out64, int negate, const void *init, uint64_t n_init, hipStream_t st) {
+    const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
+    const RegionBlocks rb{};
+    const RegionArgs ra{};
+    const bool wide = r.dtype == 2;
+#define QSC_LAUNCH(W, O) \
+    launch_layout<W, O>(r, mask, complement, stride, n_visited, out, out64, negate, init, n_init, rb, ra, st)
+    if (op == Op::Sum) {
+        if (wide) QSC_LAUNCH(true, Op::Sum); else QSC_LAUNCH(false, Op::Sum);
+    } else {
+        if (wide) QSC_LAUNCH(true, Op::Moments); else QSC_LAUNCH(false, Op::Moments);
+    }
+#undef QSC_LAUNCH
     return hipGetLastError();
 }
 
@@ -1246,31 +1402,10 @@ hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, 
 }
 
 hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const RegionArgs &ra, hipStream_t st) {
-    const uint32_t cus = (uint32_t)device_cu_count();
-    const bool wide = r.dtype == 2;
-    if (r.layout == 0) {
-        const uint32_t cands[2] = {2 * kRansWG, kRansWG};
-        const uint32_t tile = pick_tile(r.P, blocks.n, 3 * cus, cands, 2);
-        const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * blocks.n;
-        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, 8ull * cus));
-        if (wide)
-            hipLaunchKernelGGL((k_reduce_rans<true, Op::Region>), dim3(grid), dim3(kRansWG), 0, st, r, nullptr, 0, 1,
-                               blocks.n, tile, nullptr, 0, 0, blocks, ra);
-        else
-            hipLaunchKernelGGL((k_reduce_rans<false, Op::Region>), dim3(grid), dim3(kRansWG), 0, st, r, nullptr, 0, 1,
-                               blocks.n, tile, nullptr, 0, 0, blocks, ra);
-    } else {
-        const uint32_t cands[2] = {2 * kPairWG, kPairWG};
-        const uint32_t tile = pick_tile(r.P, blocks.n, cus, cands, 2);
-        const uint64_t items = (uint64_t)((r.P + tile - 1) / tile) * blocks.n;
-        const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, cus));
-        if (wide)
-            hipLaunchKernelGGL((k_reduce_paired<true, Op::Region>), dim3(grid), dim3(kPairWG), 0, st, r, nullptr, 0, 1,
-                               blocks.n, tile, nullptr, 0, 0, blocks, ra);
-        else
-            hipLaunchKernelGGL((k_reduce_paired<false, Op::Region>), dim3(grid), dim3(kPairWG), 0, st, r, nullptr, 0,
-                               1, blocks.n, tile, nullptr, 0, 0, blocks, ra);
-    }
+    if (r.dtype == 2)
+        launch_layout<true, Op::Region>(r, nullptr, 0, 1, blocks.n, nullptr, 0, 0, nullptr, 0, blocks, ra, st);
+    else
+        launch_layout<false, Op::Region>(r, nullptr, 0, 1, blocks.n, nullptr, 0, 0, nullptr, 0, blocks, ra, st);
     return hipGetLastError();
 }
 

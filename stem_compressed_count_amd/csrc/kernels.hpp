@@ -10,6 +10,9 @@ namespace qsc {
 // entry (values 0, no bits, next state 0) padded to 16 bytes.
 constexpr uint32_t kPairTable = 32 * 1024 + 4;
 
+// Pixel tiles a query plan covers; detectors with more tiles decode every tile.
+constexpr uint32_t kMaxPlanTiles = 1024;
+
 // Device view of a resident (all pointers are device memory).
 struct DevResident {
     const uint8_t *payload;  // stream bytes, followed by zero padding
@@ -21,6 +24,7 @@ struct DevResident {
     const uint8_t *valid;    // P bytes, nonzero = valid
     const double *calib;     // scaled: n_blocks x {scale, offset}
     unsigned long long *err; // first malformed stream: (block + 1) << 32 | pixel, 0 = none
+    uint32_t *tile_counts;   // query plan: selected pixels per pixel tile (kMaxPlanTiles entries)
     uint64_t S;
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };
@@ -42,13 +46,14 @@ struct RegionBlocks {
 };
 
 // Launch wrappers (enqueue only; return hipSuccess or the launch error).
-//  out[i] = init[i] (or 0 when init is null), n elements of 4 or 8 bytes.
-hipError_t launch_init(void *out, int out64, const void *init, uint64_t n, hipStream_t st);
-//  fused selection + decode + reduce over the visited blocks (b % stride == 0):
-//  adds (negate: subtracts) the sums over pixels with (mask[p] != 0) != complement
-//  (all pixels when mask is null) and valid[p]. Sum: out[s]; Moments: u64 [3][S].
-hipError_t launch_reduce(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
-                         int out64, int negate, hipStream_t st);
+//  One reduce query: out is zeroed (or copied from init, n_init elements of 4
+//  or 8 bytes) and the pixel tiles the mask selects nothing from are planned
+//  out; then every pixel with (mask[p] != 0) != complement (all pixels when
+//  mask is null) and valid[p] of every visited block (b % stride == 0) is
+//  decoded and added (negate: subtracted) into out: u32/u64 per scan for
+//  Op::Sum, u64 [3][S] moments for Op::Moments.
+hipError_t launch_query(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
+                        int out64, int negate, const void *init, uint64_t n_init, hipStream_t st);
 //  CoM from exact moments.
 hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, float *col, hipStream_t st);
 //  decode of a scan rectangle over the listed touched blocks.

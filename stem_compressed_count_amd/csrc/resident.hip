@@ -32,6 +32,7 @@ struct qsc_resident {
     uint32_t *d_model_info = nullptr;
     uint8_t *d_valid = nullptr;
     unsigned long long *d_err = nullptr;
+    uint32_t *d_plan = nullptr;  // per-tile selected-pixel counts of the current query
     void *d_total = nullptr;
     bool total_ready = false;
     uint64_t *d_moments = nullptr;
@@ -66,7 +67,7 @@ hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
 
 void free_all(qsc_resident *res) {
     for (void *p : {(void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
-                    (void *)res->d_err, res->d_total, (void *)res->d_moments})
+                    (void *)res->d_err, (void *)res->d_plan, res->d_total, (void *)res->d_moments})
         if (p) (void)hipFree(p);
 }
 
@@ -176,6 +177,7 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     if ((e = dalloc(res.get(), &res->d_valid, g.P())) != hipSuccess) return bail(e, "valid");
     if ((e = hipMemcpy(res->d_valid, valid.data(), g.P(), hipMemcpyHostToDevice)) != hipSuccess)
         return bail(e, "valid upload");
+    if ((e = dalloc(res.get(), &res->d_plan, 4 * kMaxPlanTiles)) != hipSuccess) return bail(e, "query plan");
     if ((e = dalloc(res.get(), &res->d_err, 256)) != hipSuccess) return bail(e, "error word");
     if ((e = hipMemset(res->d_err, 0, 256)) != hipSuccess) return bail(e, "error word");
     if ((e = hipStreamSynchronize(strm)) != hipSuccess) return bail(e, "synchronize");
@@ -190,6 +192,7 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     d.valid = res->d_valid;
     d.calib = g.scaled ? reinterpret_cast<const double *>(res->d_blob + s.calib) : nullptr;
     d.err = res->d_err;
+    d.tile_counts = res->d_plan;
     d.S = g.S();
     d.P = g.P();
     d.G = g.G();
@@ -230,8 +233,8 @@ qsc_status qsc_masked_sum(qsc_resident *res, const uint8_t *d_mask, uint32_t blo
     if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const int out64 = res->g.sum_bits() == 64;
-    hipError_t e = launch_init(d_out, out64, nullptr, res->g.S(), st);
-    if (e == hipSuccess) e = launch_reduce(res->dev, d_mask, 0, block_stride, Op::Sum, d_out, out64, 0, st);
+    const hipError_t e = launch_query(res->dev, d_mask, 0, block_stride, Op::Sum, d_out, out64, 0, nullptr,
+                                      res->g.S(), st);
     return finish_query(res, e, st, wait);
 }
 
@@ -247,14 +250,12 @@ qsc_status qsc_dense_df(qsc_resident *res, const uint8_t *d_mask, void *d_out, v
         return hip_fail(res, e, "total cache");
     if (!res->total_ready) {
         // cold: full-detector total over the valid pixels, decoded once and kept
-        e = launch_init(res->d_total, out64, nullptr, res->g.S(), st);
-        if (e == hipSuccess) e = launch_reduce(res->dev, nullptr, 0, 1, Op::Sum, res->d_total, out64, 0, st);
+        e = launch_query(res->dev, nullptr, 0, 1, Op::Sum, res->d_total, out64, 0, nullptr, res->g.S(), st);
         if (e != hipSuccess) return hip_fail(res, e, "total cache build");
         res->total_ready = true;
     }
     // warm: out = total - sum over valid & ~mask
-    e = launch_init(d_out, out64, res->d_total, res->g.S(), st);
-    if (e == hipSuccess) e = launch_reduce(res->dev, d_mask, 1, 1, Op::Sum, d_out, out64, 1, st);
+    e = launch_query(res->dev, d_mask, 1, 1, Op::Sum, d_out, out64, 1, res->d_total, res->g.S(), st);
     return finish_query(res, e, st, wait);
 }
 
@@ -266,8 +267,7 @@ qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float
     hipError_t e = hipSuccess;
     if (!res->d_moments && (e = dalloc(res, &res->d_moments, 3 * 8 * res->g.S())) != hipSuccess)
         return hip_fail(res, e, "moment buffer");
-    e = launch_init(res->d_moments, 1, nullptr, 3 * res->g.S(), st);
-    if (e == hipSuccess) e = launch_reduce(res->dev, d_mask, 0, 1, Op::Moments, res->d_moments, 1, 0, st);
+    e = launch_query(res->dev, d_mask, 0, 1, Op::Moments, res->d_moments, 1, 0, nullptr, 3 * res->g.S(), st);
     if (e == hipSuccess) e = launch_com_finalize(res->d_moments, res->g.S(), d_row, d_col, st);
     return finish_query(res, e, st, wait);
 }
