@@ -39,7 +39,7 @@ def build(force=False):
     """Compile liboracle.so with gcc (plain C)."""
     src = os.path.join(_HERE, "oracle.c")
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
-        cmd = f"gcc -O2 -fPIC -shared -o {_LIB_PATH}.tmp {src} -lm && mv {_LIB_PATH}.tmp {_LIB_PATH}"
+        cmd = f"gcc -O2 -ffp-contract=off -fPIC -shared -o {_LIB_PATH}.tmp {src} -lm && mv {_LIB_PATH}.tmp {_LIB_PATH}"
         if os.system(cmd) != 0:
             raise RuntimeError("failed to build liboracle.so")
 
@@ -58,6 +58,7 @@ def _load():
         lib.orc_calibration.argtypes = [vp, u64, vp]
         lib.orc_masked_sum.argtypes = [vp, u32, u64, u64, vp, vp, u32, vp]
         lib.orc_com.argtypes = [vp, u32, u64, u32, u32, vp, vp, vp, vp, vp]
+        lib.orc_sum_dp.argtypes = [vp, u32, u64, u64, vp, vp, u32, vp, vp, vp]
         lib.orc_calibrate.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), vp]
         lib.orc_reconstruct.argtypes = [vp, u64, ctypes.c_double, ctypes.c_double, vp]
         lib.orc_reconstruct.restype = None
@@ -170,6 +171,27 @@ def com(counts, det_rows, det_cols, mask=None, valid=None):
     return row, col, m0
 
 
+def sum_dp(counts, scan_mask=None, valid=None, stride=1, calib=None):
+    """Sum (uint64) and mean (float32) diffraction pattern over the selected scans.
+
+    calib: (n_blocks, 2) float64 (scale, offset) per 512-scan region of a scaled
+    resident; the mean is then that of the reconstructed intensities.
+    """
+    c = np.ascontiguousarray(counts)
+    S, P = c.shape
+    dtype = 1 if c.dtype == np.uint8 else 2
+    m = None if scan_mask is None else np.ascontiguousarray(scan_mask, dtype=np.uint8)
+    v = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    cal = None if calib is None else np.ascontiguousarray(calib, dtype=np.float64)
+    out = np.empty(P, dtype=np.uint64)
+    mean = np.empty(P, dtype=np.float32)
+    rc = _load().orc_sum_dp(c.ctypes.data, dtype, S, P, _ptr(m), _ptr(v), stride, _ptr(cal), out.ctypes.data,
+                            mean.ctypes.data)
+    if rc:
+        raise OracleError(rc, "sum_dp")
+    return out, mean
+
+
 def region(counts, scan_cols, r0, r1, c0, c1, valid=None):
     """counts of the half-open scan rectangle, (h*w, P), invalid pixels zeroed."""
     rows = []
@@ -221,6 +243,20 @@ def brute_masked_sum(counts, mask, valid=None, stride=1):
     blocks = np.arange(counts.shape[0]) // BLOCK
     out[blocks % stride != 0] = 0
     return out
+
+
+def brute_sum_dp(counts, scan_mask=None, valid=None, stride=1):
+    """NumPy sum and mean diffraction pattern over the selected scans."""
+    S, P = counts.shape
+    sel = (np.arange(S) // BLOCK) % stride == 0
+    if scan_mask is not None:
+        sel &= np.asarray(scan_mask) != 0
+    total = counts[sel].astype(np.uint64).sum(axis=0)
+    if valid is not None:
+        total[np.asarray(valid) == 0] = 0
+    n = int(sel.sum())
+    mean = (total.astype(np.float64) / n).astype(np.float32) if n else np.zeros(P, np.float32)
+    return total, mean
 
 
 def brute_com(counts, det_rows, det_cols, mask=None, valid=None):

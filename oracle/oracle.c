@@ -1018,6 +1018,49 @@ int orc_masked_sum(const void *counts, uint32_t dtype, uint64_t S, uint64_t P, c
     return ORC_OK;
 }
 
+/* Sum and mean diffraction pattern: the dual of a virtual image, summing the
+ * frames of the selected scans ("Scaled uint16 resident intensities", "MPS
+ * implementation": mean diffraction queries accumulated straight from the
+ * resident). Selected scans: scan_mask[s] != 0 (every scan when scan_mask is
+ * NULL) in visited blocks ((s / 512) % stride == 0); n is their number.
+ *   sum[p]  = sum of I[s,p] over the selected scans, for valid p (0 otherwise)
+ *   mean[p] = (float)((double)sum[p] / n), 0 when n = 0
+ * For scaled residents (calib = (scale, offset) per 512-scan region) the mean
+ * is that of the reconstructed intensities code*scale + offset, accumulated
+ * region by region in increasing order: acc += scale_b * C_b[p] + n_b * offset_b,
+ * every product and sum rounded in float64, then acc / n rounded to float32. */
+int orc_sum_dp(const void *counts, uint32_t dtype, uint64_t S, uint64_t P, const uint8_t *scan_mask,
+               const uint8_t *valid, uint32_t stride, const double *calib, uint64_t *sum, float *mean) {
+    if (stride < 1) return ORC_ERR_ARG;
+    const uint64_t nb = (S + BLOCK - 1) / BLOCK;
+    uint64_t n = 0;
+    for (uint64_t s = 0; s < S; s++)
+        if ((s / BLOCK) % stride == 0 && (!scan_mask || scan_mask[s])) n++;
+    for (uint64_t p = 0; p < P; p++) {
+        sum[p] = 0;
+        mean[p] = 0.0f;
+        if (valid && !valid[p]) continue;
+        volatile double acc = 0.0;
+        for (uint64_t b = 0; b < nb; b += stride) {
+            uint64_t cb = 0, n_b = 0;
+            for (uint64_t s = b * BLOCK; s < S && s < (b + 1) * BLOCK; s++) {
+                if (scan_mask && !scan_mask[s]) continue;
+                cb += at(counts, dtype, s, P, p);
+                n_b++;
+            }
+            sum[p] += cb;
+            if (calib) {
+                volatile double t1 = calib[2 * b] * (double)cb;
+                volatile double t2 = (double)n_b * calib[2 * b + 1];
+                volatile double t = t1 + t2;
+                acc = acc + t;
+            }
+        }
+        if (n) mean[p] = calib ? (float)(acc / (double)n) : (float)((double)sum[p] / (double)n);
+    }
+    return ORC_OK;
+}
+
 /* exact moments, then one float64 division rounded to float32 (0 when M0 = 0) */
 int orc_com(const void *counts, uint32_t dtype, uint64_t S, uint32_t det_rows, uint32_t det_cols,
             const uint8_t *mask, const uint8_t *valid, float *row, float *col, uint64_t *m0_out) {

@@ -422,3 +422,65 @@ def test_workload_masks_match_the_pages():
     assert synth.annulus_mask(64, 64, 32, 32, 14, 30).sum() == 2212
     assert synth.annulus_mask(192, 192, 96, 96, 60, 90).sum() == 14168
     assert len(synth.sweep_masks(synth.WORKLOADS["scan512_u8_lowdose"])) == 64
+
+
+# ---------------------------------------------------------------------------
+# sum / mean diffraction pattern (the dual of a virtual image)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
+def test_sum_dp_matches_numpy_brute_force(dtype):
+    rng = np.random.default_rng(61)
+    S, P = 1100, 37  # two full blocks and a partial one
+    c = rng.poisson(3.0, size=(S, P)).astype(dtype)
+    c[5] = np.iinfo(dtype).max
+    valid = np.ones(P, np.uint8)
+    valid[[0, 11]] = 0
+    for scan_mask in (None, (rng.random(S) < 0.3).astype(np.uint8)):
+        for stride in (1, 2):
+            for v in (None, valid):
+                got = oracle.sum_dp(c, scan_mask, v, stride)
+                want = oracle.brute_sum_dp(c, scan_mask, v, stride)
+                assert np.array_equal(got[0], want[0])
+                assert np.array_equal(got[1], want[1])
+
+
+def test_sum_dp_closed_forms():
+    S, P = 1024, 9
+    c = np.full((S, P), 3, np.uint16)
+    s, m = oracle.sum_dp(c)
+    assert np.all(s == 3 * S) and np.all(m == 3.0)
+    # one bright frame among zeros: the mean is its value over the scan count
+    z = np.zeros((S, P), np.uint16)
+    z[700] = 65535
+    s, m = oracle.sum_dp(z)
+    assert np.all(s == 65535) and np.all(m == np.float32(65535 / 1024))
+    # stride 2 visits block 0 only: the bright frame (block 1) drops out
+    s, m = oracle.sum_dp(z, stride=2)
+    assert not s.any() and not m.any()
+    # an empty scan selection gives zeros
+    s, m = oracle.sum_dp(z, scan_mask=np.zeros(S, np.uint8))
+    assert not s.any() and not m.any()
+
+
+def test_sum_dp_scaled_mean_is_the_mean_of_the_intensities():
+    rng = np.random.default_rng(62)
+    S, P = 1200, 24
+    # integer-valued intensities holding 0 and 65535 in every region: the
+    # calibration is exactly scale 1, offset 0, so the mean must be the plain mean
+    x = rng.integers(0, 65536, size=(S, P)).astype(np.float32)
+    x[0::512, 0] = 0.0
+    x[1::512, 0] = 65535.0
+    blob = oracle.encode(x, 1, S, 4, 6, scaled=True)
+    codes, cal = oracle.decode(blob), oracle.calibration(blob)
+    assert np.all(cal[:, 0] == 1.0) and np.all(cal[:, 1] == 0.0)
+    sel = (rng.random(S) < 0.5).astype(np.uint8)
+    _, mean = oracle.sum_dp(codes, sel, calib=cal)
+    assert np.array_equal(mean, x[sel != 0].astype(np.float64).mean(axis=0).astype(np.float32))
+    # general data: within half a code step of the mean of the raw intensities
+    y = synth.scaled(synth.WORKLOADS["scan256_u16_sentinel"].with_scans(5, 240))[:, :200]
+    blob = oracle.encode(y, 5, 240, 10, 20, scaled=True)
+    codes, cal = oracle.decode(blob), oracle.calibration(blob)
+    _, mean = oracle.sum_dp(codes, calib=cal)
+    want = y.astype(np.float64).mean(axis=0)
+    assert np.abs(mean - want).max() <= 0.5 * cal[:, 0].max() + 1e-6 * np.abs(want).max()
