@@ -229,6 +229,24 @@ def main():
     value = step_cnt / (ms_per_step * 1e-3)
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # widened rows, timed on the same resident (not part of the step): the sum and
+    # mean diffraction pattern over every scan
+    dsum = torch.empty(w.P, dtype=torch.int64, device=dev)
+    dmean = torch.empty(w.P, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        res.sum_dp(None, 1, out_sum=dsum, out_mean=dmean, wait=False)
+    dp_ev = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        res.sum_dp(None, 1, out_sum=dsum, out_mean=dmean, wait=False)
+        b.record(stream)
+        dp_ev.append((a, b))
+    torch.cuda.synchronize()
+    res.finish()
+    dp_ms = float(np.median([a.elapsed_time(b) for a, b in dp_ev]))
+    dp_counts = w.S * int((np.ones(w.P, bool) if valid is None else valid.astype(bool)).sum())
+
     com_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["com_full"]]))
     com_gbps = by_full / (com_ms * 1e-3) / 1e9
     tops = cn_full * ALG_OPS_MOMENTS / (com_ms * 1e-3) / 1e12
@@ -259,6 +277,8 @@ def main():
         "host_ms_per_step": round(host_s * 1e3 / args.steps, 4), "cold_dense_df_ms": round(cold_ms, 3),
         "setup_s": round(t_setup, 2),
         "roofline": roofline,
+        "next_rows": {"sum_dp": {"ms": round(dp_ms, 4), "counts_per_s": round(dp_counts / (dp_ms * 1e-3), 1),
+                                 "what": "sum + mean diffraction pattern over every scan (not in the step)"}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, masks, df_mask, args.cpu_sample_blocks)

@@ -137,6 +137,20 @@ qsc_status qsc_resident_info(const qsc_resident *res, qsc_info *info);
  *   0: native dtype; 1: float32 calibrated intensity code*scale+offset of the
  *   scan's region (scaled residents only). Empty or out-of-range rectangle,
  *   or out_kind 1 on an unscaled resident -> INVALID_ARG.
+ * qsc_sum_dp: sum and mean diffraction pattern over the selected scans, the
+ *   dual of a virtual image (scaled-uint16 page, "MPS implementation": mean
+ *   diffraction queries accumulated straight from the encoded resident; the
+ *   optimization matrix page, "Current Measured Checkpoints", gates the mean
+ *   diffraction pattern as bit-exact). Selected scans: d_scan_mask[s] != 0
+ *   (every scan when NULL; device, scans bytes) in the blocks block_stride
+ *   visits; n is their number. d_sum[p] = exact sum of I[s, p] over them for
+ *   valid p, 0 for invalid p (device uint64[P]). d_mean (nullable, device
+ *   float32[P]) = (float)((double)sum / n), 0 when n = 0; for a scaled
+ *   resident it is the mean of the calibrated intensities code*scale+offset,
+ *   accumulated region by region in increasing order as
+ *   scale_b * C_b + n_b * offset_b in float64, then divided by n and rounded
+ *   to float32. The first call allocates scans/512 x P x 4 bytes of resident
+ *   scratch.
  * qsc_finish: synchronises hip_stream and reports (then clears) the first
  *   malformed stream found by queries enqueued since the last check.
  * qsc_last_error: message of the resident's last failure, naming the first
@@ -149,6 +163,8 @@ qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float
                    int wait);
 qsc_status qsc_decode_region(qsc_resident *res, uint32_t r0, uint32_t r1, uint32_t c0, uint32_t c1, int out_kind,
                              void *d_out, void *hip_stream, int wait);
+qsc_status qsc_sum_dp(qsc_resident *res, const uint8_t *d_scan_mask, uint32_t block_stride, uint64_t *d_sum,
+                      float *d_mean, void *hip_stream, int wait);
 qsc_status qsc_finish(qsc_resident *res, void *hip_stream);
 const char *qsc_last_error(const qsc_resident *res);
 

@@ -13,6 +13,7 @@ Entry points mirror include/qsc.h:
     Resident.dense_df(mask)                  qsc_dense_df
     Resident.com(mask=None)                  qsc_com
     Resident.decode_region(r0, r1, c0, c1)   qsc_decode_region
+    Resident.sum_dp(scan_mask, stride)       qsc_sum_dp
     Resident.finish()                        qsc_finish
     Resident.query_bytes(mask, stride)       qsc_query_bytes
 """
@@ -71,6 +72,7 @@ _SIGS = {
     "qsc_dense_df": ([_vp, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_com": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_decode_region": ([_vp, _u32, _u32, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
+    "qsc_sum_dp": ([_vp, _vp, _u32, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_finish": ([_vp, _vp], _i32),
     "qsc_last_error": ([_vp], ctypes.c_char_p),
     "qsc_query_bytes": ([_vp, _vp, _u32, ctypes.POINTER(_u64), ctypes.POINTER(_u64)], _i32),
@@ -233,6 +235,20 @@ class Resident:
         self._check(lib.qsc_decode_region(self._h, r0, r1, c0, c1, 1 if calibrated else 0, o.data_ptr(),
                                           _stream_handle(stream), int(wait)), "decode_region")
         return o.view((r1 - r0) * (c1 - c0), self.P)
+
+    def sum_dp(self, scan_mask=None, block_stride=1, out_sum=None, out_mean=None, stream=None, wait=True):
+        """Sum (int64 storage of uint64) and mean (float32) diffraction pattern over the selected scans."""
+        import torch
+        m = None
+        if scan_mask is not None:
+            m = torch.as_tensor(scan_mask, dtype=torch.uint8, device=self.device).contiguous()
+            if m.numel() != self.S:
+                raise ValueError(f"scan_mask must have {self.S} entries")
+        s = self._out(out_sum, torch.int64, self.P)
+        mean = self._out(out_mean, torch.float32, self.P)
+        self._check(lib.qsc_sum_dp(self._h, None if m is None else m.data_ptr(), block_stride, s.data_ptr(),
+                                   mean.data_ptr(), _stream_handle(stream), int(wait)), "sum_dp")
+        return s, mean
 
     def finish(self, stream=None):
         self._check(lib.qsc_finish(self._h, _stream_handle(stream)), "finish")

@@ -301,6 +301,42 @@ __device__ __forceinline__ void add_event(const Partials<OP> &pt, int pos, uint3
     }
 }
 
+// ------------------------------------------------------------------ diffraction-pattern tiles
+// One (visited block, tile) item of a diffraction-pattern query: the block's
+// row of per-pixel partial sums, its selected scans as 16 bitmask words in LDS
+// and their number.
+struct DpTile {
+    uint32_t *row;
+    const uint32_t *bits;
+    uint32_t n_sel;
+};
+
+__device__ __forceinline__ uint32_t scan_bit(const DpTile &dt, uint32_t j) { return (dt.bits[j >> 5] >> (j & 31u)) & 1u; }
+
+// Selected scans of a block as 16 bitmask words (scan j is bit j % 32 of word
+// j / 32): one ballot per wave, then the caller synchronises and counts.
+template <int WG>
+__device__ __forceinline__ void dp_scan_bits(const uint8_t *scan_mask, uint64_t s0, uint32_t n, uint32_t *bits) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    for (uint32_t base = 0; base < 512; base += WG) {
+        const uint32_t j = base + tid;
+        const bool f = j < n && (!scan_mask || scan_mask[s0 + j] != 0);
+        const unsigned long long bal = __ballot(f);
+        const uint32_t word = (base + 64 * wave) >> 5;
+        if (lane == 0 && word < 16) {
+            bits[word] = (uint32_t)bal;
+            bits[word + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t dp_count(const uint32_t *bits) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) c += __popc(bits[i]);
+    return c;
+}
+
 // ------------------------------------------------------------------ region output
 template <bool WIDE>
 __device__ __forceinline__ void region_put(void *out, int out_kind, uint64_t idx, uint32_t v, double scale,
@@ -380,7 +416,7 @@ struct RSlot {
 template <int K, bool WIDE, Op OP>
 __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
                           uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt,
-                          const RegionArgs &ra) {
+                          const RegionArgs &ra, const DpTile &dt) {
     const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
@@ -415,6 +451,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             }
             if constexpr (OP == Op::Region) {
                 region_fill<WIDE>(r, b, n, z.p, v, ra);
+            } else if constexpr (OP == Op::Dp) {
+                dt.row[z.p] = v * dt.n_sel;
             } else {
                 const uint32_t kr = z.p / r.det_cols;
                 if (v) add_event<OP>(pt, -1, v, kr, z.p - kr * r.det_cols);
@@ -545,6 +583,40 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 put(v);
                 if ((j & 1) || j + 1 == n) refill();
             }
+        } else if constexpr (OP == Op::Dp) {
+            // per-lane sums over the selected scans, no reduction across lanes
+            constexpr int CH = 32;
+            uint32_t acc[K];
+#pragma unroll
+            for (int k = 0; k < K; k++) acc[k] = 0;
+            const uint32_t nfull = n / CH;
+            for (uint32_t c = 0; c < nfull; c++) {
+                const uint32_t word = dt.bits[c];
+#pragma unroll
+                for (int jj = 0; jj < CH; jj++) {
+                    uint32_t v[K];
+                    step(form, (jj & 1) == 0, v);
+                    const uint32_t m = (word >> jj) & 1u;
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        acc[k] = __umul24(v[k], m) + acc[k];
+                        asm volatile("" : "+v"(acc[k]));  // keep the sum in the loop (see the reduce chunks)
+                    }
+                    if (jj & 1) refill();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            for (uint32_t j = nfull * CH; j < n; j++) {
+                uint32_t v[K];
+                step(form, (j & 1) == 0, v);
+                const uint32_t m = scan_bit(dt, j);
+#pragma unroll
+                for (int k = 0; k < K; k++) acc[k] = __umul24(v[k], m) + acc[k];
+                if ((j & 1) || j + 1 == n) refill();
+            }
+#pragma unroll
+            for (int k = 0; k < K; k++)
+                if (sl[k].live) dt.row[sl[k].p] = acc[k];
         } else {
             constexpr int CH = 16;
             const uint32_t my = lane_scan<CH>();
@@ -684,7 +756,7 @@ __device__ __forceinline__ uint32_t pair_literal(BBits &s, Rsrc rs, uint32_t inf
 template <int K, bool WIDE, Op OP>
 __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
                             uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt,
-                            const RegionArgs &ra) {
+                            const RegionArgs &ra, const DpTile &dt) {
     const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
@@ -718,6 +790,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         if (mode == 0) {  // EMPTY
             if (z.len != 2) report(r, b, z.p);
             if constexpr (OP == Op::Region) region_fill<WIDE>(r, b, kBlk, z.p, 0, ra);
+            if constexpr (OP == Op::Dp) dt.row[z.p] = 0;
             continue;
         }
         if (mode == 1) {  // CONST
@@ -726,6 +799,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 report(r, b, z.p);
             else if constexpr (OP == Op::Region)
                 region_fill<WIDE>(r, b, kBlk, z.p, v, ra);
+            else if constexpr (OP == Op::Dp)
+                dt.row[z.p] = v * dt.n_sel;
             else
                 add_event<OP>(pt, -1, v, kr, kc);
             continue;
@@ -739,6 +814,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             }
             int prev = -1;
             bool ok = true;
+            uint32_t dsum = 0;
             if constexpr (OP == Op::Region) region_fill<WIDE>(r, b, kBlk, z.p, 0, ra);
             for (uint32_t t = 0; t < nnz; t++) {
                 const int pos = (int)ld16(r.payload, e.start + 4 + 2 * t);
@@ -754,6 +830,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     rw.row = (uint32_t)(s / r.scan_cols);
                     rw.col = (uint32_t)(s % r.scan_cols);
                     if (rw.inside()) region_put<WIDE>(ra.out, ra.out_kind, rw.index(r.P) + z.p, v, rw.scale, rw.offset);
+                } else if constexpr (OP == Op::Dp) {
+                    dsum += v * scan_bit(dt, (uint32_t)pos);
                 } else {
                     add_event<OP>(pt, pos, v, kr, kc);
                 }
@@ -761,6 +839,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             }
             if (ok && !WIDE && (nnz & 1)) ok = r.payload[e.start + 4 + 3 * nnz] == 0;
             if (!ok) report(r, b, z.p);
+            if constexpr (OP == Op::Dp) dt.row[z.p] = dsum;
             continue;
         }
         z.meta = hdr & 0xFFu;  // mode and model
@@ -879,6 +958,34 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     }
                     rw.next();
                 }
+            }
+        } else if constexpr (OP == Op::Dp) {
+            // per-lane sums over the selected scans; a PAIRED slot's window base
+            // counts once per selected scan
+            uint32_t acc[K];
+#pragma unroll
+            for (int k = 0; k < K; k++) acc[k] = sl[k].a0 * dt.n_sel;
+            for (uint32_t c = 0; c < kBlk / 32; c++) {
+                const uint32_t word = dt.bits[c];
+#pragma unroll
+                for (int tt = 0; tt < 16; tt++) {
+                    uint32_t v0[K], v1[K];
+                    step(form, c * 16 + tt, v0, v1);
+                    // window-relative values wrap below zero for literals under the
+                    // window base, so select with full-width masks (sums stay exact mod 2^32)
+                    const uint32_t m0 = 0u - ((word >> (2 * tt)) & 1u), m1 = 0u - ((word >> (2 * tt + 1)) & 1u);
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        acc[k] += (v0[k] & m0) + (v1[k] & m1);
+                        asm volatile("" : "+v"(acc[k]));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                const uint32_t mode = sl[k].meta & 7u;
+                if (mode == 3 || mode == 4) dt.row[sl[k].p] = acc[k];
             }
         } else {
             // paired workgroups have 128 VGPRs per lane: moments reduce every 8 scans
@@ -1128,12 +1235,13 @@ template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                          const uint32_t *plan, void *out, int out64, int negate,
-                                                         RegionBlocks rb, RegionArgs ra) {
+                                                         RegionBlocks rb, RegionArgs ra, DpArgs da) {
     __shared__ uint32_t tbl[2 * 4096];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kRansWG];
     __shared__ uint32_t wtot[kRansWG / 64];
     __shared__ uint16_t tiles[kMaxPlanTiles];
+    __shared__ uint32_t sbits[OP == Op::Dp ? 16 : 1];
     // with a plan, tile_px is the fine tile the counts were taken over
     uint32_t n_live = (r.P + tile_px - 1) / tile_px;
     if (plan) {
@@ -1149,30 +1257,38 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = t * tile_px;
         __syncthreads();
         const uint32_t n_sel = select_tile<kRansWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
-        if (n_sel == 0) continue;
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
+        DpTile dt{nullptr, sbits, 0};
+        if constexpr (OP == Op::Dp) {
+            dp_scan_bits<kRansWG>(da.scan_mask, (uint64_t)b * kBlk, n, sbits);
+            __syncthreads();
+            dt.row = da.part + (uint64_t)vb * r.P;
+            dt.n_sel = dp_count(sbits);
+            if (threadIdx.x == 0 && w % n_live == 0) da.nb[vb] = dt.n_sel;  // once per visited block
+        }
+        if (n_sel == 0) continue;
         if (b != loaded) {
             const uint4 *src = reinterpret_cast<const uint4 *>(r.tables + 8192ull * b);
             uint4 *dst = reinterpret_cast<uint4 *>(tbl);
             for (uint32_t i = threadIdx.x; i < 2048; i += kRansWG) dst[i] = src[i];
             loaded = b;
         }
-        if (OP != Op::Region) zero_partials<OP>(sp, n);
+        if (OP == Op::Sum || OP == Op::Moments) zero_partials<OP>(sp, n);
         __syncthreads();
         // at most two slots per lane: with three decode forms, more do not fit 3 waves per SIMD
         const uint32_t K = n_sel <= kRansWG ? 1 : 2;
         const uint32_t first = (threadIdx.x >> 6) * 64 * K;
         if (first < n_sel) {  // whole waves without a stream skip the decode
             if (K == 2)
-                rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra);
+                rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt);
             else
-                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra);
+                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt);
         }
         __syncthreads();
-        if (OP != Op::Region) flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate);
+        if (OP == Op::Sum || OP == Op::Moments) flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate);
     }
 }
 
@@ -1180,11 +1296,12 @@ template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const uint8_t *mask, int complement,
                                                            uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                            const uint32_t *plan, void *out, int out64, int negate,
-                                                           RegionBlocks rb, RegionArgs ra) {
+                                                           RegionBlocks rb, RegionArgs ra, DpArgs da) {
     __shared__ uint32_t tbl[kPairTable];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kPairWG];
     __shared__ uint32_t wtot[kPairWG / 64];
+    __shared__ uint32_t sbits[OP == Op::Dp ? 16 : 1];
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(r.tables);
         uint4 *dst = reinterpret_cast<uint4 *>(tbl);
@@ -1205,23 +1322,31 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
         const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = t * tile_px;
         __syncthreads();
         const uint32_t n_sel = select_tile<kPairWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
-        if (n_sel == 0) continue;
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
-        if (OP != Op::Region) zero_partials<OP>(sp, kBlk);
+        DpTile dt{nullptr, sbits, 0};
+        if constexpr (OP == Op::Dp) {
+            dp_scan_bits<kPairWG>(da.scan_mask, (uint64_t)b * kBlk, kBlk, sbits);
+            __syncthreads();
+            dt.row = da.part + (uint64_t)vb * r.P;
+            dt.n_sel = dp_count(sbits);
+            if (threadIdx.x == 0 && w % n_live == 0) da.nb[vb] = dt.n_sel;  // once per visited block
+        }
+        if (n_sel == 0) continue;
+        if (OP == Op::Sum || OP == Op::Moments) zero_partials<OP>(sp, kBlk);
         __syncthreads();
         // at most two slots per lane: 1024-thread workgroups have 128 VGPRs per lane
         const uint32_t K = n_sel <= kPairWG ? 1 : 2;
         const uint32_t first = (threadIdx.x >> 6) * 64 * K;
         if (first < n_sel) {
             if (K == 2)
-                paired_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt, ra);
+                paired_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt, ra, dt);
             else
-                paired_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt, ra);
+                paired_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt, ra, dt);
         }
         __syncthreads();
-        if (OP != Op::Region) flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate);
+        if (OP == Op::Sum || OP == Op::Moments) flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate);
     }
 }
 
@@ -1271,6 +1396,33 @@ __global__ void k_zero_bytes(uint8_t *out, uint64_t n) {
     const uint64_t nv = (n - head) / 16;
     for (uint64_t i = i0; i < nv; i += step) body[i] = make_uint4(0, 0, 0, 0);
     for (uint64_t i = head + 16 * nv + i0; i < n; i += step) out[i] = 0;
+}
+
+// Diffraction pattern from the per-(visited block, pixel) partial sums: the
+// exact u64 sum, and the mean over the selected scans in float64 rounded to
+// float32 (for scaled residents, of the reconstructed intensities, block by
+// block in increasing order, each product and sum rounded in float64).
+__global__ void k_dp_finalize(const uint32_t *part, const uint32_t *nb, uint32_t n_visited, uint32_t stride,
+                              uint32_t P, const uint8_t *valid, const double *calib, uint64_t *sum, float *mean) {
+    const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= P) return;
+    uint64_t s = 0, n = 0;
+    double acc = 0.0;
+    const bool ok = valid[p] != 0;
+    for (uint32_t vb = 0; vb < n_visited; vb++) {
+        n += nb[vb];
+        if (!ok) continue;
+        const uint32_t c = part[(uint64_t)vb * P + p];
+        s += c;
+        if (calib) {
+            const uint64_t b = (uint64_t)vb * stride;
+            const double t1 = __dmul_rn(calib[2 * b], (double)c);
+            const double t2 = __dmul_rn((double)nb[vb], calib[2 * b + 1]);
+            acc = __dadd_rn(acc, __dadd_rn(t1, t2));
+        }
+    }
+    sum[p] = ok ? s : 0;
+    if (mean) mean[p] = (ok && n) ? (float)__ddiv_rn(calib ? acc : (double)s, (double)n) : 0.0f;
 }
 
 __global__ void k_com_finalize(const uint64_t *m, uint64_t S, float *row, float *col) {
@@ -1342,7 +1494,8 @@ static uint32_t resident_wgs(F kern, int threads) {
 template <typename F>
 static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, hipStream_t st, const DevResident &r,
                          const uint8_t *mask, int complement, uint32_t stride, uint32_t n_visited, void *out, int out64,
-                         int negate, const void *init, uint64_t n_init, const RegionBlocks &rb, const RegionArgs &ra) {
+                         int negate, const void *init, uint64_t n_init, const RegionBlocks &rb, const RegionArgs &ra,
+                         const DpArgs &da) {
     const uint32_t slots = resident_wgs(kern, threads);
     // a planned query counts the finest tiles and lets the reduce pick the
     // item size; without a plan (region reads, or too many tiles) the host picks
@@ -1360,21 +1513,21 @@ static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, 
     const uint64_t items = (uint64_t)n_tiles * n_visited;
     const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, slots));
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, r, mask, complement, stride, n_visited, tile, plan, out,
-                       out64, negate, rb, ra);
+                       out64, negate, rb, ra, da);
 }
 
 template <bool W, Op O>
 static void launch_layout(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride,
                           uint32_t n_visited, void *out, int out64, int negate, const void *init, uint64_t n_init,
-                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st) {
+                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st, const DpArgs &da = DpArgs{}) {
     if (r.layout == 0) {
         const uint32_t cands[2] = {2 * kRansWG, kRansWG};
         launch_items(k_reduce_rans<W, O>, kRansWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
-                     negate, init, n_init, rb, ra);
+                     negate, init, n_init, rb, ra, da);
     } else {
         const uint32_t cands[2] = {2 * kPairWG, kPairWG};
         launch_items(k_reduce_paired<W, O>, kPairWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
-                     negate, init, n_init, rb, ra);
+                     negate, init, n_init, rb, ra, da);
     }
 }
 
@@ -1406,6 +1559,22 @@ hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const
         launch_layout<true, Op::Region>(r, nullptr, 0, 1, blocks.n, nullptr, 0, 0, nullptr, 0, blocks, ra, st);
     else
         launch_layout<false, Op::Region>(r, nullptr, 0, 1, blocks.n, nullptr, 0, 0, nullptr, 0, blocks, ra, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_dp(const DevResident &r, const uint8_t *scan_mask, uint32_t stride, uint32_t *part, uint32_t *nb,
+                     uint64_t *sum, float *mean, hipStream_t st) {
+    const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
+    const DpArgs da{scan_mask, part, nb};
+    // the init kernel zeroes the per-block scan counts and plans the valid pixels
+    if (r.dtype == 2)
+        launch_layout<true, Op::Dp>(r, nullptr, 0, stride, n_visited, nb, 0, 0, nullptr, n_visited, RegionBlocks{},
+                                    RegionArgs{}, st, da);
+    else
+        launch_layout<false, Op::Dp>(r, nullptr, 0, stride, n_visited, nb, 0, 0, nullptr, n_visited, RegionBlocks{},
+                                     RegionArgs{}, st, da);
+    hipLaunchKernelGGL(k_dp_finalize, dim3((r.P + 255) / 256), dim3(256), 0, st, part, nb, n_visited, stride, r.P,
+                       r.valid, r.calib, sum, mean);
     return hipGetLastError();
 }
 

@@ -29,7 +29,16 @@ struct DevResident {
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };
 
-enum class Op : int { Sum = 0, Moments = 1, Region = 2 };
+enum class Op : int { Sum = 0, Moments = 1, Region = 2, Dp = 3 };
+
+// A diffraction-pattern query: the selected scans (null: every scan), the
+// per-(visited block, pixel) partial sums and the per-visited-block count of
+// selected scans it fills.
+struct DpArgs {
+    const uint8_t *scan_mask;
+    uint32_t *part;  // n_visited x P
+    uint32_t *nb;    // n_visited
+};
 
 // A region read: half-open scan rectangle, output buffer and kind
 // (0 native dtype, 1 float32 code*scale+offset of the scan's region).
@@ -58,6 +67,11 @@ hipError_t launch_query(const DevResident &r, const uint8_t *mask, int complemen
 hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, float *col, hipStream_t st);
 //  decode of a scan rectangle over the listed touched blocks.
 hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const RegionArgs &ra, hipStream_t st);
+//  Sum (u64[P]) and mean (f32[P], nullable) diffraction pattern over the
+//  selected scans of the visited blocks; part holds n_visited x P u32 and nb
+//  n_visited u32 of device scratch.
+hipError_t launch_dp(const DevResident &r, const uint8_t *scan_mask, uint32_t stride, uint32_t *part, uint32_t *nb,
+                     uint64_t *sum, float *mean, hipStream_t st);
 //  zero n bytes (region outputs of residents with invalid pixels)
 hipError_t launch_zero_bytes(void *out, uint64_t n, hipStream_t st);
 

@@ -33,6 +33,7 @@ struct qsc_resident {
     uint8_t *d_valid = nullptr;
     unsigned long long *d_err = nullptr;
     uint32_t *d_plan = nullptr;  // per-tile selected-pixel counts of the current query
+    uint32_t *d_dp_part = nullptr;  // diffraction pattern: n_blocks x P partial sums, then n_blocks scan counts
     void *d_total = nullptr;
     bool total_ready = false;
     uint64_t *d_moments = nullptr;
@@ -67,7 +68,8 @@ hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
 
 void free_all(qsc_resident *res) {
     for (void *p : {(void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
-                    (void *)res->d_err, (void *)res->d_plan, res->d_total, (void *)res->d_moments})
+                    (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, res->d_total,
+                    (void *)res->d_moments})
         if (p) (void)hipFree(p);
 }
 
@@ -269,6 +271,20 @@ qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float
         return hip_fail(res, e, "moment buffer");
     e = launch_query(res->dev, d_mask, 0, 1, Op::Moments, res->d_moments, 1, 0, nullptr, 3 * res->g.S(), st);
     if (e == hipSuccess) e = launch_com_finalize(res->d_moments, res->g.S(), d_row, d_col, st);
+    return finish_query(res, e, st, wait);
+}
+
+qsc_status qsc_sum_dp(qsc_resident *res, const uint8_t *d_scan_mask, uint32_t block_stride, uint64_t *d_sum,
+                      float *d_mean, void *hip_stream, int wait) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    if (!d_sum || block_stride < 1) return fail(res, QSC_ERR_INVALID_ARG, "sum_dp: bad argument");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const uint64_t nb = res->g.n_blocks(), P = res->g.P();
+    hipError_t e = hipSuccess;
+    if (!res->d_dp_part && (e = dalloc(res, &res->d_dp_part, 4 * (nb * P + nb))) != hipSuccess)
+        return hip_fail(res, e, "diffraction-pattern scratch");
+    e = launch_dp(res->dev, d_scan_mask, block_stride, res->d_dp_part, res->d_dp_part + nb * P, d_sum, d_mean, st);
     return finish_query(res, e, st, wait);
 }
 

@@ -7,7 +7,10 @@ variant, from its own calibration of the sampled regions). Properties that hold
 at any size are checked on every scan:
 - dense DF plus the masked sum of its complement equals the full total;
 - a stride-k output equals the stride-1 output on visited blocks and is zero
-  elsewhere.
+  elsewhere;
+- the diffraction pattern summed over pixels equals the full-detector virtual
+  image summed over the same scans (the pattern itself is checked on sampled
+  pixels, whose values over every scan are kept while encoding).
 """
 import numpy as np
 import pytest
@@ -37,18 +40,37 @@ def u(t):
     return q().as_unsigned(t).astype(np.uint64)
 
 
-def encode_full(w, scaled=False):
-    """The whole workload, generated and encoded in order, 16 blocks at a time."""
+def encode_full(w, scaled=False, keep=None):
+    """The whole workload, generated and encoded in order, 16 blocks at a time.
+
+    keep: pixel indices whose values over every scan are returned as well
+    (counts, or for a scaled workload the oracle's codes, with the oracle's
+    calibration of each region), for sampled diffraction-pattern checks.
+    """
     enc = q().Encoder(w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, dtype=w.dtype, layout=w.layout,
                       scaled=scaled)
+    cols, cal = [], []
     try:
         step = 16 * BLOCK
         for s0 in range(0, w.S, step):
             n = min(step, w.S - s0)
-            enc.add(synth.scaled(w, s0, n) if scaled else synth.counts(w, s0, n))
-        return enc.blob()
+            x = synth.scaled(w, s0, n) if scaled else synth.counts(w, s0, n)
+            enc.add(x)
+            if keep is None:
+                continue
+            if not scaled:
+                cols.append(x[:, keep])
+                continue
+            for b0 in range(0, n, BLOCK):
+                sc, off, codes = oracle.calibrate(x[b0:b0 + BLOCK])
+                cal.append((sc, off))
+                cols.append(codes.reshape(-1, w.P)[:, keep])
+        blob = enc.blob()
     finally:
         enc.close()
+    if keep is None:
+        return blob
+    return blob, np.concatenate(cols), (np.array(cal) if scaled else None)
 
 
 def sample_scans(w, n, seed):
@@ -91,6 +113,31 @@ def check_rects(res, w, valid, rects):
         assert np.array_equal(got, want), (r0, r1, c0, c1)
 
 
+def check_dp_sampled(res, w, keep, cols, valid, calib=None, strides=(1, 4)):
+    """Sum and mean diffraction pattern on the kept pixels, plus a property on
+    every pixel: the sum over pixels equals the full-detector virtual image
+    summed over the same scans."""
+    vk = None if valid is None else valid[keep]
+    scan_mask = (np.random.default_rng(w.S).random(w.S) < 0.25).astype(np.uint8)
+    for m in (None, scan_mask):
+        for k in strides:
+            s, mean = res.sum_dp(m, k)
+            s = u(s)
+            ws, wm = oracle.sum_dp(cols, m, vk, k, calib)
+            assert np.array_equal(s[keep], ws), k
+            assert np.array_equal(mean.cpu().numpy()[keep], wm), k
+            if calib is None:
+                vi = u(res.masked_sum(np.ones(w.P, np.uint8), block_stride=k))
+                sel = np.ones(w.S, bool) if m is None else m != 0
+                assert int(s.sum()) == int(vi[sel].sum()), k
+
+
+def keep_pixels(w, n, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, w.P // 2 + w.det_cols // 2, w.P - 1]  # a corner, the disk centre, the last pixel
+    return np.array(sorted(set(fixed) | set(int(p) for p in rng.choice(w.P, size=n, replace=False))))
+
+
 def rects_for(w, seed):
     rng = np.random.default_rng(seed)
     out = [(0, 8, 0, 8), (1, 9, w.scan_cols // 2 - 4, w.scan_cols // 2 + 4),
@@ -110,7 +157,9 @@ def test_u16_256x256_with_sentinels_full_size():
     full = np.ones(w.P, np.uint8)
     scans = sample_scans(w, 40, 31)
     sampled = rows(w, scans)
-    with q().Resident(encode_full(w), valid=valid) as res:
+    keep = keep_pixels(w, 12, 34)
+    blob, cols, _ = encode_full(w, keep=keep)
+    with q().Resident(blob, valid=valid) as res:
         s1 = u(res.masked_sum(bf))
         assert np.array_equal(s1[scans], oracle.masked_sum(sampled, bf, valid))
         check_stride(s1, u(res.masked_sum(bf, block_stride=4)), 4)
@@ -123,6 +172,7 @@ def test_u16_256x256_with_sentinels_full_size():
         check_com_rows(res, w, None, valid, scans, sampled)
         check_com_rows(res, w, bf, valid, scans, sampled)
         check_rects(res, w, valid, rects_for(w, 32))
+        check_dp_sampled(res, w, keep, cols, valid)
         res.finish()
 
 
@@ -130,7 +180,10 @@ def test_scaled_u16_256x256_full_size():
     w = synth.WORKLOADS["scan256_u16_sentinel"]
     bf = synth.query_masks(w)["bf"]
     rects = rects_for(w, 33)
-    with q().Resident(encode_full(w, scaled=True)) as res:
+    keep = keep_pixels(w, 8, 35)
+    blob, cols, cal = encode_full(w, scaled=True, keep=keep)
+    with q().Resident(blob) as res:
+        check_dp_sampled(res, w, keep, cols, None, calib=cal, strides=(1, 3))
         sums = u(res.masked_sum(bf))
         region_cache = {}
 
@@ -167,7 +220,10 @@ def test_u8_512x512_low_dose_full_size():
     sweep = synth.sweep_masks(w)
     scans = sample_scans(w, 32, 41)
     sampled = rows(w, scans)
-    with q().Resident(encode_full(w)) as res:
+    keep = keep_pixels(w, 12, 43)
+    blob, cols, _ = encode_full(w, keep=keep)
+    with q().Resident(blob) as res:
+        check_dp_sampled(res, w, keep, cols, None)
         for name, m in masks.items():
             s1 = u(res.masked_sum(m))
             assert np.array_equal(s1[scans], oracle.masked_sum(sampled, m)), name
@@ -186,8 +242,11 @@ def test_paired_u16_1024x1024_full_size():
     bf, df = masks["bf"], masks["df"]
     scans = sample_scans(w, 24, 51)
     sampled = rows(w, scans)
-    with q().Resident(encode_full(w)) as res:
+    keep = keep_pixels(w, 12, 53)
+    blob, cols, _ = encode_full(w, keep=keep)
+    with q().Resident(blob) as res:
         assert res.info.geom.layout == 1
+        check_dp_sampled(res, w, keep, cols, None)
         s1 = u(res.masked_sum(bf))
         assert np.array_equal(s1[scans], oracle.masked_sum(sampled, bf))
         check_stride(s1, u(res.masked_sum(bf, block_stride=4)), 4)

@@ -73,7 +73,20 @@ def check_all_products(w, counts, valid, blob, masks, df_mask, rects, strides=(1
         for (r0, r1, c0, c1) in rects:
             got = q().as_unsigned(res.decode_region(r0, r1, c0, c1))
             assert np.array_equal(got, oracle.region(counts, w.scan_cols, r0, r1, c0, c1, valid)), (r0, r1, c0, c1)
+        check_dp(res, counts, valid, strides)
         res.finish()
+
+
+def check_dp(res, counts, valid, strides=(1,), calib=None):
+    """Sum and mean diffraction pattern: every scan, a random scan selection, each stride."""
+    S = counts.shape[0]
+    rng = np.random.default_rng(S)
+    for scan_mask in (None, (rng.random(S) < 0.3).astype(np.uint8)):
+        for k in strides:
+            s, m = res.sum_dp(scan_mask, k)
+            ws, wm = oracle.sum_dp(counts, scan_mask, valid, k, calib)
+            assert np.array_equal(u(s), ws), k
+            assert np.array_equal(m.cpu().numpy(), wm), k
 
 
 def random_rects(w, n, seed, size=8):
@@ -131,6 +144,8 @@ def test_scaled_region_reads():
         # integer products of a scaled resident are exact sums of the codes
         bf = synth.query_masks(w)["bf"]
         assert np.array_equal(u(res.masked_sum(bf)), oracle.masked_sum(codes, bf))
+        # the mean diffraction pattern of a scaled resident is that of its calibrated intensities
+        check_dp(res, codes, None, (1, 2), calib=cal)
 
 
 def test_u8_low_dose():
@@ -185,6 +200,7 @@ def test_uint64_sums_257_detector(layout):
         check_com(res, c, synth.Workload("x", 2, 512, 257, 257, 2, 0, 0, 0, 0, 0, 0, 0, 0, layout), None, valid)
         got = q().as_unsigned(res.decode_region(0, 1, 3, 8))
         assert np.array_equal(got, oracle.region(c, 512, 0, 1, 3, 8, valid))
+        check_dp(res, c, valid)  # per-pixel sums of 1024 scans of 65535 pass 2^26: u64 storage
 
 
 @pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
@@ -203,6 +219,22 @@ def test_adversarial_streams(dtype, layout, det):
     masks = {"all": np.ones(P, np.uint8), "half": (np.arange(P) % 2).astype(np.uint8)}
     check_all_products(w, c, valid, blob, masks, masks["half"], [(0, sr, 0, sc), (1, 2, 5, 40)],
                        strides=(1, 2))
+
+
+def test_sum_dp_edge_cases():
+    w, counts, valid, blob = case("tiny_u8")
+    with q().Resident(blob) as res:
+        s, m = res.sum_dp(np.zeros(w.S, np.uint8))  # no scan selected
+        assert not u(s).any() and not m.cpu().numpy().any()
+        one = np.zeros(w.S, np.uint8)
+        one[37] = 1  # a single scan: the sum is that frame
+        s, m = res.sum_dp(one)
+        assert np.array_equal(u(s), counts[37].astype(np.uint64))
+        assert np.array_equal(m.cpu().numpy(), counts[37].astype(np.float32))
+        a, _ = res.sum_dp()
+        b, _ = res.sum_dp()
+        assert np.array_equal(u(a), u(b))
+        res.finish()
 
 
 def test_empty_mask_and_determinism():
@@ -256,6 +288,8 @@ def test_malformed_stream_fails_the_query():
             res.decode_region(0, 16, 0, 16)
         with pytest.raises(qq.QscValueError):
             res.com()
+        with pytest.raises(qq.QscValueError):
+            res.sum_dp()
 
 
 def test_argument_errors():
