@@ -247,6 +247,26 @@ def main():
     dp_ms = float(np.median([a.elapsed_time(b) for a, b in dp_ev]))
     dp_counts = w.S * int((np.ones(w.P, bool) if valid is None else valid.astype(bool)).sum())
 
+    # the reconstruction feed: every block decoded back to frames, native counts
+    # and float32 square-root amplitude (the paired-resident page's feed table)
+    feed = {}
+    for kind in ("native", "amplitude"):
+        fbuf = res.decode_blocks(0, res.info.n_blocks, kind, wait=True)
+        f_ev = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            res.decode_blocks(0, res.info.n_blocks, kind, out=fbuf.view(-1), wait=False)
+            b.record(stream)
+            f_ev.append((a, b))
+        torch.cuda.synchronize()
+        res.finish()
+        f_ms = float(np.median([a.elapsed_time(b) for a, b in f_ev]))
+        feed[kind] = {"ms": round(f_ms, 4), "counts_per_s": round(w.S * w.P / (f_ms * 1e-3), 1),
+                      "out_GBps": round(fbuf.numel() * fbuf.element_size() / (f_ms * 1e-3) / 1e9, 1)}
+        del fbuf
+        torch.cuda.empty_cache()
+
     com_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["com_full"]]))
     com_gbps = by_full / (com_ms * 1e-3) / 1e9
     tops = cn_full * ALG_OPS_MOMENTS / (com_ms * 1e-3) / 1e12
@@ -278,7 +298,8 @@ def main():
         "setup_s": round(t_setup, 2),
         "roofline": roofline,
         "next_rows": {"sum_dp": {"ms": round(dp_ms, 4), "counts_per_s": round(dp_counts / (dp_ms * 1e-3), 1),
-                                 "what": "sum + mean diffraction pattern over every scan (not in the step)"}},
+                                 "what": "sum + mean diffraction pattern over every scan (not in the step)"},
+                      "decode_blocks": dict(feed, what="every block decoded to frames (not in the step)")},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, masks, df_mask, args.cpu_sample_blocks)

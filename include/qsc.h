@@ -137,6 +137,14 @@ qsc_status qsc_resident_info(const qsc_resident *res, qsc_info *info);
  *   0: native dtype; 1: float32 calibrated intensity code*scale+offset of the
  *   scan's region (scaled residents only). Empty or out-of-range rectangle,
  *   or out_kind 1 on an unscaled resident -> INVALID_ARG.
+ * qsc_decode_blocks: every scan of blocks first_block .. first_block +
+ *   n_blocks - 1 decoded back to frames, the reconstruction feed of the
+ *   paired-resident page ("Operation pipeline" item 6, decode_blocks; the
+ *   feed table gives native counts and counts with a float32 square-root
+ *   amplitude): out[(s - 512*first_block) * P + p]; invalid pixels read 0.
+ *   out_kind 0: native dtype; 1: float32 calibrated intensity (scaled
+ *   residents only); 2: float32 sqrt(count), correctly rounded. A range past
+ *   the last block or a bad kind -> INVALID_ARG.
  * qsc_sum_dp: sum and mean diffraction pattern over the selected scans, the
  *   dual of a virtual image (scaled-uint16 page, "MPS implementation": mean
  *   diffraction queries accumulated straight from the encoded resident; the
@@ -163,6 +171,8 @@ qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float
                    int wait);
 qsc_status qsc_decode_region(qsc_resident *res, uint32_t r0, uint32_t r1, uint32_t c0, uint32_t c1, int out_kind,
                              void *d_out, void *hip_stream, int wait);
+qsc_status qsc_decode_blocks(qsc_resident *res, uint32_t first_block, uint32_t n_blocks, int out_kind, void *d_out,
+                             void *hip_stream, int wait);
 qsc_status qsc_sum_dp(qsc_resident *res, const uint8_t *d_scan_mask, uint32_t block_stride, uint64_t *d_sum,
                       float *d_mean, void *hip_stream, int wait);
 qsc_status qsc_finish(qsc_resident *res, void *hip_stream);

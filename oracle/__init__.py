@@ -203,6 +203,26 @@ def region(counts, scan_cols, r0, r1, c0, c1, valid=None):
     return out
 
 
+def frames(counts, first_block, n_blocks, valid=None, kind="native", calib=None):
+    """Every scan of the block range as frames (scans, P), invalid pixels zeroed.
+
+    kind "native": the counts; "amplitude": float32 square root of each count
+    (NumPy's float32 sqrt, correctly rounded); "calibrated": code*scale+offset
+    of each scan's region (calib: (n_blocks, 2) float64 of a scaled resident).
+    """
+    s0 = first_block * BLOCK
+    s1 = min(counts.shape[0], (first_block + n_blocks) * BLOCK)
+    out = counts[s0:s1].copy()
+    if kind == "amplitude":
+        out = np.sqrt(out.astype(np.float32))
+    elif kind == "calibrated":
+        rows = [reconstruct(out[i], *calib[(s0 + i) // BLOCK]) for i in range(out.shape[0])]
+        out = np.stack(rows)
+    if valid is not None:
+        out[:, np.asarray(valid) == 0] = 0
+    return out
+
+
 def calibrate(x):
     """(scale, offset, codes) of one region of float32 values."""
     a = np.ascontiguousarray(x, dtype=np.float32).ravel()

@@ -14,6 +14,7 @@ Entry points mirror include/qsc.h:
     Resident.com(mask=None)                  qsc_com
     Resident.decode_region(r0, r1, c0, c1)   qsc_decode_region
     Resident.sum_dp(scan_mask, stride)       qsc_sum_dp
+    Resident.decode_blocks(first, n, kind)   qsc_decode_blocks
     Resident.finish()                        qsc_finish
     Resident.query_bytes(mask, stride)       qsc_query_bytes
 """
@@ -73,6 +74,7 @@ _SIGS = {
     "qsc_com": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_decode_region": ([_vp, _u32, _u32, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
     "qsc_sum_dp": ([_vp, _vp, _u32, _vp, _vp, _vp, ctypes.c_int], _i32),
+    "qsc_decode_blocks": ([_vp, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
     "qsc_finish": ([_vp, _vp], _i32),
     "qsc_last_error": ([_vp], ctypes.c_char_p),
     "qsc_query_bytes": ([_vp, _vp, _u32, ctypes.POINTER(_u64), ctypes.POINTER(_u64)], _i32),
@@ -235,6 +237,20 @@ class Resident:
         self._check(lib.qsc_decode_region(self._h, r0, r1, c0, c1, 1 if calibrated else 0, o.data_ptr(),
                                           _stream_handle(stream), int(wait)), "decode_region")
         return o.view((r1 - r0) * (c1 - c0), self.P)
+
+    def decode_blocks(self, first_block, n_blocks, kind="native", out=None, stream=None, wait=True):
+        """(scans, P) frames of whole blocks: "native" counts, "calibrated" (scaled) or "amplitude" float32 sqrt."""
+        import torch
+        kinds = {"native": 0, "calibrated": 1, "amplitude": 2}
+        if kind not in kinds:
+            raise ValueError(f"kind must be one of {sorted(kinds)}")
+        s0 = first_block * 512
+        n = max(0, min(self.S, (first_block + n_blocks) * 512) - s0) * self.P
+        dt = torch.float32 if kinds[kind] else (torch.uint8 if self.dtype == 1 else torch.int16)
+        o = self._out(out, dt, n)
+        self._check(lib.qsc_decode_blocks(self._h, first_block, n_blocks, kinds[kind], o.data_ptr(),
+                                          _stream_handle(stream), int(wait)), "decode_blocks")
+        return o.view(-1, self.P)
 
     def sum_dp(self, scan_mask=None, block_stride=1, out_sum=None, out_mean=None, stream=None, wait=True):
         """Sum (int64 storage of uint64) and mean (float32) diffraction pattern over the selected scans."""

@@ -339,30 +339,37 @@ __device__ __forceinline__ uint32_t dp_count(const uint32_t *bits) {
 
 // ------------------------------------------------------------------ region output
 template <bool WIDE>
-__device__ __forceinline__ void region_put(void *out, int out_kind, uint64_t idx, uint32_t v, double scale,
+__device__ __forceinline__ void region_put(const RegionArgs &ra, uint64_t idx, uint32_t v, double scale,
                                            double offset) {
+    void *out = ra.out;
+    const int out_kind = ra.out_kind;
     if (out_kind == 1)
         reinterpret_cast<float *>(out)[idx] = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
+    else if (out_kind == 2)
+        reinterpret_cast<float *>(out)[idx] = ra.amp[v & 0xFFFFu];  // counts are at most 65535
     else if (WIDE)
         reinterpret_cast<uint16_t *>(out)[idx] = (uint16_t)v;
     else
         reinterpret_cast<uint8_t *>(out)[idx] = (uint8_t)v;
 }
 
-// Scan walk of one block for a region read: (row, col) of scan s0 + j, the
-// output index of an in-rectangle scan, and the calibration of the block.
+// Scan walk of one block for a region read: (row, col) and index s of scan
+// s0 + j, the output index of a written scan, and the calibration of the block.
 struct RegionWalk {
     uint32_t row, col;
+    uint64_t s;
     uint32_t scan_cols;
     const RegionArgs *ra;
     double scale, offset;
     __device__ __forceinline__ bool inside() const {
-        return row >= ra->r0 && row < ra->r1 && col >= ra->c0 && col < ra->c1;
+        return ra->frames || (row >= ra->r0 && row < ra->r1 && col >= ra->c0 && col < ra->c1);
     }
     __device__ __forceinline__ uint64_t index(uint32_t P) const {
+        if (ra->frames) return (s - ra->s_first) * P;
         return ((uint64_t)(row - ra->r0) * (ra->c1 - ra->c0) + (col - ra->c0)) * P;
     }
     __device__ __forceinline__ void next() {
+        s++;
         if (++col == scan_cols) {
             col = 0;
             row++;
@@ -375,6 +382,7 @@ __device__ __forceinline__ RegionWalk region_walk(const DevResident &r, uint32_t
     const uint64_t s0 = (uint64_t)b * kBlk;
     rw.row = (uint32_t)(s0 / r.scan_cols);
     rw.col = (uint32_t)(s0 % r.scan_cols);
+    rw.s = s0;
     rw.scan_cols = r.scan_cols;
     rw.ra = &ra;
     rw.scale = 1.0;
@@ -392,7 +400,7 @@ __device__ __forceinline__ void region_fill(const DevResident &r, uint32_t b, ui
                                             const RegionArgs &ra) {
     RegionWalk rw = region_walk(r, b, ra);
     for (uint32_t j = 0; j < n; j++, rw.next())
-        if (rw.inside()) region_put<WIDE>(ra.out, ra.out_kind, rw.index(r.P) + p, v, rw.scale, rw.offset);
+        if (rw.inside()) region_put<WIDE>(ra, rw.index(r.P) + p, v, rw.scale, rw.offset);
 }
 
 // ------------------------------------------------------------------ byte-rANS tile
@@ -562,7 +570,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     const uint64_t idx = rw.index(r.P);
 #pragma unroll
                     for (int k = 0; k < K; k++)
-                        if (sl[k].live) region_put<WIDE>(ra.out, ra.out_kind, idx + sl[k].p, v[k], rw.scale, rw.offset);
+                        if (sl[k].live) region_put<WIDE>(ra, idx + sl[k].p, v[k], rw.scale, rw.offset);
                 }
                 rw.next();
             };
@@ -829,7 +837,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     const uint64_t s = (uint64_t)b * kBlk + (uint32_t)pos;
                     rw.row = (uint32_t)(s / r.scan_cols);
                     rw.col = (uint32_t)(s % r.scan_cols);
-                    if (rw.inside()) region_put<WIDE>(ra.out, ra.out_kind, rw.index(r.P) + z.p, v, rw.scale, rw.offset);
+                    rw.s = s;
+                    if (rw.inside()) region_put<WIDE>(ra, rw.index(r.P) + z.p, v, rw.scale, rw.offset);
                 } else if constexpr (OP == Op::Dp) {
                     dsum += v * scan_bit(dt, (uint32_t)pos);
                 } else {
@@ -952,7 +961,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                         for (int k = 0; k < K; k++) {
                             const uint32_t mode = sl[k].meta & 7u;
                             if (mode == 3 || mode == 4)
-                                region_put<WIDE>(ra.out, ra.out_kind, idx + sl[k].p, sl[k].a0 + (h ? v1[k] : v0[k]),
+                                region_put<WIDE>(ra, idx + sl[k].p, sl[k].a0 + (h ? v1[k] : v0[k]),
                                                  rw.scale, rw.offset);
                         }
                     }

@@ -40,12 +40,18 @@ struct DpArgs {
     uint32_t *nb;    // n_visited
 };
 
-// A region read: half-open scan rectangle, output buffer and kind
-// (0 native dtype, 1 float32 code*scale+offset of the scan's region).
+// A region read: half-open scan rectangle, output buffer and kind (0 native
+// dtype, 1 float32 code*scale+offset of the scan's region, 2 float32 square
+// root of the count, looked up in amp: 65536 correctly rounded values). With
+// frames set, every scan of the listed blocks is written instead, at row
+// s - s_first.
 struct RegionArgs {
     uint32_t r0, r1, c0, c1;
     int out_kind;
     void *out;
+    int frames;
+    uint64_t s_first;
+    const float *amp;
 };
 
 // Blocks touched by a region read, passed by value to one launch.

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <memory>
 #include <new>
 
@@ -34,6 +35,7 @@ struct qsc_resident {
     unsigned long long *d_err = nullptr;
     uint32_t *d_plan = nullptr;  // per-tile selected-pixel counts of the current query
     uint32_t *d_dp_part = nullptr;  // diffraction pattern: n_blocks x P partial sums, then n_blocks scan counts
+    float *d_amp = nullptr;         // sqrt of 0..65535, correctly rounded (amplitude frames)
     void *d_total = nullptr;
     bool total_ready = false;
     uint64_t *d_moments = nullptr;
@@ -68,7 +70,7 @@ hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
 
 void free_all(qsc_resident *res) {
     for (void *p : {(void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
-                    (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, res->d_total,
+                    (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, (void *)res->d_amp, res->d_total,
                     (void *)res->d_moments})
         if (p) (void)hipFree(p);
 }
@@ -311,11 +313,45 @@ qsc_status qsc_decode_region(qsc_resident *res, uint32_t r0, uint32_t r1, uint32
         e = launch_zero_bytes(d_out, uint64_t(r1 - r0) * (c1 - c0) * g.P() * elem, st);
     }
     // the touched-block list travels as kernel launches of up to 64 blocks each (no device staging buffer)
-    const RegionArgs ra{r0, r1, c0, c1, out_kind, d_out};
+    const RegionArgs ra{r0, r1, c0, c1, out_kind, d_out, 0, 0, nullptr};
     for (size_t i = 0; i < blocks.size() && e == hipSuccess; i += 64) {
         RegionBlocks rb{};
         rb.n = uint32_t(std::min<size_t>(64, blocks.size() - i));
         for (uint32_t k = 0; k < rb.n; k++) rb.b[k] = blocks[i + k];
+        e = launch_region(res->dev, rb, ra, st);
+    }
+    return finish_query(res, e, st, wait);
+}
+
+qsc_status qsc_decode_blocks(qsc_resident *res, uint32_t first_block, uint32_t n_blocks, int out_kind, void *d_out,
+                             void *hip_stream, int wait) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    const Geometry &g = res->g;
+    if (!d_out || n_blocks < 1 || first_block >= g.n_blocks() || n_blocks > g.n_blocks() - first_block ||
+        out_kind < 0 || out_kind > 2 || (out_kind == 1 && !g.scaled))
+        return fail(res, QSC_ERR_INVALID_ARG, "decode_blocks: bad block range or output kind");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const uint64_t s0 = uint64_t(first_block) * kBlock;
+    const uint64_t s1 = std::min<uint64_t>(g.S(), uint64_t(first_block + n_blocks) * kBlock);
+    hipError_t e = hipSuccess;
+    if (res->n_valid < g.P()) {  // invalid pixels read 0
+        const uint64_t elem = out_kind ? 4 : g.dtype;
+        e = launch_zero_bytes(d_out, (s1 - s0) * g.P() * elem, st);
+    }
+    if (out_kind == 2 && !res->d_amp) {
+        // the host's IEEE square root, rounded once to float32, for every count
+        std::vector<float> amp(65536);
+        for (uint32_t c = 0; c < 65536; c++) amp[c] = std::sqrt(float(c));
+        if ((e = dalloc(res, &res->d_amp, 4 * amp.size())) != hipSuccess) return hip_fail(res, e, "amplitude table");
+        if ((e = hipMemcpy(res->d_amp, amp.data(), 4 * amp.size(), hipMemcpyHostToDevice)) != hipSuccess)
+            return hip_fail(res, e, "amplitude table upload");
+    }
+    const RegionArgs ra{0, 0, 0, 0, out_kind, d_out, 1, s0, res->d_amp};
+    for (uint32_t i = 0; i < n_blocks && e == hipSuccess; i += 64) {
+        RegionBlocks rb{};
+        rb.n = std::min<uint32_t>(64, n_blocks - i);
+        for (uint32_t k = 0; k < rb.n; k++) rb.b[k] = first_block + i + k;
         e = launch_region(res->dev, rb, ra, st);
     }
     return finish_query(res, e, st, wait);

@@ -74,7 +74,21 @@ def check_all_products(w, counts, valid, blob, masks, df_mask, rects, strides=(1
             got = q().as_unsigned(res.decode_region(r0, r1, c0, c1))
             assert np.array_equal(got, oracle.region(counts, w.scan_cols, r0, r1, c0, c1, valid)), (r0, r1, c0, c1)
         check_dp(res, counts, valid, strides)
+        check_frames(res, counts, valid)
         res.finish()
+
+
+def check_frames(res, counts, valid, calib=None):
+    """Whole-block frames: the first block, the last (possibly partial) one and a run of two."""
+    nb = (counts.shape[0] + 511) // 512
+    ranges = [(0, 1), (nb - 1, 1)] + ([(1, 2)] if nb > 2 else [])
+    kinds = ("native", "amplitude") + (("calibrated",) if calib is not None else ())
+    for first, n in ranges:
+        for kind in kinds:
+            got = res.decode_blocks(first, n, kind)
+            got = q().as_unsigned(got) if kind == "native" else got.cpu().numpy()
+            want = oracle.frames(counts, first, n, valid, kind, calib)
+            assert np.array_equal(got, want), (first, n, kind)
 
 
 def check_dp(res, counts, valid, strides=(1,), calib=None):
@@ -146,6 +160,7 @@ def test_scaled_region_reads():
         assert np.array_equal(u(res.masked_sum(bf)), oracle.masked_sum(codes, bf))
         # the mean diffraction pattern of a scaled resident is that of its calibrated intensities
         check_dp(res, codes, None, (1, 2), calib=cal)
+        check_frames(res, codes, None, calib=cal)
 
 
 def test_u8_low_dose():
@@ -290,6 +305,8 @@ def test_malformed_stream_fails_the_query():
             res.com()
         with pytest.raises(qq.QscValueError):
             res.sum_dp()
+        with pytest.raises(qq.QscValueError):
+            res.decode_blocks(0, 1)
 
 
 def test_argument_errors():
@@ -305,3 +322,10 @@ def test_argument_errors():
         with pytest.raises(ValueError):
             res.masked_sum(np.ones(5, np.uint8))
         assert qq.lib.qsc_masked_sum(res._h, None, 1, None, None, 1) == qq.ERR_INVALID_ARG
+        with pytest.raises(ValueError):
+            res.decode_blocks(0, 1, "calibrated")  # not a scaled resident
+        with pytest.raises(ValueError):
+            res.decode_blocks(0, 2)  # one block only
+        with pytest.raises(ValueError):
+            res.sum_dp(np.ones(3, np.uint8))
+        assert qq.lib.qsc_sum_dp(res._h, None, 0, None, None, None, 1) == qq.ERR_INVALID_ARG

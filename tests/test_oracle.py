@@ -484,3 +484,30 @@ def test_sum_dp_scaled_mean_is_the_mean_of_the_intensities():
     _, mean = oracle.sum_dp(codes, calib=cal)
     want = y.astype(np.float64).mean(axis=0)
     assert np.abs(mean - want).max() <= 0.5 * cal[:, 0].max() + 1e-6 * np.abs(want).max()
+
+
+# ---------------------------------------------------------------------------
+# frames of whole blocks (the reconstruction feed)
+# ---------------------------------------------------------------------------
+
+def test_frames_amplitude_is_the_correctly_rounded_square_root():
+    c = np.arange(65536, dtype=np.uint16)[None, :]
+    amp = oracle.frames(c, 0, 1, kind="amplitude")[0]
+    # float32 sqrt equals the float64 sqrt rounded once to float32 (no double-rounding case
+    # exists for square roots at these widths) and is exact on perfect squares
+    assert np.array_equal(amp, np.sqrt(c[0].astype(np.float64)).astype(np.float32))
+    k = np.arange(256)
+    assert np.array_equal(amp[k * k], k.astype(np.float32))
+
+
+def test_frames_are_the_decoded_scans():
+    w = synth.WORKLOADS["scan256_u16_sentinel"].with_scans(5, 240)  # 1200 scans: blocks of 512, 512, 176
+    c = synth.counts(w)
+    valid = synth.valid_pixels(w)
+    blob = oracle.encode(c, 5, 240, w.det_rows, w.det_cols)
+    dec = oracle.decode(blob)
+    f = oracle.frames(dec, 1, 2, valid)
+    assert f.shape == (1200 - 512, w.P)
+    want = c[512:].copy()
+    want[:, valid == 0] = 0
+    assert np.array_equal(f, want)
