@@ -132,6 +132,18 @@ def check_dp_sampled(res, w, keep, cols, valid, calib=None, strides=(1, 4)):
                 assert int(s.sum()) == int(vi[sel].sum()), k
 
 
+def check_frames_ends(res, w, valid):
+    """The first and the last block decoded to frames, native and amplitude."""
+    nb = res.info.n_blocks
+    for first in (0, nb - 1):
+        s0, s1 = first * BLOCK, min(w.S, (first + 1) * BLOCK)
+        counts = synth.counts(w, s0, s1 - s0)
+        for kind in ("native", "amplitude"):
+            got = res.decode_blocks(first, 1, kind)
+            got = q().as_unsigned(got) if kind == "native" else got.cpu().numpy()
+            assert np.array_equal(got, oracle.frames(counts, 0, 1, valid, kind)), (first, kind)
+
+
 def keep_pixels(w, n, seed):
     rng = np.random.default_rng(seed)
     fixed = [0, w.P // 2 + w.det_cols // 2, w.P - 1]  # a corner, the disk centre, the last pixel
@@ -173,6 +185,7 @@ def test_u16_256x256_with_sentinels_full_size():
         check_com_rows(res, w, bf, valid, scans, sampled)
         check_rects(res, w, valid, rects_for(w, 32))
         check_dp_sampled(res, w, keep, cols, valid)
+        check_frames_ends(res, w, valid)
         res.finish()
 
 
@@ -233,6 +246,7 @@ def test_u8_512x512_low_dose_full_size():
             assert np.array_equal(outs[i][scans], oracle.masked_sum(sampled, sweep[i])), i
         check_com_rows(res, w, None, None, scans, sampled)
         check_rects(res, w, None, rects_for(w, 42)[:3])
+        check_frames_ends(res, w, None)
         res.finish()
 
 
@@ -256,4 +270,5 @@ def test_paired_u16_1024x1024_full_size():
         assert np.array_equal(d + s1, total)
         check_com_rows(res, w, bf, None, scans, sampled)
         check_rects(res, w, None, rects_for(w, 52)[:3])
+        check_frames_ends(res, w, None)
         res.finish()
