@@ -223,6 +223,85 @@ def frames(counts, first_block, n_blocks, valid=None, kind="native", calib=None)
     return out
 
 
+# ---------------------------------------------------------------------------
+# polar interaction index ("Paired-count resident layout", "Operation pipeline"
+# items 3-4): exact per-scan sums over radial-angular pixel groups, 64-pixel
+# leaves and 16-leaf roots; a mask is answered as index fields plus residual
+# pixels that are decoded
+# ---------------------------------------------------------------------------
+
+LEAF = 64
+ROOT = 16
+
+
+def polar_order(det_rows, det_cols, cr, cc):
+    """Pixels ordered by squared distance from (cr, cc), then by angle.
+
+    The angle is atan2(kr - cr, kc - cc); distinct directions at one distance
+    differ far more than its rounding error, so the order is exact.
+    """
+    kr, kc = np.meshgrid(np.arange(det_rows), np.arange(det_cols), indexing="ij")
+    dr, dc = (kr - cr).ravel(), (kc - cc).ravel()
+    d2 = dr.astype(np.int64) ** 2 + dc.astype(np.int64) ** 2
+    ang = np.arctan2(dr.astype(np.float64), dc.astype(np.float64))
+    return np.lexsort((ang, d2))
+
+
+def index_fields(counts, order, valid=None):
+    """Per-scan exact sums of the valid pixels of every leaf and every root: (S, leaves), (S, roots)."""
+    c = counts.astype(np.uint64)
+    if valid is not None:
+        c = c * (np.asarray(valid) != 0)
+    P = c.shape[1]
+    n_leaves = (P + LEAF - 1) // LEAF
+    leaves = np.stack([c[:, order[LEAF * i: LEAF * (i + 1)]].sum(axis=1) for i in range(n_leaves)], axis=1)
+    n_roots = (n_leaves + ROOT - 1) // ROOT
+    roots = np.stack([leaves[:, ROOT * i: ROOT * (i + 1)].sum(axis=1) for i in range(n_roots)], axis=1)
+    return leaves, roots
+
+
+def decompose(mask, order, valid=None):
+    """(full roots, full leaves outside them, residual mask) of mask & valid.
+
+    A leaf (root) is a field of the query when every valid pixel in it is
+    selected and it has one; the residual is every selected valid pixel that
+    no field covers.
+    """
+    P = len(order)
+    v = np.ones(P, bool) if valid is None else np.asarray(valid) != 0
+    sel = (np.asarray(mask) != 0) & v
+    n_leaves = (P + LEAF - 1) // LEAF
+    full_leaf = np.zeros(n_leaves, bool)
+    for i in range(n_leaves):
+        px = order[LEAF * i: LEAF * (i + 1)]
+        full_leaf[i] = v[px].any() and np.array_equal(sel[px], v[px])
+    n_roots = (n_leaves + ROOT - 1) // ROOT
+    full_root = np.zeros(n_roots, bool)
+    for j in range(n_roots):
+        lv = np.arange(ROOT * j, min(n_leaves, ROOT * (j + 1)))
+        px = order[LEAF * lv[0]: min(P, LEAF * (lv[-1] + 1))]
+        full_root[j] = v[px].any() and np.array_equal(sel[px], v[px])
+    leaves = [i for i in range(n_leaves) if full_leaf[i] and not full_root[i // ROOT]]
+    roots = [j for j in range(n_roots) if full_root[j]]
+    covered = np.zeros(P, bool)
+    for i in range(n_leaves):
+        if full_leaf[i] or full_root[i // ROOT]:
+            covered[order[LEAF * i: LEAF * (i + 1)]] = True
+    residual = (sel & ~covered).astype(np.uint8)
+    return roots, leaves, residual
+
+
+def indexed_masked_sum(counts, mask, order, valid=None, stride=1):
+    """masked_sum answered the index way: field sums plus the residual pixels' sums."""
+    leaves, roots = index_fields(counts, order, valid)
+    r, l, residual = decompose(mask, order, valid)
+    out = masked_sum(counts, residual, valid, stride)
+    fields = roots[:, r].sum(axis=1) + leaves[:, l].sum(axis=1)
+    S = counts.shape[0]
+    visited = (np.arange(S) // BLOCK) % stride == 0
+    return out + np.where(visited, fields, 0).astype(np.uint64)
+
+
 def calibrate(x):
     """(scale, offset, codes) of one region of float32 values."""
     a = np.ascontiguousarray(x, dtype=np.float32).ravel()

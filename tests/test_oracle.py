@@ -511,3 +511,65 @@ def test_frames_are_the_decoded_scans():
     want = c[512:].copy()
     want[:, valid == 0] = 0
     assert np.array_equal(f, want)
+
+
+# ---------------------------------------------------------------------------
+# polar interaction index
+# ---------------------------------------------------------------------------
+
+def test_polar_order_puts_centred_disks_first():
+    order = oracle.polar_order(192, 192, 96, 96)
+    assert np.array_equal(np.sort(order), np.arange(192 * 192))
+    pos = np.empty_like(order)
+    pos[order] = np.arange(order.size)
+    for r in (0, 1, 8, 30, 53, 90):
+        disk = np.nonzero(synth.disk_mask(192, 192, 96, 96, r))[0]
+        assert pos[disk].max() == disk.size - 1  # a centred disk is exactly a prefix of the order
+    # within one distance the angle increases
+    kr, kc = np.divmod(order, 192)
+    d2 = (kr - 96) ** 2 + (kc - 96) ** 2
+    ang = np.arctan2(kr - 96, kc - 96)
+    same = d2[1:] == d2[:-1]
+    assert np.all(ang[1:][same] > ang[:-1][same])
+
+
+def test_index_decomposition_partitions_the_mask_and_sums_exactly():
+    rng = np.random.default_rng(71)
+    det = 40
+    P = det * det
+    S = 1100
+    c = rng.poisson(2.0, size=(S, P)).astype(np.uint16)
+    c[:, 7] = 65535
+    valid = np.ones(P, np.uint8)
+    valid[[3, 400, 1000]] = 0
+    order = oracle.polar_order(det, det, 20, 20)
+    leaves, roots = oracle.index_fields(c, order, valid)
+    assert leaves.shape == (S, 25) and roots.shape == (S, 2)
+    assert np.array_equal(roots.sum(axis=1), leaves.sum(axis=1))
+    assert np.array_equal(leaves.sum(axis=1), oracle.masked_sum(c, np.ones(P, np.uint8), valid))
+    masks = {
+        "full": np.ones(P, np.uint8),
+        "empty": np.zeros(P, np.uint8),
+        "disk": synth.disk_mask(det, det, 20, 20, 12),
+        "shifted": synth.disk_mask(det, det, 23, 18, 12),
+        "annulus": synth.annulus_mask(det, det, 20, 20, 6, 15),
+        "random": (rng.random(P) < 0.5).astype(np.uint8),
+    }
+    for name, m in masks.items():
+        r, l, residual = oracle.decompose(m, order, valid)
+        # fields and residual partition mask & valid
+        cover = np.zeros(P, int)
+        for j in r:
+            cover[order[1024 * j: 1024 * (j + 1)]] += 1
+        for i in l:
+            cover[order[64 * i: 64 * (i + 1)]] += 1
+        cover += residual
+        sel = (m != 0) & (valid != 0)
+        assert np.array_equal(cover[valid != 0], sel[valid != 0].astype(int)), name
+        for stride in (1, 2):
+            assert np.array_equal(oracle.indexed_masked_sum(c, m, order, valid, stride),
+                                  oracle.masked_sum(c, m, valid, stride)), (name, stride)
+    r, l, residual = oracle.decompose(masks["full"], order, valid)
+    assert r == [0, 1] and not l and not residual.any()
+    r, l, residual = oracle.decompose(masks["disk"], order, valid)
+    assert not r and len(l) >= 1 and residual.sum() < 64  # a centred disk: leaves plus one partial leaf
