@@ -63,6 +63,7 @@ typedef struct {
     uint64_t resident_bytes; /* device bytes held by the resident */
     uint64_t payload_bytes; /* encoded stream bytes */
     uint64_t mode_counts[8]; /* streams per mode number (FORMAT 2.4 / 3.4) */
+    uint64_t index_bytes;   /* device bytes of the polar interaction index, 0 when none is built */
 } qsc_info;
 
 /* ABI strings of the stream layouts this build reads:
@@ -177,6 +178,22 @@ qsc_status qsc_sum_dp(qsc_resident *res, const uint8_t *d_scan_mask, uint32_t bl
                       float *d_mean, void *hip_stream, int wait);
 qsc_status qsc_finish(qsc_resident *res, void *hip_stream);
 const char *qsc_last_error(const qsc_resident *res);
+
+/* ---------------------------------------------------------------- polar interaction index
+ * qsc_index_build: builds the resident's interaction index (paired-resident
+ *   page, "Operation pipeline" items 3-4): the valid pixels ordered by squared
+ *   distance from (center_row, center_col), then by angle atan2(dr, dc), are
+ *   cut into 64-pixel leaves, and 16 consecutive leaves form a root; the exact
+ *   per-scan sum of every leaf and root is bit-packed per block (each field's
+ *   512 values at the width of its largest). One full decode builds it;
+ *   hip_stream is synchronised. From then on qsc_masked_sum answers a mask as
+ *   the index fields it covers (every valid pixel of a leaf or root selected)
+ *   plus a decode of the residual pixels; results are unchanged, bit for bit.
+ *   Detectors above 65,535 pixels -> UNSUPPORTED; a center outside the
+ *   detector -> INVALID_ARG; a malformed stream -> MALFORMED and no index.
+ *   Building again replaces the index.
+ */
+qsc_status qsc_index_build(qsc_resident *res, int32_t center_row, int32_t center_col, void *hip_stream);
 
 /* Exact encoded bytes and logical counts a masked_sum with this host mask
  * (P bytes) and stride touches: stream bytes of every selected (block, pixel)

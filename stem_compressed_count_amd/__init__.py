@@ -15,6 +15,7 @@ Entry points mirror include/qsc.h:
     Resident.decode_region(r0, r1, c0, c1)   qsc_decode_region
     Resident.sum_dp(scan_mask, stride)       qsc_sum_dp
     Resident.decode_blocks(first, n, kind)   qsc_decode_blocks
+    Resident.index_build(center)             qsc_index_build
     Resident.finish()                        qsc_finish
     Resident.query_bytes(mask, stride)       qsc_query_bytes
 """
@@ -49,7 +50,7 @@ class Geometry(ctypes.Structure):
 class Info(ctypes.Structure):
     _fields_ = [("geom", Geometry), ("n_blocks", ctypes.c_uint32), ("sum_bits", ctypes.c_uint32),
                 ("resident_bytes", ctypes.c_uint64), ("payload_bytes", ctypes.c_uint64),
-                ("mode_counts", ctypes.c_uint64 * 8)]
+                ("mode_counts", ctypes.c_uint64 * 8), ("index_bytes", ctypes.c_uint64)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -76,6 +77,7 @@ _SIGS = {
     "qsc_sum_dp": ([_vp, _vp, _u32, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_decode_blocks": ([_vp, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
     "qsc_finish": ([_vp, _vp], _i32),
+    "qsc_index_build": ([_vp, ctypes.c_int32, ctypes.c_int32, _vp], _i32),
     "qsc_last_error": ([_vp], ctypes.c_char_p),
     "qsc_query_bytes": ([_vp, _vp, _u32, ctypes.POINTER(_u64), ctypes.POINTER(_u64)], _i32),
 }
@@ -170,8 +172,7 @@ class Resident:
                                      _stream_handle(stream), ctypes.byref(self._h))
         if rc:
             _raise(rc, "resident_create")
-        info = Info()
-        lib.qsc_resident_info(self._h, ctypes.byref(info))
+        info = self._info()
         self.info = info
         g = info.geom
         self.scan_rows, self.scan_cols, self.det_rows, self.det_cols = g.scan_rows, g.scan_cols, g.det_rows, g.det_cols
@@ -182,6 +183,11 @@ class Resident:
         self.device = torch.device("cuda", torch.cuda.current_device())
 
     # -- helpers
+    def _info(self):
+        info = Info()
+        lib.qsc_resident_info(self._h, ctypes.byref(info))
+        return info
+
     def _check(self, rc, what):
         if rc:
             _raise(rc, f"{what}: {lib.qsc_last_error(self._h).decode()}")
@@ -265,6 +271,13 @@ class Resident:
         self._check(lib.qsc_sum_dp(self._h, None if m is None else m.data_ptr(), block_stride, s.data_ptr(),
                                    mean.data_ptr(), _stream_handle(stream), int(wait)), "sum_dp")
         return s, mean
+
+    def index_build(self, center=None, stream=None):
+        """Build the polar interaction index around center (default: the detector's middle pixel)."""
+        g = self.info.geom
+        cr, cc = center if center is not None else (g.det_rows // 2, g.det_cols // 2)
+        self._check(lib.qsc_index_build(self._h, int(cr), int(cc), _stream_handle(stream)), "index_build")
+        self.info = self._info()
 
     def finish(self, stream=None):
         self._check(lib.qsc_finish(self._h, _stream_handle(stream)), "finish")

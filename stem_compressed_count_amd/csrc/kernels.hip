@@ -32,6 +32,7 @@ namespace qsc {
 namespace {
 
 constexpr uint32_t kBlk = 512;
+constexpr uint16_t kHole = 0xFFFF;  // a selection-list lane without a pixel (index leaves with invalid pixels)
 constexpr uint32_t kRansWG = 256;   // threads per byte-rANS workgroup
 constexpr uint32_t kPairWG = 1024;  // threads per paired workgroup (one per CU: all 32 tables in LDS)
 
@@ -221,6 +222,13 @@ __device__ __forceinline__ uint32_t wave_transpose_sum(uint32_t (&a)[CH]) {
         v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, false);
         v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, false);
     }
+    return v;
+}
+
+// Sum of one value over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
     return v;
 }
 
@@ -429,7 +437,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
     RSlot sl[K];
-    uint32_t bad = 0, touched = 0;
+    uint32_t bad = 0, touched = 0, cst = 0;
 #pragma unroll
     for (int k = 0; k < K; k++) {
         RSlot &z = sl[k];
@@ -444,7 +452,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         z.s.off = 0x80000000u;
         z.s.pf = 0;
         const uint32_t i = first + k * 64 + lane;
-        if (i >= n_sel) continue;
+        if (i >= n_sel || sel[i] == kHole) continue;
         z.p = p0 + sel[i];
         const Extent e = locate(r, b, z.p, base, nbytes);
         z.org = (uint32_t)(e.start - base);
@@ -461,6 +469,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 region_fill<WIDE>(r, b, n, z.p, v, ra);
             } else if constexpr (OP == Op::Dp) {
                 dt.row[z.p] = v * dt.n_sel;
+            } else if constexpr (OP == Op::Index) {
+                cst += v;  // a constant stream adds v to every scan of the leaf row
             } else {
                 const uint32_t kr = z.p / r.det_cols;
                 if (v) add_event<OP>(pt, -1, v, kr, z.p - kr * r.det_cols);
@@ -631,6 +641,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             const bool writer = lane_writes<CH>();
             const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
             const uint32_t nfull = n / CH;
+            const uint32_t cw = OP == Op::Index ? wave_sum(cst) : 0u;  // the leaf's constant streams
             for (uint32_t c = 0; c < nfull; c++) {
                 uint32_t a0[CH];
                 uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
@@ -661,7 +672,14 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     // keep the scheduler's interleaving to the K independent slots of one step
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
+                if constexpr (OP == Op::Index) {
+                    // one leaf per wave: its per-scan totals go to the leaf's index row
+                    const uint32_t t0 = wave_transpose_sum<CH>(a0) + cw;
+                    if (writer && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + c * CH + my], t0);
+                } else {
+                    chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH,
+                                         pt.mc + c * CH);
+                }
             }
             // ragged end of a final partial block: one scan at a time, reduced per scan
             for (uint32_t j = nfull * CH; j < n; j++) {
@@ -675,6 +693,12 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                         tr += v[k] * kr[k];
                         tc += v[k] * kc[k];
                     }
+                }
+                if constexpr (OP == Op::Index) {
+                    t0 = wave_sum(t0) + cw;
+                    if (lane == 0 && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + j], t0);
+                    if ((j & 1) || j + 1 == n) refill();
+                    continue;
                 }
                 if (t0) atomicAdd(&pt.m0[j], t0);
                 if (OP == Op::Moments) {
@@ -769,7 +793,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
     PSlot sl[K];
-    uint32_t bad = 0, touched = 0;
+    uint32_t bad = 0, touched = 0, cst = 0;
     // window-base contributions, added once per chunk instead of once per value
     uint32_t base0 = 0, baseR = 0, baseC = 0;
 #pragma unroll
@@ -786,7 +810,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         z.s.off = 0x80000000u;
         z.s.pf = 0;
         const uint32_t i = first + k * 64 + lane;
-        if (i >= n_sel) continue;
+        if (i >= n_sel || sel[i] == kHole) continue;
         z.p = p0 + sel[i];
         const uint32_t kr = z.p / r.det_cols, kc = z.p - kr * r.det_cols;
         const Extent e = locate(r, b, z.p, base, nbytes);
@@ -809,6 +833,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 region_fill<WIDE>(r, b, kBlk, z.p, v, ra);
             else if constexpr (OP == Op::Dp)
                 dt.row[z.p] = v * dt.n_sel;
+            else if constexpr (OP == Op::Index)
+                cst += v;
             else
                 add_event<OP>(pt, -1, v, kr, kc);
             continue;
@@ -841,6 +867,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     if (rw.inside()) region_put<WIDE>(ra, rw.index(r.P) + z.p, v, rw.scale, rw.offset);
                 } else if constexpr (OP == Op::Dp) {
                     dsum += v * scan_bit(dt, (uint32_t)pos);
+                } else if constexpr (OP == Op::Index) {
+                    atomicAdd(&dt.row[(first >> 6) * kBlk + (uint32_t)pos], v);
                 } else {
                     add_event<OP>(pt, pos, v, kr, kc);
                 }
@@ -1002,6 +1030,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             const uint32_t my = lane_scan<CH>();
             const bool writer = lane_writes<CH>();
             const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
+            const uint32_t cw = OP == Op::Index ? wave_sum(cst) : 0u;  // the leaf's constant streams
             for (uint32_t c = 0; c < kBlk / CH; c++) {
                 uint32_t a0[CH];
                 uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
@@ -1034,7 +1063,13 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                         asm volatile("" : "+v"(ar[2 * tt]), "+v"(ar[2 * tt + 1]), "+v"(ac[2 * tt]), "+v"(ac[2 * tt + 1]));
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH, pt.mc + c * CH);
+                if constexpr (OP == Op::Index) {
+                    const uint32_t t0 = wave_transpose_sum<CH>(a0) + cw;
+                    if (writer && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + c * CH + my], t0);
+                } else {
+                    chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH,
+                                         pt.mc + c * CH);
+                }
             }
         }
     };
@@ -1153,6 +1188,24 @@ __device__ __forceinline__ Plan plan_items(const uint32_t *counts, uint32_t n_fi
     return Plan{total, mult};
 }
 
+// ------------------------------------------------------------------ index groups
+// One work item of the index build: WG consecutive polar positions, lane l of
+// wave w at position (group * WG / 64 + w) * 64 + l, so every wave decodes one
+// leaf. Invalid pixels and positions past the detector are holes.
+template <int WG>
+__device__ __forceinline__ uint32_t index_group(const DevResident &r, const uint16_t *perm, uint32_t group,
+                                                uint16_t *sel) {
+    const uint32_t pos = group * WG + threadIdx.x;
+    uint16_t px = kHole;
+    if (pos < r.P) {
+        const uint16_t p = perm[pos];
+        if (r.valid[p]) px = p;
+    }
+    sel[threadIdx.x] = px;
+    __syncthreads();
+    return WG;
+}
+
 // ------------------------------------------------------------------ reduce kernels
 template <Op OP>
 struct SharedPartials {
@@ -1244,7 +1297,7 @@ template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                          const uint32_t *plan, void *out, int out64, int negate,
-                                                         RegionBlocks rb, RegionArgs ra, DpArgs da) {
+                                                         RegionBlocks rb, RegionArgs ra, AuxArgs da) {
     __shared__ uint32_t tbl[2 * 4096];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kRansWG];
@@ -1263,14 +1316,17 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     uint32_t loaded = 0xFFFFFFFFu;
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = plan ? tiles[w % n_live] : w % n_live;
-        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = t * tile_px;
+        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = OP == Op::Index ? 0 : t * tile_px;
         __syncthreads();
-        const uint32_t n_sel = select_tile<kRansWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
+        const uint32_t n_sel = OP == Op::Index ? index_group<kRansWG>(r, da.perm, t, sel)
+                                               : select_tile<kRansWG>(r, mask, complement, p0,
+                                                                      min(tile_px, r.P - p0), sel, wtot);
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
         DpTile dt{nullptr, sbits, 0};
+        if constexpr (OP == Op::Index) dt.row = da.rows + ((uint64_t)b * da.n_fields + (uint64_t)t * (kRansWG / 64)) * kBlk;
         if constexpr (OP == Op::Dp) {
             dp_scan_bits<kRansWG>(da.scan_mask, (uint64_t)b * kBlk, n, sbits);
             __syncthreads();
@@ -1288,7 +1344,7 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         if (OP == Op::Sum || OP == Op::Moments) zero_partials<OP>(sp, n);
         __syncthreads();
         // at most two slots per lane: with three decode forms, more do not fit 3 waves per SIMD
-        const uint32_t K = n_sel <= kRansWG ? 1 : 2;
+        const uint32_t K = (OP == Op::Index || n_sel <= kRansWG) ? 1 : 2;  // an index leaf is one wave
         const uint32_t first = (threadIdx.x >> 6) * 64 * K;
         if (first < n_sel) {  // whole waves without a stream skip the decode
             if (K == 2)
@@ -1305,7 +1361,7 @@ template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const uint8_t *mask, int complement,
                                                            uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                            const uint32_t *plan, void *out, int out64, int negate,
-                                                           RegionBlocks rb, RegionArgs ra, DpArgs da) {
+                                                           RegionBlocks rb, RegionArgs ra, AuxArgs da) {
     __shared__ uint32_t tbl[kPairTable];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kPairWG];
@@ -1328,13 +1384,16 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = plan ? tiles[w % n_live] : w % n_live;
-        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = t * tile_px;
+        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = OP == Op::Index ? 0 : t * tile_px;
         __syncthreads();
-        const uint32_t n_sel = select_tile<kPairWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
+        const uint32_t n_sel = OP == Op::Index ? index_group<kPairWG>(r, da.perm, t, sel)
+                                               : select_tile<kPairWG>(r, mask, complement, p0,
+                                                                      min(tile_px, r.P - p0), sel, wtot);
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
         DpTile dt{nullptr, sbits, 0};
+        if constexpr (OP == Op::Index) dt.row = da.rows + ((uint64_t)b * da.n_fields + (uint64_t)t * (kPairWG / 64)) * kBlk;
         if constexpr (OP == Op::Dp) {
             dp_scan_bits<kPairWG>(da.scan_mask, (uint64_t)b * kBlk, kBlk, sbits);
             __syncthreads();
@@ -1346,7 +1405,7 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
         if (OP == Op::Sum || OP == Op::Moments) zero_partials<OP>(sp, kBlk);
         __syncthreads();
         // at most two slots per lane: 1024-thread workgroups have 128 VGPRs per lane
-        const uint32_t K = n_sel <= kPairWG ? 1 : 2;
+        const uint32_t K = (OP == Op::Index || n_sel <= kPairWG) ? 1 : 2;  // an index leaf is one wave
         const uint32_t first = (threadIdx.x >> 6) * 64 * K;
         if (first < n_sel) {
             if (K == 2)
@@ -1434,6 +1493,157 @@ __global__ void k_dp_finalize(const uint32_t *part, const uint32_t *nb, uint32_t
     if (mean) mean[p] = (ok && n) ? (float)__ddiv_rn(calib ? acc : (double)s, (double)n) : 0.0f;
 }
 
+// ------------------------------------------------------------------ polar index: build
+// Root rows (sums of 16 leaf rows) and the bit width of every field row.
+__global__ void __launch_bounds__(512) k_index_widths(uint32_t n_leaves, uint32_t n_roots, uint32_t *rows,
+                                                      uint8_t *width) {
+    const uint32_t n_fields = n_leaves + n_roots;
+    const uint32_t b = blockIdx.y, f = blockIdx.x, j = threadIdx.x;
+    uint32_t *row = rows + ((uint64_t)b * n_fields + f) * kBlk;
+    uint32_t v;
+    if (f < n_leaves) {
+        v = row[j];
+    } else {
+        const uint32_t l0 = (f - n_leaves) * kRoot, l1 = min(l0 + kRoot, n_leaves);
+        v = 0;
+        for (uint32_t l = l0; l < l1; l++) v += rows[((uint64_t)b * n_fields + l) * kBlk + j];
+        row[j] = v;
+    }
+    // bits of the row's largest value
+    uint32_t m = v;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor(m, off));
+    __shared__ uint32_t wmax[kBlk / 64];
+    if ((j & 63u) == 0) wmax[j >> 6] = m;
+    __syncthreads();
+    if (j == 0) {
+        for (uint32_t w = 1; w < kBlk / 64; w++) m = max(m, wmax[w]);
+        m = max(m, wmax[0]);
+        width[(uint64_t)b * n_fields + f] = (uint8_t)(m ? 32 - __clz(m) : 0);
+    }
+}
+
+// Field row (b, f) packed: value j at bits [j*w, j*w + w) of its dword run.
+__global__ void __launch_bounds__(256) k_index_pack(uint32_t n_fields, const uint32_t *rows, const uint32_t *offset,
+                                                    const uint8_t *width, uint32_t *packed) {
+    const uint64_t bf = (uint64_t)blockIdx.y * n_fields + blockIdx.x;
+    const uint32_t w = width[bf];
+    if (!w) return;
+    const uint32_t *row = rows + bf * kBlk;
+    uint32_t *dst = packed + offset[bf];
+    const uint32_t n_dw = (kBlk * w + 31) / 32;
+    for (uint32_t d = threadIdx.x; d < n_dw; d += blockDim.x) {
+        const uint32_t bit0 = 32 * d, bit1 = bit0 + 32;
+        uint32_t word = 0;
+        for (uint32_t j = bit0 / w; j < kBlk && j * w < bit1; j++) {
+            const int sh = (int)(j * w) - (int)bit0;  // position of the value's bit 0 within the dword
+            const uint32_t v = row[j];
+            word |= sh >= 0 ? (v << sh) : (v >> -sh);
+        }
+        dst[d] = word;
+    }
+}
+
+// ------------------------------------------------------------------ polar index: query
+// Decomposition of mask & valid into index fields and residual pixels, by one
+// workgroup: leaf flags in LDS, then roots, the field list (full roots, then
+// full leaves outside them) and the residual mask.
+constexpr uint32_t kMaxLeaves = 1024;  // detectors up to 65,535 pixels
+__global__ void __launch_bounds__(1024) k_index_plan(const DevResident r, DevIndex ix, const uint8_t *mask,
+                                                     uint32_t *fields, uint8_t *residual) {
+    __shared__ uint8_t full[kMaxLeaves];
+    __shared__ uint8_t root_full[kMaxLeaves / kRoot];
+    __shared__ uint32_t wtot[1024 / 64];
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t l = tid; l < ix.n_leaves; l += blockDim.x) {
+        uint32_t c = 0;
+        const uint32_t p1 = min((l + 1) * kLeaf, r.P);
+        for (uint32_t pos = l * kLeaf; pos < p1; pos++) {
+            const uint32_t p = ix.perm[pos];
+            c += (mask[p] != 0) & (r.valid[p] != 0);
+        }
+        full[l] = ix.leaf_valid[l] != 0 && c == ix.leaf_valid[l];
+    }
+    __syncthreads();
+    for (uint32_t q = tid; q < ix.n_roots; q += blockDim.x) {
+        bool all = true, any_valid = false;
+        for (uint32_t l = q * kRoot; l < min((q + 1) * kRoot, ix.n_leaves); l++) {
+            any_valid |= ix.leaf_valid[l] != 0;
+            all &= full[l] || ix.leaf_valid[l] == 0;
+        }
+        root_full[q] = all && any_valid;
+    }
+    __syncthreads();
+    // field list by ballot compaction: roots first, then leaves not inside a full root
+    const uint32_t lane = tid & 63u, wave = tid >> 6;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const uint32_t n_cand = ix.n_roots + ix.n_leaves;
+    uint32_t total = 0;
+    for (uint32_t base = 0; base < n_cand; base += blockDim.x) {
+        const uint32_t c = base + tid;
+        bool f = false;
+        uint32_t id = 0;
+        if (c < ix.n_roots) {
+            f = root_full[c];
+            id = ix.n_leaves + c;
+        } else if (c < n_cand) {
+            const uint32_t l = c - ix.n_roots;
+            f = full[l] && !root_full[l / kRoot];
+            id = l;
+        }
+        const unsigned long long bal = __ballot(f);
+        if (lane == 0) wtot[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t before = total, all = total;
+        for (uint32_t w = 0; w < blockDim.x / 64; w++) {
+            before += w < wave ? wtot[w] : 0u;
+            all += wtot[w];
+        }
+        if (f) fields[1 + before + (uint32_t)__popcll(bal & below)] = id;
+        __syncthreads();
+        total = all;
+    }
+    if (tid == 0) fields[0] = total;
+    // residual: selected valid pixels no field covers (a full root's leaves are all full or empty)
+    for (uint32_t pos = tid; pos < r.P; pos += blockDim.x) {
+        const uint32_t p = ix.perm[pos];
+        residual[p] = (mask[p] != 0) && (r.valid[p] != 0) && !full[pos / kLeaf];
+    }
+}
+
+// Sum of the listed fields of each visited block, added into out (u32/u64 per scan).
+constexpr uint32_t kFieldChunk = 64;
+__global__ void __launch_bounds__(256) k_index_sum(DevIndex ix, const uint32_t *fields, uint32_t stride,
+                                                   uint32_t n_blocks, uint64_t S, void *out, int out64) {
+    const uint32_t n_sel = fields[0];
+    const uint32_t f0 = blockIdx.y * kFieldChunk;
+    if (f0 >= n_sel) return;
+    const uint32_t f1 = min(f0 + kFieldChunk, n_sel);
+    const uint32_t b = blockIdx.x * stride;
+    if (b >= n_blocks) return;
+    const uint32_t n_fields = ix.n_leaves + ix.n_roots;
+    for (uint32_t j = threadIdx.x; j < kBlk; j += blockDim.x) {
+        const uint64_t s = (uint64_t)b * kBlk + j;
+        if (s >= S) break;
+        uint64_t acc = 0;
+        for (uint32_t i = f0; i < f1; i++) {
+            const uint64_t bf = (uint64_t)b * n_fields + fields[1 + i];
+            const uint32_t w = ix.width[bf];
+            if (!w) continue;
+            const uint32_t bit = j * w;
+            const uint32_t *src = ix.packed + ix.offset[bf] + (bit >> 5);
+            // two dwords hold any value of at most 32 bits; the packed buffer is padded
+            const uint64_t two = (uint64_t)src[0] | ((uint64_t)src[1] << 32);
+            acc += (uint32_t)(two >> (bit & 31u)) & (w == 32 ? 0xFFFFFFFFu : ((1u << w) - 1u));
+        }
+        if (!acc) continue;
+        if (out64)
+            atomicAdd(reinterpret_cast<unsigned long long *>(out) + s, (unsigned long long)acc);
+        else
+            atomicAdd(reinterpret_cast<uint32_t *>(out) + s, (uint32_t)acc);
+    }
+}
+
 __global__ void k_com_finalize(const uint64_t *m, uint64_t S, float *row, float *col) {
     for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < S; s += (uint64_t)gridDim.x * blockDim.x) {
         const uint64_t m0 = m[s];
@@ -1504,7 +1714,7 @@ template <typename F>
 static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, hipStream_t st, const DevResident &r,
                          const uint8_t *mask, int complement, uint32_t stride, uint32_t n_visited, void *out, int out64,
                          int negate, const void *init, uint64_t n_init, const RegionBlocks &rb, const RegionArgs &ra,
-                         const DpArgs &da) {
+                         const AuxArgs &da) {
     const uint32_t slots = resident_wgs(kern, threads);
     // a planned query counts the finest tiles and lets the reduce pick the
     // item size; without a plan (region reads, or too many tiles) the host picks
@@ -1528,7 +1738,7 @@ static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, 
 template <bool W, Op O>
 static void launch_layout(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride,
                           uint32_t n_visited, void *out, int out64, int negate, const void *init, uint64_t n_init,
-                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st, const DpArgs &da = DpArgs{}) {
+                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st, const AuxArgs &da = AuxArgs{}) {
     if (r.layout == 0) {
         const uint32_t cands[2] = {2 * kRansWG, kRansWG};
         launch_items(k_reduce_rans<W, O>, kRansWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
@@ -1574,7 +1784,7 @@ hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const
 hipError_t launch_dp(const DevResident &r, const uint8_t *scan_mask, uint32_t stride, uint32_t *part, uint32_t *nb,
                      uint64_t *sum, float *mean, hipStream_t st) {
     const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
-    const DpArgs da{scan_mask, part, nb};
+    const AuxArgs da{scan_mask, part, nb};
     // the init kernel zeroes the per-block scan counts and plans the valid pixels
     if (r.dtype == 2)
         launch_layout<true, Op::Dp>(r, nullptr, 0, stride, n_visited, nb, 0, 0, nullptr, n_visited, RegionBlocks{},
@@ -1584,6 +1794,62 @@ hipError_t launch_dp(const DevResident &r, const uint8_t *scan_mask, uint32_t st
                                      RegionArgs{}, st, da);
     hipLaunchKernelGGL(k_dp_finalize, dim3((r.P + 255) / 256), dim3(256), 0, st, part, nb, n_visited, stride, r.P,
                        r.valid, r.calib, sum, mean);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_leaves(const DevResident &r, const uint16_t *perm, uint32_t n_leaves, uint32_t n_roots,
+                               uint32_t *rows, hipStream_t st) {
+    AuxArgs da{};
+    da.perm = perm;
+    da.rows = rows;
+    da.n_fields = n_leaves + n_roots;
+    const uint32_t n_visited = r.n_blocks;
+    const RegionBlocks rb{};
+    const RegionArgs ra{};
+    // one item = one group of leaves (a workgroup's waves), no plan: tile_px is the group size
+    if (r.layout == 0) {
+        const uint32_t cands[1] = {kRansWG};
+        if (r.dtype == 2)
+            launch_items(k_reduce_rans<true, Op::Index>, kRansWG, cands, 1, st, r, nullptr, 0, 1, n_visited, nullptr,
+                         0, 0, nullptr, 0, rb, ra, da);
+        else
+            launch_items(k_reduce_rans<false, Op::Index>, kRansWG, cands, 1, st, r, nullptr, 0, 1, n_visited, nullptr,
+                         0, 0, nullptr, 0, rb, ra, da);
+    } else {
+        const uint32_t cands[1] = {kPairWG};
+        if (r.dtype == 2)
+            launch_items(k_reduce_paired<true, Op::Index>, kPairWG, cands, 1, st, r, nullptr, 0, 1, n_visited,
+                         nullptr, 0, 0, nullptr, 0, rb, ra, da);
+        else
+            launch_items(k_reduce_paired<false, Op::Index>, kPairWG, cands, 1, st, r, nullptr, 0, 1, n_visited,
+                         nullptr, 0, 0, nullptr, 0, rb, ra, da);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_index_widths(uint32_t n_blocks, uint32_t n_leaves, uint32_t n_roots, uint32_t *rows,
+                               uint8_t *width, hipStream_t st) {
+    hipLaunchKernelGGL(k_index_widths, dim3(n_leaves + n_roots, n_blocks), dim3(kBlk), 0, st, n_leaves, n_roots, rows,
+                       width);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_pack(uint32_t n_blocks, uint32_t n_fields, const uint32_t *rows, const uint32_t *offset,
+                             const uint8_t *width, uint32_t *packed, hipStream_t st) {
+    hipLaunchKernelGGL(k_index_pack, dim3(n_fields, n_blocks), dim3(256), 0, st, n_fields, rows, offset, width, packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_indexed_sum(const DevResident &r, const DevIndex &ix, const uint8_t *mask, uint32_t stride,
+                              void *out, int out64, uint32_t *fields, uint8_t *residual, hipStream_t st) {
+    hipLaunchKernelGGL(k_index_plan, dim3(1), dim3(1024), 0, st, r, ix, mask, fields, residual);
+    // zero the output and decode the residual pixels, then add the index fields
+    hipError_t e = launch_query(r, residual, 0, stride, Op::Sum, out, out64, 0, nullptr, r.S, st);
+    if (e != hipSuccess) return e;
+    const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
+    const uint32_t chunks = (ix.n_leaves + ix.n_roots + kFieldChunk - 1) / kFieldChunk;
+    hipLaunchKernelGGL(k_index_sum, dim3(n_visited, chunks), dim3(256), 0, st, ix, fields, stride, r.n_blocks, r.S,
+                       out, out64);
     return hipGetLastError();
 }
 

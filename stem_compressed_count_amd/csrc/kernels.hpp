@@ -29,15 +29,20 @@ struct DevResident {
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };
 
-enum class Op : int { Sum = 0, Moments = 1, Region = 2, Dp = 3 };
+enum class Op : int { Sum = 0, Moments = 1, Region = 2, Dp = 3, Index = 4 };
 
-// A diffraction-pattern query: the selected scans (null: every scan), the
-// per-(visited block, pixel) partial sums and the per-visited-block count of
-// selected scans it fills.
-struct DpArgs {
+// Buffers of the queries beyond sums and moments.
+//  diffraction pattern: the selected scans (null: every scan), the
+//  per-(visited block, pixel) partial sums and the per-visited-block count of
+//  selected scans it fills;
+//  index build: the polar pixel order and the field rows it fills.
+struct AuxArgs {
     const uint8_t *scan_mask;
     uint32_t *part;  // n_visited x P
     uint32_t *nb;    // n_visited
+    const uint16_t *perm;  // P
+    uint32_t *rows;        // n_blocks x n_fields x 512
+    uint32_t n_fields;
 };
 
 // A region read: half-open scan rectangle, output buffer and kind (0 native
@@ -78,6 +83,33 @@ hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const
 //  n_visited u32 of device scratch.
 hipError_t launch_dp(const DevResident &r, const uint8_t *scan_mask, uint32_t stride, uint32_t *part, uint32_t *nb,
                      uint64_t *sum, float *mean, hipStream_t st);
+// Polar interaction index of a resident: pixels in radial-angular order, 64-pixel
+// leaves, 16-leaf roots; fields = leaves then roots, each block's field rows
+// bit-packed at dword offsets.
+constexpr uint32_t kLeaf = 64, kRoot = 16;
+struct DevIndex {
+    const uint16_t *perm;        // P: pixel at each polar position
+    const uint16_t *leaf_valid;  // n_leaves: valid pixels per leaf
+    const uint32_t *packed;      // bit-packed field rows
+    const uint32_t *offset;      // n_blocks x n_fields dword offsets into packed
+    const uint8_t *width;        // n_blocks x n_fields bits per value
+    uint32_t n_leaves, n_roots;
+};
+//  index build, step 1: exact per-scan leaf sums of every block into rows
+//  (n_blocks x (n_leaves + n_roots) x 512 u32, root rows filled in step 2).
+hipError_t launch_index_leaves(const DevResident &r, const uint16_t *perm, uint32_t n_leaves, uint32_t n_roots,
+                               uint32_t *rows, hipStream_t st);
+//  step 2: root rows and the bit width of every field row.
+hipError_t launch_index_widths(uint32_t n_blocks, uint32_t n_leaves, uint32_t n_roots, uint32_t *rows,
+                               uint8_t *width, hipStream_t st);
+//  step 3: pack every field row at its dword offset.
+hipError_t launch_index_pack(uint32_t n_blocks, uint32_t n_fields, const uint32_t *rows, const uint32_t *offset,
+                             const uint8_t *width, uint32_t *packed, hipStream_t st);
+//  masked_sum through the index: fields covered by mask & valid are summed from
+//  the index, the residual pixels decoded; scratch holds n_leaves + n_roots + 1
+//  u32 (the field list) and P bytes (the residual mask).
+hipError_t launch_indexed_sum(const DevResident &r, const DevIndex &ix, const uint8_t *mask, uint32_t stride,
+                              void *out, int out64, uint32_t *fields, uint8_t *residual, hipStream_t st);
 //  zero n bytes (region outputs of residents with invalid pixels)
 hipError_t launch_zero_bytes(void *out, uint64_t n, hipStream_t st);
 

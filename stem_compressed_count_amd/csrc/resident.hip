@@ -9,6 +9,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
+#include <string>
+#include <tuple>
 #include <cmath>
 #include <memory>
 #include <new>
@@ -36,6 +39,14 @@ struct qsc_resident {
     uint32_t *d_plan = nullptr;  // per-tile selected-pixel counts of the current query
     uint32_t *d_dp_part = nullptr;  // diffraction pattern: n_blocks x P partial sums, then n_blocks scan counts
     float *d_amp = nullptr;         // sqrt of 0..65535, correctly rounded (amplitude frames)
+    // polar interaction index (built on request)
+    std::vector<uint8_t> h_valid;
+    uint16_t *d_ix_perm = nullptr, *d_ix_leaf_valid = nullptr;
+    uint32_t *d_ix_packed = nullptr, *d_ix_offset = nullptr, *d_ix_fields = nullptr;
+    uint8_t *d_ix_width = nullptr, *d_ix_residual = nullptr;
+    DevIndex ix{};
+    bool has_index = false;
+    uint64_t index_bytes = 0;
     void *d_total = nullptr;
     bool total_ready = false;
     uint64_t *d_moments = nullptr;
@@ -70,7 +81,10 @@ hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
 
 void free_all(qsc_resident *res) {
     for (void *p : {(void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
-                    (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, (void *)res->d_amp, res->d_total,
+                    (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, (void *)res->d_amp,
+                    (void *)res->d_ix_perm, (void *)res->d_ix_leaf_valid, (void *)res->d_ix_packed,
+                    (void *)res->d_ix_offset, (void *)res->d_ix_fields, (void *)res->d_ix_width,
+                    (void *)res->d_ix_residual, res->d_total,
                     (void *)res->d_moments})
         if (p) (void)hipFree(p);
 }
@@ -178,6 +192,7 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     if (host_valid)
         for (uint32_t p = 0; p < g.P(); p++) valid[p] = host_valid[p] ? 1 : 0;
     for (uint8_t v : valid) res->n_valid += v;
+    res->h_valid = valid;
     if ((e = dalloc(res.get(), &res->d_valid, g.P())) != hipSuccess) return bail(e, "valid");
     if ((e = hipMemcpy(res->d_valid, valid.data(), g.P(), hipMemcpyHostToDevice)) != hipSuccess)
         return bail(e, "valid upload");
@@ -227,6 +242,7 @@ qsc_status qsc_resident_info(const qsc_resident *res, qsc_info *info) {
     info->resident_bytes = res->device_bytes;
     info->payload_bytes = res->sec.payload_bytes;
     std::copy(res->mode_counts, res->mode_counts + 8, info->mode_counts);
+    info->index_bytes = res->index_bytes;
     return QSC_OK;
 }
 
@@ -237,7 +253,10 @@ qsc_status qsc_masked_sum(qsc_resident *res, const uint8_t *d_mask, uint32_t blo
     if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const int out64 = res->g.sum_bits() == 64;
-    const hipError_t e = launch_query(res->dev, d_mask, 0, block_stride, Op::Sum, d_out, out64, 0, nullptr,
+    const hipError_t e =
+        res->has_index ? launch_indexed_sum(res->dev, res->ix, d_mask, block_stride, d_out, out64, res->d_ix_fields,
+                                            res->d_ix_residual, st)
+                       : launch_query(res->dev, d_mask, 0, block_stride, Op::Sum, d_out, out64, 0, nullptr,
                                       res->g.S(), st);
     return finish_query(res, e, st, wait);
 }
@@ -355,6 +374,113 @@ qsc_status qsc_decode_blocks(qsc_resident *res, uint32_t first_block, uint32_t n
         e = launch_region(res->dev, rb, ra, st);
     }
     return finish_query(res, e, st, wait);
+}
+
+static void drop_index(qsc_resident *res) {
+    for (void **p : {(void **)&res->d_ix_perm, (void **)&res->d_ix_leaf_valid, (void **)&res->d_ix_packed,
+                     (void **)&res->d_ix_offset, (void **)&res->d_ix_fields, (void **)&res->d_ix_width,
+                     (void **)&res->d_ix_residual})
+        if (*p) {
+            (void)hipFree(*p);
+            *p = nullptr;
+        }
+    res->device_bytes -= res->index_bytes;
+    res->index_bytes = 0;
+    res->has_index = false;
+    res->ix = DevIndex{};
+}
+
+qsc_status qsc_index_build(qsc_resident *res, int32_t center_row, int32_t center_col, void *hip_stream) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    const Geometry &g = res->g;
+    const uint32_t P = g.P();
+    if (P > 65535) return fail(res, QSC_ERR_UNSUPPORTED, "index_build: detectors above 65,535 pixels");
+    if (center_row < 0 || center_col < 0 || uint32_t(center_row) >= g.det_rows || uint32_t(center_col) >= g.det_cols)
+        return fail(res, QSC_ERR_INVALID_ARG, "index_build: center outside the detector");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    drop_index(res);
+    // polar order: squared distance, then angle; the sort is stable on pixel index for ties
+    std::vector<std::tuple<int64_t, double, uint32_t>> key(P);
+    for (uint32_t p = 0; p < P; p++) {
+        const int64_t dr = int64_t(p / g.det_cols) - center_row, dc = int64_t(p % g.det_cols) - center_col;
+        key[p] = {dr * dr + dc * dc, std::atan2(double(dr), double(dc)), p};
+    }
+    std::sort(key.begin(), key.end());
+    const uint32_t n_leaves = (P + kLeaf - 1) / kLeaf, n_roots = (n_leaves + kRoot - 1) / kRoot;
+    const uint32_t n_fields = n_leaves + n_roots, nb = g.n_blocks();
+    std::vector<uint16_t> perm(P), leaf_valid(n_leaves, 0);
+    for (uint32_t i = 0; i < P; i++) {
+        perm[i] = uint16_t(std::get<2>(key[i]));
+        leaf_valid[i / kLeaf] += res->h_valid[perm[i]];
+    }
+    const uint64_t bytes0 = res->device_bytes;
+    auto bail = [&](qsc_status s, hipError_t e, const char *what) {
+        drop_index(res);
+        res->device_bytes = bytes0;
+        return e != hipSuccess ? hip_fail(res, e, what) : fail(res, s, what);
+    };
+    hipError_t e;
+    if ((e = dalloc(res, &res->d_ix_perm, 2ull * P)) != hipSuccess ||
+        (e = dalloc(res, &res->d_ix_leaf_valid, 2ull * n_leaves)) != hipSuccess ||
+        (e = dalloc(res, &res->d_ix_width, uint64_t(nb) * n_fields)) != hipSuccess ||
+        (e = dalloc(res, &res->d_ix_offset, 4ull * nb * n_fields)) != hipSuccess ||
+        (e = dalloc(res, &res->d_ix_fields, 4ull * (n_fields + 1))) != hipSuccess ||
+        (e = dalloc(res, &res->d_ix_residual, P)) != hipSuccess)
+        return bail(QSC_OK, e, "index buffers");
+    if ((e = hipMemcpy(res->d_ix_perm, perm.data(), 2ull * P, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(res->d_ix_leaf_valid, leaf_valid.data(), 2ull * n_leaves, hipMemcpyHostToDevice)) != hipSuccess)
+        return bail(QSC_OK, e, "index upload");
+    // exact field rows of every block (a temporary buffer), then their widths
+    uint32_t *rows = nullptr;
+    const uint64_t row_bytes = 4ull * nb * n_fields * kBlock;
+    if ((e = hipMalloc(&rows, row_bytes)) != hipSuccess) return bail(QSC_OK, e, "index rows");
+    e = hipMemsetAsync(rows, 0, row_bytes, st);
+    if (e == hipSuccess) e = launch_index_leaves(res->dev, res->d_ix_perm, n_leaves, n_roots, rows, st);
+    if (e == hipSuccess) e = launch_index_widths(nb, n_leaves, n_roots, rows, res->d_ix_width, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    unsigned long long err = 0;
+    if (e == hipSuccess) e = hipMemcpy(&err, res->dev.err, sizeof(err), hipMemcpyDeviceToHost);
+    if (e != hipSuccess || err) {
+        (void)hipFree(rows);
+        if (e != hipSuccess) return bail(QSC_OK, e, "index build");
+        (void)check_done(res, st);  // reports the malformed stream and clears the error word
+        const std::string why = res->last_error;
+        drop_index(res);
+        res->device_bytes = bytes0;
+        return fail(res, QSC_ERR_MALFORMED, ("index_build: " + why).c_str());
+    }
+    std::vector<uint8_t> width(uint64_t(nb) * n_fields);
+    std::vector<uint32_t> offset(width.size());
+    if ((e = hipMemcpy(width.data(), res->d_ix_width, width.size(), hipMemcpyDeviceToHost)) != hipSuccess) {
+        (void)hipFree(rows);
+        return bail(QSC_OK, e, "index widths");
+    }
+    uint64_t dw = 0;
+    for (size_t i = 0; i < width.size(); i++) {
+        offset[i] = uint32_t(dw);
+        dw += (uint64_t(kBlock) * width[i] + 31) / 32;
+        if (dw >= (1ull << 32) - 4) {
+            (void)hipFree(rows);
+            return bail(QSC_ERR_UNSUPPORTED, hipSuccess, "index_build: index above 16 GB");
+        }
+    }
+    // two spare dwords: a reader fetches the dword after a value's first
+    if ((e = dalloc(res, &res->d_ix_packed, 4 * (dw + 2))) != hipSuccess ||
+        (e = hipMemcpy(res->d_ix_offset, offset.data(), 4 * offset.size(), hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemsetAsync(res->d_ix_packed, 0, 4 * (dw + 2), st)) != hipSuccess) {
+        (void)hipFree(rows);
+        return bail(QSC_OK, e, "index pack buffers");
+    }
+    e = launch_index_pack(nb, n_fields, rows, res->d_ix_offset, res->d_ix_width, res->d_ix_packed, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    (void)hipFree(rows);
+    if (e != hipSuccess) return bail(QSC_OK, e, "index pack");
+    res->ix = DevIndex{res->d_ix_perm, res->d_ix_leaf_valid, res->d_ix_packed, res->d_ix_offset, res->d_ix_width,
+                       n_leaves, n_roots};
+    res->index_bytes = res->device_bytes - bytes0;
+    res->has_index = true;
+    return QSC_OK;
 }
 
 qsc_status qsc_finish(qsc_resident *res, void *hip_stream) {
