@@ -1545,25 +1545,40 @@ __global__ void __launch_bounds__(256) k_index_pack(uint32_t n_fields, const uin
 }
 
 // ------------------------------------------------------------------ polar index: query
-// Decomposition of mask & valid into index fields and residual pixels, by one
-// workgroup: leaf flags in LDS, then roots, the field list (full roots, then
-// full leaves outside them) and the residual mask.
+// Decomposition of mask & valid into index fields and residual pixels, in two
+// kernels. k_index_leaf_flags: one wave per leaf counts the leaf's selected
+// valid pixels (a ballot over its 64 polar positions), flags the leaf full when
+// every valid pixel is selected, and writes the residual mask of its pixels:
+// selected, valid and not in a full leaf (a full root's leaves are all full or
+// without valid pixels, so the leaf flag decides).
 constexpr uint32_t kMaxLeaves = 1024;  // detectors up to 65,535 pixels
-__global__ void __launch_bounds__(1024) k_index_plan(const DevResident r, DevIndex ix, const uint8_t *mask,
-                                                     uint32_t *fields, uint8_t *residual) {
+__global__ void __launch_bounds__(256) k_index_leaf_flags(const DevResident r, DevIndex ix, const uint8_t *mask,
+                                                          uint8_t *leaf_full, uint8_t *residual) {
+    const uint32_t l = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63u;
+    if (l >= ix.n_leaves) return;
+    const uint32_t pos = l * kLeaf + lane;
+    uint32_t p = 0;
+    bool sel = false, val = false;
+    if (pos < r.P) {
+        p = ix.perm[pos];
+        val = r.valid[p] != 0;
+        sel = val && mask[p] != 0;
+    }
+    const uint32_t n_sel = (uint32_t)__popcll(__ballot(sel));
+    const bool full = ix.leaf_valid[l] != 0 && n_sel == ix.leaf_valid[l];
+    if (pos < r.P) residual[p] = sel && !full;
+    if (lane == 0) leaf_full[l] = full;
+}
+
+// k_index_list: roots (every leaf full or without valid pixels, one valid
+// pixel at least) and the field list: full roots, then full leaves outside
+// them; fields[0] holds the count.
+__global__ void __launch_bounds__(1024) k_index_list(DevIndex ix, const uint8_t *leaf_full, uint32_t *fields) {
     __shared__ uint8_t full[kMaxLeaves];
     __shared__ uint8_t root_full[kMaxLeaves / kRoot];
     __shared__ uint32_t wtot[1024 / 64];
     const uint32_t tid = threadIdx.x;
-    for (uint32_t l = tid; l < ix.n_leaves; l += blockDim.x) {
-        uint32_t c = 0;
-        const uint32_t p1 = min((l + 1) * kLeaf, r.P);
-        for (uint32_t pos = l * kLeaf; pos < p1; pos++) {
-            const uint32_t p = ix.perm[pos];
-            c += (mask[p] != 0) & (r.valid[p] != 0);
-        }
-        full[l] = ix.leaf_valid[l] != 0 && c == ix.leaf_valid[l];
-    }
+    for (uint32_t l = tid; l < ix.n_leaves; l += blockDim.x) full[l] = leaf_full[l];
     __syncthreads();
     for (uint32_t q = tid; q < ix.n_roots; q += blockDim.x) {
         bool all = true, any_valid = false;
@@ -1574,7 +1589,6 @@ __global__ void __launch_bounds__(1024) k_index_plan(const DevResident r, DevInd
         root_full[q] = all && any_valid;
     }
     __syncthreads();
-    // field list by ballot compaction: roots first, then leaves not inside a full root
     const uint32_t lane = tid & 63u, wave = tid >> 6;
     const unsigned long long below = (1ull << lane) - 1ull;
     const uint32_t n_cand = ix.n_roots + ix.n_leaves;
@@ -1604,11 +1618,6 @@ __global__ void __launch_bounds__(1024) k_index_plan(const DevResident r, DevInd
         total = all;
     }
     if (tid == 0) fields[0] = total;
-    // residual: selected valid pixels no field covers (a full root's leaves are all full or empty)
-    for (uint32_t pos = tid; pos < r.P; pos += blockDim.x) {
-        const uint32_t p = ix.perm[pos];
-        residual[p] = (mask[p] != 0) && (r.valid[p] != 0) && !full[pos / kLeaf];
-    }
 }
 
 // Sum of the listed fields of each visited block, added into out (u32/u64 per scan).
@@ -1842,7 +1851,11 @@ hipError_t launch_index_pack(uint32_t n_blocks, uint32_t n_fields, const uint32_
 
 hipError_t launch_indexed_sum(const DevResident &r, const DevIndex &ix, const uint8_t *mask, uint32_t stride,
                               void *out, int out64, uint32_t *fields, uint8_t *residual, hipStream_t st) {
-    hipLaunchKernelGGL(k_index_plan, dim3(1), dim3(1024), 0, st, r, ix, mask, fields, residual);
+    // the leaf flags sit after the field list in the same scratch
+    uint8_t *leaf_full = reinterpret_cast<uint8_t *>(fields + ix.n_leaves + ix.n_roots + 1);
+    hipLaunchKernelGGL(k_index_leaf_flags, dim3((ix.n_leaves + 3) / 4), dim3(256), 0, st, r, ix, mask, leaf_full,
+                       residual);
+    hipLaunchKernelGGL(k_index_list, dim3(1), dim3(1024), 0, st, ix, leaf_full, fields);
     // zero the output and decode the residual pixels, then add the index fields
     hipError_t e = launch_query(r, residual, 0, stride, Op::Sum, out, out64, 0, nullptr, r.S, st);
     if (e != hipSuccess) return e;

@@ -106,8 +106,9 @@ hipError_t launch_index_widths(uint32_t n_blocks, uint32_t n_leaves, uint32_t n_
 hipError_t launch_index_pack(uint32_t n_blocks, uint32_t n_fields, const uint32_t *rows, const uint32_t *offset,
                              const uint8_t *width, uint32_t *packed, hipStream_t st);
 //  masked_sum through the index: fields covered by mask & valid are summed from
-//  the index, the residual pixels decoded; scratch holds n_leaves + n_roots + 1
-//  u32 (the field list) and P bytes (the residual mask).
+//  the index, the residual pixels decoded; scratch: fields holds n_leaves +
+//  n_roots + 1 u32 (the field list) then n_leaves bytes (leaf flags),
+//  residual P bytes.
 hipError_t launch_indexed_sum(const DevResident &r, const DevIndex &ix, const uint8_t *mask, uint32_t stride,
                               void *out, int out64, uint32_t *fields, uint8_t *residual, hipStream_t st);
 //  zero n bytes (region outputs of residents with invalid pixels)

@@ -425,7 +425,7 @@ qsc_status qsc_index_build(qsc_resident *res, int32_t center_row, int32_t center
         (e = dalloc(res, &res->d_ix_leaf_valid, 2ull * n_leaves)) != hipSuccess ||
         (e = dalloc(res, &res->d_ix_width, uint64_t(nb) * n_fields)) != hipSuccess ||
         (e = dalloc(res, &res->d_ix_offset, 4ull * nb * n_fields)) != hipSuccess ||
-        (e = dalloc(res, &res->d_ix_fields, 4ull * (n_fields + 1))) != hipSuccess ||
+        (e = dalloc(res, &res->d_ix_fields, 4ull * (n_fields + 1) + n_leaves)) != hipSuccess ||
         (e = dalloc(res, &res->d_ix_residual, P)) != hipSuccess)
         return bail(QSC_OK, e, "index buffers");
     if ((e = hipMemcpy(res->d_ix_perm, perm.data(), 2ull * P, hipMemcpyHostToDevice)) != hipSuccess ||
