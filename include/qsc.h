@@ -195,6 +195,22 @@ const char *qsc_last_error(const qsc_resident *res);
  */
 qsc_status qsc_index_build(qsc_resident *res, int32_t center_row, int32_t center_col, void *hip_stream);
 
+/* qsc_masked_sum_delta: the virtual image of mask computed from that of a
+ *   previous mask (paired-resident page, "Operation pipeline" item 4: a mask
+ *   is decomposed as its difference from the previous mask; the baseline is
+ *   kept per stride): out = prev_out + sum over mask & ~prev_mask -
+ *   sum over prev_mask & ~mask, both over valid pixels of the visited blocks,
+ *   exact (modular arithmetic of the output width cannot overflow the true
+ *   result). d_prev_out must hold masked_sum(prev_mask, block_stride) of this
+ *   resident; d_out may be d_prev_out (in place). Devices pointers as in
+ *   qsc_masked_sum; the first call allocates 2 x P bytes of scratch. After a
+ *   failed query (MALFORMED) the caller's baseline is invalid and must be
+ *   recomputed with qsc_masked_sum.
+ */
+qsc_status qsc_masked_sum_delta(qsc_resident *res, const uint8_t *d_prev_mask, const void *d_prev_out,
+                                const uint8_t *d_mask, uint32_t block_stride, void *d_out, void *hip_stream,
+                                int wait);
+
 /* Exact encoded bytes and logical counts a masked_sum with this host mask
  * (P bytes) and stride touches: stream bytes of every selected (block, pixel)
  * plus its offset entries, and n_visited_scans x n_selected counts. This is

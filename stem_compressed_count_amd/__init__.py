@@ -16,6 +16,7 @@ Entry points mirror include/qsc.h:
     Resident.sum_dp(scan_mask, stride)       qsc_sum_dp
     Resident.decode_blocks(first, n, kind)   qsc_decode_blocks
     Resident.index_build(center)             qsc_index_build
+    Resident.masked_sum_delta(prev, ...)     qsc_masked_sum_delta
     Resident.finish()                        qsc_finish
     Resident.query_bytes(mask, stride)       qsc_query_bytes
 """
@@ -78,6 +79,7 @@ _SIGS = {
     "qsc_decode_blocks": ([_vp, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
     "qsc_finish": ([_vp, _vp], _i32),
     "qsc_index_build": ([_vp, ctypes.c_int32, ctypes.c_int32, _vp], _i32),
+    "qsc_masked_sum_delta": ([_vp, _vp, _vp, _vp, _u32, _vp, _vp, ctypes.c_int], _i32),
     "qsc_last_error": ([_vp], ctypes.c_char_p),
     "qsc_query_bytes": ([_vp, _vp, _u32, ctypes.POINTER(_u64), ctypes.POINTER(_u64)], _i32),
 }
@@ -214,6 +216,16 @@ class Resident:
         o = self._out(out, self.sum_dtype, self.S)
         self._check(lib.qsc_masked_sum(self._h, m.data_ptr(), block_stride, o.data_ptr(), _stream_handle(stream),
                                        int(wait)), "masked_sum")
+        return o
+
+    def masked_sum_delta(self, prev_mask, prev_out, mask, block_stride=1, out=None, stream=None, wait=True):
+        """masked_sum(mask) from prev_out = masked_sum(prev_mask): only the changed pixels are decoded."""
+        pm, m = self._mask(prev_mask), self._mask(mask)
+        if prev_out.dtype != self.sum_dtype or prev_out.numel() != self.S or not prev_out.is_contiguous():
+            raise ValueError(f"prev_out must be a contiguous {self.sum_dtype} tensor of {self.S} elements")
+        o = self._out(out, self.sum_dtype, self.S)
+        self._check(lib.qsc_masked_sum_delta(self._h, pm.data_ptr(), prev_out.data_ptr(), m.data_ptr(), block_stride,
+                                             o.data_ptr(), _stream_handle(stream), int(wait)), "masked_sum_delta")
         return o
 
     def dense_df(self, mask, out=None, stream=None, wait=True):

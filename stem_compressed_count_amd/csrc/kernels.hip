@@ -1653,6 +1653,15 @@ __global__ void __launch_bounds__(256) k_index_sum(DevIndex ix, const uint32_t *
     }
 }
 
+// Masks of a change between two detector masks.
+__global__ void k_mask_delta(const uint8_t *prev, const uint8_t *mask, uint32_t P, uint8_t *added, uint8_t *removed) {
+    for (uint32_t p = blockIdx.x * blockDim.x + threadIdx.x; p < P; p += gridDim.x * blockDim.x) {
+        const bool a = prev[p] != 0, b = mask[p] != 0;
+        added[p] = b && !a;
+        removed[p] = a && !b;
+    }
+}
+
 __global__ void k_com_finalize(const uint64_t *m, uint64_t S, float *row, float *col) {
     for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < S; s += (uint64_t)gridDim.x * blockDim.x) {
         const uint64_t m0 = m[s];
@@ -1723,16 +1732,17 @@ template <typename F>
 static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, hipStream_t st, const DevResident &r,
                          const uint8_t *mask, int complement, uint32_t stride, uint32_t n_visited, void *out, int out64,
                          int negate, const void *init, uint64_t n_init, const RegionBlocks &rb, const RegionArgs &ra,
-                         const AuxArgs &da) {
+                         const AuxArgs &da, bool accumulate = false) {
     const uint32_t slots = resident_wgs(kern, threads);
     // a planned query counts the finest tiles and lets the reduce pick the
     // item size; without a plan (region reads, or too many tiles) the host picks
     const uint32_t fine = cands[ncand - 1], n_fine = (r.P + fine - 1) / fine;
-    const bool planned = n_init && n_fine <= kMaxPlanTiles;
+    const bool planned = (n_init || accumulate) && n_fine <= kMaxPlanTiles;
     const uint32_t tile = planned ? fine : pick_tile(r.P, n_visited, slots, cands, ncand);
     const uint32_t n_tiles = (r.P + tile - 1) / tile;
     uint32_t *plan = planned ? r.tile_counts : nullptr;
-    if (n_init) {
+    if (accumulate) n_init = 0;  // the init kernel only plans
+    if (n_init || planned) {
         const PlanArgs pa{mask, r.valid, complement, r.P, tile, n_tiles, plan};
         const uint32_t grid = (uint32_t)std::max<uint64_t>(
             planned ? n_tiles : 1, std::max<uint64_t>(1, std::min<uint64_t>(2048, (n_init + 255) / 256)));
@@ -1747,26 +1757,28 @@ static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, 
 template <bool W, Op O>
 static void launch_layout(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride,
                           uint32_t n_visited, void *out, int out64, int negate, const void *init, uint64_t n_init,
-                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st, const AuxArgs &da = AuxArgs{}) {
+                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st, const AuxArgs &da = AuxArgs{},
+                          bool accumulate = false) {
     if (r.layout == 0) {
         const uint32_t cands[2] = {2 * kRansWG, kRansWG};
         launch_items(k_reduce_rans<W, O>, kRansWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
-                     negate, init, n_init, rb, ra, da);
+                     negate, init, n_init, rb, ra, da, accumulate);
     } else {
         const uint32_t cands[2] = {2 * kPairWG, kPairWG};
         launch_items(k_reduce_paired<W, O>, kPairWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
-                     negate, init, n_init, rb, ra, da);
+                     negate, init, n_init, rb, ra, da, accumulate);
     }
 }
 
 hipError_t launch_query(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
-                        int out64, int negate, const void *init, uint64_t n_init, hipStream_t st) {
+                        int out64, int negate, const void *init, uint64_t n_init, hipStream_t st, bool accumulate) {
     const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
     const RegionBlocks rb{};
     const RegionArgs ra{};
     const bool wide = r.dtype == 2;
 #define QSC_LAUNCH(W, O) \
-    launch_layout<W, O>(r, mask, complement, stride, n_visited, out, out64, negate, init, n_init, rb, ra, st)
+    launch_layout<W, O>(r, mask, complement, stride, n_visited, out, out64, negate, init, n_init, rb, ra, st, \
+                        AuxArgs{}, accumulate)
     if (op == Op::Sum) {
         if (wide) QSC_LAUNCH(true, Op::Sum); else QSC_LAUNCH(false, Op::Sum);
     } else {
@@ -1863,6 +1875,13 @@ hipError_t launch_indexed_sum(const DevResident &r, const DevIndex &ix, const ui
     const uint32_t chunks = (ix.n_leaves + ix.n_roots + kFieldChunk - 1) / kFieldChunk;
     hipLaunchKernelGGL(k_index_sum, dim3(n_visited, chunks), dim3(256), 0, st, ix, fields, stride, r.n_blocks, r.S,
                        out, out64);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask_delta(const uint8_t *prev, const uint8_t *mask, uint32_t P, uint8_t *added, uint8_t *removed,
+                             hipStream_t st) {
+    hipLaunchKernelGGL(k_mask_delta, dim3(std::max(1u, std::min(1024u, (P + 255) / 256))), dim3(256), 0, st, prev,
+                       mask, P, added, removed);
     return hipGetLastError();
 }
 

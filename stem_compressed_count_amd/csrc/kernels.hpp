@@ -72,8 +72,14 @@ struct RegionBlocks {
 //  mask is null) and valid[p] of every visited block (b % stride == 0) is
 //  decoded and added (negate: subtracted) into out: u32/u64 per scan for
 //  Op::Sum, u64 [3][S] moments for Op::Moments.
+//  With accumulate set, out is left as it is (the plan still runs) and the sums
+//  are added to it.
 hipError_t launch_query(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
-                        int out64, int negate, const void *init, uint64_t n_init, hipStream_t st);
+                        int out64, int negate, const void *init, uint64_t n_init, hipStream_t st,
+                        bool accumulate = false);
+//  Masks of a change from prev to mask: added = mask & ~prev, removed = prev & ~mask (P bytes each).
+hipError_t launch_mask_delta(const uint8_t *prev, const uint8_t *mask, uint32_t P, uint8_t *added, uint8_t *removed,
+                             hipStream_t st);
 //  CoM from exact moments.
 hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, float *col, hipStream_t st);
 //  decode of a scan rectangle over the listed touched blocks.

@@ -44,6 +44,7 @@ struct qsc_resident {
     uint16_t *d_ix_perm = nullptr, *d_ix_leaf_valid = nullptr;
     uint32_t *d_ix_packed = nullptr, *d_ix_offset = nullptr, *d_ix_fields = nullptr;
     uint8_t *d_ix_width = nullptr, *d_ix_residual = nullptr;
+    uint8_t *d_delta = nullptr;  // added and removed pixels of a mask change (2 x P bytes)
     DevIndex ix{};
     bool has_index = false;
     uint64_t index_bytes = 0;
@@ -84,7 +85,7 @@ void free_all(qsc_resident *res) {
                     (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, (void *)res->d_amp,
                     (void *)res->d_ix_perm, (void *)res->d_ix_leaf_valid, (void *)res->d_ix_packed,
                     (void *)res->d_ix_offset, (void *)res->d_ix_fields, (void *)res->d_ix_width,
-                    (void *)res->d_ix_residual, res->d_total,
+                    (void *)res->d_ix_residual, (void *)res->d_delta, res->d_total,
                     (void *)res->d_moments})
         if (p) (void)hipFree(p);
 }
@@ -258,6 +259,29 @@ qsc_status qsc_masked_sum(qsc_resident *res, const uint8_t *d_mask, uint32_t blo
                                             res->d_ix_residual, st)
                        : launch_query(res->dev, d_mask, 0, block_stride, Op::Sum, d_out, out64, 0, nullptr,
                                       res->g.S(), st);
+    return finish_query(res, e, st, wait);
+}
+
+qsc_status qsc_masked_sum_delta(qsc_resident *res, const uint8_t *d_prev_mask, const void *d_prev_out,
+                                const uint8_t *d_mask, uint32_t block_stride, void *d_out, void *hip_stream,
+                                int wait) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    if (!d_prev_mask || !d_prev_out || !d_mask || !d_out || block_stride < 1)
+        return fail(res, QSC_ERR_INVALID_ARG, "masked_sum_delta: bad argument");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const int out64 = res->g.sum_bits() == 64;
+    const uint32_t P = res->g.P();
+    hipError_t e = hipSuccess;
+    if (!res->d_delta && (e = dalloc(res, &res->d_delta, 2ull * P)) != hipSuccess)
+        return hip_fail(res, e, "mask delta scratch");
+    uint8_t *added = res->d_delta, *removed = res->d_delta + P;
+    e = launch_mask_delta(d_prev_mask, d_mask, P, added, removed, st);
+    // out = prev_out + the added pixels' sums, then minus the removed pixels' sums
+    if (e == hipSuccess)
+        e = launch_query(res->dev, added, 0, block_stride, Op::Sum, d_out, out64, 0, d_prev_out, res->g.S(), st);
+    if (e == hipSuccess)
+        e = launch_query(res->dev, removed, 0, block_stride, Op::Sum, d_out, out64, 1, nullptr, 0, st, true);
     return finish_query(res, e, st, wait);
 }
 

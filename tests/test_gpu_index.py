@@ -139,3 +139,21 @@ def test_index_errors():
         with pytest.raises(qq.QscValueError):
             res.index_build()
         assert res.info.index_bytes == 0
+
+
+def test_masked_sum_delta_follows_a_moving_mask():
+    w, counts, valid, blob = case("scan256_u16_sentinel", 12, 256)
+    shifts = [(0, 0), (2, 0), (2, 2), (-3, 1), (-3, 1), (5, -4)]
+    masks = [synth.disk_mask(w.det_rows, w.det_cols, 96 + dr, 96 + dc, 30) for dr, dc in shifts]
+    for stride in (1, 3):
+        with q().Resident(blob, valid=valid) as res:
+            prev = masks[0]
+            out = res.masked_sum(prev, block_stride=stride)
+            for m in masks[1:]:
+                nxt = res.masked_sum_delta(prev, out, m, block_stride=stride)
+                assert np.array_equal(u(nxt), oracle.masked_sum(counts, m, valid, stride=stride)), stride
+                prev, out = m, nxt
+            # in place, and back to an empty mask
+            res.masked_sum_delta(prev, out, np.zeros(w.P, np.uint8), block_stride=stride, out=out)
+            assert not u(out).any()
+            res.finish()
