@@ -1104,88 +1104,130 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
 }
 
 // ------------------------------------------------------------------ query plan
-// The init kernel counts the selected pixels of every fine pixel tile. Each
-// reduce workgroup then reads the counts, picks the work-item size (one or two
-// fine tiles), and lists the non-empty items in LDS by ballot compaction, so
-// no work item is spent on pixels the mask misses.
+// The init kernel counts the selected pixels of every 64-pixel tile. Each
+// reduce workgroup then numbers the selected pixels in pixel order (a prefix
+// sum over the counts) and cuts them into work items of exactly `cap` pixels
+// (the last item keeps the rest), so every item of a visited block decodes
+// `cap` streams, however the mask scatters them over the detector, and no
+// item is spent on pixels the mask misses. An item is described by its first
+// tile and the selected pixels of that tile before the item's first.
 //
-// Item size: a sparse mask leaves items latency-bound (their streams decode
-// side by side, whatever their number), a dense one makes them throughput-bound
-// (cost grows with the streams per item). The estimate is rounds of the
-// resident workgroups times max(1, selected per item / fine tile).
-struct Plan {
-    uint32_t n_items;  // non-empty items per visited block
-    uint32_t mult;     // fine tiles per item
+// Item size: half the workgroup, the workgroup (one stream per lane), or twice
+// it (two per lane). An item's decode is a chain of dependent steps, so the
+// time of a round of resident workgroups hardly depends on the streams per
+// lane while they are few; two per lane take about 1.7 times as long as one
+// (measured). The plan estimates rounds times that factor; on a tie the
+// smaller items spread the work over more compute units.
+struct PlanArgs {
+    const uint8_t *mask;
+    const uint8_t *valid;
+    int complement;
+    uint32_t P, n_tiles;  // 64-pixel tiles
+    uint32_t *counts;     // null: no plan
 };
 
+constexpr float kTwoSlotTime = 1.7f;
+
+struct PlanView {
+    uint32_t n_items, cap, end;  // items per visited block, pixels per item, end of the last non-empty tile
+};
+
+// Most items a plan can hold: detectors of kMaxPlanTiles tiles cut in halves of a workgroup.
 template <int WG>
-__device__ __forceinline__ Plan plan_items(const uint32_t *counts, uint32_t n_fine, uint32_t fine_px, uint32_t n_visited,
-                                           uint16_t *list, uint32_t *wtot) {
+constexpr uint32_t kMaxItems = kMaxPlanTiles * kPlanFine / (WG / 2);
+
+template <int WG>
+__device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P, uint32_t n_visited, uint16_t *desc,
+                                             uint32_t *wtot) {
+    constexpr uint32_t kPer = kMaxPlanTiles / WG > 0 ? kMaxPlanTiles / WG : 1;
+    constexpr uint32_t kWaves = WG / 64;
+    __shared__ uint32_t wlast[kWaves];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-    // totals: selected pixels, non-empty single and paired fine tiles
-    uint32_t sel = 0, live1 = 0, live2 = 0;
-    for (uint32_t t = tid; t < n_fine; t += WG) {
-        const uint32_t c = counts[t];
-        sel += c;
-        live1 += c != 0;
-        if ((t & 1u) == 0) live2 += (c + (t + 1 < n_fine ? counts[t + 1] : 0u)) != 0;
+    const uint32_t n_tiles = (P + kPlanFine - 1) / kPlanFine;
+    uint32_t c[kPer], s = 0, last = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kPer; j++) {
+        const uint32_t t = tid * kPer + j;
+        c[j] = t < n_tiles ? counts[t] : 0u;
+        s += c[j];
+        if (c[j]) last = t + 1;
+    }
+    // exclusive prefix of the per-thread sums, and the end of the last non-empty tile
+    uint32_t x = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= (uint32_t)off) x += y;
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        sel += __shfl_xor(sel, off);
-        live1 += __shfl_xor(live1, off);
-        live2 += __shfl_xor(live2, off);
+    for (int off = 32; off >= 1; off >>= 1) last = max(last, (uint32_t)__shfl_xor(last, off));
+    __syncthreads();  // wtot may still be read by the previous user
+    if (lane == 63) wtot[wave] = x;
+    if (lane == 0) wlast[wave] = last;
+    __syncthreads();
+    uint32_t before = 0, total = 0, end = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kWaves; w++) {
+        before += w < wave ? wtot[w] : 0u;
+        total += wtot[w];
+        end = max(end, wlast[w]);
     }
-    __shared__ uint32_t part[3][WG / 64];
-    if (lane == 0) {
-        part[0][wave] = sel;
-        part[1][wave] = live1;
-        part[2][wave] = live2;
+    const float slots = (float)gridDim.x;
+    auto cost = [&](uint32_t cap) {
+        const float items = (float)((total + cap - 1) / cap) * (float)n_visited;
+        return ceilf(items / slots) * (cap > (uint32_t)WG ? kTwoSlotTime : 1.0f);
+    };
+    uint32_t cap = WG / 2;
+    if (cost(WG) < cost(cap)) cap = WG;
+    // 1024-lane workgroups fill a compute unit alone: two streams per lane pay
+    // only when most pixels are selected (measured)
+    if ((WG < 1024 || 2 * total >= P) && cost(2 * WG) < cost(cap)) cap = 2 * WG;
+    // tile t starts item k when it holds the pixel numbered k * cap
+    uint32_t e = before + x - s;  // selected pixels before this thread's first tile
+#pragma unroll
+    for (uint32_t j = 0; j < kPer; j++) {
+        if (c[j]) {
+            const uint32_t k = (e + cap - 1) / cap;
+            if (k * cap < e + c[j]) desc[k] = (uint16_t)(((tid * kPer + j) << 6) | (k * cap - e));
+        }
+        e += c[j];
     }
     __syncthreads();
-    sel = live1 = live2 = 0;
-#pragma unroll
-    for (uint32_t w = 0; w < WG / 64; w++) {
-        sel += part[0][w];
-        live1 += part[1][w];
-        live2 += part[2][w];
-    }
-    const double slots = gridDim.x;
-    auto cost = [&](uint32_t live, uint32_t mult) {
-        if (!live) return 0.0;
-        const double rounds = ceil((double)live * n_visited / slots);
-        return rounds * fmax(1.0, (double)sel / live / fine_px);
-    };
-    // on a tie, dense items prefer two slots per lane (more independent work per
-    // wave), sparse ones more workgroups
-    const double c1 = cost(live1, 1), c2 = cost(live2, 2);
-    const bool dense = live1 && (double)sel / live1 > 0.5 * fine_px;
-    const uint32_t mult = (c2 < c1 || (c2 == c1 && dense)) ? 2u : 1u;
-    const uint32_t n_items = (n_fine + mult - 1) / mult;
+    return PlanView{(total + cap - 1) / cap, cap, min(end * kPlanFine, P)};
+}
+
+// The pixels of one planned item: from tile (desc >> 6) on, skipping that
+// tile's first (desc & 63) selected pixels, the next `cap` selected ones
+// (fewer for the last item), as offsets from the tile's first pixel.
+template <int WG>
+__device__ __forceinline__ uint32_t select_range(const DevResident &r, const uint8_t *mask, int complement,
+                                                 uint32_t desc, uint32_t cap, uint32_t end, uint32_t &p0,
+                                                 uint16_t *sel, uint32_t *wtot) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
     const unsigned long long below = (1ull << lane) - 1ull;
-    uint32_t total = 0;
-    for (uint32_t base = 0; base < n_items; base += WG) {
-        const uint32_t it = base + tid;
+    const uint32_t skip = desc & 63u, want = skip + cap;
+    p0 = (desc >> 6) * kPlanFine;
+    uint32_t seen = 0;  // selected pixels from p0 on, skipped ones included
+    for (uint32_t base = p0; base < end && seen < want; base += WG) {
+        const uint32_t p = base + tid;
         bool f = false;
-        if (it < n_items) {
-            const uint32_t t = it * mult;
-            f = counts[t] != 0 || (mult == 2 && t + 1 < n_fine && counts[t + 1] != 0);
-        }
+        if (p < end) f = r.valid[p] != 0 && (mask ? ((mask[p] != 0) != (complement != 0)) : true);
         const unsigned long long bal = __ballot(f);
         if (lane == 0) wtot[wave] = (uint32_t)__popcll(bal);
         __syncthreads();
-        uint32_t before = total, all = total;
+        uint32_t before = seen, all = seen;
 #pragma unroll
         for (uint32_t w = 0; w < WG / 64; w++) {
             const uint32_t c = wtot[w];
             before += w < wave ? c : 0u;
             all += c;
         }
-        if (f) list[before + (uint32_t)__popcll(bal & below)] = (uint16_t)it;
+        const uint32_t ord = before + (uint32_t)__popcll(bal & below);
+        if (f && ord >= skip && ord < want) sel[ord - skip] = (uint16_t)(p - p0);
         __syncthreads();
-        total = all;
+        seen = all;
     }
-    return Plan{total, mult};
+    return seen > skip ? min(seen, want) - skip : 0u;
 }
 
 // ------------------------------------------------------------------ index groups
@@ -1302,25 +1344,28 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kRansWG];
     __shared__ uint32_t wtot[kRansWG / 64];
-    __shared__ uint16_t tiles[kMaxPlanTiles];
     __shared__ uint32_t sbits[OP == Op::Dp ? 16 : 1];
-    // with a plan, tile_px is the fine tile the counts were taken over
-    uint32_t n_live = (r.P + tile_px - 1) / tile_px;
+    __shared__ uint16_t desc[kMaxItems<kRansWG>];
+    // planned: items of `cap` selected pixels; else every pixel tile of tile_px
+    uint32_t n_live = (r.P + tile_px - 1) / tile_px, cap = 0, end = 0;
     if (plan) {
-        const Plan pl = plan_items<kRansWG>(plan, n_live, tile_px, n_visited, tiles, wtot);
-        n_live = pl.n_items;
-        tile_px *= pl.mult;
+        const PlanView pv = plan_cut<kRansWG>(plan, r.P, n_visited, desc, wtot);
+        n_live = pv.n_items;
+        cap = pv.cap;
+        end = pv.end;
     }
     const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     uint32_t loaded = 0xFFFFFFFFu;
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-        const uint32_t vb = w / n_live, t = plan ? tiles[w % n_live] : w % n_live;
-        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = OP == Op::Index ? 0 : t * tile_px;
+        const uint32_t vb = w / n_live, t = w % n_live;
+        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride;
+        uint32_t p0 = OP == Op::Index ? 0 : t * tile_px;
         __syncthreads();
-        const uint32_t n_sel = OP == Op::Index ? index_group<kRansWG>(r, da.perm, t, sel)
-                                               : select_tile<kRansWG>(r, mask, complement, p0,
-                                                                      min(tile_px, r.P - p0), sel, wtot);
+        const uint32_t n_sel =
+            OP == Op::Index ? index_group<kRansWG>(r, da.perm, t, sel)
+            : plan ? select_range<kRansWG>(r, mask, complement, desc[t], cap, end, p0, sel, wtot)
+                   : select_tile<kRansWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
@@ -1372,23 +1417,26 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
         uint4 *dst = reinterpret_cast<uint4 *>(tbl);
         for (uint32_t i = threadIdx.x; i < kPairTable / 4; i += kPairWG) dst[i] = src[i];
     }
-    __shared__ uint16_t tiles[kMaxPlanTiles];
-    // with a plan, tile_px is the fine tile the counts were taken over
-    uint32_t n_live = (r.P + tile_px - 1) / tile_px;
+    __shared__ uint16_t desc[kMaxItems<kPairWG>];
+    // planned: items of `cap` selected pixels; else every pixel tile of tile_px
+    uint32_t n_live = (r.P + tile_px - 1) / tile_px, cap = 0, end = 0;
     if (plan) {
-        const Plan pl = plan_items<kPairWG>(plan, n_live, tile_px, n_visited, tiles, wtot);
-        n_live = pl.n_items;
-        tile_px *= pl.mult;
+        const PlanView pv = plan_cut<kPairWG>(plan, r.P, n_visited, desc, wtot);
+        n_live = pv.n_items;
+        cap = pv.cap;
+        end = pv.end;
     }
     const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-        const uint32_t vb = w / n_live, t = plan ? tiles[w % n_live] : w % n_live;
-        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride, p0 = OP == Op::Index ? 0 : t * tile_px;
+        const uint32_t vb = w / n_live, t = w % n_live;
+        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride;
+        uint32_t p0 = OP == Op::Index ? 0 : t * tile_px;
         __syncthreads();
-        const uint32_t n_sel = OP == Op::Index ? index_group<kPairWG>(r, da.perm, t, sel)
-                                               : select_tile<kPairWG>(r, mask, complement, p0,
-                                                                      min(tile_px, r.P - p0), sel, wtot);
+        const uint32_t n_sel =
+            OP == Op::Index ? index_group<kPairWG>(r, da.perm, t, sel)
+            : plan ? select_range<kPairWG>(r, mask, complement, desc[t], cap, end, p0, sel, wtot)
+                   : select_tile<kPairWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
@@ -1419,15 +1467,8 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
 }
 
 // out[i] = init[i], or 0 without init (u32 or u64 elements); with a plan,
-// workgroup t also counts the selected pixels of pixel tile t.
-struct PlanArgs {
-    const uint8_t *mask;
-    const uint8_t *valid;
-    int complement;
-    uint32_t P, tile_px, n_tiles;
-    uint32_t *counts;  // null: no plan
-};
-
+// wave w of workgroup g counts the selected pixels of 64-pixel tile 4g + w
+// (grid-strided).
 __global__ void __launch_bounds__(256) k_init(void *out, int out64, const void *init, uint64_t n, PlanArgs pa) {
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
         if (out64)
@@ -1436,19 +1477,13 @@ __global__ void __launch_bounds__(256) k_init(void *out, int out64, const void *
             reinterpret_cast<uint32_t *>(out)[i] = init ? reinterpret_cast<const uint32_t *>(init)[i] : 0;
     }
     if (!pa.counts) return;
-    __shared__ uint32_t wsum[4];
-    for (uint32_t t = blockIdx.x; t < pa.n_tiles; t += gridDim.x) {
-        const uint32_t p0 = t * pa.tile_px, p1 = min(p0 + pa.tile_px, pa.P);
-        uint32_t c = 0;
-        for (uint32_t p = p0 + threadIdx.x; p < p1; p += blockDim.x)
-            c += pa.valid[p] != 0 && (pa.mask ? ((pa.mask[p] != 0) != (pa.complement != 0)) : true);
-        // the tile's count: a wave sum, then the four waves
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
-        if ((threadIdx.x & 63u) == 0) wsum[threadIdx.x >> 6] = c;
-        __syncthreads();
-        if (threadIdx.x == 0) pa.counts[t] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        __syncthreads();
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    for (uint32_t t = blockIdx.x * 4 + wave; t < pa.n_tiles; t += gridDim.x * 4) {
+        const uint32_t p = t * kPlanFine + lane;
+        bool f = false;
+        if (p < pa.P) f = pa.valid[p] != 0 && (pa.mask ? ((pa.mask[p] != 0) != (pa.complement != 0)) : true);
+        const uint32_t c = (uint32_t)__popcll(__ballot(f));
+        if (lane == 0) pa.counts[t] = c;
     }
 }
 
@@ -1734,20 +1769,22 @@ static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, 
                          int negate, const void *init, uint64_t n_init, const RegionBlocks &rb, const RegionArgs &ra,
                          const AuxArgs &da, bool accumulate = false) {
     const uint32_t slots = resident_wgs(kern, threads);
-    // a planned query counts the finest tiles and lets the reduce pick the
-    // item size; without a plan (region reads, or too many tiles) the host picks
-    const uint32_t fine = cands[ncand - 1], n_fine = (r.P + fine - 1) / fine;
+    // a planned query counts 64-pixel tiles and the reduce cuts the items;
+    // without a plan (region reads, or too many tiles) every pixel tile
+    // of the host's size is an item
+    const uint32_t n_fine = (r.P + kPlanFine - 1) / kPlanFine;
     const bool planned = (n_init || accumulate) && n_fine <= kMaxPlanTiles;
-    const uint32_t tile = planned ? fine : pick_tile(r.P, n_visited, slots, cands, ncand);
+    const uint32_t tile = planned ? kPlanFine : pick_tile(r.P, n_visited, slots, cands, ncand);
     const uint32_t n_tiles = (r.P + tile - 1) / tile;
-    uint32_t *plan = planned ? r.tile_counts : nullptr;
+    uint32_t *plan = planned ? r.plan : nullptr;
     if (accumulate) n_init = 0;  // the init kernel only plans
     if (n_init || planned) {
-        const PlanArgs pa{mask, r.valid, complement, r.P, tile, n_tiles, plan};
+        const PlanArgs pa{mask, r.valid, complement, r.P, n_tiles, plan};
         const uint32_t grid = (uint32_t)std::max<uint64_t>(
-            planned ? n_tiles : 1, std::max<uint64_t>(1, std::min<uint64_t>(2048, (n_init + 255) / 256)));
+            planned ? (n_tiles + 3) / 4 : 1, std::max<uint64_t>(1, std::min<uint64_t>(2048, (n_init + 255) / 256)));
         hipLaunchKernelGGL(k_init, dim3(grid), dim3(256), 0, st, out, out64, init, n_init, pa);
     }
+    // planned items number at most one per 64-pixel tile
     const uint64_t items = (uint64_t)n_tiles * n_visited;
     const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, slots));
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, r, mask, complement, stride, n_visited, tile, plan, out,

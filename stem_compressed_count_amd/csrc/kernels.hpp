@@ -10,8 +10,13 @@ namespace qsc {
 // entry (values 0, no bits, next state 0) padded to 16 bytes.
 constexpr uint32_t kPairTable = 32 * 1024 + 4;
 
-// Pixel tiles a query plan covers; detectors with more tiles decode every tile.
+// Query plan: the selected pixels are counted per 64-pixel tile (at most
+// kMaxPlanTiles tiles, so detectors up to 65,536 pixels; larger ones decode
+// every pixel tile), then cut into work items of equal numbers of selected
+// pixels in pixel order.
+constexpr uint32_t kPlanFine = 64;
 constexpr uint32_t kMaxPlanTiles = 1024;
+constexpr uint32_t kPlanWords = kMaxPlanTiles;
 
 // Device view of a resident (all pointers are device memory).
 struct DevResident {
@@ -24,7 +29,7 @@ struct DevResident {
     const uint8_t *valid;    // P bytes, nonzero = valid
     const double *calib;     // scaled: n_blocks x {scale, offset}
     unsigned long long *err; // first malformed stream: (block + 1) << 32 | pixel, 0 = none
-    uint32_t *tile_counts;   // query plan: selected pixels per pixel tile (kMaxPlanTiles entries)
+    uint32_t *plan;          // query plan: selected pixels per 64-pixel tile (kPlanWords words)
     uint64_t S;
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };

@@ -197,7 +197,8 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     if ((e = dalloc(res.get(), &res->d_valid, g.P())) != hipSuccess) return bail(e, "valid");
     if ((e = hipMemcpy(res->d_valid, valid.data(), g.P(), hipMemcpyHostToDevice)) != hipSuccess)
         return bail(e, "valid upload");
-    if ((e = dalloc(res.get(), &res->d_plan, 4 * kMaxPlanTiles)) != hipSuccess) return bail(e, "query plan");
+    if ((e = dalloc(res.get(), &res->d_plan, 4 * kPlanWords)) != hipSuccess) return bail(e, "query plan");
+    if ((e = hipMemset(res->d_plan, 0, 4 * kPlanWords)) != hipSuccess) return bail(e, "query plan");
     if ((e = dalloc(res.get(), &res->d_err, 256)) != hipSuccess) return bail(e, "error word");
     if ((e = hipMemset(res->d_err, 0, 256)) != hipSuccess) return bail(e, "error word");
     if ((e = hipStreamSynchronize(strm)) != hipSuccess) return bail(e, "synchronize");
@@ -212,7 +213,7 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     d.valid = res->d_valid;
     d.calib = g.scaled ? reinterpret_cast<const double *>(res->d_blob + s.calib) : nullptr;
     d.err = res->d_err;
-    d.tile_counts = res->d_plan;
+    d.plan = res->d_plan;
     d.S = g.S();
     d.P = g.P();
     d.G = g.G();
