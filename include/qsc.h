@@ -202,7 +202,7 @@ qsc_status qsc_index_build(qsc_resident *res, int32_t center_row, int32_t center
  *   sum over prev_mask & ~mask, both over valid pixels of the visited blocks,
  *   exact (modular arithmetic of the output width cannot overflow the true
  *   result). d_prev_out must hold masked_sum(prev_mask, block_stride) of this
- *   resident; d_out may be d_prev_out (in place). Devices pointers as in
+ *   resident; d_out may be d_prev_out (in place). Device pointers as in
  *   qsc_masked_sum; the first call allocates 2 x P bytes of scratch. After a
  *   failed query (MALFORMED) the caller's baseline is invalid and must be
  *   recomputed with qsc_masked_sum.
