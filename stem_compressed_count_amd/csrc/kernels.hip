@@ -346,53 +346,69 @@ __device__ __forceinline__ uint32_t dp_count(const uint32_t *bits) {
 }
 
 // ------------------------------------------------------------------ region output
-template <bool WIDE>
+constexpr bool is_frames(Op op) { return op == Op::Frames || op == Op::Amp; }
+constexpr bool is_region(Op op) { return op == Op::Region || is_frames(op); }
+
+template <bool WIDE, bool AMP>
 __device__ __forceinline__ void region_put(const RegionArgs &ra, uint64_t idx, uint32_t v, double scale,
                                            double offset) {
     void *out = ra.out;
-    const int out_kind = ra.out_kind;
-    if (out_kind == 1)
-        reinterpret_cast<float *>(out)[idx] = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
-    else if (out_kind == 2)
+    if constexpr (AMP)
         reinterpret_cast<float *>(out)[idx] = ra.amp[v & 0xFFFFu];  // counts are at most 65535
+    else if (ra.out_kind == 1)
+        reinterpret_cast<float *>(out)[idx] = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
     else if (WIDE)
         reinterpret_cast<uint16_t *>(out)[idx] = (uint16_t)v;
     else
         reinterpret_cast<uint8_t *>(out)[idx] = (uint8_t)v;
 }
 
-// Scan walk of one block for a region read: (row, col) and index s of scan
-// s0 + j, the output index of a written scan, and the calibration of the block.
+// Scan walk of one block for a region read (FRAMES false: scans inside the
+// rectangle, at their row of the rectangle) or a frames read (every scan, at
+// row s - s_first): (row, col) and index s of scan s0 + j, and the
+// calibration of the block.
+template <bool FRAMES>
 struct RegionWalk {
     uint32_t row, col;
     uint64_t s;
     uint32_t scan_cols;
-    const RegionArgs *ra;
+    uint32_t r0, r1, c0, c1;
+    uint64_t s_first;
     double scale, offset;
     __device__ __forceinline__ bool inside() const {
-        return ra->frames || (row >= ra->r0 && row < ra->r1 && col >= ra->c0 && col < ra->c1);
+        return FRAMES || (row >= r0 && row < r1 && col >= c0 && col < c1);
     }
     __device__ __forceinline__ uint64_t index(uint32_t P) const {
-        if (ra->frames) return (s - ra->s_first) * P;
-        return ((uint64_t)(row - ra->r0) * (ra->c1 - ra->c0) + (col - ra->c0)) * P;
+        if constexpr (FRAMES) return (s - s_first) * P;
+        return ((uint64_t)(row - r0) * (c1 - c0) + (col - c0)) * P;
     }
     __device__ __forceinline__ void next() {
-        s++;
-        if (++col == scan_cols) {
+        if constexpr (FRAMES) {
+            s++;
+        } else if (++col == scan_cols) {
             col = 0;
             row++;
         }
     }
+    __device__ __forceinline__ void seek(const DevResident &r, uint64_t s_) {
+        s = s_;
+        if constexpr (!FRAMES) {
+            row = (uint32_t)(s_ / r.scan_cols);
+            col = (uint32_t)(s_ % r.scan_cols);
+        }
+    }
 };
 
-__device__ __forceinline__ RegionWalk region_walk(const DevResident &r, uint32_t b, const RegionArgs &ra) {
-    RegionWalk rw;
-    const uint64_t s0 = (uint64_t)b * kBlk;
-    rw.row = (uint32_t)(s0 / r.scan_cols);
-    rw.col = (uint32_t)(s0 % r.scan_cols);
-    rw.s = s0;
+template <bool FRAMES>
+__device__ __forceinline__ RegionWalk<FRAMES> region_walk(const DevResident &r, uint32_t b, const RegionArgs &ra) {
+    RegionWalk<FRAMES> rw;
     rw.scan_cols = r.scan_cols;
-    rw.ra = &ra;
+    rw.seek(r, (uint64_t)b * kBlk);
+    rw.r0 = ra.r0;
+    rw.r1 = ra.r1;
+    rw.c0 = ra.c0;
+    rw.c1 = ra.c1;
+    rw.s_first = ra.s_first;
     rw.scale = 1.0;
     rw.offset = 0.0;
     if (ra.out_kind == 1) {
@@ -403,12 +419,13 @@ __device__ __forceinline__ RegionWalk region_walk(const DevResident &r, uint32_t
 }
 
 // A stream whose scans hold one value (constant, or zero): written directly.
-template <bool WIDE>
+template <bool WIDE, Op OP>
 __device__ __forceinline__ void region_fill(const DevResident &r, uint32_t b, uint32_t n, uint32_t p, uint32_t v,
                                             const RegionArgs &ra) {
-    RegionWalk rw = region_walk(r, b, ra);
+    constexpr bool AMP = OP == Op::Amp;
+    auto rw = region_walk<is_frames(OP)>(r, b, ra);
     for (uint32_t j = 0; j < n; j++, rw.next())
-        if (rw.inside()) region_put<WIDE>(ra, rw.index(r.P) + p, v, rw.scale, rw.offset);
+        if (rw.inside()) region_put<WIDE, AMP>(ra, rw.index(r.P) + p, v, rw.scale, rw.offset);
 }
 
 // ------------------------------------------------------------------ byte-rANS tile
@@ -465,8 +482,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 report(r, b, z.p);
                 continue;
             }
-            if constexpr (OP == Op::Region) {
-                region_fill<WIDE>(r, b, n, z.p, v, ra);
+            if constexpr (is_region(OP)) {
+                region_fill<WIDE, OP>(r, b, n, z.p, v, ra);
             } else if constexpr (OP == Op::Dp) {
                 dt.row[z.p] = v * dt.n_sel;
             } else if constexpr (OP == Op::Index) {
@@ -571,16 +588,16 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     };
 
     auto run = [&](auto form) {
-        if constexpr (OP == Op::Region) {
+        if constexpr (is_region(OP)) {
             // values of scans inside the rectangle go straight to the output
             constexpr int CH = 16;
-            RegionWalk rw = region_walk(r, b, ra);
+            auto rw = region_walk<is_frames(OP)>(r, b, ra);
             auto put = [&](const uint32_t (&v)[K]) {
                 if (rw.inside()) {
                     const uint64_t idx = rw.index(r.P);
 #pragma unroll
                     for (int k = 0; k < K; k++)
-                        if (sl[k].live) region_put<WIDE>(ra, idx + sl[k].p, v[k], rw.scale, rw.offset);
+                        if (sl[k].live) region_put<WIDE, OP == Op::Amp>(ra, idx + sl[k].p, v[k], rw.scale, rw.offset);
                 }
                 rw.next();
             };
@@ -821,7 +838,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         if (mode >= 3) touched += touch_stream(rs, z.org, z.len);
         if (mode == 0) {  // EMPTY
             if (z.len != 2) report(r, b, z.p);
-            if constexpr (OP == Op::Region) region_fill<WIDE>(r, b, kBlk, z.p, 0, ra);
+            if constexpr (is_region(OP)) region_fill<WIDE, OP>(r, b, kBlk, z.p, 0, ra);
             if constexpr (OP == Op::Dp) dt.row[z.p] = 0;
             continue;
         }
@@ -829,8 +846,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             const uint32_t v = ld16(r.payload, e.start + 2);
             if (z.len != 4 || v == 0 || v > maxv)
                 report(r, b, z.p);
-            else if constexpr (OP == Op::Region)
-                region_fill<WIDE>(r, b, kBlk, z.p, v, ra);
+            else if constexpr (is_region(OP))
+                region_fill<WIDE, OP>(r, b, kBlk, z.p, v, ra);
             else if constexpr (OP == Op::Dp)
                 dt.row[z.p] = v * dt.n_sel;
             else if constexpr (OP == Op::Index)
@@ -849,7 +866,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             int prev = -1;
             bool ok = true;
             uint32_t dsum = 0;
-            if constexpr (OP == Op::Region) region_fill<WIDE>(r, b, kBlk, z.p, 0, ra);
+            if constexpr (is_region(OP)) region_fill<WIDE, OP>(r, b, kBlk, z.p, 0, ra);
             for (uint32_t t = 0; t < nnz; t++) {
                 const int pos = (int)ld16(r.payload, e.start + 4 + 2 * t);
                 const uint32_t v = WIDE ? ld16(r.payload, e.start + 4 + 2 * nnz + 2 * t)
@@ -858,13 +875,11 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     ok = false;
                     break;
                 }
-                if constexpr (OP == Op::Region) {
-                    RegionWalk rw = region_walk(r, b, ra);
+                if constexpr (is_region(OP)) {
+                    auto rw = region_walk<is_frames(OP)>(r, b, ra);
                     const uint64_t s = (uint64_t)b * kBlk + (uint32_t)pos;
-                    rw.row = (uint32_t)(s / r.scan_cols);
-                    rw.col = (uint32_t)(s % r.scan_cols);
-                    rw.s = s;
-                    if (rw.inside()) region_put<WIDE>(ra, rw.index(r.P) + z.p, v, rw.scale, rw.offset);
+                    rw.seek(r, s);
+                    if (rw.inside()) region_put<WIDE, OP == Op::Amp>(ra, rw.index(r.P) + z.p, v, rw.scale, rw.offset);
                 } else if constexpr (OP == Op::Dp) {
                     dsum += v * scan_bit(dt, (uint32_t)pos);
                 } else if constexpr (OP == Op::Index) {
@@ -976,8 +991,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     };
 
     auto run = [&](auto form) {
-        if constexpr (OP == Op::Region) {
-            RegionWalk rw = region_walk(r, b, ra);
+        if constexpr (is_region(OP)) {
+            auto rw = region_walk<is_frames(OP)>(r, b, ra);
             for (uint32_t t = 0; t < kBlk / 2; t++) {
                 uint32_t v0[K], v1[K];
                 step(form, t, v0, v1);
@@ -989,7 +1004,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                         for (int k = 0; k < K; k++) {
                             const uint32_t mode = sl[k].meta & 7u;
                             if (mode == 3 || mode == 4)
-                                region_put<WIDE>(ra, idx + sl[k].p, sl[k].a0 + (h ? v1[k] : v0[k]),
+                                region_put<WIDE, OP == Op::Amp>(ra, idx + sl[k].p, sl[k].a0 + (h ? v1[k] : v0[k]),
                                                  rw.scale, rw.offset);
                         }
                     }
@@ -1359,7 +1374,7 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     uint32_t loaded = 0xFFFFFFFFu;
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = w % n_live;
-        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride;
+        const uint32_t b = is_region(OP) ? rb.b[vb] : vb * stride;
         uint32_t p0 = OP == Op::Index ? 0 : t * tile_px;
         __syncthreads();
         const uint32_t n_sel =
@@ -1430,7 +1445,7 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = w % n_live;
-        const uint32_t b = OP == Op::Region ? rb.b[vb] : vb * stride;
+        const uint32_t b = is_region(OP) ? rb.b[vb] : vb * stride;
         uint32_t p0 = OP == Op::Index ? 0 : t * tile_px;
         __syncthreads();
         const uint32_t n_sel =
@@ -1832,10 +1847,15 @@ hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, 
 }
 
 hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const RegionArgs &ra, hipStream_t st) {
-    if (r.dtype == 2)
-        launch_layout<true, Op::Region>(r, nullptr, 0, 1, blocks.n, nullptr, 0, 0, nullptr, 0, blocks, ra, st);
-    else
-        launch_layout<false, Op::Region>(r, nullptr, 0, 1, blocks.n, nullptr, 0, 0, nullptr, 0, blocks, ra, st);
+#define QSC_REGION(W, O) launch_layout<W, O>(r, nullptr, 0, 1, blocks.n, nullptr, 0, 0, nullptr, 0, blocks, ra, st)
+    if (ra.out_kind == 2) {
+        if (r.dtype == 2) QSC_REGION(true, Op::Amp); else QSC_REGION(false, Op::Amp);
+    } else if (ra.frames) {
+        if (r.dtype == 2) QSC_REGION(true, Op::Frames); else QSC_REGION(false, Op::Frames);
+    } else {
+        if (r.dtype == 2) QSC_REGION(true, Op::Region); else QSC_REGION(false, Op::Region);
+    }
+#undef QSC_REGION
     return hipGetLastError();
 }
 

@@ -34,7 +34,11 @@ struct DevResident {
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };
 
-enum class Op : int { Sum = 0, Moments = 1, Region = 2, Dp = 3, Index = 4 };
+// Region reads (a scan rectangle), Frames (whole blocks) and Amp (whole
+// blocks as square-root amplitudes) write decoded values; each is its own
+// instantiation, so the rectangle tests and the table gather stay out of the
+// loops that do not need them.
+enum class Op : int { Sum = 0, Moments = 1, Region = 2, Dp = 3, Index = 4, Amp = 5, Frames = 6 };
 
 // Buffers of the queries beyond sums and moments.
 //  diffraction pattern: the selected scans (null: every scan), the
