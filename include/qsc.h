@@ -25,7 +25,7 @@
  *  - Calls that enqueue work on the same resident must not run concurrently
  *    from several host threads, and the queries of one resident must run in
  *    order on the device: issue them on one stream, or order the streams. They
- *    share the resident's total and moment caches and its work-claim counter.
+ *    share the resident's total and moment caches and its query-plan buffer.
  */
 #ifndef QSC_H
 #define QSC_H
@@ -95,6 +95,28 @@ qsc_status qsc_encoder_size(const qsc_encoder *enc, uint64_t *nbytes);
 qsc_status qsc_encoder_write(const qsc_encoder *enc, void *host_out, uint64_t capacity);
 qsc_status qsc_encoder_destroy(qsc_encoder *enc);
 
+/* ---------------------------------------------------------------- device encoder
+ * The same containers, encoded on the GPU from values already in device
+ * memory (paired-resident page, "Operation pipeline" items 1-2: complete
+ * 512-scan blocks coded per detector-pixel stream; scaled-uint16 page: each
+ * float32 region calibrated to uint16 codes first). The output is
+ * byte-identical to the host encoder's. Byte-rANS layout only (layout 1 ->
+ * UNSUPPORTED).
+ *
+ * qsc_encode_device_bound: the largest container the geometry can encode to
+ *   (every stream raw); a capacity that always suffices.
+ * qsc_encode_device: d_data holds S x P values, scan-major, native dtype
+ *   (float32 when scaled), device memory. The container is written to d_blob
+ *   (device, capacity bytes) and its size to *nbytes. Temporary device memory
+ *   (about 12 bytes per value, plus 2 per value when scaled) is allocated and
+ *   freed inside; hip_stream is synchronised. A capacity below the size ->
+ *   INVALID_ARG with *nbytes set and the payload not written; NaN or Inf in
+ *   scaled input -> INVALID_ARG.
+ */
+qsc_status qsc_encode_device_bound(const qsc_geometry *geom, uint64_t *nbytes);
+qsc_status qsc_encode_device(const qsc_geometry *geom, const void *d_data, void *d_blob, uint64_t capacity,
+                             uint64_t *nbytes, void *hip_stream);
+
 /* ---------------------------------------------------------------- resident
  * qsc_resident_create: validates a host blob (header, ABI tag, block
  *   directory, grouped offsets, table sums, every stream header: reserved
@@ -110,6 +132,15 @@ qsc_status qsc_encoder_destroy(qsc_encoder *enc);
  */
 qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uint8_t *host_valid,
                                void *hip_stream, qsc_resident **out);
+/* qsc_resident_create_device: as qsc_resident_create for a container already
+ *   in device memory (d_blob, nbytes; e.g. from qsc_encode_device). The
+ *   sections before the payload (and the calibration) are copied to the host
+ *   and validated there; the stream headers are validated on the device; the
+ *   container is copied device to device into the resident, so d_blob may be
+ *   freed afterwards. Same errors as qsc_resident_create.
+ */
+qsc_status qsc_resident_create_device(const void *d_blob, uint64_t nbytes, const uint8_t *host_valid,
+                                      void *hip_stream, qsc_resident **out);
 qsc_status qsc_resident_destroy(qsc_resident *res);
 qsc_status qsc_resident_info(const qsc_resident *res, qsc_info *info);
 

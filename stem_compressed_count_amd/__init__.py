@@ -8,7 +8,9 @@ fallback: if libqsc.so is missing the import fails.
 
 Entry points mirror include/qsc.h:
     encode(data, geometry) -> bytes          qsc_encoder_*
-    Resident(blob, valid=None)               qsc_resident_create / destroy / info
+    encode_device(tensor, geometry)          qsc_encode_device_bound / qsc_encode_device
+    Resident(blob, valid=None)               qsc_resident_create (host blob) or
+                                             qsc_resident_create_device (device tensor); destroy / info
     Resident.masked_sum(mask, block_stride)  qsc_masked_sum
     Resident.dense_df(mask)                  qsc_dense_df
     Resident.com(mask=None)                  qsc_com
@@ -69,6 +71,9 @@ _SIGS = {
     "qsc_encoder_write": ([_vp, _vp, _u64], _i32),
     "qsc_encoder_destroy": ([_vp], _i32),
     "qsc_resident_create": ([_vp, _u64, _vp, _vp, ctypes.POINTER(_vp)], _i32),
+    "qsc_resident_create_device": ([_vp, _u64, _vp, _vp, ctypes.POINTER(_vp)], _i32),
+    "qsc_encode_device_bound": ([ctypes.POINTER(Geometry), ctypes.POINTER(_u64)], _i32),
+    "qsc_encode_device": ([ctypes.POINTER(Geometry), _vp, _vp, _u64, ctypes.POINTER(_u64), _vp], _i32),
     "qsc_resident_destroy": ([_vp], _i32),
     "qsc_resident_info": ([_vp, ctypes.POINTER(Info)], _i32),
     "qsc_masked_sum": ([_vp, _vp, _u32, _vp, _vp, ctypes.c_int], _i32),
@@ -112,6 +117,38 @@ def encode(data, scan_rows, scan_cols, det_rows, det_cols, layout=0, scaled=Fals
         return enc.blob()
     finally:
         enc.close()
+
+
+def encode_device(data, scan_rows, scan_cols, det_rows, det_cols, layout=0, scaled=False, stream=None):
+    """Encode (S x P) values already on the GPU (a torch tensor: uint8, 16-bit integers, or float32 when
+    scaled) into a container in device memory; returns a uint8 tensor holding exactly the container."""
+    import torch
+    if not isinstance(data, torch.Tensor) or not data.is_cuda or not data.is_contiguous():
+        raise ValueError("data must be a contiguous CUDA tensor")
+    if scaled:
+        if data.dtype != torch.float32:
+            raise ValueError("scaled input must be float32")
+        dtype = 2
+    elif data.dtype == torch.uint8:
+        dtype = 1
+    elif data.element_size() == 2 and not data.is_floating_point():
+        dtype = 2
+    else:
+        raise ValueError("counts must be uint8 or 16-bit integers")
+    g = Geometry(scan_rows, scan_cols, det_rows, det_cols, dtype, layout, 1 if scaled else 0)
+    if data.numel() != scan_rows * scan_cols * det_rows * det_cols:
+        raise ValueError("data must hold scans x detector pixels values")
+    cap = _u64()
+    rc = lib.qsc_encode_device_bound(ctypes.byref(g), ctypes.byref(cap))
+    if rc:
+        _raise(rc, "encode_device geometry")
+    out = torch.empty(cap.value, dtype=torch.uint8, device=data.device)
+    n = _u64()
+    rc = lib.qsc_encode_device(ctypes.byref(g), data.data_ptr(), out.data_ptr(), cap.value, ctypes.byref(n),
+                               _stream_handle(stream))
+    if rc:
+        _raise(rc, "encode_device")
+    return out[:n.value]
 
 
 class Encoder:
@@ -165,13 +202,20 @@ class Resident:
     """An encoded acquisition resident in device memory (qsc_resident)."""
 
     def __init__(self, blob, valid=None, stream=None):
+        """blob: a host container (bytes or numpy uint8), or a CUDA uint8 tensor holding one."""
         import torch
-        b = np.ascontiguousarray(np.frombuffer(blob, dtype=np.uint8) if isinstance(blob, (bytes, bytearray))
-                                 else blob, dtype=np.uint8)
         v = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
         self._h = _vp()
-        rc = lib.qsc_resident_create(b.ctypes.data, b.size, None if v is None else v.ctypes.data,
-                                     _stream_handle(stream), ctypes.byref(self._h))
+        if isinstance(blob, torch.Tensor) and blob.is_cuda:
+            if blob.dtype != torch.uint8 or not blob.is_contiguous():
+                raise ValueError("a device container must be a contiguous uint8 tensor")
+            rc = lib.qsc_resident_create_device(blob.data_ptr(), blob.numel(), None if v is None else v.ctypes.data,
+                                                _stream_handle(stream), ctypes.byref(self._h))
+        else:
+            b = np.ascontiguousarray(np.frombuffer(blob, dtype=np.uint8) if isinstance(blob, (bytes, bytearray))
+                                     else blob, dtype=np.uint8)
+            rc = lib.qsc_resident_create(b.ctypes.data, b.size, None if v is None else v.ctypes.data,
+                                         _stream_handle(stream), ctypes.byref(self._h))
         if rc:
             _raise(rc, "resident_create")
         info = self._info()

@@ -11,7 +11,7 @@ OUT = os.path.join(HERE, "libqsc.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kernels.hip", "resident.hip", "encoder.cpp", "container.cpp"]
+SOURCES = ["kernels.hip", "resident.hip", "encode.hip", "encoder.cpp", "container.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

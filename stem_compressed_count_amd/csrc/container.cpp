@@ -50,6 +50,20 @@ Sections layout_sections(const Geometry &g, uint64_t payload_bytes) {
     return s;
 }
 
+void write_header(const Geometry &g, const Sections &s, uint8_t *out) {
+    std::memset(out, 0, kHeaderBytes);
+    auto st32 = [&](uint64_t off, uint32_t v) { std::memcpy(out + off, &v, 4); };
+    auto st64 = [&](uint64_t off, uint64_t v) { std::memcpy(out + off, &v, 8); };
+    std::memcpy(out, "QSCRES01", 8);
+    const char *tag = g.layout == 0 ? kAbiRans : kAbiPaired;
+    std::memcpy(out + 8, tag, std::strlen(tag));
+    const uint32_t hdr[10] = {1, g.layout, g.scan_rows, g.scan_cols, g.det_rows, g.det_cols, g.dtype, kBlock,
+                              g.n_blocks(), g.scaled};
+    for (int i = 0; i < 10; i++) st32(40 + 4 * i, hdr[i]);
+    const uint64_t offs[8] = {s.dir, s.table, s.gbase, s.rel, s.payload, s.payload_bytes, s.calib, s.total};
+    for (int i = 0; i < 8; i++) st64(80 + 8 * i, offs[i]);
+}
+
 // ---------------------------------------------------------------- pair models
 
 static PairModels compute_pair_models() {
@@ -160,7 +174,8 @@ void build_pair_tables(uint32_t *out) {
 
 // ---------------------------------------------------------------- validation
 
-qsc_status parse_and_validate(const uint8_t *blob, uint64_t nbytes, Parsed *out, std::string *msg) {
+qsc_status parse_and_validate(const uint8_t *blob, uint64_t nbytes, Parsed *out, std::string *msg, bool streams,
+                              const uint8_t *calib) {
     auto fail = [&](qsc_status st, const std::string &m) {
         *msg = m;
         return st;
@@ -270,18 +285,19 @@ qsc_status parse_and_validate(const uint8_t *blob, uint64_t nbytes, Parsed *out,
                 const uint64_t st = gb + ld16(rel + 2 * i);
                 const uint64_t en = i + 1 < used ? gb + ld16(rel + 2 * (i + 1)) : group_end;
                 const uint32_t p = gi * 32 + i;
-                const std::string where = " (block " + std::to_string(b) + ", pixel " + std::to_string(p) + ")";
-                if (en < st + 2 || (st & 1) || (en & 1)) return fail(QSC_ERR_MALFORMED, "stream extent invalid" + where);
+                auto where = [&]() { return " (block " + std::to_string(b) + ", pixel " + std::to_string(p) + ")"; };
+                if (en < st + 2 || (st & 1) || (en & 1)) return fail(QSC_ERR_MALFORMED, "stream extent invalid" + where());
+                if (!streams) continue;  // the stream headers are checked elsewhere
                 const uint32_t hdr = ld16(blob + s.payload + base + st);
                 const uint32_t mode = hdr & 7, model = (hdr >> 3) & 31;
-                if (hdr >> 8) return fail(QSC_ERR_MALFORMED, "reserved stream header bits set" + where);
+                if (hdr >> 8) return fail(QSC_ERR_MALFORMED, "reserved stream header bits set" + where());
                 if (g.layout == 0) {
-                    if (mode > R_RAW || model) return fail(QSC_ERR_MALFORMED, "invalid stream mode" + where);
+                    if (mode > R_RAW || model) return fail(QSC_ERR_MALFORMED, "invalid stream mode" + where());
                     if (mode == R_RANS && !table_usable)
-                        return fail(QSC_ERR_MALFORMED, "RANS stream with an unusable table" + where);
+                        return fail(QSC_ERR_MALFORMED, "RANS stream with an unusable table" + where());
                 } else {
                     if (mode > P_RAW || (model && mode != P_PAIRED))
-                        return fail(QSC_ERR_MALFORMED, "invalid stream mode" + where);
+                        return fail(QSC_ERR_MALFORMED, "invalid stream mode" + where());
                 }
                 out->mode_counts[mode]++;
             }
@@ -293,7 +309,7 @@ qsc_status parse_and_validate(const uint8_t *blob, uint64_t nbytes, Parsed *out,
     if (g.scaled)
         for (uint32_t i = 0; i < 2 * nb; i++) {
             double v;
-            std::memcpy(&v, blob + s.calib + 8ull * i, 8);
+            std::memcpy(&v, (calib ? calib : blob + s.calib) + 8ull * i, 8);
             if (!std::isfinite(v)) return fail(QSC_ERR_MALFORMED, "non-finite calibration");
         }
     out->g = g;

@@ -484,14 +484,7 @@ qsc_status qsc_encoder_write(const qsc_encoder *enc, void *host_out, uint64_t ca
     std::memset(o, 0, total);
     auto st32 = [&](uint64_t off, uint32_t v) { std::memcpy(o + off, &v, 4); };
     auto st64 = [&](uint64_t off, uint64_t v) { std::memcpy(o + off, &v, 8); };
-    std::memcpy(o, "QSCRES01", 8);
-    const char *tag = g.layout == 0 ? "qsc-byte-rans-v1" : "qsc-paired-v1";
-    std::memcpy(o + 8, tag, std::strlen(tag));
-    const uint32_t hdr[10] = {1, g.layout, g.scan_rows, g.scan_cols, g.det_rows, g.det_cols, g.dtype, kBlock,
-                              g.n_blocks(), g.scaled};
-    for (int i = 0; i < 10; i++) st32(40 + 4 * i, hdr[i]);
-    const uint64_t offs[8] = {s.dir, s.table, s.gbase, s.rel, s.payload, s.payload_bytes, s.calib, s.total};
-    for (int i = 0; i < 8; i++) st64(80 + 8 * i, offs[i]);
+    write_header(g, s, o);
     const uint32_t G = g.G();
     uint64_t base = 0;
     for (uint32_t b = 0; b < enc->blocks.size(); b++) {

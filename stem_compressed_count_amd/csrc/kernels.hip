@@ -1712,6 +1712,36 @@ __global__ void k_mask_delta(const uint8_t *prev, const uint8_t *mask, uint32_t 
     }
 }
 
+// Stream headers of a resident built from a device container (FORMAT 1.4,
+// 2.4, 3.4): reserved bits clear, a mode the layout defines, the model bits
+// only on a paired stream, and byte-rANS streams only with a usable table.
+// counts[mode] gets the valid streams; bad the first bad (block << 32 | pixel).
+__global__ void __launch_bounds__(256) k_check_headers(DevResident r, const uint8_t *usable, unsigned long long *counts,
+                                                       unsigned long long *bad) {
+    __shared__ uint32_t c[8];
+    if (threadIdx.x < 8) c[threadIdx.x] = 0;
+    __syncthreads();
+    const uint32_t b = blockIdx.y, p = blockIdx.x * 256 + threadIdx.x;
+    if (p < r.P) {
+        const uint64_t base = *reinterpret_cast<const uint64_t *>(r.dir + 16ull * b);
+        const uint64_t gi = (uint64_t)b * r.G + (p >> 5);
+        const uint64_t st = base + r.gbase[gi] + r.rel[gi * 32 + (p & 31u)];
+        const uint32_t hdr = *reinterpret_cast<const uint16_t *>(r.payload + st);
+        const uint32_t mode = hdr & 7u, model = (hdr >> 3) & 31u;
+        bool ok = (hdr >> 8) == 0;
+        if (r.layout == 0)
+            ok = ok && mode <= 2 && model == 0 && !(mode == 1 && !usable[b]);  // 0 CONST, 1 RANS, 2 RAW
+        else
+            ok = ok && mode <= 4 && !(model && mode != 3);  // 3 PAIRED
+        if (ok)
+            atomicAdd(&c[mode], 1u);
+        else
+            atomicMin(bad, ((unsigned long long)b << 32) | p);
+    }
+    __syncthreads();
+    if (threadIdx.x < 8 && c[threadIdx.x]) atomicAdd(counts + threadIdx.x, (unsigned long long)c[threadIdx.x]);
+}
+
 __global__ void k_com_finalize(const uint64_t *m, uint64_t S, float *row, float *col) {
     for (uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; s < S; s += (uint64_t)gridDim.x * blockDim.x) {
         const uint64_t m0 = m[s];
@@ -1939,6 +1969,12 @@ hipError_t launch_mask_delta(const uint8_t *prev, const uint8_t *mask, uint32_t 
                              hipStream_t st) {
     hipLaunchKernelGGL(k_mask_delta, dim3(std::max(1u, std::min(1024u, (P + 255) / 256))), dim3(256), 0, st, prev,
                        mask, P, added, removed);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_headers(const DevResident &r, const uint8_t *usable, unsigned long long *counts,
+                                unsigned long long *bad, hipStream_t st) {
+    hipLaunchKernelGGL(k_check_headers, dim3((r.P + 255) / 256, r.n_blocks), dim3(256), 0, st, r, usable, counts, bad);
     return hipGetLastError();
 }
 

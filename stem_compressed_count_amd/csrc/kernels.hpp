@@ -127,6 +127,9 @@ hipError_t launch_index_pack(uint32_t n_blocks, uint32_t n_fields, const uint32_
 hipError_t launch_indexed_sum(const DevResident &r, const DevIndex &ix, const uint8_t *mask, uint32_t stride,
                               void *out, int out64, uint32_t *fields, uint8_t *residual, hipStream_t st);
 //  zero n bytes (region outputs of residents with invalid pixels)
+// Stream-header checks of a resident built from a device container.
+hipError_t launch_check_headers(const DevResident &r, const uint8_t *usable, unsigned long long *counts,
+                                unsigned long long *bad, hipStream_t st);
 hipError_t launch_zero_bytes(void *out, uint64_t n, hipStream_t st);
 
 int device_cu_count();

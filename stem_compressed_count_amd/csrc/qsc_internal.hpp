@@ -43,6 +43,9 @@ struct Sections {
 // Section layout the encoder writes for a geometry and payload size.
 Sections layout_sections(const Geometry &g, uint64_t payload_bytes);
 
+// The 256-byte container header (FORMAT 1.1) of a geometry and its sections.
+void write_header(const Geometry &g, const Sections &s, uint8_t *out256);
+
 // A parsed and structurally validated blob.
 struct Parsed {
     Geometry g;
@@ -53,8 +56,11 @@ struct Parsed {
 };
 
 // Full host validation (FORMAT 1.x headers, offsets, tables, stream headers).
-// Returns QSC_OK or an error with a message.
-qsc_status parse_and_validate(const uint8_t *blob, uint64_t nbytes, Parsed *out, std::string *msg);
+// Returns QSC_OK or an error with a message. With streams = false the stream
+// headers are not read (blob then needs to hold only the sections before the
+// payload) and the calibration is read from calib when that is not null.
+qsc_status parse_and_validate(const uint8_t *blob, uint64_t nbytes, Parsed *out, std::string *msg,
+                              bool streams = true, const uint8_t *calib = nullptr);
 
 // Paired pair models (FORMAT 3.1): counts[32][256], window bases, in-use masks.
 struct PairModels {

@@ -116,40 +116,19 @@ qsc_status finish_query(qsc_resident *res, hipError_t launch, hipStream_t st, in
     return wait ? check_done(res, st) : QSC_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char *qsc_abi(void) { return "qsc-byte-rans-v1;qsc-paired-v1"; }
-
-const char *qsc_status_string(qsc_status s) {
-    switch (s) {
-    case QSC_OK: return "ok";
-    case QSC_ERR_INVALID_ARG: return "invalid argument";
-    case QSC_ERR_MALFORMED: return "malformed container or stream";
-    case QSC_ERR_UNSUPPORTED: return "unsupported ABI or format version";
-    case QSC_ERR_OOM: return "out of memory";
-    case QSC_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-    }
-}
-
-qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uint8_t *host_valid, void *hip_stream,
-                               qsc_resident **out) {
-    if (!host_blob || !out) return QSC_ERR_INVALID_ARG;
-    *out = nullptr;
-    Parsed ps;
-    std::string msg;
-    std::unique_ptr<qsc_resident> res(new (std::nothrow) qsc_resident);
+// A resident around a validated blob. blob holds at least the sections
+// before the payload (host memory); the whole blob is copied to the device
+// from host_blob or, when that is null, from dev_blob.
+qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *host_blob, const uint8_t *dev_blob,
+                          uint64_t nbytes, const uint8_t *host_valid, void *hip_stream,
+                          std::unique_ptr<qsc_resident> &res) {
+    res.reset(new (std::nothrow) qsc_resident);
     if (!res) return QSC_ERR_OOM;
-    qsc_status st = parse_and_validate(static_cast<const uint8_t *>(host_blob), nbytes, &ps, &msg);
-    if (st != QSC_OK) return st;  // no resident exists to carry the message
     const Geometry &g = ps.g;
     const Sections &s = ps.sec;
     res->g = g;
     res->sec = s;
     std::copy(ps.mode_counts, ps.mode_counts + 8, res->mode_counts);
-    const uint8_t *blob = static_cast<const uint8_t *>(host_blob);
     const uint64_t nb = g.n_blocks(), G = g.G();
     res->dir.assign(blob + s.dir, blob + s.dir + 16 * nb);
     res->gbase.resize(nb * G);
@@ -165,7 +144,9 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     };
     // the whole blob, plus zero padding that the decoders may read ahead into
     if ((e = dalloc(res.get(), &res->d_blob, nbytes + kDevicePad)) != hipSuccess) return bail(e, "blob");
-    if ((e = hipMemcpy(res->d_blob, blob, nbytes, hipMemcpyHostToDevice)) != hipSuccess) return bail(e, "upload");
+    if ((e = hipMemcpy(res->d_blob, host_blob ? host_blob : dev_blob, nbytes,
+                       host_blob ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice)) != hipSuccess)
+        return bail(e, "upload");
     if ((e = hipMemset(res->d_blob + nbytes, 0, kDevicePad)) != hipSuccess) return bail(e, "pad");
     // decode tables
     std::vector<uint32_t> tables;
@@ -222,6 +203,108 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     d.n_blocks = g.n_blocks();
     d.dtype = g.dtype;
     d.layout = g.layout;
+    return QSC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qsc_abi(void) { return "qsc-byte-rans-v1;qsc-paired-v1"; }
+
+const char *qsc_status_string(qsc_status s) {
+    switch (s) {
+    case QSC_OK: return "ok";
+    case QSC_ERR_INVALID_ARG: return "invalid argument";
+    case QSC_ERR_MALFORMED: return "malformed container or stream";
+    case QSC_ERR_UNSUPPORTED: return "unsupported ABI or format version";
+    case QSC_ERR_OOM: return "out of memory";
+    case QSC_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uint8_t *host_valid, void *hip_stream,
+                               qsc_resident **out) {
+    if (!host_blob || !out) return QSC_ERR_INVALID_ARG;
+    *out = nullptr;
+    Parsed ps;
+    std::string msg;
+    const uint8_t *blob = static_cast<const uint8_t *>(host_blob);
+    qsc_status st = parse_and_validate(blob, nbytes, &ps, &msg);
+    if (st != QSC_OK) return st;  // no resident exists to carry the message
+    std::unique_ptr<qsc_resident> res;
+    if ((st = build_resident(ps, blob, blob, nullptr, nbytes, host_valid, hip_stream, res)) != QSC_OK) return st;
+    *out = res.release();
+    return QSC_OK;
+}
+
+qsc_status qsc_resident_create_device(const void *d_blob, uint64_t nbytes, const uint8_t *host_valid,
+                                      void *hip_stream, qsc_resident **out) {
+    if (!d_blob || !out) return QSC_ERR_INVALID_ARG;
+    *out = nullptr;
+    const uint8_t *dev = static_cast<const uint8_t *>(d_blob);
+    if (nbytes < kHeaderBytes) return QSC_ERR_MALFORMED;
+    // the header fixes the size of the sections before the payload
+    uint8_t hdr[kHeaderBytes];
+    if (hipMemcpy(hdr, dev, kHeaderBytes, hipMemcpyDeviceToHost) != hipSuccess) return QSC_ERR_HIP;
+    Geometry g;
+    g.layout = ld32(hdr + 44);
+    g.scan_rows = ld32(hdr + 48);
+    g.scan_cols = ld32(hdr + 52);
+    g.det_rows = ld32(hdr + 56);
+    g.det_cols = ld32(hdr + 60);
+    g.dtype = ld32(hdr + 64);
+    g.scaled = ld32(hdr + 76) & 1;
+    if (!check_geometry(g).empty()) return QSC_ERR_MALFORMED;
+    const Sections want = layout_sections(g, ld64(hdr + 120));
+    if (want.payload != ld64(hdr + 112) || want.total != nbytes) return QSC_ERR_MALFORMED;
+    std::vector<uint8_t> pre(want.payload), cal(g.scaled ? 16ull * g.n_blocks() : 0);
+    if (hipMemcpy(pre.data(), dev, pre.size(), hipMemcpyDeviceToHost) != hipSuccess) return QSC_ERR_HIP;
+    if (g.scaled && hipMemcpy(cal.data(), dev + want.calib, cal.size(), hipMemcpyDeviceToHost) != hipSuccess)
+        return QSC_ERR_HIP;
+    Parsed ps;
+    std::string msg;
+    qsc_status st = parse_and_validate(pre.data(), nbytes, &ps, &msg, false, g.scaled ? cal.data() : nullptr);
+    if (st != QSC_OK) return st;
+    std::unique_ptr<qsc_resident> res;
+    if ((st = build_resident(ps, pre.data(), nullptr, dev, nbytes, host_valid, hip_stream, res)) != QSC_OK) return st;
+    // stream headers on the device: reserved bits, modes, RANS only with a usable table
+    const uint32_t nb = g.n_blocks();
+    std::vector<uint8_t> usable(nb, 1);
+    if (g.layout == 0)
+        for (uint32_t b = 0; b < nb; b++) {
+            uint32_t nz = 0, full = 0;
+            for (int i = 0; i < 256; i++) {
+                const uint32_t f = ld16(pre.data() + ps.sec.table + 512ull * b + 2 * i);
+                nz += f != 0;
+                full |= f == kRansM;
+            }
+            usable[b] = nz > 0 && !full;
+        }
+    uint8_t *d_usable = nullptr;
+    unsigned long long *d_chk = nullptr;  // 8 mode counts, then the first bad stream
+    hipError_t e = hipMalloc(&d_usable, nb);
+    if (e == hipSuccess) e = hipMalloc(&d_chk, 9 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipMemcpy(d_usable, usable.data(), nb, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(d_chk, 0, 8 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipMemset(d_chk + 8, 0xFF, sizeof(unsigned long long));
+    hipStream_t strm = static_cast<hipStream_t>(hip_stream);
+    if (e == hipSuccess) e = launch_check_headers(res->dev, d_usable, d_chk, d_chk + 8, strm);
+    unsigned long long chk[9] = {0};
+    if (e == hipSuccess) e = hipStreamSynchronize(strm);
+    if (e == hipSuccess) e = hipMemcpy(chk, d_chk, sizeof(chk), hipMemcpyDeviceToHost);
+    if (d_usable) (void)hipFree(d_usable);
+    if (d_chk) (void)hipFree(d_chk);
+    if (e != hipSuccess) {
+        free_all(res.get());
+        return e == hipErrorOutOfMemory ? QSC_ERR_OOM : QSC_ERR_HIP;
+    }
+    if (chk[8] != ~0ull) {
+        free_all(res.get());
+        return QSC_ERR_MALFORMED;
+    }
+    std::copy(chk, chk + 8, res->mode_counts);
     *out = res.release();
     return QSC_OK;
 }
