@@ -100,8 +100,7 @@ qsc_status qsc_encoder_destroy(qsc_encoder *enc);
  * memory (paired-resident page, "Operation pipeline" items 1-2: complete
  * 512-scan blocks coded per detector-pixel stream; scaled-uint16 page: each
  * float32 region calibrated to uint16 codes first). The output is
- * byte-identical to the host encoder's. Byte-rANS layout only (layout 1 ->
- * UNSUPPORTED).
+ * byte-identical to the host encoder's, for both layouts.
  *
  * qsc_encode_device_bound: the largest container the geometry can encode to
  *   (every stream raw); a capacity that always suffices.

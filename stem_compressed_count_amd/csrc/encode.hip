@@ -1,5 +1,5 @@
-// Device encoder: byte-rANS containers (FORMAT.md sections 1 and 2) built
-// from values already in device memory, byte-identical to the host encoder.
+// Device encoder: containers of both stream layouts (FORMAT.md) built from
+// values already in device memory, byte-identical to the host encoder.
 //
 // The paired-resident page ("Operation pipeline" items 1-2) has counts arrive
 // as complete 512-scan blocks and be coded per detector-pixel stream with a
@@ -16,6 +16,12 @@
 //     sizes and bases;
 //   k_enc_write: one lane per stream writes its header and payload, the rANS
 //     words straight to their final place (the last pushed word first).
+// The paired layout (FORMAT 3) replaces the table and size steps: one lane per
+// stream finds EMPTY / CONST, the SPARSE size, the static cost of all 32 pair
+// models at once (32 accumulators, one pass over the pairs), then runs the
+// tANS coder of the cheapest model in reverse for its exact bit count; the
+// writer runs it again and fills the code section from its end, 16 bits at a
+// time, since the pairs are coded last to first but read first to last.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -407,6 +413,186 @@ __global__ __launch_bounds__(kWG) void k_enc_write(const T *data, EncGeom g, con
     }
 }
 
+// ------------------------------------------------------------------ paired tANS (FORMAT 3)
+// Device copy of the pair models' encode tables.
+struct PairDev {
+    uint16_t n[kModels][256];
+    uint16_t first[kModels][257];
+    uint16_t states[kModels][kTansL];
+    uint16_t cost[kModels][256];
+    uint32_t a0[kModels], use[kModels];
+};
+
+__device__ __forceinline__ uint32_t wsym(uint32_t v, uint32_t a0, uint32_t use) {
+    const uint32_t d = v - a0;
+    return (v >= a0 && d < 15 && ((use >> d) & 1u)) ? d : 15u;
+}
+
+// smallest k with (x >> k) < 2 n (x < 2048, n >= 1)
+__device__ __forceinline__ uint32_t tans_shift(uint32_t x, uint32_t n) {
+    uint32_t k = 0;
+    while ((x >> k) >= 2 * n) k++;
+    return k;
+}
+
+// size[b][p] = mode << 16 | bytes; aux[b][p] = model | code bits << 8 (PAIRED)
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_penc_size(const T *data, EncGeom g, const PairDev *pd, uint32_t *size,
+                                                   uint32_t *aux) {
+    __shared__ uint16_t cost[kModels * 256];
+    __shared__ uint32_t a0s[kModels], uses[kModels];
+    for (uint32_t i = threadIdx.x; i < kModels * 256; i += kWG) cost[i] = pd->cost[i / 256][i % 256];
+    if (threadIdx.x < kModels) {
+        a0s[threadIdx.x] = pd->a0[threadIdx.x];
+        uses[threadIdx.x] = pd->use[threadIdx.x];
+    }
+    __syncthreads();
+    const uint32_t b = blockIdx.y, p = blockIdx.x * kWG + threadIdx.x;
+    if (p >= g.P) return;
+    const uint64_t i = (uint64_t)b * g.P + p;
+    const bool wide = sizeof(T) == 2;
+    const uint32_t lit = wide ? 16 : 8;
+    const uint32_t v0 = value_at(data, g, b, 0, p);
+    uint32_t nnz = 0;
+    bool eq = true;
+    for (uint32_t j = 0; j < kBlock; j++) {
+        const uint32_t v = value_at(data, g, b, j, p);
+        eq &= v == v0;
+        nnz += v != 0;
+    }
+    if (nnz == 0) {
+        size[i] = (P_EMPTY << 16) | 2u;
+        return;
+    }
+    if (eq) {
+        size[i] = (P_CONST << 16) | 4u;
+        return;
+    }
+    const uint32_t sparse = 4 + 2 * nnz + (wide ? 2 * nnz : nnz + (nnz & 1u));
+    // static cost of every model (1/256 bits), lowest model on ties
+    uint32_t c[kModels];
+#pragma unroll
+    for (uint32_t m = 0; m < kModels; m++) c[m] = 0;
+    for (uint32_t t = 0; t < 256; t++) {
+        const uint32_t x0 = value_at(data, g, b, 2 * t, p), x1 = value_at(data, g, b, 2 * t + 1, p);
+#pragma unroll
+        for (uint32_t m = 0; m < kModels; m++) {
+            const uint32_t a = wsym(x0, a0s[m], uses[m]), e = wsym(x1, a0s[m], uses[m]);
+            c[m] += cost[m * 256 + a * 16 + e] + (a == 15 ? 256 * lit : 0) + (e == 15 ? 256 * lit : 0);
+        }
+    }
+    uint32_t best = 0, best_c = c[0];
+#pragma unroll
+    for (uint32_t m = 1; m < kModels; m++)
+        if (c[m] < best_c) {
+            best_c = c[m];
+            best = m;
+        }
+    // exact code bits of the chosen model: the coder in reverse
+    const uint32_t a0 = a0s[best], use = uses[best];
+    uint32_t x = kTansL, bits = 10;
+    for (int t = 255; t >= 0; t--) {
+        const uint32_t x0 = value_at(data, g, b, 2 * t, p), x1 = value_at(data, g, b, 2 * t + 1, p);
+        const uint32_t a = wsym(x0, a0, use), e = wsym(x1, a0, use), s = a * 16 + e;
+        const uint32_t ns = pd->n[best][s], k = tans_shift(x, ns);
+        bits += k + (a == 15 ? lit : 0) + (e == 15 ? lit : 0);
+        x = kTansL + pd->states[best][pd->first[best][s] + ((x >> k) - ns)];
+    }
+    const uint32_t paired = 2 + (bits + 15) / 16 * 2;
+    uint32_t mode = P_SPARSE, bytes = sparse;
+    if (sparse >= paired + 2) {
+        mode = P_PAIRED;
+        bytes = paired;
+    }
+    const uint32_t raw = raw_bytes(kBlock, wide);
+    if (raw < bytes) {
+        mode = P_RAW;
+        bytes = raw;
+    }
+    size[i] = (mode << 16) | bytes;
+    aux[i] = best | (bits << 8);
+}
+
+// Code section writer that runs backwards: bits are prepended below the
+// buffer, and each completed 16-bit word at its top is stored.
+struct BackBits {
+    uint16_t *words;  // the code section
+    uint64_t acc;     // buffered bits, lowest = the lowest buffered position
+    uint32_t nb, top; // buffered bit count; position just above the buffer
+    __device__ __forceinline__ void put(uint32_t v, uint32_t k) {
+        acc = (acc << k) | v;
+        nb += k;
+        while (nb >= 32) flush16();
+    }
+    __device__ __forceinline__ void flush16() {
+        words[(top - 16) / 16] = (uint16_t)(acc >> (nb - 16));
+        top -= 16;
+        nb -= 16;
+        acc &= (1ull << nb) - 1;
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void k_penc_write(const T *data, EncGeom g, const PairDev *pd, const uint32_t *size,
+                                                    const uint32_t *aux, const uint32_t *soff, const uint64_t *bbase,
+                                                    uint8_t *payload) {
+    const uint32_t b = blockIdx.y, p = blockIdx.x * kWG + threadIdx.x;
+    if (p >= g.P) return;
+    const uint64_t i = (uint64_t)b * g.P + p;
+    const bool wide = sizeof(T) == 2;
+    const uint32_t mode = size[i] >> 16;
+    uint8_t *dst = payload + bbase[b] + soff[i];
+    uint16_t *d16 = reinterpret_cast<uint16_t *>(dst);
+    if (mode == P_EMPTY) {
+        d16[0] = P_EMPTY;
+    } else if (mode == P_CONST) {
+        d16[0] = P_CONST;
+        d16[1] = (uint16_t)value_at(data, g, b, 0, p);
+    } else if (mode == P_RAW) {
+        d16[0] = P_RAW;
+        if (wide)
+            for (uint32_t j = 0; j < kBlock; j++) d16[1 + j] = (uint16_t)value_at(data, g, b, j, p);
+        else
+            for (uint32_t j = 0; j < kBlock; j++) dst[2 + j] = (uint8_t)value_at(data, g, b, j, p);
+    } else if (mode == P_SPARSE) {
+        d16[0] = P_SPARSE;
+        uint32_t nnz = 0;
+        for (uint32_t j = 0; j < kBlock; j++)
+            if (value_at(data, g, b, j, p)) d16[2 + nnz++] = (uint16_t)j;
+        d16[1] = (uint16_t)nnz;
+        uint8_t *vals = dst + 4 + 2 * nnz;
+        uint32_t k = 0;
+        for (uint32_t j = 0; j < kBlock; j++) {
+            const uint32_t v = value_at(data, g, b, j, p);
+            if (!v) continue;
+            if (wide)
+                reinterpret_cast<uint16_t *>(vals)[k++] = (uint16_t)v;
+            else
+                vals[k++] = (uint8_t)v;
+        }
+        if (!wide && (nnz & 1u)) vals[nnz] = 0;
+    } else {
+        const uint32_t m = aux[i] & 0xFFu, bits = aux[i] >> 8, lit = wide ? 16 : 8;
+        d16[0] = (uint16_t)(P_PAIRED | (m << 3));
+        const uint32_t a0 = pd->a0[m], use = pd->use[m];
+        const uint32_t padded = (bits + 15) / 16 * 16;
+        BackBits w{d16 + 1, 0, padded - bits, padded};  // the zero padding is buffered first
+        uint32_t x = kTansL;
+        for (int t = 255; t >= 0; t--) {
+            const uint32_t x0 = value_at(data, g, b, 2 * t, p), x1 = value_at(data, g, b, 2 * t + 1, p);
+            const uint32_t a = wsym(x0, a0, use), e = wsym(x1, a0, use), s = a * 16 + e;
+            const uint32_t ns = pd->n[m][s], k = tans_shift(x, ns);
+            // pair t reads: state bits, then the first literal, then the second
+            if (e == 15) w.put(x1, lit);
+            if (a == 15) w.put(x0, lit);
+            w.put(x & ((1u << k) - 1u), k);
+            x = kTansL + pd->states[m][pd->first[m][s] + ((x >> k) - ns)];
+        }
+        w.put(x - kTansL, 10);
+        while (w.nb) w.flush16();
+    }
+}
+
 template <typename T>
 hipError_t encode_rans(const T *data, const EncGeom &g, const Sections &s0, uint8_t *blob, uint32_t *hist,
                        uint32_t *enc, uint8_t *usable, uint32_t *meta, uint32_t *size, uint32_t *soff,
@@ -433,6 +619,50 @@ hipError_t write_rans(const T *data, const EncGeom &g, const Sections &s0, uint8
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t encode_paired(const T *data, const EncGeom &g, const Sections &s0, uint8_t *blob, const PairDev *pd,
+                         uint32_t *size, uint32_t *aux, uint32_t *soff, uint64_t *bbytes, uint64_t *bbase,
+                         uint64_t *total, hipStream_t st) {
+    const dim3 grid((g.P + kWG - 1) / kWG, g.nb);
+    hipLaunchKernelGGL(k_penc_size<T>, grid, dim3(kWG), 0, st, data, g, pd, size, aux);
+    hipLaunchKernelGGL(k_enc_offsets, dim3(g.nb), dim3(1024), 0, st, g, size, soff,
+                       reinterpret_cast<uint32_t *>(blob + s0.gbase), reinterpret_cast<uint16_t *>(blob + s0.rel),
+                       bbytes);
+    hipLaunchKernelGGL(k_enc_dir, dim3(1), dim3(1024), 0, st, g, bbytes, blob + s0.dir, bbase, total);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t write_paired(const T *data, const EncGeom &g, const Sections &s0, uint8_t *blob, const PairDev *pd,
+                        const uint32_t *size, const uint32_t *aux, const uint32_t *soff, const uint64_t *bbase,
+                        hipStream_t st) {
+    const dim3 grid((g.P + kWG - 1) / kWG, g.nb);
+    hipLaunchKernelGGL(k_penc_write<T>, grid, dim3(kWG), 0, st, data, g, pd, size, aux, soff, bbase,
+                       blob + s0.payload);
+    return hipGetLastError();
+}
+
+// Host copy of the pair models' encode tables in the device layout.
+const PairDev &pair_dev() {
+    static const PairDev t = [] {
+        PairDev d{};
+        const PairModels &pm = pair_models();
+        const PairEncodeTables &pt = pair_encode_tables();
+        for (uint32_t m = 0; m < kModels; m++) {
+            for (uint32_t i = 0; i < 256; i++) {
+                d.n[m][i] = pm.n[m][i];
+                d.cost[m][i] = (uint16_t)pt.cost[m][i];  // at most 256 * 10
+            }
+            for (uint32_t i = 0; i < 257; i++) d.first[m][i] = pt.first[m][i];
+            for (uint32_t X = 0; X < kTansL; X++) d.states[m][X] = pt.states[m][X];
+            d.a0[m] = pm.a0[m];
+            d.use[m] = pm.in_use[m];
+        }
+        return d;
+    }();
+    return t;
+}
+
 // Device workspace of one encode, carved from a single allocation.
 struct Workspace {
     void *base = nullptr;
@@ -442,6 +672,7 @@ struct Workspace {
     unsigned long long *lo = nullptr, *hi = nullptr;
     double *calib = nullptr;
     uint16_t *codes = nullptr;
+    PairDev *pair = nullptr;
     ~Workspace() {
         if (base) (void)hipFree(base);
     }
@@ -458,6 +689,7 @@ struct Workspace {
         const uint64_t o_bbytes = take(8 * nb), o_bbase = take(8 * nb), o_total = take(8), o_bad = take(4);
         const uint64_t o_lo = take(8 * nb), o_hi = take(8 * nb), o_calib = take(16 * nb);
         const uint64_t o_codes = g.scaled ? take(2 * g.S() * P) : 0;
+        const uint64_t o_pair = g.layout == 1 ? take(sizeof(PairDev)) : 0;
         hipError_t e = hipMalloc(&base, off);
         if (e != hipSuccess) {
             base = nullptr;
@@ -478,6 +710,7 @@ struct Workspace {
         hi = reinterpret_cast<unsigned long long *>(b8 + o_hi);
         calib = reinterpret_cast<double *>(b8 + o_calib);
         codes = g.scaled ? reinterpret_cast<uint16_t *>(b8 + o_codes) : nullptr;
+        pair = g.layout == 1 ? reinterpret_cast<PairDev *>(b8 + o_pair) : nullptr;
         return hipSuccess;
     }
 };
@@ -521,7 +754,6 @@ qsc_status qsc_encode_device(const qsc_geometry *geom, const void *d_data, void 
     g.layout = geom->layout;
     g.scaled = geom->scaled;
     if (!check_geometry(g).empty()) return QSC_ERR_INVALID_ARG;
-    if (g.layout != 0) return QSC_ERR_UNSUPPORTED;
     const Sections s0 = layout_sections(g, 0);
     if (capacity < s0.payload) return QSC_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -549,12 +781,27 @@ qsc_status qsc_encode_device(const qsc_geometry *geom, const void *d_data, void 
                            st, x, eg, ws.calib, ws.codes);
         src = ws.codes;
     }
-    if (g.dtype == 2 || g.scaled)
+    if (g.layout == 1) {
+        // the 32 pair models' counts are the table section
+        const PairDev &pd = pair_dev();
+        if ((e = hipMemcpyAsync(ws.pair, &pd, sizeof(PairDev), hipMemcpyHostToDevice, st)) != hipSuccess)
+            return hip_status(e);
+        if ((e = hipMemcpyAsync(blob + s0.table, pair_models().n, sizeof(pair_models().n), hipMemcpyHostToDevice,
+                                st)) != hipSuccess)
+            return hip_status(e);
+        if (g.dtype == 2)
+            e = encode_paired(static_cast<const uint16_t *>(src), eg, s0, blob, ws.pair, ws.size, ws.meta, ws.soff,
+                              ws.bbytes, ws.bbase, ws.total, st);
+        else
+            e = encode_paired(static_cast<const uint8_t *>(src), eg, s0, blob, ws.pair, ws.size, ws.meta, ws.soff,
+                              ws.bbytes, ws.bbase, ws.total, st);
+    } else if (g.dtype == 2 || g.scaled) {
         e = encode_rans(static_cast<const uint16_t *>(src), eg, s0, blob, ws.hist, ws.enc, ws.usable, ws.meta,
                         ws.size, ws.soff, ws.bbytes, ws.bbase, ws.total, st);
-    else
+    } else {
         e = encode_rans(static_cast<const uint8_t *>(src), eg, s0, blob, ws.hist, ws.enc, ws.usable, ws.meta,
                         ws.size, ws.soff, ws.bbytes, ws.bbase, ws.total, st);
+    }
     if (e != hipSuccess) return hip_status(e);
     uint64_t pay = 0;
     uint32_t bad = 0;
@@ -566,12 +813,20 @@ qsc_status qsc_encode_device(const qsc_geometry *geom, const void *d_data, void 
     const Sections s = layout_sections(g, pay);
     *nbytes = s.total;
     if (s.total > capacity) return QSC_ERR_INVALID_ARG;
-    if (g.dtype == 2 || g.scaled)
+    if (g.layout == 1) {
+        if (g.dtype == 2)
+            e = write_paired(static_cast<const uint16_t *>(src), eg, s0, blob, ws.pair, ws.size, ws.meta, ws.soff,
+                             ws.bbase, st);
+        else
+            e = write_paired(static_cast<const uint8_t *>(src), eg, s0, blob, ws.pair, ws.size, ws.meta, ws.soff,
+                             ws.bbase, st);
+    } else if (g.dtype == 2 || g.scaled) {
         e = write_rans(static_cast<const uint16_t *>(src), eg, s0, blob, ws.enc, ws.meta, ws.size, ws.soff, ws.bbase,
                        st);
-    else
+    } else {
         e = write_rans(static_cast<const uint8_t *>(src), eg, s0, blob, ws.enc, ws.meta, ws.size, ws.soff, ws.bbase,
                        st);
+    }
     if (e != hipSuccess) return hip_status(e);
     if (g.scaled) {
         const uint64_t end = s.payload + s.payload_bytes;

@@ -116,40 +116,41 @@ void emit_values(std::vector<uint8_t> &o, const uint32_t *v, uint32_t n, uint32_
 
 // ------------------------------------------------------------ paired tANS
 
-struct PairEncodeTables {
-    // occurrence states of each symbol in spread order, flattened per model
-    uint16_t first[kModels][257];
-    uint16_t states[kModels][kTansL];
-    uint32_t cost[kModels][256]; // ceil(256 * log2(1024 / n)), static cost in 1/256 bits
-    PairEncodeTables() {
-        const PairModels &pm = pair_models();
-        for (uint32_t m = 0; m < kModels; m++) {
-            uint16_t spread[kTansL];
-            uint32_t pos = 0;
-            for (uint32_t i = 0; i < 256; i++)
-                for (uint32_t k = 0; k < pm.n[m][i]; k++) {
-                    spread[pos] = uint16_t(i);
-                    pos = (pos + 643) & (kTansL - 1);
-                }
-            uint32_t acc = 0;
-            for (uint32_t i = 0; i < 256; i++) {
-                first[m][i] = uint16_t(acc);
-                acc += pm.n[m][i];
-            }
-            first[m][256] = uint16_t(acc);
-            uint32_t fill[256];
-            for (uint32_t i = 0; i < 256; i++) fill[i] = first[m][i];
-            for (uint32_t X = 0; X < kTansL; X++) states[m][fill[spread[X]]++] = uint16_t(X);
-            for (uint32_t i = 0; i < 256; i++)
-                cost[m][i] = pm.n[m][i] ? uint32_t(std::ceil(256.0 * std::log2(1024.0 / double(pm.n[m][i])))) : 0;
-        }
-    }
-};
+} // namespace
 
-const PairEncodeTables &pair_tables() {
+// The paired encode tables, built once from the format's pair models.
+qsc::PairEncodeTables::PairEncodeTables() {
+    const PairModels &pm = pair_models();
+    for (uint32_t m = 0; m < kModels; m++) {
+        uint16_t spread[kTansL];
+        uint32_t pos = 0;
+        for (uint32_t i = 0; i < 256; i++)
+            for (uint32_t k = 0; k < pm.n[m][i]; k++) {
+                spread[pos] = uint16_t(i);
+                pos = (pos + 643) & (kTansL - 1);
+            }
+        uint32_t acc = 0;
+        for (uint32_t i = 0; i < 256; i++) {
+            first[m][i] = uint16_t(acc);
+            acc += pm.n[m][i];
+        }
+        first[m][256] = uint16_t(acc);
+        uint32_t fill[256];
+        for (uint32_t i = 0; i < 256; i++) fill[i] = first[m][i];
+        for (uint32_t X = 0; X < kTansL; X++) states[m][fill[spread[X]]++] = uint16_t(X);
+        for (uint32_t i = 0; i < 256; i++)
+            cost[m][i] = pm.n[m][i] ? uint32_t(std::ceil(256.0 * std::log2(1024.0 / double(pm.n[m][i])))) : 0;
+    }
+}
+
+const PairEncodeTables &qsc::pair_encode_tables() {
     static PairEncodeTables t;
     return t;
 }
+
+namespace {
+
+const PairEncodeTables &pair_tables() { return pair_encode_tables(); }
 
 inline uint32_t wsym(uint32_t v, uint32_t a0, uint32_t use) {
     const uint32_t d = v - a0;

@@ -70,6 +70,17 @@ struct PairModels {
 };
 const PairModels &pair_models();
 
+// Paired encode tables (FORMAT 3.2, 3.4): per model, the states of each pair
+// symbol's occurrences in spread order (states[first[i] .. first[i+1])), and
+// the static cost ceil(256 * log2(1024 / n[i])) in 1/256 bits.
+struct PairEncodeTables {
+    uint16_t first[kModels][257];
+    uint16_t states[kModels][kTansL];
+    uint32_t cost[kModels][256];
+    PairEncodeTables();
+};
+const PairEncodeTables &pair_encode_tables();
+
 // Device decode-table entries.
 //  byte-rANS (per block, two planes of 4096 entries): f | symbol << 24, then slot - c
 //  paired (per model, 1024 entries): a | b << 8 | nbits << 16 | newX << 20 | escape << 31

@@ -5,8 +5,8 @@ qsc_encode_device must write the container the format's reference encoder
 tables, offsets, every stream's mode and words, calibration. Cases cover
 partial blocks, detectors that are not a multiple of 32 pixels, constant and
 all-zero blocks, u16 escapes, a block whose table degenerates to one symbol
-(its streams go raw), and scaled float32 input with signed zeros and constant
-regions. A resident created from the device container answers queries like
+(its streams go raw), scaled float32 input with signed zeros and constant
+regions, and the paired layout's five modes and model choice. A resident created from the device container answers queries like
 the oracle; malformed device containers are refused.
 """
 import ctypes
@@ -41,9 +41,9 @@ def dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def check_identical(data, sr, sc, dr, dc, scaled=False):
-    got = q().encode_device(dev(data), sr, sc, dr, dc, scaled=scaled).cpu().numpy()
-    want = np.frombuffer(oracle.encode(data, sr, sc, dr, dc, scaled=scaled), dtype=np.uint8)
+def check_identical(data, sr, sc, dr, dc, scaled=False, layout=0):
+    got = q().encode_device(dev(data), sr, sc, dr, dc, layout=layout, scaled=scaled).cpu().numpy()
+    want = np.frombuffer(oracle.encode(data, sr, sc, dr, dc, layout=layout, scaled=scaled), dtype=np.uint8)
     assert got.size == want.size
     if not np.array_equal(got, want):
         first = int(np.nonzero(got != want)[0][0])
@@ -74,6 +74,26 @@ def test_adversarial_blocks_byte_identical():
     u8[:, 0] = 255
     u8[::3, 1] = 255
     check_identical(u8, 700, 1, 3, 11)
+
+
+def test_paired_byte_identical():
+    w = synth.WORKLOADS["scan1024_u16_paired"].with_scans(1, 1024)  # two blocks
+    check_identical(synth.counts(w), w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, layout=1)
+    rng = np.random.default_rng(8)
+    x = rng.poisson(0.7, size=(1024, 70)).astype(np.uint16)
+    x[:, 0] = 0                                         # EMPTY
+    x[:, 1] = 9                                         # CONST
+    x[:, 2] = 0
+    x[::97, 2] = 3                                      # SPARSE
+    x[:, 3] = rng.integers(0, 65536, size=1024)         # RAW
+    x[:, 4] = rng.poisson(18.0, size=1024)              # a high-rate model
+    x[::5, 5] = 60000                                   # escapes with literals
+    x[:512, 6:10] = rng.poisson(0.02, size=(512, 4))    # the lowest-rate models
+    check_identical(x, 1024, 1, 7, 10, layout=1)
+    u8 = rng.poisson(2.0, size=(512, 33)).astype(np.uint8)
+    u8[::7, 0] = 250
+    u8[:, 1] = rng.integers(0, 256, size=512)
+    check_identical(u8, 512, 1, 3, 11, layout=1)
 
 
 def test_scaled_byte_identical():
@@ -110,6 +130,14 @@ def test_resident_from_device_container():
         assert np.array_equal(got, oracle.region(sub, 6, 0, 2, 0, 6, valid))
         res.finish()
     del blob  # the resident keeps its own copy
+    wp = synth.WORKLOADS["scan1024_u16_paired"].with_scans(2, 1024)
+    cp = synth.counts(wp)
+    pblob = qq.encode_device(dev(cp), wp.scan_rows, wp.scan_cols, wp.det_rows, wp.det_cols, layout=1)
+    with qq.Resident(pblob) as res:
+        assert res.info.geom.layout == 1
+        bf = synth.query_masks(wp)["bf"]
+        assert np.array_equal(qq.as_unsigned(res.masked_sum(bf)).astype(np.uint64), oracle.masked_sum(cp, bf))
+        res.finish()
     scaled = synth.scaled(w)
     sblob = qq.encode_device(dev(scaled), w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, scaled=True)
     with qq.Resident(sblob) as res:
@@ -122,9 +150,8 @@ def test_device_encoder_errors():
     import torch
     qq = q()
     x = np.zeros((512, 64), np.uint16)
-    with pytest.raises(qq.QscError) as e:
-        qq.encode_device(dev(x), 512, 1, 8, 8, layout=1)
-    assert e.value.code == qq.ERR_UNSUPPORTED
+    with pytest.raises(qq.QscValueError):
+        qq.encode_device(dev(x[:500]), 500, 1, 8, 8, layout=1)  # the paired layout needs whole blocks
     f = np.ones((512, 64), np.float32)
     f[100, 3] = np.nan
     with pytest.raises(qq.QscValueError):
@@ -149,3 +176,10 @@ def test_device_encoder_errors():
     blob[0] = ord("X")  # bad magic
     with pytest.raises(qq.QscValueError):
         qq.Resident(blob)
+
+
+@pytest.mark.slow
+def test_full_size_128x128_byte_identical():
+    """The whole 128x128-scan u16 workload (604 M values) against the oracle encoder."""
+    w = synth.WORKLOADS["scan128_u16"]
+    check_identical(synth.counts(w), w.scan_rows, w.scan_cols, w.det_rows, w.det_cols)
