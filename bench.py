@@ -267,6 +267,61 @@ def main():
         del fbuf
         torch.cuda.empty_cache()
 
+    # the moving-mask sweep (64 positions of a BF disk), three ways: a full
+    # decode per mask, one decode then 63 deltas, and the polar index
+    sweep = [torch.as_tensor(m, device=dev) for m in synth.sweep_masks(w)]
+    souts = [torch.empty_like(out) for _ in range(2)]
+
+    def timed_sweep(run):
+        run()  # warm
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def sweep_decode(r):
+        def run():
+            for m in sweep:
+                r.masked_sum(m, 1, out=souts[0], wait=False)
+        return run
+
+    def sweep_delta():
+        res.masked_sum(sweep[0], 1, out=souts[0], wait=False)
+        for j in range(1, len(sweep)):
+            res.masked_sum_delta(sweep[j - 1], souts[(j - 1) % 2], sweep[j], 1, out=souts[j % 2], wait=False)
+
+    sw_decode = timed_sweep(sweep_decode(res))
+    sw_delta = timed_sweep(sweep_delta)
+    res.finish()
+    sweep_exact = bool(torch.equal(souts[(len(sweep) - 1) % 2], res.masked_sum(sweep[-1], 1)))
+    ires = qsc.Resident(blob, valid=valid)
+    t0 = time.perf_counter()
+    ires.index_build()
+    ix_build_ms = (time.perf_counter() - t0) * 1e3
+    sw_index = timed_sweep(sweep_decode(ires))
+    ires.finish()
+    ix_bytes = int(ires.info.index_bytes)
+    ires.close()
+
+    # the device encoder: the whole workload from native counts in HBM
+    raw = torch.from_numpy(synth.counts(w).view(np.int16) if w.dtype == 2 else synth.counts(w)).to(dev)
+    dblob = qsc.encode_device(raw, w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, layout=w.layout)
+    enc_identical = bool(np.array_equal(dblob.cpu().numpy(), blob))
+    del dblob
+    enc_ms = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dblob = qsc.encode_device(raw, w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, layout=w.layout)
+        torch.cuda.synchronize()
+        enc_ms.append((time.perf_counter() - t0) * 1e3)
+        del dblob
+    del raw
+    torch.cuda.empty_cache()
+
     com_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["com_full"]]))
     com_gbps = by_full / (com_ms * 1e-3) / 1e9
     tops = cn_full * ALG_OPS_MOMENTS / (com_ms * 1e-3) / 1e12
@@ -299,7 +354,18 @@ def main():
         "roofline": roofline,
         "next_rows": {"sum_dp": {"ms": round(dp_ms, 4), "counts_per_s": round(dp_counts / (dp_ms * 1e-3), 1),
                                  "what": "sum + mean diffraction pattern over every scan (not in the step)"},
-                      "decode_blocks": dict(feed, what="every block decoded to frames (not in the step)")},
+                      "decode_blocks": dict(feed, what="every block decoded to frames (not in the step)"),
+                      "mask_sweep": {"positions": len(sweep), "decode_ms": round(sw_decode, 3),
+                                     "delta_ms": round(sw_delta, 3), "index_ms": round(sw_index, 3),
+                                     "index_build_ms": round(ix_build_ms, 2), "index_bytes": ix_bytes,
+                                     "delta_exact": sweep_exact,
+                                     "what": "64-position moving BF disk (r = 53): a full decode per mask, "
+                                             "one decode then deltas, or the polar index"},
+                      "encode_device": {"ms": round(min(enc_ms), 3),
+                                        "values_per_s": round(w.S * w.P / (min(enc_ms) * 1e-3), 1),
+                                        "identical_to_host_encoder": enc_identical,
+                                        "what": "the whole workload encoded on the GPU from native counts in "
+                                                "device memory (host-timed, synchronised, workspace included)"}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, masks, df_mask, args.cpu_sample_blocks)

@@ -10,7 +10,9 @@ at any size are checked on every scan:
   elsewhere;
 - the diffraction pattern summed over pixels equals the full-detector virtual
   image summed over the same scans (the pattern itself is checked on sampled
-  pixels, whose values over every scan are kept while encoding).
+  pixels, whose values over every scan are kept while encoding);
+- on the low-dose workload, the 64-position sweep answered by deltas and by
+  the polar index equals the per-mask decodes on every scan.
 """
 import numpy as np
 import pytest
@@ -247,6 +249,16 @@ def test_u8_512x512_low_dose_full_size():
         check_com_rows(res, w, None, None, scans, sampled)
         check_rects(res, w, None, rects_for(w, 42)[:3])
         check_frames_ends(res, w, None)
+        # the sweep as one decode and 63 deltas equals the per-mask decodes on every scan
+        prev = res.masked_sum(sweep[0])
+        for i in range(1, len(sweep)):
+            prev = res.masked_sum_delta(sweep[i - 1], prev, sweep[i])
+            if i % 9 == 0 or i == len(sweep) - 1:
+                assert np.array_equal(u(prev), outs[i]), i
+        # and through the polar index
+        res.index_build((96, 96))
+        for i in (0, 5, 21, 42, 63):
+            assert np.array_equal(u(res.masked_sum(sweep[i])), outs[i]), i
         res.finish()
 
 
