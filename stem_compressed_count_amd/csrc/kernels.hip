@@ -349,18 +349,22 @@ __device__ __forceinline__ uint32_t dp_count(const uint32_t *bits) {
 constexpr bool is_frames(Op op) { return op == Op::Frames || op == Op::Amp; }
 constexpr bool is_region(Op op) { return op == Op::Region || is_frames(op); }
 
+// Value v of pixel p in the output row starting at element `row` (one scan):
+// the row's address is uniform and the pixel's byte offset a 32-bit lane
+// value, so the store needs no 64-bit address arithmetic per lane.
 template <bool WIDE, bool AMP>
-__device__ __forceinline__ void region_put(const RegionArgs &ra, uint64_t idx, uint32_t v, double scale,
+__device__ __forceinline__ void region_put(const RegionArgs &ra, uint64_t row, uint32_t p, uint32_t v, double scale,
                                            double offset) {
-    void *out = ra.out;
-    if constexpr (AMP)
-        reinterpret_cast<float *>(out)[idx] = ra.amp[v & 0xFFFFu];  // counts are at most 65535
-    else if (ra.out_kind == 1)
-        reinterpret_cast<float *>(out)[idx] = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
-    else if (WIDE)
-        reinterpret_cast<uint16_t *>(out)[idx] = (uint16_t)v;
-    else
-        reinterpret_cast<uint8_t *>(out)[idx] = (uint8_t)v;
+    uint8_t *out = static_cast<uint8_t *>(ra.out);
+    if constexpr (AMP) {
+        *reinterpret_cast<float *>(out + 4 * row + 4u * p) = ra.amp[v & 0xFFFFu];  // counts are at most 65535
+    } else if (ra.out_kind == 1) {
+        *reinterpret_cast<float *>(out + 4 * row + 4u * p) = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
+    } else if (WIDE) {
+        *reinterpret_cast<uint16_t *>(out + 2 * row + 2u * p) = (uint16_t)v;
+    } else {
+        out[row + p] = (uint8_t)v;
+    }
 }
 
 // Scan walk of one block for a region read (FRAMES false: scans inside the
@@ -425,7 +429,7 @@ __device__ __forceinline__ void region_fill(const DevResident &r, uint32_t b, ui
     constexpr bool AMP = OP == Op::Amp;
     auto rw = region_walk<is_frames(OP)>(r, b, ra);
     for (uint32_t j = 0; j < n; j++, rw.next())
-        if (rw.inside()) region_put<WIDE, AMP>(ra, rw.index(r.P) + p, v, rw.scale, rw.offset);
+        if (rw.inside()) region_put<WIDE, AMP>(ra, rw.index(r.P), p, v, rw.scale, rw.offset);
 }
 
 // ------------------------------------------------------------------ byte-rANS tile
@@ -589,15 +593,17 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
 
     auto run = [&](auto form) {
         if constexpr (is_region(OP)) {
-            // values of scans inside the rectangle go straight to the output
-            constexpr int CH = 16;
+            // values of scans inside the rectangle go straight to the output;
+            // frames store every step, and a shorter unroll keeps their
+            // calibrated (float64) path out of spills
+            constexpr int CH = is_frames(OP) ? 4 : 16;
             auto rw = region_walk<is_frames(OP)>(r, b, ra);
             auto put = [&](const uint32_t (&v)[K]) {
                 if (rw.inside()) {
                     const uint64_t idx = rw.index(r.P);
 #pragma unroll
                     for (int k = 0; k < K; k++)
-                        if (sl[k].live) region_put<WIDE, OP == Op::Amp>(ra, idx + sl[k].p, v[k], rw.scale, rw.offset);
+                        if (sl[k].live) region_put<WIDE, OP == Op::Amp>(ra, idx, sl[k].p, v[k], rw.scale, rw.offset);
                 }
                 rw.next();
             };
@@ -879,7 +885,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     auto rw = region_walk<is_frames(OP)>(r, b, ra);
                     const uint64_t s = (uint64_t)b * kBlk + (uint32_t)pos;
                     rw.seek(r, s);
-                    if (rw.inside()) region_put<WIDE, OP == Op::Amp>(ra, rw.index(r.P) + z.p, v, rw.scale, rw.offset);
+                    if (rw.inside()) region_put<WIDE, OP == Op::Amp>(ra, rw.index(r.P), z.p, v, rw.scale, rw.offset);
                 } else if constexpr (OP == Op::Dp) {
                     dsum += v * scan_bit(dt, (uint32_t)pos);
                 } else if constexpr (OP == Op::Index) {
@@ -1004,7 +1010,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                         for (int k = 0; k < K; k++) {
                             const uint32_t mode = sl[k].meta & 7u;
                             if (mode == 3 || mode == 4)
-                                region_put<WIDE, OP == Op::Amp>(ra, idx + sl[k].p, sl[k].a0 + (h ? v1[k] : v0[k]),
+                                region_put<WIDE, OP == Op::Amp>(ra, idx, sl[k].p, sl[k].a0 + (h ? v1[k] : v0[k]),
                                                  rw.scale, rw.offset);
                         }
                     }
