@@ -1141,39 +1141,48 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
 // smaller items spread the work over more compute units.
 struct PlanArgs {
     const uint8_t *mask;
+    const uint8_t *mask2;  // a second (subtracted) mask counted after the first, or null
     const uint8_t *valid;
     int complement;
-    uint32_t P, n_tiles;  // 64-pixel tiles
+    uint32_t P, n_tiles;  // 64-pixel tiles of one mask
     uint32_t *counts;     // null: no plan
 };
 
 constexpr float kTwoSlotTime = 1.7f;
 
 struct PlanView {
-    uint32_t n_items, cap, end;  // items per visited block, pixels per item, end of the last non-empty tile
+    uint32_t n_items, n_first;  // items per visited block; of them, items of the first mask
+    uint32_t cap;               // selected pixels per item
+    uint32_t end[2];            // per mask, the end of its last non-empty tile (pixels)
 };
 
-// Most items a plan can hold: detectors of kMaxPlanTiles tiles cut in halves of a workgroup.
+// Most items a plan can hold: two masks of kMaxPlanTiles tiles cut in halves of a workgroup.
 template <int WG>
-constexpr uint32_t kMaxItems = kMaxPlanTiles * kPlanFine / (WG / 2);
+constexpr uint32_t kMaxItems = 2 * kMaxPlanTiles * kPlanFine / (WG / 2);
 
+// With `two`, the counts of a second mask follow those of the first, and its
+// items (whose values the query subtracts) start after the first mask's:
+// its pixel numbering starts at the first multiple of cap past the first's.
 template <int WG>
-__device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P, uint32_t n_visited, uint16_t *desc,
-                                             uint32_t *wtot) {
-    constexpr uint32_t kPer = kMaxPlanTiles / WG > 0 ? kMaxPlanTiles / WG : 1;
+__device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P, uint32_t n_visited, bool two,
+                                             uint16_t *desc, uint32_t *wtot) {
+    constexpr uint32_t kPer = 2 * kMaxPlanTiles / WG;
     constexpr uint32_t kWaves = WG / 64;
-    __shared__ uint32_t wlast[kWaves];
+    __shared__ uint32_t wpart[4][kWaves];  // per wave: the second mask's sum, and each mask's last tile
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-    const uint32_t n_tiles = (P + kPlanFine - 1) / kPlanFine;
-    uint32_t c[kPer], s = 0, last = 0;
+    const uint32_t n_tiles = (P + kPlanFine - 1) / kPlanFine, n_all = two ? 2 * n_tiles : n_tiles;
+    uint32_t c[kPer], s = 0, s2 = 0, last[2] = {0, 0};
 #pragma unroll
     for (uint32_t j = 0; j < kPer; j++) {
         const uint32_t t = tid * kPer + j;
-        c[j] = t < n_tiles ? counts[t] : 0u;
+        c[j] = t < n_all ? counts[t] : 0u;
         s += c[j];
-        if (c[j]) last = t + 1;
+        const uint32_t second = t >= n_tiles;
+        s2 += second ? c[j] : 0u;
+        if (c[j]) last[second] = t - (second ? n_tiles : 0u) + 1;
     }
-    // exclusive prefix of the per-thread sums, and the end of the last non-empty tile
+    // exclusive prefix of the per-thread sums over both masks, the second
+    // mask's total, and the end of each mask's last non-empty tile
     uint32_t x = s;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -1181,21 +1190,32 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
         if (lane >= (uint32_t)off) x += y;
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) last = max(last, (uint32_t)__shfl_xor(last, off));
+    for (int off = 32; off >= 1; off >>= 1) {
+        s2 += __shfl_xor(s2, off);
+        last[0] = max(last[0], (uint32_t)__shfl_xor(last[0], off));
+        last[1] = max(last[1], (uint32_t)__shfl_xor(last[1], off));
+    }
     __syncthreads();  // wtot may still be read by the previous user
     if (lane == 63) wtot[wave] = x;
-    if (lane == 0) wlast[wave] = last;
+    if (lane == 0) {
+        wpart[0][wave] = s2;
+        wpart[1][wave] = last[0];
+        wpart[2][wave] = last[1];
+    }
     __syncthreads();
-    uint32_t before = 0, total = 0, end = 0;
+    uint32_t before = 0, total = 0, total2 = 0, end0 = 0, end1 = 0;
 #pragma unroll
     for (uint32_t w = 0; w < kWaves; w++) {
         before += w < wave ? wtot[w] : 0u;
         total += wtot[w];
-        end = max(end, wlast[w]);
+        total2 += wpart[0][w];
+        end0 = max(end0, wpart[1][w]);
+        end1 = max(end1, wpart[2][w]);
     }
+    const uint32_t total1 = total - total2;
     const float slots = (float)gridDim.x;
     auto cost = [&](uint32_t cap) {
-        const float items = (float)((total + cap - 1) / cap) * (float)n_visited;
+        const float items = (float)((total1 + cap - 1) / cap + (total2 + cap - 1) / cap) * (float)n_visited;
         return ceilf(items / slots) * (cap > (uint32_t)WG ? kTwoSlotTime : 1.0f);
     };
     uint32_t cap = WG / 2;
@@ -1203,18 +1223,23 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
     // 1024-lane workgroups fill a compute unit alone: two streams per lane pay
     // only when most pixels are selected (measured)
     if ((WG < 1024 || 2 * total >= P) && cost(2 * WG) < cost(cap)) cap = 2 * WG;
+    const uint32_t n_first = (total1 + cap - 1) / cap, pad = n_first * cap - total1;
     // tile t starts item k when it holds the pixel numbered k * cap
     uint32_t e = before + x - s;  // selected pixels before this thread's first tile
 #pragma unroll
     for (uint32_t j = 0; j < kPer; j++) {
+        const uint32_t t = tid * kPer + j;
+        const bool second = t >= n_tiles;
+        const uint32_t ee = e + (second ? pad : 0u);
         if (c[j]) {
-            const uint32_t k = (e + cap - 1) / cap;
-            if (k * cap < e + c[j]) desc[k] = (uint16_t)(((tid * kPer + j) << 6) | (k * cap - e));
+            const uint32_t k = (ee + cap - 1) / cap;
+            if (k * cap < ee + c[j]) desc[k] = (uint16_t)(((t - (second ? n_tiles : 0u)) << 6) | (k * cap - ee));
         }
         e += c[j];
     }
     __syncthreads();
-    return PlanView{(total + cap - 1) / cap, cap, min(end * kPlanFine, P)};
+    return PlanView{n_first + (total2 + cap - 1) / cap, n_first, cap,
+                    {min(end0 * kPlanFine, P), min(end1 * kPlanFine, P)}};
 }
 
 // The pixels of one planned item: from tile (desc >> 6) on, skipping that
@@ -1367,13 +1392,17 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     __shared__ uint32_t wtot[kRansWG / 64];
     __shared__ uint32_t sbits[OP == Op::Dp ? 16 : 1];
     __shared__ uint16_t desc[kMaxItems<kRansWG>];
-    // planned: items of `cap` selected pixels; else every pixel tile of tile_px
-    uint32_t n_live = (r.P + tile_px - 1) / tile_px, cap = 0, end = 0;
+    // planned: items of `cap` selected pixels; else every pixel tile of
+    // tile_px. With a subtracted mask, its items follow those of mask.
+    const bool two = da.neg_mask != nullptr;
+    uint32_t n_first = (r.P + tile_px - 1) / tile_px, n_live = two ? 2 * n_first : n_first, cap = 0, end[2] = {0, 0};
     if (plan) {
-        const PlanView pv = plan_cut<kRansWG>(plan, r.P, n_visited, desc, wtot);
+        const PlanView pv = plan_cut<kRansWG>(plan, r.P, n_visited, two, desc, wtot);
         n_live = pv.n_items;
+        n_first = pv.n_first;
         cap = pv.cap;
-        end = pv.end;
+        end[0] = pv.end[0];
+        end[1] = pv.end[1];
     }
     const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
@@ -1381,12 +1410,14 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = w % n_live;
         const uint32_t b = is_region(OP) ? rb.b[vb] : vb * stride;
-        uint32_t p0 = OP == Op::Index ? 0 : t * tile_px;
+        const bool sub = two && t >= n_first;  // an item of the subtracted mask
+        const uint8_t *m = sub ? da.neg_mask : mask;
+        uint32_t p0 = OP == Op::Index ? 0 : (sub && !plan ? t - n_first : t) * tile_px;
         __syncthreads();
         const uint32_t n_sel =
             OP == Op::Index ? index_group<kRansWG>(r, da.perm, t, sel)
-            : plan ? select_range<kRansWG>(r, mask, complement, desc[t], cap, end, p0, sel, wtot)
-                   : select_tile<kRansWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
+            : plan ? select_range<kRansWG>(r, m, complement, desc[t], cap, end[sub], p0, sel, wtot)
+                   : select_tile<kRansWG>(r, m, complement, p0, min(tile_px, r.P - p0), sel, wtot);
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
@@ -1419,7 +1450,8 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
                 rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt);
         }
         __syncthreads();
-        if (OP == Op::Sum || OP == Op::Moments) flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate);
+        if (OP == Op::Sum || OP == Op::Moments)
+            flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate ^ (int)sub);
     }
 }
 
@@ -1439,25 +1471,31 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
         for (uint32_t i = threadIdx.x; i < kPairTable / 4; i += kPairWG) dst[i] = src[i];
     }
     __shared__ uint16_t desc[kMaxItems<kPairWG>];
-    // planned: items of `cap` selected pixels; else every pixel tile of tile_px
-    uint32_t n_live = (r.P + tile_px - 1) / tile_px, cap = 0, end = 0;
+    // planned: items of `cap` selected pixels; else every pixel tile of
+    // tile_px. With a subtracted mask, its items follow those of mask.
+    const bool two = da.neg_mask != nullptr;
+    uint32_t n_first = (r.P + tile_px - 1) / tile_px, n_live = two ? 2 * n_first : n_first, cap = 0, end[2] = {0, 0};
     if (plan) {
-        const PlanView pv = plan_cut<kPairWG>(plan, r.P, n_visited, desc, wtot);
+        const PlanView pv = plan_cut<kPairWG>(plan, r.P, n_visited, two, desc, wtot);
         n_live = pv.n_items;
+        n_first = pv.n_first;
         cap = pv.cap;
-        end = pv.end;
+        end[0] = pv.end[0];
+        end[1] = pv.end[1];
     }
     const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = w % n_live;
         const uint32_t b = is_region(OP) ? rb.b[vb] : vb * stride;
-        uint32_t p0 = OP == Op::Index ? 0 : t * tile_px;
+        const bool sub = two && t >= n_first;  // an item of the subtracted mask
+        const uint8_t *m = sub ? da.neg_mask : mask;
+        uint32_t p0 = OP == Op::Index ? 0 : (sub && !plan ? t - n_first : t) * tile_px;
         __syncthreads();
         const uint32_t n_sel =
             OP == Op::Index ? index_group<kPairWG>(r, da.perm, t, sel)
-            : plan ? select_range<kPairWG>(r, mask, complement, desc[t], cap, end, p0, sel, wtot)
-                   : select_tile<kPairWG>(r, mask, complement, p0, min(tile_px, r.P - p0), sel, wtot);
+            : plan ? select_range<kPairWG>(r, m, complement, desc[t], cap, end[sub], p0, sel, wtot)
+                   : select_tile<kPairWG>(r, m, complement, p0, min(tile_px, r.P - p0), sel, wtot);
         const uint8_t *d = r.dir + 16ull * b;
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
@@ -1483,13 +1521,14 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
                 paired_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt, ra, dt);
         }
         __syncthreads();
-        if (OP == Op::Sum || OP == Op::Moments) flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate);
+        if (OP == Op::Sum || OP == Op::Moments)
+            flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate ^ (int)sub);
     }
 }
 
 // out[i] = init[i], or 0 without init (u32 or u64 elements); with a plan,
 // wave w of workgroup g counts the selected pixels of 64-pixel tile 4g + w
-// (grid-strided).
+// (grid-strided; the tiles of a second mask follow those of the first).
 __global__ void __launch_bounds__(256) k_init(void *out, int out64, const void *init, uint64_t n, PlanArgs pa) {
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
         if (out64)
@@ -1499,10 +1538,13 @@ __global__ void __launch_bounds__(256) k_init(void *out, int out64, const void *
     }
     if (!pa.counts) return;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    for (uint32_t t = blockIdx.x * 4 + wave; t < pa.n_tiles; t += gridDim.x * 4) {
-        const uint32_t p = t * kPlanFine + lane;
+    const uint32_t n_all = pa.mask2 ? 2 * pa.n_tiles : pa.n_tiles;
+    for (uint32_t t = blockIdx.x * 4 + wave; t < n_all; t += gridDim.x * 4) {
+        const bool second = t >= pa.n_tiles;
+        const uint8_t *mask = second ? pa.mask2 : pa.mask;
+        const uint32_t p = (t - (second ? pa.n_tiles : 0u)) * kPlanFine + lane;
         bool f = false;
-        if (p < pa.P) f = pa.valid[p] != 0 && (pa.mask ? ((pa.mask[p] != 0) != (pa.complement != 0)) : true);
+        if (p < pa.P) f = pa.valid[p] != 0 && (mask ? ((mask[p] != 0) != (pa.complement != 0)) : true);
         const uint32_t c = (uint32_t)__popcll(__ballot(f));
         if (lane == 0) pa.counts[t] = c;
     }
@@ -1818,25 +1860,25 @@ template <typename F>
 static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, hipStream_t st, const DevResident &r,
                          const uint8_t *mask, int complement, uint32_t stride, uint32_t n_visited, void *out, int out64,
                          int negate, const void *init, uint64_t n_init, const RegionBlocks &rb, const RegionArgs &ra,
-                         const AuxArgs &da, bool accumulate = false) {
+                         const AuxArgs &da) {
     const uint32_t slots = resident_wgs(kern, threads);
     // a planned query counts 64-pixel tiles and the reduce cuts the items;
     // without a plan (region reads, or too many tiles) every pixel tile
     // of the host's size is an item
     const uint32_t n_fine = (r.P + kPlanFine - 1) / kPlanFine;
-    const bool planned = (n_init || accumulate) && n_fine <= kMaxPlanTiles;
+    const bool planned = n_init && n_fine <= kMaxPlanTiles;
     const uint32_t tile = planned ? kPlanFine : pick_tile(r.P, n_visited, slots, cands, ncand);
-    const uint32_t n_tiles = (r.P + tile - 1) / tile;
+    const uint32_t n_tiles = (r.P + tile - 1) / tile, n_masks = da.neg_mask ? 2 : 1;
     uint32_t *plan = planned ? r.plan : nullptr;
-    if (accumulate) n_init = 0;  // the init kernel only plans
-    if (n_init || planned) {
-        const PlanArgs pa{mask, r.valid, complement, r.P, n_tiles, plan};
+    if (n_init) {
+        const PlanArgs pa{mask, da.neg_mask, r.valid, complement, r.P, n_tiles, plan};
         const uint32_t grid = (uint32_t)std::max<uint64_t>(
-            planned ? (n_tiles + 3) / 4 : 1, std::max<uint64_t>(1, std::min<uint64_t>(2048, (n_init + 255) / 256)));
+            planned ? (n_masks * n_tiles + 3) / 4 : 1,
+            std::max<uint64_t>(1, std::min<uint64_t>(2048, (n_init + 255) / 256)));
         hipLaunchKernelGGL(k_init, dim3(grid), dim3(256), 0, st, out, out64, init, n_init, pa);
     }
-    // planned items number at most one per 64-pixel tile
-    const uint64_t items = (uint64_t)n_tiles * n_visited;
+    // planned items number at most one per 64-pixel tile and mask
+    const uint64_t items = (uint64_t)n_masks * n_tiles * n_visited;
     const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, slots));
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, r, mask, complement, stride, n_visited, tile, plan, out,
                        out64, negate, rb, ra, da);
@@ -1845,28 +1887,29 @@ static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, 
 template <bool W, Op O>
 static void launch_layout(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride,
                           uint32_t n_visited, void *out, int out64, int negate, const void *init, uint64_t n_init,
-                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st, const AuxArgs &da = AuxArgs{},
-                          bool accumulate = false) {
+                          const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st, const AuxArgs &da = AuxArgs{}) {
     if (r.layout == 0) {
         const uint32_t cands[2] = {2 * kRansWG, kRansWG};
         launch_items(k_reduce_rans<W, O>, kRansWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
-                     negate, init, n_init, rb, ra, da, accumulate);
+                     negate, init, n_init, rb, ra, da);
     } else {
         const uint32_t cands[2] = {2 * kPairWG, kPairWG};
         launch_items(k_reduce_paired<W, O>, kPairWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
-                     negate, init, n_init, rb, ra, da, accumulate);
+                     negate, init, n_init, rb, ra, da);
     }
 }
 
 hipError_t launch_query(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
-                        int out64, int negate, const void *init, uint64_t n_init, hipStream_t st, bool accumulate) {
+                        int out64, int negate, const void *init, uint64_t n_init, hipStream_t st,
+                        const uint8_t *neg_mask) {
     const uint32_t n_visited = (r.n_blocks + stride - 1) / stride;
     const RegionBlocks rb{};
     const RegionArgs ra{};
     const bool wide = r.dtype == 2;
+    AuxArgs da{};
+    da.neg_mask = neg_mask;
 #define QSC_LAUNCH(W, O) \
-    launch_layout<W, O>(r, mask, complement, stride, n_visited, out, out64, negate, init, n_init, rb, ra, st, \
-                        AuxArgs{}, accumulate)
+    launch_layout<W, O>(r, mask, complement, stride, n_visited, out, out64, negate, init, n_init, rb, ra, st, da)
     if (op == Op::Sum) {
         if (wide) QSC_LAUNCH(true, Op::Sum); else QSC_LAUNCH(false, Op::Sum);
     } else {

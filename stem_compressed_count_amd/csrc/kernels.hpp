@@ -16,7 +16,7 @@ constexpr uint32_t kPairTable = 32 * 1024 + 4;
 // pixels in pixel order.
 constexpr uint32_t kPlanFine = 64;
 constexpr uint32_t kMaxPlanTiles = 1024;
-constexpr uint32_t kPlanWords = kMaxPlanTiles;
+constexpr uint32_t kPlanWords = 2 * kMaxPlanTiles;  // the counts of a second, subtracted mask follow
 
 // Device view of a resident (all pointers are device memory).
 struct DevResident {
@@ -52,6 +52,7 @@ struct AuxArgs {
     const uint16_t *perm;  // P
     uint32_t *rows;        // n_blocks x n_fields x 512
     uint32_t n_fields;
+    const uint8_t *neg_mask;  // planned sums: pixels whose values are subtracted (P bytes), or null
 };
 
 // A region read: half-open scan rectangle, output buffer and kind (0 native
@@ -81,11 +82,11 @@ struct RegionBlocks {
 //  mask is null) and valid[p] of every visited block (b % stride == 0) is
 //  decoded and added (negate: subtracted) into out: u32/u64 per scan for
 //  Op::Sum, u64 [3][S] moments for Op::Moments.
-//  With accumulate set, out is left as it is (the plan still runs) and the sums
-//  are added to it.
+//  With neg_mask (Op::Sum, n_init > 0), the valid pixels of neg_mask are
+//  decoded in the same launch and subtracted instead.
 hipError_t launch_query(const DevResident &r, const uint8_t *mask, int complement, uint32_t stride, Op op, void *out,
                         int out64, int negate, const void *init, uint64_t n_init, hipStream_t st,
-                        bool accumulate = false);
+                        const uint8_t *neg_mask = nullptr);
 //  Masks of a change from prev to mask: added = mask & ~prev, removed = prev & ~mask (P bytes each).
 hipError_t launch_mask_delta(const uint8_t *prev, const uint8_t *mask, uint32_t P, uint8_t *added, uint8_t *removed,
                              hipStream_t st);

@@ -361,11 +361,10 @@ qsc_status qsc_masked_sum_delta(qsc_resident *res, const uint8_t *d_prev_mask, c
         return hip_fail(res, e, "mask delta scratch");
     uint8_t *added = res->d_delta, *removed = res->d_delta + P;
     e = launch_mask_delta(d_prev_mask, d_mask, P, added, removed, st);
-    // out = prev_out + the added pixels' sums, then minus the removed pixels' sums
+    // out = prev_out + the added pixels' sums - the removed pixels' sums, one launch
     if (e == hipSuccess)
-        e = launch_query(res->dev, added, 0, block_stride, Op::Sum, d_out, out64, 0, d_prev_out, res->g.S(), st);
-    if (e == hipSuccess)
-        e = launch_query(res->dev, removed, 0, block_stride, Op::Sum, d_out, out64, 1, nullptr, 0, st, true);
+        e = launch_query(res->dev, added, 0, block_stride, Op::Sum, d_out, out64, 0, d_prev_out, res->g.S(), st,
+                         removed);
     return finish_query(res, e, st, wait);
 }
 

@@ -157,3 +157,19 @@ def test_masked_sum_delta_follows_a_moving_mask():
             res.masked_sum_delta(prev, out, np.zeros(w.P, np.uint8), block_stride=stride, out=out)
             assert not u(out).any()
             res.finish()
+
+
+def test_masked_sum_delta_without_a_plan():
+    """A detector above 65,536 pixels is decoded without a query plan; deltas still hold."""
+    rng = np.random.default_rng(11)
+    dr = dc = 257
+    counts = rng.poisson(0.3, size=(600, dr * dc)).astype(np.uint8)
+    blob = q().encode(counts, 600, 1, dr, dc)
+    a = synth.disk_mask(dr, dc, 128, 128, 40)
+    b = synth.disk_mask(dr, dc, 131, 126, 40)
+    with q().Resident(blob) as res:
+        for stride in (1, 2):
+            prev = res.masked_sum(a, block_stride=stride)
+            got = res.masked_sum_delta(a, prev, b, block_stride=stride)
+            assert np.array_equal(u(got), oracle.masked_sum(counts, b, stride=stride)), stride
+        res.finish()
