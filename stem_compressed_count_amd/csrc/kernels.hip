@@ -684,8 +684,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     for (int k = 0; k < K; k++) {
                         a0[jj] += v[k];
                         if (OP == Op::Moments) {
-                            ar[jj] += v[k] * kr[k];
-                            ac[jj] += v[k] * kc[k];
+                            ar[jj] += __umul24(v[k], kr[k]);  // 24-bit multiplies run at full rate
+                            ac[jj] += __umul24(v[k], kc[k]);
                         }
                     }
                     // materialise the sums here: deferring them to the chunk end keeps every step's table entry live
@@ -713,8 +713,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 for (int k = 0; k < K; k++) {
                     t0 += v[k];
                     if (OP == Op::Moments) {
-                        tr += v[k] * kr[k];
-                        tc += v[k] * kc[k];
+                        tr += __umul24(v[k], kr[k]);
+                        tc += __umul24(v[k], kc[k]);
                     }
                 }
                 if constexpr (OP == Op::Index) {
@@ -1072,7 +1072,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                         a0[2 * tt] += v0[k];
                         a0[2 * tt + 1] += v1[k];
                         if (OP == Op::Moments) {
-                            ar[2 * tt] += v0[k] * kr[k];
+                            ar[2 * tt] += v0[k] * kr[k];  // window-relative values wrap: full 32-bit products
                             ar[2 * tt + 1] += v1[k] * kr[k];
                             ac[2 * tt] += v0[k] * kc[k];
                             ac[2 * tt + 1] += v1[k] * kc[k];
