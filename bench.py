@@ -216,6 +216,41 @@ def main():
     gpu_ms = e0.elapsed_time(e1)
     ms_per_step = gpu_ms / args.steps
 
+    # each query of the step alone: median and p95 of 20 runs, warm, and with a
+    # 1 GiB scratch write before every run so the 256 MB MALL and the L2s hold
+    # nothing of the resident (flushed)
+    queries = {
+        "masked_sum_bf_k1": lambda: res.masked_sum(d_bf, 1, out=out, wait=False),
+        "masked_sum_bf_k4": lambda: res.masked_sum(d_bf, 4, out=out4, wait=False),
+        "dense_df_warm": lambda: res.dense_df(d_df, out=outdf, wait=False),
+        "com_full": lambda: res.com(None, out_row=row, out_col=col, wait=False),
+        "com_bf": lambda: res.com(d_bf, out_row=rowb, out_col=colb, wait=False),
+        "decode_region_8x8": lambda: res.decode_region(0, 8, 0, 8, out=reg, wait=False),
+    }
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    per_query = {}
+    for name, q in queries.items():
+        row_stats = {}
+        for flushed in (False, True):
+            ts = []
+            for _ in range(20):
+                if flushed:
+                    scratch.fill_(1)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                q()
+                b.record(stream)
+                ts.append((a, b))
+            torch.cuda.synchronize()
+            ms = np.array([a.elapsed_time(b) for a, b in ts])
+            key = "flushed" if flushed else "warm"
+            row_stats[key + "_median_ms"] = round(float(np.median(ms)), 4)
+            row_stats[key + "_p95_ms"] = round(float(np.percentile(ms, 95)), 4)
+        per_query[name] = row_stats
+    res.finish()
+    del scratch
+    torch.cuda.empty_cache()
+
     # logical counts and encoded bytes each query of the step reads
     P = w.P
     full = np.ones(P, np.uint8) if valid is None else valid
@@ -352,6 +387,7 @@ def main():
         "host_ms_per_step": round(host_s * 1e3 / args.steps, 4), "cold_dense_df_ms": round(cold_ms, 3),
         "setup_s": round(t_setup, 2),
         "roofline": roofline,
+        "queries": per_query,
         "next_rows": {"sum_dp": {"ms": round(dp_ms, 4), "counts_per_s": round(dp_counts / (dp_ms * 1e-3), 1),
                                  "what": "sum + mean diffraction pattern over every scan (not in the step)"},
                       "decode_blocks": dict(feed, what="every block decoded to frames (not in the step)"),
