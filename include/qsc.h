@@ -140,6 +140,14 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
  */
 qsc_status qsc_resident_create_device(const void *d_blob, uint64_t nbytes, const uint8_t *host_valid,
                                       void *hip_stream, qsc_resident **out);
+/* qsc_resident_create_device_borrow: as qsc_resident_create_device, but the
+ *   resident uses the caller's buffer in place instead of copying it: d_blob
+ *   holds the container (nbytes) within capacity bytes, and capacity must
+ *   leave at least 16384 bytes after the container, which the call zeroes
+ *   (the decoders read ahead into them). The caller keeps ownership and must
+ *   keep the buffer alive and unchanged until the resident is destroyed. */
+qsc_status qsc_resident_create_device_borrow(void *d_blob, uint64_t nbytes, uint64_t capacity,
+                                             const uint8_t *host_valid, void *hip_stream, qsc_resident **out);
 qsc_status qsc_resident_destroy(qsc_resident *res);
 qsc_status qsc_resident_info(const qsc_resident *res, qsc_info *info);
 

@@ -31,6 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsc.so")
 
 OK, ERR_INVALID_ARG, ERR_MALFORMED, ERR_UNSUPPORTED, ERR_OOM, ERR_HIP = 0, -1, -2, -3, -4, -5
+DEVICE_PAD = 16384  # zero bytes a borrowed device container needs after it
 
 
 class QscError(RuntimeError):
@@ -72,6 +73,7 @@ _SIGS = {
     "qsc_encoder_destroy": ([_vp], _i32),
     "qsc_resident_create": ([_vp, _u64, _vp, _vp, ctypes.POINTER(_vp)], _i32),
     "qsc_resident_create_device": ([_vp, _u64, _vp, _vp, ctypes.POINTER(_vp)], _i32),
+    "qsc_resident_create_device_borrow": ([_vp, _u64, _u64, _vp, _vp, ctypes.POINTER(_vp)], _i32),
     "qsc_encode_device_bound": ([ctypes.POINTER(Geometry), ctypes.POINTER(_u64)], _i32),
     "qsc_encode_device": ([ctypes.POINTER(Geometry), _vp, _vp, _u64, ctypes.POINTER(_u64), _vp], _i32),
     "qsc_resident_destroy": ([_vp], _i32),
@@ -142,7 +144,7 @@ def encode_device(data, scan_rows, scan_cols, det_rows, det_cols, layout=0, scal
     rc = lib.qsc_encode_device_bound(ctypes.byref(g), ctypes.byref(cap))
     if rc:
         _raise(rc, "encode_device geometry")
-    out = torch.empty(cap.value, dtype=torch.uint8, device=data.device)
+    out = torch.empty(cap.value + DEVICE_PAD, dtype=torch.uint8, device=data.device)  # room to borrow it
     n = _u64()
     rc = lib.qsc_encode_device(ctypes.byref(g), data.data_ptr(), out.data_ptr(), cap.value, ctypes.byref(n),
                                _stream_handle(stream))
@@ -201,16 +203,27 @@ def _stream_handle(stream):
 class Resident:
     """An encoded acquisition resident in device memory (qsc_resident)."""
 
-    def __init__(self, blob, valid=None, stream=None):
-        """blob: a host container (bytes or numpy uint8), or a CUDA uint8 tensor holding one."""
+    def __init__(self, blob, valid=None, stream=None, borrow=False):
+        """blob: a host container (bytes or numpy uint8), or a CUDA uint8 tensor holding one.
+        borrow=True uses a device container in place (its storage needs 16384 spare bytes after it,
+        as encode_device leaves) and keeps a reference to it for the resident's lifetime."""
         import torch
         v = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
         self._h = _vp()
+        self._borrowed = None
         if isinstance(blob, torch.Tensor) and blob.is_cuda:
             if blob.dtype != torch.uint8 or not blob.is_contiguous():
                 raise ValueError("a device container must be a contiguous uint8 tensor")
-            rc = lib.qsc_resident_create_device(blob.data_ptr(), blob.numel(), None if v is None else v.ctypes.data,
-                                                _stream_handle(stream), ctypes.byref(self._h))
+            if borrow:
+                cap = blob.untyped_storage().nbytes() - blob.storage_offset()
+                rc = lib.qsc_resident_create_device_borrow(blob.data_ptr(), blob.numel(), cap,
+                                                           None if v is None else v.ctypes.data,
+                                                           _stream_handle(stream), ctypes.byref(self._h))
+                self._borrowed = blob
+            else:
+                rc = lib.qsc_resident_create_device(blob.data_ptr(), blob.numel(),
+                                                    None if v is None else v.ctypes.data,
+                                                    _stream_handle(stream), ctypes.byref(self._h))
         else:
             b = np.ascontiguousarray(np.frombuffer(blob, dtype=np.uint8) if isinstance(blob, (bytes, bytearray))
                                      else blob, dtype=np.uint8)
@@ -347,9 +360,10 @@ class Resident:
         return by.value, cn.value
 
     def close(self):
-        if getattr(self, "_h", None):
+        if getattr(self, "_h", None) and lib is not None:  # lib is gone at interpreter exit
             lib.qsc_resident_destroy(self._h)
             self._h = _vp()
+        self._borrowed = None
 
     def __enter__(self):
         return self

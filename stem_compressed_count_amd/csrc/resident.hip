@@ -32,6 +32,7 @@ struct qsc_resident {
     std::vector<uint16_t> rel;
     // device memory owned by the resident
     uint8_t *d_blob = nullptr;
+    bool borrowed = false;  // d_blob belongs to the caller
     uint32_t *d_tables = nullptr;
     uint32_t *d_model_info = nullptr;
     uint8_t *d_valid = nullptr;
@@ -81,7 +82,7 @@ hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
 }
 
 void free_all(qsc_resident *res) {
-    for (void *p : {(void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
+    for (void *p : {res->borrowed ? nullptr : (void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
                     (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, (void *)res->d_amp,
                     (void *)res->d_ix_perm, (void *)res->d_ix_leaf_valid, (void *)res->d_ix_packed,
                     (void *)res->d_ix_offset, (void *)res->d_ix_fields, (void *)res->d_ix_width,
@@ -121,7 +122,7 @@ qsc_status finish_query(qsc_resident *res, hipError_t launch, hipStream_t st, in
 // from host_blob or, when that is null, from dev_blob.
 qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *host_blob, const uint8_t *dev_blob,
                           uint64_t nbytes, const uint8_t *host_valid, void *hip_stream,
-                          std::unique_ptr<qsc_resident> &res) {
+                          std::unique_ptr<qsc_resident> &res, bool borrow = false) {
     res.reset(new (std::nothrow) qsc_resident);
     if (!res) return QSC_ERR_OOM;
     const Geometry &g = ps.g;
@@ -142,11 +143,17 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
         free_all(res.get());
         return err == hipErrorOutOfMemory ? QSC_ERR_OOM : QSC_ERR_HIP;
     };
-    // the whole blob, plus zero padding that the decoders may read ahead into
-    if ((e = dalloc(res.get(), &res->d_blob, nbytes + kDevicePad)) != hipSuccess) return bail(e, "blob");
-    if ((e = hipMemcpy(res->d_blob, host_blob ? host_blob : dev_blob, nbytes,
-                       host_blob ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice)) != hipSuccess)
-        return bail(e, "upload");
+    // the whole blob, plus zero padding that the decoders may read ahead into;
+    // a borrowed device blob is used in place (its padding is zeroed here)
+    if (borrow) {
+        res->d_blob = const_cast<uint8_t *>(dev_blob);
+        res->borrowed = true;
+    } else {
+        if ((e = dalloc(res.get(), &res->d_blob, nbytes + kDevicePad)) != hipSuccess) return bail(e, "blob");
+        if ((e = hipMemcpy(res->d_blob, host_blob ? host_blob : dev_blob, nbytes,
+                           host_blob ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice)) != hipSuccess)
+            return bail(e, "upload");
+    }
     if ((e = hipMemset(res->d_blob + nbytes, 0, kDevicePad)) != hipSuccess) return bail(e, "pad");
     // decode tables
     std::vector<uint32_t> tables;
@@ -239,10 +246,8 @@ qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uin
     return QSC_OK;
 }
 
-qsc_status qsc_resident_create_device(const void *d_blob, uint64_t nbytes, const uint8_t *host_valid,
-                                      void *hip_stream, qsc_resident **out) {
-    if (!d_blob || !out) return QSC_ERR_INVALID_ARG;
-    *out = nullptr;
+static qsc_status create_from_device(const void *d_blob, uint64_t nbytes, const uint8_t *host_valid, void *hip_stream,
+                              qsc_resident **out, bool borrow) {
     const uint8_t *dev = static_cast<const uint8_t *>(d_blob);
     if (nbytes < kHeaderBytes) return QSC_ERR_MALFORMED;
     // the header fixes the size of the sections before the payload
@@ -268,7 +273,8 @@ qsc_status qsc_resident_create_device(const void *d_blob, uint64_t nbytes, const
     qsc_status st = parse_and_validate(pre.data(), nbytes, &ps, &msg, false, g.scaled ? cal.data() : nullptr);
     if (st != QSC_OK) return st;
     std::unique_ptr<qsc_resident> res;
-    if ((st = build_resident(ps, pre.data(), nullptr, dev, nbytes, host_valid, hip_stream, res)) != QSC_OK) return st;
+    if ((st = build_resident(ps, pre.data(), nullptr, dev, nbytes, host_valid, hip_stream, res, borrow)) != QSC_OK)
+        return st;
     // stream headers on the device: reserved bits, modes, RANS only with a usable table
     const uint32_t nb = g.n_blocks();
     std::vector<uint8_t> usable(nb, 1);
@@ -307,6 +313,21 @@ qsc_status qsc_resident_create_device(const void *d_blob, uint64_t nbytes, const
     std::copy(chk, chk + 8, res->mode_counts);
     *out = res.release();
     return QSC_OK;
+}
+
+qsc_status qsc_resident_create_device(const void *d_blob, uint64_t nbytes, const uint8_t *host_valid,
+                                      void *hip_stream, qsc_resident **out) {
+    if (!d_blob || !out) return QSC_ERR_INVALID_ARG;
+    *out = nullptr;
+    return create_from_device(d_blob, nbytes, host_valid, hip_stream, out, false);
+}
+
+qsc_status qsc_resident_create_device_borrow(void *d_blob, uint64_t nbytes, uint64_t capacity,
+                                             const uint8_t *host_valid, void *hip_stream, qsc_resident **out) {
+    if (!d_blob || !out) return QSC_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (capacity < nbytes || capacity - nbytes < kDevicePad) return QSC_ERR_INVALID_ARG;
+    return create_from_device(d_blob, nbytes, host_valid, hip_stream, out, true);
 }
 
 qsc_status qsc_resident_destroy(qsc_resident *res) {

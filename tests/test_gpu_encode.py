@@ -183,3 +183,25 @@ def test_full_size_128x128_byte_identical():
     """The whole 128x128-scan u16 workload (604 M values) against the oracle encoder."""
     w = synth.WORKLOADS["scan128_u16"]
     check_identical(synth.counts(w), w.scan_rows, w.scan_cols, w.det_rows, w.det_cols)
+
+
+def test_borrowed_device_container():
+    import torch
+    qq = q()
+    w = synth.WORKLOADS["scan128_u16"].with_scans(4, 128)
+    counts = synth.counts(w)
+    blob = qq.encode_device(dev(counts), w.scan_rows, w.scan_cols, w.det_rows, w.det_cols)
+    keep = blob.clone()
+    bf = synth.query_masks(w)["bf"]
+    with qq.Resident(blob, borrow=True) as res, qq.Resident(keep) as copied:
+        assert res.info.resident_bytes < copied.info.resident_bytes  # the container is not copied
+        got = qq.as_unsigned(res.masked_sum(bf)).astype(np.uint64)
+        assert np.array_equal(got, oracle.masked_sum(counts, bf))
+        res.finish()
+    assert torch.equal(blob, keep)  # the caller's container is unchanged and still usable
+    # no room after the container for the decoders' read-ahead
+    tight = blob.clone()
+    n = ctypes.c_void_p()
+    rc = qq.lib.qsc_resident_create_device_borrow(tight.data_ptr(), tight.numel(), tight.numel(), None, None,
+                                                  ctypes.byref(n))
+    assert rc == qq.ERR_INVALID_ARG
