@@ -1,8 +1,9 @@
 // Fused ANS decode + virtual-detector reduction kernels for gfx950 (CDNA4).
 //
 // Hot path of the paired-resident page ("Operation pipeline", steps 3-4): each
-// workgroup takes one (visited 512-scan block, detector-pixel tile) work item,
-// selects the tile's pixels that the mask and valid_pixels keep (wave ballots
+// workgroup takes one work item, (visited 512-scan block, a run of the
+// selected pixels cut by the query plan) or for region reads (block, pixel
+// tile), gathers the pixels that the mask and valid_pixels keep (wave ballots
 // into an LDS list), stages the block's decode table in LDS and decodes every
 // selected stream with one lane per stream. A lane keeps a 64-bit bit
 // reservoir refilled 32 bits at a time from a prefetched dword on a
