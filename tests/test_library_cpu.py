@@ -154,3 +154,35 @@ def test_paired_model_tables_are_validated():
     h = oracle.header(bytes(blob))
     blob[h["table_off"] + 2] ^= 1  # one count of model 0 changed
     assert create_status(bytes(blob)) == qsc().ERR_MALFORMED
+
+
+def test_device_encoder_bound_and_argument_errors():
+    """Host logic of the device encoder: its capacity bound follows the format's
+    section layout with every stream raw, and bad arguments fail before any GPU work."""
+    q = qsc()
+    for (sr, sc, dr, dc, dtype, layout, scaled) in [(3, 301, 7, 9, 2, 0, 0), (1, 700, 3, 11, 1, 0, 0),
+                                                  (2, 512, 5, 8, 2, 1, 0), (1, 1124, 5, 8, 2, 0, 1)]:
+        g = q.Geometry(sr, sc, dr, dc, dtype, layout, scaled)
+        n = ctypes.c_uint64()
+        assert q.lib.qsc_encode_device_bound(ctypes.byref(g), ctypes.byref(n)) == q.OK
+        S, P, G = sr * sc, dr * dc, (dr * dc + 31) // 32
+        nb = (S + 511) // 512
+        up = lambda o: (o + 255) // 256 * 256
+        payload_off = up(up(up(up(256 + 16 * nb) + (512 * nb if layout == 0 else 2 * 32 * 256)) + 4 * nb * G)
+                         + 64 * nb * G)
+        raw = sum(P * (2 + (2 * m if dtype == 2 else m + m % 2)) for m in
+                  [min(512, S - 512 * b) for b in range(nb)])
+        want = payload_off + raw
+        if scaled:
+            want = up(want) + 16 * nb
+        assert n.value == want, (sr, sc, dr, dc, dtype, layout, scaled)
+    bad = q.Geometry(3, 301, 7, 9, 3, 0, 0)  # dtype 3
+    n = ctypes.c_uint64()
+    assert q.lib.qsc_encode_device_bound(ctypes.byref(bad), ctypes.byref(n)) == q.ERR_INVALID_ARG
+    g = q.Geometry(3, 301, 7, 9, 2, 0, 0)
+    assert q.lib.qsc_encode_device(ctypes.byref(g), None, None, 0, ctypes.byref(n), None) == q.ERR_INVALID_ARG
+    assert q.lib.qsc_encode_device(ctypes.byref(bad), ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 20,
+                                   ctypes.byref(n), None) == q.ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert q.lib.qsc_resident_create_device(None, 4096, None, None, ctypes.byref(h)) == q.ERR_INVALID_ARG
+    assert q.lib.qsc_resident_create_device_borrow(None, 4096, 8192, None, None, ctypes.byref(h)) == q.ERR_INVALID_ARG
