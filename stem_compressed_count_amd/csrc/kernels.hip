@@ -451,10 +451,14 @@ struct RSlot {
 // stream is a renormalisation that always takes a word, and an idle slot is a
 // RAW stream whose reads fall outside the buffer range and return zero. With
 // no per-slot branches the K table reads of a step issue together.
+//
+// half: 0 decodes whole streams; 1 the first kSplit scans of each stream
+// (checked against its split point); 2 the rest, resumed from the split point
+// (a complete block's streams then take two lanes, one per half).
 template <int K, bool WIDE, Op OP>
 __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
                           uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt,
-                          const RegionArgs &ra, const DpTile &dt) {
+                          const RegionArgs &ra, const DpTile &dt, uint32_t half = 0) {
     const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
@@ -482,6 +486,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         const uint32_t hdr = ld16(r.payload, e.start);
         const uint32_t mode = hdr & 7u;
         if (mode == 0) {  // CONST
+            if (half == 2 || OP == Op::Split) continue;  // folded once, by the first half
             const uint32_t v = ld16(r.payload, e.start + 2);
             if (z.len != 4 || v > maxv) {
                 report(r, b, z.p);
@@ -501,12 +506,22 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         }
         z.live = true;
         z.raw = mode == 2;
-        touched += touch_stream(rs, z.org, z.len);
-        bbits_init(z.s, rs, z.org);
-        pop16(z.s);  // header
-        if (mode == 1) {
-            z.x = pop16(z.s);
-            z.x |= pop16(z.s) << 16;
+        if (half == 2) {
+            // resume where the first half ends: a RAW stream at its value kSplit, a
+            // RANS stream at its split point (state, byte offset from the stream start)
+            const uint64_t si = 2 * ((uint64_t)b * r.P + z.p);
+            const uint32_t off = z.raw ? 2u + kSplit * (WIDE ? 2u : 1u) : r.split[si + 1];
+            touched += touch_stream(rs, z.org + off, z.len > off ? z.len - off : 0u);
+            bbits_init(z.s, rs, z.org + off);
+            if (!z.raw) z.x = r.split[si];
+        } else {
+            touched += touch_stream(rs, z.org, z.len);
+            bbits_init(z.s, rs, z.org);
+            pop16(z.s);  // header
+            if (mode == 1) {
+                z.x = pop16(z.s);
+                z.x |= pop16(z.s) << 16;
+            }
         }
         bbits_refill(z.s, rs);
     }
@@ -599,6 +614,9 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             // calibrated (float64) path out of spills
             constexpr int CH = is_frames(OP) ? 4 : 16;
             auto rw = region_walk<is_frames(OP)>(r, b, ra);
+            // a split item's lanes cover kSplit scans from 0 (first half) or kSplit (second)
+            const uint32_t nsteps = half == 0 ? n : (half == 1 ? kSplit : n - kSplit);
+            if (half == 2) rw.seek(r, (uint64_t)b * kBlk + kSplit);
             auto put = [&](const uint32_t (&v)[K]) {
                 if (rw.inside()) {
                     const uint64_t idx = rw.index(r.P);
@@ -608,7 +626,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 }
                 rw.next();
             };
-            const uint32_t nfull = n / CH;
+            const uint32_t nfull = nsteps / CH;
             for (uint32_t c = 0; c < nfull; c++) {
 #pragma unroll
                 for (int jj = 0; jj < CH; jj++) {
@@ -619,11 +637,11 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            for (uint32_t j = nfull * CH; j < n; j++) {
+            for (uint32_t j = nfull * CH; j < nsteps; j++) {
                 uint32_t v[K];
                 step(form, (j & 1) == 0, v);
                 put(v);
-                if ((j & 1) || j + 1 == n) refill();
+                if ((j & 1) || j + 1 == nsteps) refill();
             }
         } else if constexpr (OP == Op::Dp) {
             // per-lane sums over the selected scans, no reduction across lanes
@@ -659,12 +677,21 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
 #pragma unroll
             for (int k = 0; k < K; k++)
                 if (sl[k].live) dt.row[sl[k].p] = acc[k];
+        } else if constexpr (OP == Op::Split) {
+            // decode the first kSplit scans only; the state and position are stored below
+            for (uint32_t j = 0; j < kSplit; j++) {
+                uint32_t v[K];
+                step(form, (j & 1) == 0, v);
+                if (j & 1) refill();
+            }
         } else {
             constexpr int CH = 16;
             const uint32_t my = lane_scan<CH>();
             const bool writer = lane_writes<CH>();
             const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
-            const uint32_t nfull = n / CH;
+            // the scans this lane's half covers: [j0, j0 + nsteps)
+            const uint32_t j0 = half == 2 ? kSplit : 0u, nsteps = half == 0 ? n : (half == 1 ? kSplit : n - kSplit);
+            const uint32_t nfull = nsteps / CH;
             const uint32_t cw = OP == Op::Index ? wave_sum(cst) : 0u;  // the leaf's constant streams
             for (uint32_t c = 0; c < nfull; c++) {
                 uint32_t a0[CH];
@@ -701,12 +728,12 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     const uint32_t t0 = wave_transpose_sum<CH>(a0) + cw;
                     if (writer && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + c * CH + my], t0);
                 } else {
-                    chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH,
-                                         pt.mc + c * CH);
+                    chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + j0 + c * CH, pt.mr + j0 + c * CH,
+                                         pt.mc + j0 + c * CH);
                 }
             }
-            // ragged end of a final partial block: one scan at a time, reduced per scan
-            for (uint32_t j = nfull * CH; j < n; j++) {
+            // ragged end of a final partial block (never split): one scan at a time, reduced per scan
+            for (uint32_t j = nfull * CH; j < nsteps; j++) {
                 uint32_t v[K];
                 step(form, (j & 1) == 0, v);
                 uint32_t t0 = 0, tr = 0, tc = 0;
@@ -754,14 +781,33 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         run(std::integral_constant<int, kPlain>{});
     }
     asm volatile("" ::"v"(touched));
-    // end checks (FORMAT 2.3-2.4)
+    if constexpr (OP == Op::Split) {
+        // the split point: state and byte offset after kSplit scans
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            const RSlot &z = sl[k];
+            if (!z.live) continue;
+            const uint64_t si = 2 * ((uint64_t)b * r.P + z.p);
+            dt.row[si] = z.x;
+            dt.row[si + 1] = bbits_used(z.s, z.org) / 8u;
+        }
+        return;
+    }
+    // end checks (FORMAT 2.3-2.4); a first half ends at its split point
 #pragma unroll
     for (int k = 0; k < K; k++) {
         const RSlot &z = sl[k];
         if (!z.live) continue;
-        bool ok = bbits_used(z.s, z.org) == 8u * z.len;
-        if (!z.raw) ok = ok && z.x == 65536u;
-        if (z.raw && !WIDE && (n & 1)) ok = ok && z.hold == 0;
+        bool ok;
+        if (half == 1) {
+            const uint64_t si = 2 * ((uint64_t)b * r.P + z.p);
+            const uint32_t off = z.raw ? 2u + kSplit * (WIDE ? 2u : 1u) : r.split[si + 1];
+            ok = bbits_used(z.s, z.org) == 8u * off && (z.raw || z.x == r.split[si]);
+        } else {
+            ok = bbits_used(z.s, z.org) == 8u * z.len;
+            if (!z.raw) ok = ok && z.x == 65536u;
+            if (z.raw && !WIDE && (n & 1)) ok = ok && z.hold == 0;
+        }
         if (!ok || bad) report(r, b, z.p);
     }
 }
@@ -1155,6 +1201,7 @@ struct PlanView {
     uint32_t n_items, n_first;  // items per visited block; of them, items of the first mask
     uint32_t cap;               // selected pixels per item
     uint32_t end[2];            // per mask, the end of its last non-empty tile (pixels)
+    bool halves;                // decode each stream's two halves side by side (split points)
 };
 
 // Most items a plan can hold: two masks of kMaxPlanTiles tiles cut in halves of a workgroup.
@@ -1164,9 +1211,14 @@ constexpr uint32_t kMaxItems = 2 * kMaxPlanTiles * kPlanFine / (WG / 2);
 // With `two`, the counts of a second mask follow those of the first, and its
 // items (whose values the query subtracts) start after the first mask's:
 // its pixel numbering starts at the first multiple of cap past the first's.
+//
+// can_split: the streams have split points. When every item of half-workgroup
+// size fits one round of the resident workgroups, the query is latency-bound:
+// each item then takes half a workgroup of streams and the other half of the
+// lanes decodes their second halves, so the chain of dependent steps halves.
 template <int WG>
 __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P, uint32_t n_visited, bool two,
-                                             uint16_t *desc, uint32_t *wtot) {
+                                             bool can_split, uint16_t *desc, uint32_t *wtot) {
     constexpr uint32_t kPer = 2 * kMaxPlanTiles / WG;
     constexpr uint32_t kWaves = WG / 64;
     __shared__ uint32_t wpart[4][kWaves];  // per wave: the second mask's sum, and each mask's last tile
@@ -1224,6 +1276,7 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
     // 1024-lane workgroups fill a compute unit alone: two streams per lane pay
     // only when most pixels are selected (measured)
     if ((WG < 1024 || 2 * total >= P) && cost(2 * WG) < cost(cap)) cap = 2 * WG;
+    const bool halves = can_split && cap == WG / 2 && cost(WG / 2) <= 1.0f;
     const uint32_t n_first = (total1 + cap - 1) / cap, pad = n_first * cap - total1;
     // tile t starts item k when it holds the pixel numbered k * cap
     uint32_t e = before + x - s;  // selected pixels before this thread's first tile
@@ -1240,7 +1293,7 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
     }
     __syncthreads();
     return PlanView{n_first + (total2 + cap - 1) / cap, n_first, cap,
-                    {min(end0 * kPlanFine, P), min(end1 * kPlanFine, P)}};
+                    {min(end0 * kPlanFine, P), min(end1 * kPlanFine, P)}, halves};
 }
 
 // The pixels of one planned item: from tile (desc >> 6) on, skipping that
@@ -1397,13 +1450,18 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     // tile_px. With a subtracted mask, its items follow those of mask.
     const bool two = da.neg_mask != nullptr;
     uint32_t n_first = (r.P + tile_px - 1) / tile_px, n_live = two ? 2 * n_first : n_first, cap = 0, end[2] = {0, 0};
+    bool halves = false;
     if (plan) {
-        const PlanView pv = plan_cut<kRansWG>(plan, r.P, n_visited, two, desc, wtot);
+        const PlanView pv =
+            plan_cut<kRansWG>(plan, r.P, n_visited, two, (OP == Op::Sum || OP == Op::Moments) && r.split, desc, wtot);
         n_live = pv.n_items;
         n_first = pv.n_first;
         cap = pv.cap;
         end[0] = pv.end[0];
         end[1] = pv.end[1];
+        halves = pv.halves;
+    } else if constexpr (OP == Op::Region) {
+        halves = da.halves && r.split;  // a latency-bound region read: items of half a workgroup
     }
     const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
@@ -1423,8 +1481,10 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
+        if (OP == Op::Split && n != kBlk) continue;  // a final partial block has no split points
         DpTile dt{nullptr, sbits, 0};
         if constexpr (OP == Op::Index) dt.row = da.rows + ((uint64_t)b * da.n_fields + (uint64_t)t * (kRansWG / 64)) * kBlk;
+        if constexpr (OP == Op::Split) dt.row = da.rows;
         if constexpr (OP == Op::Dp) {
             dp_scan_bits<kRansWG>(da.scan_mask, (uint64_t)b * kBlk, n, sbits);
             __syncthreads();
@@ -1443,12 +1503,17 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         __syncthreads();
         // at most two slots per lane: with three decode forms, more do not fit 3 waves per SIMD
         const uint32_t K = (OP == Op::Index || n_sel <= kRansWG) ? 1 : 2;  // an index leaf is one wave
-        const uint32_t first = (threadIdx.x >> 6) * 64 * K;
+        // split items (at most half a workgroup of streams): waves 0-1 decode the
+        // first halves of the streams, waves 2-3 the second halves
+        const uint32_t wave = threadIdx.x >> 6;
+        const bool split_item = halves && n == kBlk;
+        const uint32_t half = split_item ? 1u + (wave >> 1) : 0u;
+        const uint32_t first = split_item ? (wave & 1u) * 64u : wave * 64 * K;
         if (first < n_sel) {  // whole waves without a stream skip the decode
             if (K == 2)
                 rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt);
             else
-                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt);
+                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, half);
         }
         __syncthreads();
         if (OP == Op::Sum || OP == Op::Moments)
@@ -1477,7 +1542,7 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     const bool two = da.neg_mask != nullptr;
     uint32_t n_first = (r.P + tile_px - 1) / tile_px, n_live = two ? 2 * n_first : n_first, cap = 0, end[2] = {0, 0};
     if (plan) {
-        const PlanView pv = plan_cut<kPairWG>(plan, r.P, n_visited, two, desc, wtot);
+        const PlanView pv = plan_cut<kPairWG>(plan, r.P, n_visited, two, false, desc, wtot);
         n_live = pv.n_items;
         n_first = pv.n_first;
         cap = pv.cap;
@@ -1927,6 +1992,25 @@ hipError_t launch_com_finalize(const uint64_t *moments, uint64_t S, float *row, 
 }
 
 hipError_t launch_region(const DevResident &r, const RegionBlocks &blocks, const RegionArgs &ra, hipStream_t st) {
+    // a rectangle whose items of half-workgroup tiles fit one round of the
+    // resident workgroups is latency-bound: decode both halves of each stream
+    // side by side
+    if (r.layout == 0 && r.split && !ra.frames && ra.out_kind != 2) {
+        AuxArgs da{};
+        da.halves = 1;
+        const uint32_t cands[1] = {kRansWG / 2};
+        const uint64_t items = (uint64_t)((r.P + kRansWG / 2 - 1) / (kRansWG / 2)) * blocks.n;
+        if (r.dtype == 2 && items <= resident_wgs(k_reduce_rans<true, Op::Region>, kRansWG)) {
+            launch_items(k_reduce_rans<true, Op::Region>, kRansWG, cands, 1, st, r, nullptr, 0, 1, blocks.n, nullptr,
+                         0, 0, nullptr, 0, blocks, ra, da);
+            return hipGetLastError();
+        }
+        if (r.dtype != 2 && items <= resident_wgs(k_reduce_rans<false, Op::Region>, kRansWG)) {
+            launch_items(k_reduce_rans<false, Op::Region>, kRansWG, cands, 1, st, r, nullptr, 0, 1, blocks.n, nullptr,
+                         0, 0, nullptr, 0, blocks, ra, da);
+            return hipGetLastError();
+        }
+    }
 #define QSC_REGION(W, O) launch_layout<W, O>(r, nullptr, 0, 1, blocks.n, nullptr, 0, 0, nullptr, 0, blocks, ra, st)
     if (ra.out_kind == 2) {
         if (r.dtype == 2) QSC_REGION(true, Op::Amp); else QSC_REGION(false, Op::Amp);
@@ -2019,6 +2103,22 @@ hipError_t launch_mask_delta(const uint8_t *prev, const uint8_t *mask, uint32_t 
                              hipStream_t st) {
     hipLaunchKernelGGL(k_mask_delta, dim3(std::max(1u, std::min(1024u, (P + 255) / 256))), dim3(256), 0, st, prev,
                        mask, P, added, removed);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_build(const DevResident &r, uint32_t *out, hipStream_t st) {
+    AuxArgs da{};
+    da.rows = out;
+    const RegionBlocks rb{};
+    const RegionArgs ra{};
+    // every pixel tile of every block, no plan (the partial final block is skipped)
+    const uint32_t cands[1] = {kRansWG};
+    if (r.dtype == 2)
+        launch_items(k_reduce_rans<true, Op::Split>, kRansWG, cands, 1, st, r, nullptr, 0, 1, r.n_blocks, nullptr, 0, 0,
+                     nullptr, 0, rb, ra, da);
+    else
+        launch_items(k_reduce_rans<false, Op::Split>, kRansWG, cands, 1, st, r, nullptr, 0, 1, r.n_blocks, nullptr, 0,
+                     0, nullptr, 0, rb, ra, da);
     return hipGetLastError();
 }
 

@@ -30,6 +30,8 @@ struct DevResident {
     const double *calib;     // scaled: n_blocks x {scale, offset}
     unsigned long long *err; // first malformed stream: (block + 1) << 32 | pixel, 0 = none
     uint32_t *plan;          // query plan: selected pixels per 64-pixel tile (kPlanWords words)
+    const uint32_t *split;   // byte-rANS: per (block, pixel), the state and byte offset of the stream after
+                             // its first kSplit scans (two words), or null when not built
     uint64_t S;
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };
@@ -38,7 +40,11 @@ struct DevResident {
 // blocks as square-root amplitudes) write decoded values; each is its own
 // instantiation, so the rectangle tests and the table gather stay out of the
 // loops that do not need them.
-enum class Op : int { Sum = 0, Moments = 1, Region = 2, Dp = 3, Index = 4, Amp = 5, Frames = 6 };
+enum class Op : int { Sum = 0, Moments = 1, Region = 2, Dp = 3, Index = 4, Amp = 5, Frames = 6, Split = 7 };
+
+// Scans after which byte-rANS streams of complete blocks keep a split point:
+// a latency-bound query decodes each stream's two halves side by side.
+constexpr uint32_t kSplit = 256;
 
 // Buffers of the queries beyond sums and moments.
 //  diffraction pattern: the selected scans (null: every scan), the
@@ -53,6 +59,7 @@ struct AuxArgs {
     uint32_t *rows;        // n_blocks x n_fields x 512
     uint32_t n_fields;
     const uint8_t *neg_mask;  // planned sums: pixels whose values are subtracted (P bytes), or null
+    uint32_t halves;          // region reads: items of half a workgroup whose streams' halves decode side by side
 };
 
 // A region read: half-open scan rectangle, output buffer and kind (0 native
@@ -128,6 +135,9 @@ hipError_t launch_index_pack(uint32_t n_blocks, uint32_t n_fields, const uint32_
 hipError_t launch_indexed_sum(const DevResident &r, const DevIndex &ix, const uint8_t *mask, uint32_t stride,
                               void *out, int out64, uint32_t *fields, uint8_t *residual, hipStream_t st);
 //  zero n bytes (region outputs of residents with invalid pixels)
+// Split points of every byte-rANS stream of the complete blocks (out: n_blocks
+// x P x {state, byte offset}); one decode of the first kSplit scans.
+hipError_t launch_split_build(const DevResident &r, uint32_t *out, hipStream_t st);
 // Stream-header checks of a resident built from a device container.
 hipError_t launch_check_headers(const DevResident &r, const uint8_t *usable, unsigned long long *counts,
                                 unsigned long long *bad, hipStream_t st);

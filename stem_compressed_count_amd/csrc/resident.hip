@@ -38,6 +38,7 @@ struct qsc_resident {
     uint8_t *d_valid = nullptr;
     unsigned long long *d_err = nullptr;
     uint32_t *d_plan = nullptr;  // per-tile selected-pixel counts of the current query
+    uint32_t *d_split = nullptr; // byte-rANS split points (n_blocks x P x {state, byte offset})
     uint32_t *d_dp_part = nullptr;  // diffraction pattern: n_blocks x P partial sums, then n_blocks scan counts
     float *d_amp = nullptr;         // sqrt of 0..65535, correctly rounded (amplitude frames)
     // polar interaction index (built on request)
@@ -82,7 +83,7 @@ hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
 }
 
 void free_all(qsc_resident *res) {
-    for (void *p : {res->borrowed ? nullptr : (void *)res->d_blob, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
+    for (void *p : {res->borrowed ? nullptr : (void *)res->d_blob, (void *)res->d_split, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
                     (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, (void *)res->d_amp,
                     (void *)res->d_ix_perm, (void *)res->d_ix_leaf_valid, (void *)res->d_ix_packed,
                     (void *)res->d_ix_offset, (void *)res->d_ix_fields, (void *)res->d_ix_width,
@@ -210,6 +211,16 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
     d.n_blocks = g.n_blocks();
     d.dtype = g.dtype;
     d.layout = g.layout;
+    d.split = nullptr;
+    // split points of the byte-rANS streams of complete blocks: one decode of
+    // their first halves, so that latency-bound queries decode both halves of
+    // a stream side by side
+    if (g.layout == 0 && g.S() >= kBlock) {
+        if ((e = dalloc(res.get(), &res->d_split, 8ull * g.n_blocks() * g.P())) != hipSuccess) return bail(e, "split points");
+        if ((e = launch_split_build(d, res->d_split, strm)) != hipSuccess) return bail(e, "split points");
+        if ((e = hipStreamSynchronize(strm)) != hipSuccess) return bail(e, "split points");
+        d.split = res->d_split;
+    }
     return QSC_OK;
 }
 
