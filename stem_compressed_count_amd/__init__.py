@@ -60,6 +60,13 @@ class Info(ctypes.Structure):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                       "(python -m stem_compressed_count_amd.build); there is no fallback path")
+# torch's HIP runtime is loaded first, so that the library binds to the same
+# runtime and device pointers pass between them (a second runtime loaded by
+# the library alone would not know torch's allocations)
+try:
+    import torch  # noqa: F401
+except ImportError:  # the host encoder and the pure host entry points still work
+    pass
 lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _u32, _u64, _i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32

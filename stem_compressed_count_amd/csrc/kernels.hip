@@ -1193,6 +1193,9 @@ struct PlanArgs {
     int complement;
     uint32_t P, n_tiles;  // 64-pixel tiles of one mask
     uint32_t *counts;     // null: no plan
+    const uint32_t *gbase0;  // block 0's group bases, relative offsets and directory entry: the
+    const uint16_t *rel0;    // selected streams' sizes there tell bright (densely coded) data from dim
+    const uint8_t *dir0;
 };
 
 constexpr float kTwoSlotTime = 1.7f;
@@ -1221,14 +1224,15 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
                                              bool can_split, uint16_t *desc, uint32_t *wtot) {
     constexpr uint32_t kPer = 2 * kMaxPlanTiles / WG;
     constexpr uint32_t kWaves = WG / 64;
-    __shared__ uint32_t wpart[4][kWaves];  // per wave: the second mask's sum, and each mask's last tile
+    __shared__ uint32_t wpart[5][kWaves];  // per wave: the second mask's sum, each mask's last tile, bytes
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
     const uint32_t n_tiles = (P + kPlanFine - 1) / kPlanFine, n_all = two ? 2 * n_tiles : n_tiles;
-    uint32_t c[kPer], s = 0, s2 = 0, last[2] = {0, 0};
+    uint32_t c[kPer], s = 0, s2 = 0, last[2] = {0, 0}, bytes = 0;
 #pragma unroll
     for (uint32_t j = 0; j < kPer; j++) {
         const uint32_t t = tid * kPer + j;
         c[j] = t < n_all ? counts[t] : 0u;
+        bytes += t < n_all ? counts[kPlanBytes + t] : 0u;
         s += c[j];
         const uint32_t second = t >= n_tiles;
         s2 += second ? c[j] : 0u;
@@ -1245,6 +1249,7 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         s2 += __shfl_xor(s2, off);
+        bytes += __shfl_xor(bytes, off);
         last[0] = max(last[0], (uint32_t)__shfl_xor(last[0], off));
         last[1] = max(last[1], (uint32_t)__shfl_xor(last[1], off));
     }
@@ -1254,9 +1259,11 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
         wpart[0][wave] = s2;
         wpart[1][wave] = last[0];
         wpart[2][wave] = last[1];
+        wpart[3][wave] = bytes;
     }
     __syncthreads();
     uint32_t before = 0, total = 0, total2 = 0, end0 = 0, end1 = 0;
+    uint64_t total_bytes = 0;
 #pragma unroll
     for (uint32_t w = 0; w < kWaves; w++) {
         before += w < wave ? wtot[w] : 0u;
@@ -1264,6 +1271,7 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
         total2 += wpart[0][w];
         end0 = max(end0, wpart[1][w]);
         end1 = max(end1, wpart[2][w]);
+        total_bytes += wpart[3][w];
     }
     const uint32_t total1 = total - total2;
     const float slots = (float)gridDim.x;
@@ -1273,9 +1281,12 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
     };
     uint32_t cap = WG / 2;
     if (cost(WG) < cost(cap)) cap = WG;
-    // 1024-lane workgroups fill a compute unit alone: two streams per lane pay
-    // only when most pixels are selected (measured)
-    if ((WG < 1024 || 2 * total >= P) && cost(2 * WG) < cost(cap)) cap = 2 * WG;
+    // Two streams per lane pay for dim data only (measured): streams coded in
+    // more than 0.4 bytes per count (bright pixels, 512 counts per stream in
+    // block 0) make them several times slower. 1024-lane workgroups fill a
+    // compute unit alone and pay only when most pixels are selected.
+    const bool dim = total_bytes * 10 <= (uint64_t)total * kBlk * 4;
+    if ((WG < 1024 ? dim : 2 * total >= P) && cost(2 * WG) < cost(cap)) cap = 2 * WG;
     const bool halves = can_split && cap == WG / 2 && cost(WG / 2) <= 1.0f;
     const uint32_t n_first = (total1 + cap - 1) / cap, pad = n_first * cap - total1;
     // tile t starts item k when it holds the pixel numbered k * cap
@@ -1612,7 +1623,20 @@ __global__ void __launch_bounds__(256) k_init(void *out, int out64, const void *
         bool f = false;
         if (p < pa.P) f = pa.valid[p] != 0 && (mask ? ((mask[p] != 0) != (pa.complement != 0)) : true);
         const uint32_t c = (uint32_t)__popcll(__ballot(f));
-        if (lane == 0) pa.counts[t] = c;
+        // encoded bytes of the tile's selected streams in block 0
+        uint32_t len = 0;
+        if (f) {
+            const uint32_t s0 = pa.gbase0[p >> 5] + pa.rel0[p];
+            const uint32_t s1 = p + 1 < pa.P ? pa.gbase0[(p + 1) >> 5] + pa.rel0[p + 1]
+                                             : *reinterpret_cast<const uint32_t *>(pa.dir0 + 12);
+            len = s1 - s0;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) len += __shfl_xor(len, off);
+        if (lane == 0) {
+            pa.counts[t] = c;
+            pa.counts[kPlanBytes + t] = len;
+        }
     }
 }
 
@@ -1937,7 +1961,7 @@ static void launch_items(F kern, int threads, const uint32_t *cands, int ncand, 
     const uint32_t n_tiles = (r.P + tile - 1) / tile, n_masks = da.neg_mask ? 2 : 1;
     uint32_t *plan = planned ? r.plan : nullptr;
     if (n_init) {
-        const PlanArgs pa{mask, da.neg_mask, r.valid, complement, r.P, n_tiles, plan};
+        const PlanArgs pa{mask, da.neg_mask, r.valid, complement, r.P, n_tiles, plan, r.gbase, r.rel, r.dir};
         const uint32_t grid = (uint32_t)std::max<uint64_t>(
             planned ? (n_masks * n_tiles + 3) / 4 : 1,
             std::max<uint64_t>(1, std::min<uint64_t>(2048, (n_init + 255) / 256)));

@@ -16,7 +16,10 @@ constexpr uint32_t kPairTable = 32 * 1024 + 4;
 // pixels in pixel order.
 constexpr uint32_t kPlanFine = 64;
 constexpr uint32_t kMaxPlanTiles = 1024;
-constexpr uint32_t kPlanWords = 2 * kMaxPlanTiles;  // the counts of a second, subtracted mask follow
+// plan buffer: the counts (a second, subtracted mask's follow), then as many
+// words of the selected pixels' encoded bytes in the first block
+constexpr uint32_t kPlanBytes = 2 * kMaxPlanTiles;
+constexpr uint32_t kPlanWords = 4 * kMaxPlanTiles;
 
 // Device view of a resident (all pointers are device memory).
 struct DevResident {
