@@ -1282,8 +1282,8 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
     uint32_t cap = WG / 2;
     if (cost(WG) < cost(cap)) cap = WG;
     // Two streams per lane pay for dim data only (measured): streams coded in
-    // more than 0.4 bytes per count (bright pixels, 512 counts per stream in
-    // block 0) make them several times slower. 1024-lane workgroups fill a
+    // more than 0.4 bytes per decoded value (block 0's 512 scans per stream)
+    // make them about twice as slow. 1024-lane workgroups fill a
     // compute unit alone and pay only when most pixels are selected.
     const bool dim = total_bytes * 10 <= (uint64_t)total * kBlk * 4;
     if ((WG < 1024 ? dim : 2 * total >= P) && cost(2 * WG) < cost(cap)) cap = 2 * WG;
