@@ -61,6 +61,15 @@ __device__ __forceinline__ Extent locate(const DevResident &r, uint32_t b, uint3
     return e;
 }
 
+// a * b + c on 24-bit operands (v_mad_u32_u24, full rate), for operands the
+// compiler cannot bound itself: past the selects of a mixed decode step it
+// widens __umul24 to 32-bit multiplies, which run at a quarter of the rate
+__device__ __forceinline__ uint32_t mad24(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 __device__ __forceinline__ uint32_t ld16(const uint8_t *pay, uint64_t off) {
     return *reinterpret_cast<const uint16_t *>(pay + off);
 }
@@ -712,8 +721,14 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     for (int k = 0; k < K; k++) {
                         a0[jj] += v[k];
                         if (OP == Op::Moments) {
-                            ar[jj] += __umul24(v[k], kr[k]);  // 24-bit multiplies run at full rate
-                            ac[jj] += __umul24(v[k], kc[k]);
+                            // 24-bit multiplies run at full rate
+                            if constexpr (decltype(form)::value == kMixed) {
+                                ar[jj] = mad24(v[k], kr[k], ar[jj]);
+                                ac[jj] = mad24(v[k], kc[k], ac[jj]);
+                            } else {
+                                ar[jj] += __umul24(v[k], kr[k]);
+                                ac[jj] += __umul24(v[k], kc[k]);
+                            }
                         }
                     }
                     // materialise the sums here: deferring them to the chunk end keeps every step's table entry live

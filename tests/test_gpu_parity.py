@@ -236,6 +236,36 @@ def test_adversarial_streams(dtype, layout, det):
                        strides=(1, 2))
 
 
+def test_raw_streams_among_dim_ones_two_per_lane():
+    """Dim streams with a few RAW ones, over enough blocks that the plan gives
+    every lane two streams: 72 blocks x 16 items of half a workgroup exceed the
+    resident workgroups, while the selection stays below 0.4 encoded bytes per
+    value. Waves holding a RAW stream take the mixed decode step, in its
+    two-per-lane form, for sums, moments and a mask delta."""
+    rng = np.random.default_rng(21)
+    dr = dc = 64
+    P, S = dr * dc, 72 * 512
+    # eight distinct blocks, repeated: ones at rate 1/32, and 40 uniform streams
+    base = (rng.integers(0, 32, size=(8 * 512, P), dtype=np.uint8) == 0).astype(np.uint16)
+    raw = rng.choice(P, 40, replace=False)
+    base[:, raw] = rng.integers(0, 65536, size=(base.shape[0], raw.size))
+    c = np.tile(base, (S // base.shape[0], 1))
+    blob = q().encode(c, 72, 512, dr, dc)
+    w = synth.Workload("mixed", 72, 512, dr, dc, 2, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    full = np.ones(P, np.uint8)
+    disk = synth.disk_mask(dr, dc, 30, 33, 20)
+    with q().Resident(blob) as res:
+        assert res.info.mode_counts[2] >= 72 * raw.size  # the uniform streams are stored RAW
+        for m in (full, disk):
+            for k in (1, 3):
+                assert np.array_equal(u(res.masked_sum(m, block_stride=k)), oracle.masked_sum(c, m, stride=k)), k
+            check_com(res, c, w, m, None)
+        prev = res.masked_sum(full)
+        got = res.masked_sum_delta(full, prev, disk)
+        assert np.array_equal(u(got), oracle.masked_sum(c, disk))
+        res.finish()
+
+
 def test_sum_dp_edge_cases():
     w, counts, valid, blob = case("tiny_u8")
     with q().Resident(blob) as res:
