@@ -129,9 +129,65 @@ def cpu_baseline(w, masks, df_mask, sample_blocks):
     oracle.region(dec, w.scan_cols, 0, 8, 0, 8, valid)
     dt = time.perf_counter() - t0
     done = step_counts(n, w.scan_cols, visited_scans(n, 4), bf, df_mask, valid, w.P)
-    return {"value": round(done / dt, 1), "unit": "counts/s", "cores": 1, "kind": "oracle",
+    line = {"value": round(done / dt, 1), "unit": "counts/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} scans ({(n + 511) // 512} blocks) of the same workload: one oracle decode, "
-                      f"then the step's queries on the decoded counts; {dt:.2f} s single-threaded"}
+                      f"then the step's queries on the decoded counts; {dt:.2f} s single-threaded",
+            "cpu": cpu_model()}
+    del dec
+    par = cpu_baseline_threads(w, counts, n, bf, df_mask, valid)
+    if par is not None:
+        par["value"] = round(done / par.pop("s"), 1)
+        line["all_cores"] = par
+    return line
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_threads(w, counts, n, bf, df_mask, valid):
+    """The same sample and queries, cut into runs of four blocks, each encoded as a
+    container of its own and handled by its own thread on the host's cores (the
+    oracle's C calls release the interpreter lock; it has no shared state).
+    Runs of four blocks keep the stride-4 query on the same blocks."""
+    import concurrent.futures
+    import oracle
+    import stem_compressed_count_amd as qsc
+
+    run = 4 * 512
+    if run % w.scan_cols or n % run:
+        return None
+    rows = run // w.scan_cols
+    blobs = [qsc.encode(counts[s0:s0 + run], rows, w.scan_cols, w.det_rows, w.det_cols, layout=w.layout).tobytes()
+             for s0 in range(0, n, run)]
+
+    def work(i):
+        dec = oracle.decode(blobs[i])
+        oracle.masked_sum(dec, bf, valid)
+        oracle.masked_sum(dec, bf, valid, stride=4)
+        oracle.dense_df(dec, df_mask, valid)
+        oracle.com(dec, w.det_rows, w.det_cols, None, valid)
+        oracle.com(dec, w.det_rows, w.det_cols, bf, valid)
+        a, b = max(0, i * rows), min(8, (i + 1) * rows)  # the step's region, rows 0-7, where this run holds them
+        if a < b:
+            oracle.region(dec, w.scan_cols, a - i * rows, b - i * rows, 0, 8, valid)
+
+    cores = min(len(os.sched_getaffinity(0)), len(blobs))
+    oracle.masked_sum(counts[:1], bf)  # loads the library before the threads start
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(work, range(len(blobs))))
+    dt = time.perf_counter() - t0
+    return {"s": dt, "unit": "counts/s", "cores": cores, "kind": "oracle",
+            "sample": f"the same {n} scans as {len(blobs)} containers of 4 blocks, one thread each "
+                      f"({cores} at a time); {dt:.2f} s"}
 
 
 def main():
