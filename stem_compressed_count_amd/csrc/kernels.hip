@@ -70,6 +70,14 @@ __device__ __forceinline__ uint32_t mad24(uint32_t a, uint32_t b, uint32_t c) {
     return d;
 }
 
+// a * b + c on sign-extended 24-bit operands (v_mad_i32_i24, full rate), low 32
+// bits: the modulo-2^32 product of operands in [-2^23, 2^23)
+__device__ __forceinline__ uint32_t mad24s(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 __device__ __forceinline__ uint32_t ld16(const uint8_t *pay, uint64_t off) {
     return *reinterpret_cast<const uint16_t *>(pay + off);
 }
@@ -1134,10 +1142,13 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                         a0[2 * tt] += v0[k];
                         a0[2 * tt + 1] += v1[k];
                         if (OP == Op::Moments) {
-                            ar[2 * tt] += v0[k] * kr[k];  // window-relative values wrap: full 32-bit products
-                            ar[2 * tt + 1] += v1[k] * kr[k];
-                            ac[2 * tt] += v0[k] * kc[k];
-                            ac[2 * tt + 1] += v1[k] * kc[k];
+                            // window-relative values lie in [-65535, 65535] (an escape below
+                            // the window is negative) and pixel coordinates below 1024: signed
+                            // 24-bit products give the same sums modulo 2^32 at full rate
+                            ar[2 * tt] = mad24s(v0[k], kr[k], ar[2 * tt]);
+                            ar[2 * tt + 1] = mad24s(v1[k], kr[k], ar[2 * tt + 1]);
+                            ac[2 * tt] = mad24s(v0[k], kc[k], ac[2 * tt]);
+                            ac[2 * tt + 1] = mad24s(v1[k], kc[k], ac[2 * tt + 1]);
                         }
                     }
                     // materialise the sums here (see the byte-rANS tile)
