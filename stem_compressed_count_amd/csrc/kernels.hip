@@ -974,7 +974,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         bbits_init(z.s, rs, z.org);
         pop16(z.s);  // header
         if (mode == 3) {
-            const uint32_t a0 = r.model_info[(hdr >> 3) & 31u] & 0xFFFFu;
+            const uint32_t a0 = tbl[kPairTable + ((hdr >> 3) & 31u)] & 0xFFFFu;
             z.X = popn(z.s, 10);
             z.tb = ((hdr >> 3) & 31u) << 10;
             z.a0 = a0;
@@ -1018,7 +1018,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 for (int k = 0; k < K; k++) {
                     if ((int32_t)e[k] < 0) {
                         PSlot &z = sl[k];
-                        const uint32_t info = r.model_info[z.meta >> 3];
+                        const uint32_t info = tbl[kPairTable + (z.meta >> 3)];
                         if (v0[k] == 15u) v0[k] = pair_literal<WIDE>(z.s, rs, info, bad);
                         if (v1[k] == 15u) v1[k] = pair_literal<WIDE>(z.s, rs, info, bad);
                         bbits_refill(z.s, rs);  // keep 32+ bits until the next cadence point
@@ -1044,7 +1044,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     v0[k] = pe_a(e);
                     v1[k] = pe_b(e);
                     if ((int32_t)e < 0) {
-                        const uint32_t info = r.model_info[z.meta >> 3];
+                        const uint32_t info = tbl[kPairTable + (z.meta >> 3)];
                         if (v0[k] == 15u) v0[k] = pair_literal<WIDE>(z.s, rs, info, bad);
                         if (v1[k] == 15u) v1[k] = pair_literal<WIDE>(z.s, rs, info, bad);
                         bbits_refill(z.s, rs);
@@ -1563,7 +1563,11 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
                                                            uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                            const uint32_t *plan, void *out, int out64, int negate,
                                                            RegionBlocks rb, RegionArgs ra, AuxArgs da) {
-    __shared__ uint32_t tbl[kPairTable];
+    // the 32 decode tables and the idle entry, then each model's window info:
+    // an escape reads it from LDS, not from global memory, because a global load
+    // inside the unrolled step made the compiler wait for every load in flight,
+    // the reservoir prefetch included, at each step
+    __shared__ uint32_t tbl[kPairTable + 32];
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kPairWG];
     __shared__ uint32_t wtot[kPairWG / 64];
@@ -1572,6 +1576,7 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
         const uint4 *src = reinterpret_cast<const uint4 *>(r.tables);
         uint4 *dst = reinterpret_cast<uint4 *>(tbl);
         for (uint32_t i = threadIdx.x; i < kPairTable / 4; i += kPairWG) dst[i] = src[i];
+        if (threadIdx.x < 32) tbl[kPairTable + threadIdx.x] = r.model_info[threadIdx.x];
     }
     __shared__ uint16_t desc[kMaxItems<kPairWG>];
     // planned: items of `cap` selected pixels; else every pixel tile of
