@@ -475,7 +475,7 @@ struct RSlot {
 template <int K, bool WIDE, Op OP>
 __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
                           uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt,
-                          const RegionArgs &ra, const DpTile &dt, uint32_t half = 0) {
+                          const RegionArgs &ra, const DpTile &dt, uint32_t half = 0, bool raw_block = false) {
     const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
@@ -783,6 +783,129 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             }
         }
     };
+
+    // RAW-only waves of sums and moments (a block's RAW streams are ordered
+    // first, so they fill waves of their own): no reservoir and no per-step
+    // branch. Each slot's values are read a 16-scan chunk at a time (two
+    // 16-byte loads and one dword, 4-byte aligned, shifted into place with a
+    // funnel shift), and the next chunk's loads are issued before the current
+    // chunk is reduced, unconditionally, so the memory wait is one chunk old.
+    if constexpr ((OP == Op::Sum || OP == Op::Moments) && K == 1) {
+        bool rans_live = false;
+#pragma unroll
+        for (int k = 0; k < K; k++) rans_live |= sl[k].live && !sl[k].raw;
+        if (raw_block && !__builtin_amdgcn_ballot_w64(rans_live)) {
+            constexpr int CH = 16;
+            constexpr uint32_t W = WIDE ? 2u : 1u;  // bytes per value
+            constexpr int ND = CH * (int)W / 4;     // dwords of one chunk's values
+            const uint32_t my = lane_scan<CH>();
+            const bool writer = lane_writes<CH>();
+            const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
+            const uint32_t j0 = half == 2 ? kSplit : 0u, nsteps = half == 0 ? n : (half == 1 ? kSplit : n - kSplit);
+            const uint32_t nfull = nsteps / CH;
+            uint32_t vs[K], sh[K];
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                // an idle slot reads outside the buffer range: zeros
+                const uint32_t s0 = sl[k].live ? sl[k].org + 2u + j0 * W : 0x80000000u;
+                vs[k] = s0 & ~3u;
+                sh[k] = (s0 & 3u) * 8u;
+            }
+            uint32_t bufA[K][ND + 1], bufB[K][ND + 1];
+            auto load = [&](uint32_t (&d)[K][ND + 1], uint32_t c) {
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+                    const uint32_t o = vs[k] + c * (CH * W);
+#pragma unroll
+                    for (int q = 0; q < ND / 4; q++) {
+                        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 16u * q), 0, 0);
+                        d[k][4 * q] = v[0];
+                        d[k][4 * q + 1] = v[1];
+                        d[k][4 * q + 2] = v[2];
+                        d[k][4 * q + 3] = v[3];
+                    }
+                    d[k][ND] = bload(rs, o + 4u * ND);
+                }
+            };
+            auto chunk = [&](const uint32_t (&d)[K][ND + 1], uint32_t c) {
+                uint32_t a0[CH];
+                uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+#pragma unroll
+                for (int i = 0; i < CH; i++) {
+                    a0[i] = 0;
+                    if (OP == Op::Moments) {
+                        ar[i] = 0;
+                        ac[i] = 0;
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+#pragma unroll
+                    for (int i = 0; i < ND; i++) {
+                        const uint32_t e = __builtin_amdgcn_alignbit(d[k][i + 1], d[k][i], sh[k]);
+#pragma unroll
+                        for (int q = 0; q < (int)(4 / W); q++) {
+                            const int j = i * (int)(4 / W) + q;
+                            const uint32_t v = WIDE ? __builtin_amdgcn_ubfe(e, 16 * q, 16) : __builtin_amdgcn_ubfe(e, 8 * q, 8);
+                            a0[j] += v;
+                            if constexpr (OP == Op::Moments) {
+                                ar[j] = mad24(v, kr[k], ar[j]);
+                                ac[j] = mad24(v, kc[k], ac[j]);
+                            }
+                        }
+                    }
+                }
+                chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + j0 + c * CH, pt.mr + j0 + c * CH,
+                                     pt.mc + j0 + c * CH);
+            };
+            // two chunks per iteration, so the buffers swap roles without copies;
+            // loads past a stream's end stay inside the block or return zeros
+            load(bufA, 0);
+            uint32_t c = 0;
+            for (; c + 1 < nfull; c += 2) {
+                load(bufB, c + 1);
+                chunk(bufA, c);
+                load(bufA, c + 2);
+                chunk(bufB, c + 1);
+            }
+            if (c < nfull) chunk(bufA, c);
+            // ragged end of a final partial block: one scan at a time
+            for (uint32_t j = nfull * CH; j < nsteps; j++) {
+                uint32_t t0 = 0, tr = 0, tc = 0;
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+                    const uint32_t s0 = sl[k].live ? sl[k].org + 2u + (j0 + j) * W : 0x80000000u;
+                    const uint32_t e = bload(rs, s0 & ~3u) >> ((s0 & 3u) * 8u);
+                    const uint32_t v = WIDE ? (e & 0xFFFFu) : (e & 0xFFu);
+                    t0 += v;
+                    if constexpr (OP == Op::Moments) {
+                        tr = mad24(v, kr[k], tr);
+                        tc = mad24(v, kc[k], tc);
+                    }
+                }
+                if (t0) atomicAdd(&pt.m0[j0 + j], t0);
+                if constexpr (OP == Op::Moments) {
+                    if (tr) atomicAdd(&pt.mr[j0 + j], (unsigned long long)tr);
+                    if (tc) atomicAdd(&pt.mc[j0 + j], (unsigned long long)tc);
+                }
+            }
+            asm volatile("" ::"v"(touched));
+            // end checks (FORMAT 2.4): the stream holds exactly the block's values,
+            // and a uint8 stream with an odd count ends in a zero pad byte
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                const RSlot &z = sl[k];
+                if (!z.live) continue;
+                bool ok = z.len == 2u + n * W + (WIDE ? 0u : (n & 1u));
+                if (!WIDE && (n & 1u) && ok) {
+                    const uint32_t s0 = z.org + 2u + n;
+                    ok = ((bload(rs, s0 & ~3u) >> ((s0 & 3u) * 8u)) & 0xFFu) == 0u;
+                }
+                if (!ok) report(r, b, z.p);
+            }
+            return;
+        }
+    }
 
     // The form is uniform over the wave. An idle slot (x = 0, reads outside the
     // buffer) decodes the symbol of table slot 0 forever, so the rANS-only forms
@@ -1472,6 +1595,55 @@ __device__ __forceinline__ uint32_t select_tile(const DevResident &r, const uint
 // Sums fit four workgroups per CU (36 KB of LDS, at most 128 VGPRs); the
 // moment partials (44 KB of LDS) fit three. The extra waves hide latency when
 // few streams are selected.
+// Reorders an item's pixel list so that its RAW streams come first, keeping
+// the order within each group. A wave whose streams are all rANS can then run
+// a rANS-only decode form, while a RAW stream among them would send the whole
+// wave to the unified step. Every thread reads its entries (i = tid and
+// tid + WG) before the barrier and writes them to their new places after it.
+template <int WG>
+__device__ __forceinline__ void raw_first(const DevResident &r, uint32_t b, uint64_t base, uint32_t nbytes,
+                                          uint32_t p0, uint32_t n_sel, uint16_t *sel) {
+    constexpr uint32_t kWaves = WG / 64;
+    __shared__ uint32_t rc[2 * kWaves];
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    uint32_t v[2];
+    bool raw[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const uint32_t i = tid + j * WG;
+        v[j] = i < n_sel ? sel[i] : kHole;
+        raw[j] = false;
+        if (v[j] != kHole) {
+            const Extent e = locate(r, b, p0 + v[j], base, nbytes);
+            raw[j] = (ld16(r.payload, e.start) & 7u) == 2u;
+        }
+    }
+    const uint64_t m0 = __builtin_amdgcn_ballot_w64(raw[0]), m1 = __builtin_amdgcn_ballot_w64(raw[1]);
+    if (lane == 0) {
+        rc[wave] = (uint32_t)__popcll(m0);
+        rc[kWaves + wave] = (uint32_t)__popcll(m1);
+    }
+    __syncthreads();  // every entry is read and counted
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t before0 = 0, all0 = 0, before1 = 0, total = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kWaves; w++) {
+        before0 += w < wave ? rc[w] : 0u;
+        all0 += rc[w];
+        before1 += w < wave ? rc[kWaves + w] : 0u;
+        total += rc[w] + rc[kWaves + w];
+    }
+    // raw entries before entry i, for i = tid and tid + WG
+    const uint32_t rb0 = before0 + (uint32_t)__popcll(m0 & below);
+    const uint32_t rb1 = all0 + before1 + (uint32_t)__popcll(m1 & below);
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const uint32_t i = tid + j * WG, rb = j ? rb1 : rb0;
+        if (i < n_sel) sel[raw[j] ? rb : total + (i - rb)] = (uint16_t)v[j];
+    }
+    __syncthreads();
+}
+
 template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
@@ -1518,6 +1690,8 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
         const uint32_t n = *reinterpret_cast<const uint32_t *>(d + 8);
         const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
+        // blocks holding RAW streams (a resident without any has no flags)
+        const bool raw_block = OP != Op::Index && OP != Op::Split && r.raw_blk && r.raw_blk[b];
         if (OP == Op::Split && n != kBlk) continue;  // a final partial block has no split points
         DpTile dt{nullptr, sbits, 0};
         if constexpr (OP == Op::Index) dt.row = da.rows + ((uint64_t)b * da.n_fields + (uint64_t)t * (kRansWG / 64)) * kBlk;
@@ -1536,6 +1710,9 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
             for (uint32_t i = threadIdx.x; i < 2048; i += kRansWG) dst[i] = src[i];
             loaded = b;
         }
+        // a block with RAW streams: put them in waves of their own (an index
+        // leaf must stay one wave, and the split-point build does not care)
+        if (raw_block) raw_first<kRansWG>(r, b, base, nbytes, p0, n_sel, sel);
         if (OP == Op::Sum || OP == Op::Moments) zero_partials<OP>(sp, n);
         __syncthreads();
         // at most two slots per lane: with three decode forms, more do not fit 3 waves per SIMD
@@ -1548,9 +1725,9 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         const uint32_t first = split_item ? (wave & 1u) * 64u : wave * 64 * K;
         if (first < n_sel) {  // whole waves without a stream skip the decode
             if (K == 2)
-                rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt);
+                rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, 0, raw_block);
             else
-                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, half);
+                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, half, raw_block);
         }
         __syncthreads();
         if (OP == Op::Sum || OP == Op::Moments)
@@ -1885,6 +2062,18 @@ __global__ void k_mask_delta(const uint8_t *prev, const uint8_t *mask, uint32_t 
 // 2.4, 3.4): reserved bits clear, a mode the layout defines, the model bits
 // only on a paired stream, and byte-rANS streams only with a usable table.
 // counts[mode] gets the valid streams; bad the first bad (block << 32 | pixel).
+__global__ void __launch_bounds__(256) k_raw_blocks(DevResident r, uint8_t *out) {
+    const uint32_t b = blockIdx.y, p = blockIdx.x * 256 + threadIdx.x;
+    bool raw = false;
+    if (p < r.P) {
+        const uint64_t base = *reinterpret_cast<const uint64_t *>(r.dir + 16ull * b);
+        const uint64_t gi = (uint64_t)b * r.G + (p >> 5);
+        const uint64_t st = base + r.gbase[gi] + r.rel[gi * 32 + (p & 31u)];
+        raw = (*reinterpret_cast<const uint16_t *>(r.payload + st) & 7u) == 2u;
+    }
+    if (__builtin_amdgcn_ballot_w64(raw) && (threadIdx.x & 63u) == 0) out[b] = 1;
+}
+
 __global__ void __launch_bounds__(256) k_check_headers(DevResident r, const uint8_t *usable, unsigned long long *counts,
                                                        unsigned long long *bad) {
     __shared__ uint32_t c[8];
@@ -2174,6 +2363,11 @@ hipError_t launch_split_build(const DevResident &r, uint32_t *out, hipStream_t s
     else
         launch_items(k_reduce_rans<false, Op::Split>, kRansWG, cands, 1, st, r, nullptr, 0, 1, r.n_blocks, nullptr, 0,
                      0, nullptr, 0, rb, ra, da);
+    return hipGetLastError();
+}
+
+hipError_t launch_raw_blocks(const DevResident &r, uint8_t *out, hipStream_t st) {
+    hipLaunchKernelGGL(k_raw_blocks, dim3((r.P + 255) / 256, r.n_blocks), dim3(256), 0, st, r, out);
     return hipGetLastError();
 }
 

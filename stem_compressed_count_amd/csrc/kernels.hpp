@@ -35,6 +35,7 @@ struct DevResident {
     uint32_t *plan;          // query plan: selected pixels per 64-pixel tile (kPlanWords words)
     const uint32_t *split;   // byte-rANS: per (block, pixel), the state and byte offset of the stream after
                              // its first kSplit scans (two words), or null when not built
+    const uint8_t *raw_blk;  // byte-rANS: per block, nonzero when it holds a RAW stream (null: none does)
     uint64_t S;
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };
@@ -142,6 +143,8 @@ hipError_t launch_indexed_sum(const DevResident &r, const DevIndex &ix, const ui
 // x P x {state, byte offset}); one decode of the first kSplit scans.
 hipError_t launch_split_build(const DevResident &r, uint32_t *out, hipStream_t st);
 // Stream-header checks of a resident built from a device container.
+// Marks (nonzero) the blocks that hold a RAW stream; out is zeroed by the caller.
+hipError_t launch_raw_blocks(const DevResident &r, uint8_t *out, hipStream_t st);
 hipError_t launch_check_headers(const DevResident &r, const uint8_t *usable, unsigned long long *counts,
                                 unsigned long long *bad, hipStream_t st);
 hipError_t launch_zero_bytes(void *out, uint64_t n, hipStream_t st);

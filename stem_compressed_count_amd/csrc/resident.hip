@@ -39,6 +39,7 @@ struct qsc_resident {
     unsigned long long *d_err = nullptr;
     uint32_t *d_plan = nullptr;  // per-tile selected-pixel counts of the current query
     uint32_t *d_split = nullptr; // byte-rANS split points (n_blocks x P x {state, byte offset})
+    uint8_t *d_raw_blk = nullptr;  // byte-rANS: per block, nonzero when it holds a RAW stream
     uint32_t *d_dp_part = nullptr;  // diffraction pattern: n_blocks x P partial sums, then n_blocks scan counts
     float *d_amp = nullptr;         // sqrt of 0..65535, correctly rounded (amplitude frames)
     // polar interaction index (built on request)
@@ -83,8 +84,8 @@ hipError_t dalloc(qsc_resident *res, T **p, uint64_t bytes) {
 }
 
 void free_all(qsc_resident *res) {
-    for (void *p : {res->borrowed ? nullptr : (void *)res->d_blob, (void *)res->d_split, (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid,
-                    (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, (void *)res->d_amp,
+    for (void *p : {res->borrowed ? nullptr : (void *)res->d_blob, (void *)res->d_split, (void *)res->d_raw_blk,
+                    (void *)res->d_tables, (void *)res->d_model_info, (void *)res->d_valid, (void *)res->d_err, (void *)res->d_plan, (void *)res->d_dp_part, (void *)res->d_amp,
                     (void *)res->d_ix_perm, (void *)res->d_ix_leaf_valid, (void *)res->d_ix_packed,
                     (void *)res->d_ix_offset, (void *)res->d_ix_fields, (void *)res->d_ix_width,
                     (void *)res->d_ix_residual, (void *)res->d_delta, res->d_total,
@@ -212,6 +213,21 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
     d.dtype = g.dtype;
     d.layout = g.layout;
     d.split = nullptr;
+    d.raw_blk = nullptr;
+    // blocks holding RAW streams: queries give those streams waves of their
+    // own. A resident without any keeps a null pointer, so its queries read
+    // no flag at all.
+    if (g.layout == 0) {
+        if ((e = dalloc(res.get(), &res->d_raw_blk, g.n_blocks())) != hipSuccess) return bail(e, "RAW block flags");
+        if ((e = hipMemsetAsync(res->d_raw_blk, 0, g.n_blocks(), strm)) != hipSuccess) return bail(e, "RAW block flags");
+        if ((e = launch_raw_blocks(d, res->d_raw_blk, strm)) != hipSuccess) return bail(e, "RAW block flags");
+        std::vector<uint8_t> flags(g.n_blocks());
+        if ((e = hipMemcpyAsync(flags.data(), res->d_raw_blk, flags.size(), hipMemcpyDeviceToHost, strm)) != hipSuccess ||
+            (e = hipStreamSynchronize(strm)) != hipSuccess)
+            return bail(e, "RAW block flags");
+        for (uint8_t f : flags)
+            if (f) d.raw_blk = res->d_raw_blk;
+    }
     // split points of the byte-rANS streams of complete blocks: one decode of
     // their first halves, so that latency-bound queries decode both halves of
     // a stream side by side
