@@ -266,6 +266,64 @@ def test_raw_streams_among_dim_ones_two_per_lane():
         res.finish()
 
 
+@pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
+def test_raw_streams_fill_waves(dtype):
+    """200 of 256 streams RAW. Ordered first in each item, they fill three
+    waves that decode sums and moments in the RAW-only form; the fourth wave
+    mixes RAW and rANS streams. 903 scans give a complete block (decoded in
+    two halves when a query is latency-bound) and a final block of 391 scans,
+    a ragged chunk and, for uint8, a padded odd-length stream."""
+    rng = np.random.default_rng(31)
+    dr = dc = 16
+    P, sr, sc = dr * dc, 3, 301
+    S = sr * sc
+    maxv = 255 if dtype == np.uint8 else 65535
+    c = rng.poisson(0.4, size=(S, P)).astype(dtype)
+    raw = np.sort(rng.choice(P, 200, replace=False))
+    c[:, raw] = rng.integers(0, maxv + 1, size=(S, raw.size)).astype(dtype)
+    blob = q().encode(c, sr, sc, dr, dc)
+    w = synth.Workload("raw", sr, sc, dr, dc, 1 if dtype == np.uint8 else 2, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    valid = np.ones(P, np.uint8)
+    valid[raw[7]] = 0
+    masks = {"all": np.ones(P, np.uint8), "disk": synth.disk_mask(dr, dc, 8, 8, 5),
+             "random": (rng.random(P) < 0.5).astype(np.uint8)}
+    with q().Resident(blob, valid=valid) as res:
+        assert res.info.mode_counts[2] >= 2 * raw.size
+        for name, m in masks.items():
+            for k in (1, 2):
+                got = u(res.masked_sum(m, block_stride=k))
+                assert np.array_equal(got, oracle.masked_sum(c, m, valid, stride=k)), (name, k)
+            check_com(res, c, w, m, valid)
+        check_com(res, c, w, None, valid)
+        assert np.array_equal(u(res.dense_df(masks["disk"])), oracle.dense_df(c, masks["disk"], valid))
+        prev = res.masked_sum(masks["all"])
+        got = res.masked_sum_delta(masks["all"], prev, masks["disk"])
+        assert np.array_equal(u(got), oracle.masked_sum(c, masks["disk"], valid))
+        res.finish()
+
+
+def test_raw_stream_of_the_wrong_length_fails():
+    """Moving the boundary between two RAW streams by one value keeps every
+    extent even and ordered, so the container passes the host checks; the
+    decode finds that neither stream holds exactly its block's values."""
+    rng = np.random.default_rng(32)
+    P, p = 256, 40  # pixels 40 and 41 share an offset group
+    c = rng.integers(0, 65536, size=(1024, P)).astype(np.uint16)  # every stream RAW
+    c[511, p] = 2  # the word that becomes pixel 41's header (mode RAW) in block 0
+    blob = bytearray(q().encode(c, 2, 512, 16, 16).tobytes())
+    h = oracle.header(bytes(blob))
+    at = h["rel_off"] + 2 * (p + 1)
+    struct.pack_into("<H", blob, at, struct.unpack_from("<H", blob, at)[0] - 2)
+    qq = q()
+    with qq.Resident(bytes(blob)) as res:
+        for mask in (np.ones(P, np.uint8), np.eye(1, P, p, dtype=np.uint8)[0]):
+            with pytest.raises(qq.QscValueError) as e:
+                res.masked_sum(mask)
+            assert e.value.code == qq.ERR_MALFORMED
+        with pytest.raises(qq.QscValueError):
+            res.com()
+
+
 def test_sum_dp_edge_cases():
     w, counts, valid, blob = case("tiny_u8")
     with q().Resident(blob) as res:
