@@ -168,6 +168,13 @@ __device__ __forceinline__ uint32_t popn(B &s, uint32_t nb) {
     return v;
 }
 
+// The 16-bit literal after an escape symbol, from a reservoir known to hold it.
+__device__ __forceinline__ uint32_t rans_literal(BBits &s, uint32_t &bad) {
+    const uint32_t lit = pop16(s);
+    bad |= lit < 255u;
+    return lit;
+}
+
 // The 16-bit literal after an escape symbol; refills first so it is always there.
 __device__ __forceinline__ uint32_t rans_escape(BBits &s, Rsrc rs, uint32_t &bad) {
     bbits_refill(s, rs);
@@ -613,7 +620,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         if (WIDE && F != kPlain && __builtin_amdgcn_ballot_w64(esc_any)) {  // rare: escapes of uint16 streams
 #pragma unroll
             for (int k = 0; k < K; k++)
-                if (esc[k]) v[k] = rans_escape(sl[k].s, rs, bad);
+                if (esc[k]) v[k] = F == kEscape ? rans_literal(sl[k].s, bad) : rans_escape(sl[k].s, rs, bad);
         }
     };
     // Refill on a wave-uniform cadence: two steps use at most 32 bits (an escape
@@ -625,6 +632,10 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     };
 
     auto run = [&](auto form) {
+        // the escape form refills after every step: a step then starts with at
+        // least 33 bits, enough for a renormalisation word and a literal, so an
+        // escape reads its literal without a load of its own
+        constexpr bool every = decltype(form)::value == kEscape;
         if constexpr (is_region(OP)) {
             // values of scans inside the rectangle go straight to the output;
             // frames store every step, and a shorter unroll keeps their
@@ -650,7 +661,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     uint32_t v[K];
                     step(form, (jj & 1) == 0, v);
                     put(v);
-                    if (jj & 1) refill();
+                    if (every || (jj & 1)) refill();
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -658,7 +669,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 uint32_t v[K];
                 step(form, (j & 1) == 0, v);
                 put(v);
-                if ((j & 1) || j + 1 == nsteps) refill();
+                if (every || (j & 1) || j + 1 == nsteps) refill();
             }
         } else if constexpr (OP == Op::Dp) {
             // per-lane sums over the selected scans, no reduction across lanes
@@ -679,7 +690,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                         acc[k] = __umul24(v[k], m) + acc[k];
                         asm volatile("" : "+v"(acc[k]));  // keep the sum in the loop (see the reduce chunks)
                     }
-                    if (jj & 1) refill();
+                    if (every || (jj & 1)) refill();
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -689,7 +700,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 const uint32_t m = scan_bit(dt, j);
 #pragma unroll
                 for (int k = 0; k < K; k++) acc[k] = __umul24(v[k], m) + acc[k];
-                if ((j & 1) || j + 1 == n) refill();
+                if (every || (j & 1) || j + 1 == n) refill();
             }
 #pragma unroll
             for (int k = 0; k < K; k++)
@@ -699,7 +710,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             for (uint32_t j = 0; j < kSplit; j++) {
                 uint32_t v[K];
                 step(form, (j & 1) == 0, v);
-                if (j & 1) refill();
+                if (every || (j & 1)) refill();
             }
         } else {
             constexpr int CH = 16;
@@ -742,7 +753,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     // materialise the sums here: deferring them to the chunk end keeps every step's table entry live
                     asm volatile("" : "+v"(a0[jj]));
                     if constexpr (OP == Op::Moments) asm volatile("" : "+v"(ar[jj]), "+v"(ac[jj]));
-                    if (jj & 1) refill();
+                    if (every || (jj & 1)) refill();
                     // keep the scheduler's interleaving to the K independent slots of one step
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -771,7 +782,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 if constexpr (OP == Op::Index) {
                     t0 = wave_sum(t0) + cw;
                     if (lane == 0 && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + j], t0);
-                    if ((j & 1) || j + 1 == n) refill();
+                    if (every || (j & 1) || j + 1 == n) refill();
                     continue;
                 }
                 if (t0) atomicAdd(&pt.m0[j], t0);
@@ -779,7 +790,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     if (tr) atomicAdd(&pt.mr[j], (unsigned long long)tr);
                     if (tc) atomicAdd(&pt.mc[j], (unsigned long long)tc);
                 }
-                if ((j & 1) || j + 1 == n) refill();
+                if (every || (j & 1) || j + 1 == n) refill();
             }
         }
     };
