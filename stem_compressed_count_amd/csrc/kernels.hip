@@ -656,13 +656,33 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             };
             const uint32_t nfull = nsteps / CH;
             for (uint32_t c = 0; c < nfull; c++) {
+                if constexpr (is_frames(OP)) {
+                    // Stores wait in the same in-order counter as loads, so a refill
+                    // would also wait for the stores of the steps just before it:
+                    // frames store each pair of steps after its refill, so those
+                    // stores get a whole cadence to complete, like the prefetch.
+                    // (A rectangle stores few steps; there the order is unchanged.)
 #pragma unroll
-                for (int jj = 0; jj < CH; jj++) {
-                    uint32_t v[K];
-                    step(form, (jj & 1) == 0, v);
-                    put(v);
-                    if (every || (jj & 1)) refill();
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int jj = 0; jj < CH; jj += 2) {
+                        uint32_t v0[K], v1[K];
+                        step(form, true, v0);
+                        if (every) refill();
+                        __builtin_amdgcn_sched_barrier(0);
+                        step(form, false, v1);
+                        refill();
+                        put(v0);
+                        put(v1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < CH; jj++) {
+                        uint32_t v[K];
+                        step(form, (jj & 1) == 0, v);
+                        put(v);
+                        if (every || (jj & 1)) refill();
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
             for (uint32_t j = nfull * CH; j < nsteps; j++) {
