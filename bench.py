@@ -39,6 +39,10 @@ VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 # split x>>12, slot address, multiply-add, renorm test, renorm select (5) + M0, Mr, Mc adds (3)
 ALG_OPS_MOMENTS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_reduce_rans_moments_u16_128x128x192x192_traffic.md")
+SQ_FILE = os.path.join(ROOT, "profiles", "bench_128x128x192x192_u16_sq_counters.md")
+# a wave64 VALU instruction occupies a 16-lane SIMD for 4 clocks; 1024 SIMDs at 2.4 GHz
+SIMD_CLOCKS_PER_VALU = 4
+SIMD_CLOCKS_PER_S = 256 * 4 * 2.4e9
 KERNEL_SOURCE = os.path.join(ROOT, "stem_compressed_count_amd", "csrc", "kernels.hip")
 
 
@@ -60,16 +64,21 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the dominant kernel, if recorded for the current kernel source."""
+def recorded_field(path, name):
+    """An integer recorded in a profile summary for the current kernel source, else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            fields = dict(line.split(":", 1) for line in f if line.startswith(("source_sha256:", "traffic_bytes:")))
+        with open(path) as f:
+            fields = dict(line.split(":", 1) for line in f if line.startswith(("source_sha256:", name + ":")))
     except OSError:
         return None
-    if fields.get("source_sha256", "").strip() != kernel_source_hash():
+    if fields.get("source_sha256", "").strip() != kernel_source_hash() or name not in fields:
         return None
-    return int(fields["traffic_bytes"].strip())
+    return int(fields[name].strip())
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE, copy-calibrated)."""
+    return recorded_field(TRAFFIC_FILE, "traffic_bytes")
 
 
 def copy_ceiling(torch, reps=10):
@@ -426,6 +435,12 @@ def main():
                 "encoded_bytes_per_launch": int(by_full), "encoded_GBps": round(com_gbps, 2),
                 "encoded_hbm_frac": round(com_gbps / HBM_PEAK_GBPS, 4),
                 "kernel_source_sha256": kernel_source_hash()}
+    # what the chip actually issues for it (SQ_INSTS_VALU recorded under profiles/): VALU
+    # instructions per decoded count, and the share of SIMD clocks they occupy
+    valu = recorded_field(SQ_FILE, "valu_insts_per_launch")
+    roofline["issued_valu_per_count"] = None if valu is None else round(valu * 64 / cn_full, 2)
+    roofline["valu_issue_frac"] = (None if valu is None else
+                                   round(valu * SIMD_CLOCKS_PER_VALU / (com_ms * 1e-3 * SIMD_CLOCKS_PER_S), 4))
 
     line = {
         "metric": "decode+masked_sum counts/s and encoded-byte GB/s (fraction of HBM peak)",
