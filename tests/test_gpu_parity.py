@@ -302,6 +302,28 @@ def test_raw_streams_fill_waves(dtype):
         res.finish()
 
 
+def test_raw_streams_without_a_plan():
+    """A 257 x 257 detector (more pixels than a query plan covers): items are
+    pixel tiles, and RAW streams (30 %, uniform uint16) are still ordered first
+    within each tile and decoded by RAW-only waves; a final partial block too."""
+    rng = np.random.default_rng(33)
+    dr = dc = 257
+    P, S = dr * dc, 768
+    c = (rng.integers(0, 16, size=(S, P), dtype=np.uint8) == 0).astype(np.uint16)
+    raw = np.sort(rng.choice(P, P * 3 // 10, replace=False))
+    c[:, raw] = rng.integers(0, 65536, size=(S, raw.size), dtype=np.uint16)
+    blob = q().encode(c, 3, 256, dr, dc)
+    w = synth.Workload("raw257", 3, 256, dr, dc, 2, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    disk = synth.disk_mask(dr, dc, 128, 128, 60)
+    with q().Resident(blob) as res:
+        assert res.info.mode_counts[2] >= 2 * raw.size
+        for m in (np.ones(P, np.uint8), disk):
+            for k in (1, 2):
+                assert np.array_equal(u(res.masked_sum(m, block_stride=k)), oracle.masked_sum(c, m, stride=k)), k
+            check_com(res, c, w, m, None)
+        res.finish()
+
+
 def test_raw_stream_of_the_wrong_length_fails():
     """Moving the boundary between two RAW streams by one value keeps every
     extent even and ordered, so the container passes the host checks; the
