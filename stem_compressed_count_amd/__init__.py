@@ -117,9 +117,17 @@ def _raise(code, msg):
 
 
 def encode(data, scan_rows, scan_cols, det_rows, det_cols, layout=0, scaled=False, threads=0):
-    """Encode (S x P) uint8/uint16 counts, or float32 when scaled, into a container blob (numpy uint8)."""
-    enc = Encoder(scan_rows, scan_cols, det_rows, det_cols,
-                  dtype=2 if scaled else (1 if np.asarray(data).dtype == np.uint8 else 2),
+    """Encode (S x P) uint8/uint16 counts, or float32 when scaled, into a container blob (numpy uint8).
+
+    Other dtypes are refused, float16 included: there is no float16 storage (the
+    scaled-uint16 page, "What dtype means": load and save refuse it), and scaled
+    storage keeps 16-bit codes of float32 intensities."""
+    dt = np.asarray(data).dtype
+    if scaled and dt != np.float32:
+        raise ValueError(f"scaled input must be float32, not {dt}")
+    if not scaled and dt not in (np.uint8, np.uint16):
+        raise ValueError(f"counts must be uint8 or uint16, not {dt}")
+    enc = Encoder(scan_rows, scan_cols, det_rows, det_cols, dtype=2 if scaled else (1 if dt == np.uint8 else 2),
                   layout=layout, scaled=scaled)
     try:
         enc.add(data, threads)

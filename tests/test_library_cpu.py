@@ -106,6 +106,19 @@ def test_encoder_rejects_nan_and_bad_geometry():
         q.Encoder(1, 10, 2000, 2, dtype=2)  # detector dimension above 1024
 
 
+def test_float16_is_refused():
+    """No float16 storage: neither native nor scaled encoding accepts float16 values
+    (scaled-uint16 page, "What dtype means")."""
+    q = qsc()
+    x = np.ones((512, 4), dtype=np.float16)
+    with pytest.raises(ValueError, match="float16"):
+        q.encode(x, 1, 512, 2, 2)
+    with pytest.raises(ValueError, match="float16"):
+        q.encode(x, 1, 512, 2, 2, scaled=True)
+    with pytest.raises(ValueError):
+        q.encode(x.astype(np.int32), 1, 512, 2, 2)
+
+
 def create_status(blob):
     q = qsc()
     b = np.frombuffer(blob, dtype=np.uint8)
