@@ -138,14 +138,18 @@ def cpu_baseline(w, masks, df_mask, sample_blocks):
     oracle.region(dec, w.scan_cols, 0, 8, 0, 8, valid)
     dt = time.perf_counter() - t0
     done = step_counts(n, w.scan_cols, visited_scans(n, 4), bf, df_mask, valid, w.P)
+    # the oracle decodes every stream of the sample once: its encoded-byte rate is the payload over the time
+    payload = int(oracle.header(blob)["payload_bytes"])
     line = {"value": round(done / dt, 1), "unit": "counts/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} scans ({(n + 511) // 512} blocks) of the same workload: one oracle decode, "
                       f"then the step's queries on the decoded counts; {dt:.2f} s single-threaded",
-            "cpu": cpu_model()}
+            "payload_GBps": round(payload / dt / 1e9, 3), "cpu": cpu_model()}
     del dec
     par = cpu_baseline_threads(w, counts, n, bf, df_mask, valid)
     if par is not None:
-        par["value"] = round(done / par.pop("s"), 1)
+        s = par.pop("s")
+        par["value"] = round(done / s, 1)
+        par["payload_GBps"] = round(payload / s / 1e9, 3)
         line["all_cores"] = par
     return line
 
