@@ -558,8 +558,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         }
     }
 
-    // byte-rANS decode step (FORMAT 2.3). The block table has two planes of 4096
-    // entries, read together by one ds_read2st64: f | symbol << 24
+    // byte-rANS decode step (FORMAT 2.3). The block table holds two words per
+    // slot, side by side and read by one 64-bit LDS load: f | symbol << 24
     // (v_mad_u32_u24 reads only the low 24 bits, so the symbol rides along) and
     // slot - c[symbol]. A renormalisation appends the next 16-bit word with one
     // byte permute; an escape (symbol 255 of a uint16 stream) reads its literal.
@@ -576,8 +576,9 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
 #pragma unroll
         for (int k = 0; k < K; k++) {
             const uint32_t slot = sl[k].x & 4095u;
-            e[k] = tbl[slot];
-            bias[k] = tbl[slot + 4096];
+            const uint2 eb = reinterpret_cast<const uint2 *>(tbl)[slot];
+            e[k] = eb.x;
+            bias[k] = eb.y;
         }
         bool esc_any = false;
         bool esc[K];
@@ -950,7 +951,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     const bool idle_ok = (tbl[0] >> 24) == 0u;
     if (__builtin_amdgcn_ballot_w64(raw || (idle && !idle_ok))) {
         run(std::integral_constant<int, kMixed>{});
-    } else if (WIDE && (tbl[4095] >> 24) == 255u) {
+    } else if (WIDE && (tbl[2 * 4095] >> 24) == 255u) {
         // symbols are laid out in increasing order, so the last slot holds the
         // largest coded symbol: 255 there means escapes can occur
         run(std::integral_constant<int, kEscape>{});
@@ -1680,7 +1681,7 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                          const uint32_t *plan, void *out, int out64, int negate,
                                                          RegionBlocks rb, RegionArgs ra, AuxArgs da) {
-    __shared__ uint32_t tbl[2 * 4096];
+    __shared__ __align__(16) uint32_t tbl[2 * 4096];  // per slot: f | symbol << 24, slot - c[symbol]
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kRansWG];
     __shared__ uint32_t wtot[kRansWG / 64];
