@@ -212,42 +212,42 @@ constexpr int kHalfMirror = 0x141;  // lane i <- 7-i within each 8 lanes (pairs 
 constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 
+// The first levels: the two lane-swap levels and the first DPP level. After
+// them each of the CH / 8 remaining registers holds sums of at most 8 lanes'
+// values (the moments reduce those in 32 bits for any detector).
 template <int CH>
-__device__ __forceinline__ uint32_t wave_transpose_sum(uint32_t (&a)[CH]) {
+__device__ __forceinline__ void transpose_head(uint32_t (&a)[CH]) {
     static_assert(CH == 32 || CH == 16 || CH == 8, "chunk of 8, 16 or 32 scans");
+#pragma unroll
+    for (int i = 0; i < CH / 2; i++) a[i] = bf32(a[i], a[i + CH / 2]);
+#pragma unroll
+    for (int i = 0; i < CH / 4; i++) a[i] = bf16(a[i], a[i + CH / 4]);
+#pragma unroll
+    for (int i = 0; i < CH / 8; i++) a[i] = bfdpp<kRowRor8, 8>(a[i], a[i + CH / 8]);
+}
+// The remaining levels, over a[0 .. CH / 8).
+template <int CH>
+__device__ __forceinline__ uint32_t transpose_tail(const uint32_t *a) {
     uint32_t v;
-    if (CH == 32) {
-#pragma unroll
-        for (int i = 0; i < 16; i++) a[i] = bf32(a[i], a[i + 16]);
-#pragma unroll
-        for (int i = 0; i < 8; i++) a[i] = bf16(a[i], a[i + 8]);
-#pragma unroll
-        for (int i = 0; i < 4; i++) a[i] = bfdpp<kRowRor8, 8>(a[i], a[i + 4]);
-#pragma unroll
-        for (int i = 0; i < 2; i++) a[i] = bfdpp<kHalfMirror, 4>(a[i], a[i + 2]);
-        v = bfdpp<kQuadXor2, 2>(a[0], a[1]);
+    if constexpr (CH == 32) {
+        v = bfdpp<kQuadXor2, 2>(bfdpp<kHalfMirror, 4>(a[0], a[2]), bfdpp<kHalfMirror, 4>(a[1], a[3]));
         v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, false);
-    } else if (CH == 16) {
-#pragma unroll
-        for (int i = 0; i < 8; i++) a[i] = bf32(a[i], a[i + 8]);
-#pragma unroll
-        for (int i = 0; i < 4; i++) a[i] = bf16(a[i], a[i + 4]);
-#pragma unroll
-        for (int i = 0; i < 2; i++) a[i] = bfdpp<kRowRor8, 8>(a[i], a[i + 2]);
+    } else if constexpr (CH == 16) {
         v = bfdpp<kHalfMirror, 4>(a[0], a[1]);
         v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, false);
         v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, false);
     } else {
-#pragma unroll
-        for (int i = 0; i < 4; i++) a[i] = bf32(a[i], a[i + 4]);
-#pragma unroll
-        for (int i = 0; i < 2; i++) a[i] = bf16(a[i], a[i + 2]);
-        v = bfdpp<kRowRor8, 8>(a[0], a[1]);
+        v = a[0];
         v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kHalfMirror, 0xF, 0xF, false);
         v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, false);
         v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, false);
     }
     return v;
+}
+template <int CH>
+__device__ __forceinline__ uint32_t wave_transpose_sum(uint32_t (&a)[CH]) {
+    transpose_head<CH>(a);
+    return transpose_tail<CH>(a);
 }
 
 // Sum of one value over the 64 lanes of a wave, in every lane.
@@ -273,9 +273,10 @@ __device__ __forceinline__ bool lane_writes() {
 
 // Adds the wave totals of one chunk to the LDS partials. A lane's moment term
 // is at most 4 slots x 65535 x (dim - 1); over 64 lanes that stays below 2^32
-// while both detector dimensions are at most 256 (split = false). Larger
-// detectors split the terms into 16-bit halves that reduce without overflow
-// (64 lanes x 2^16 < 2^32) and recombine in 64 bits.
+// while both detector dimensions are at most 256 (split = false), and over
+// the 8 lanes of the head levels below 2^31 for any detector (dim <= 1024).
+// Larger detectors split the head's sums into 16-bit halves for the tail
+// levels (8 x 2^16 < 2^32) and recombine them in 64 bits.
 template <int CH, Op OP>
 __device__ __forceinline__ void chunk_to_lds(uint32_t (&a0)[CH], uint32_t (&ar)[OP == Op::Moments ? CH : 1],
                                              uint32_t (&ac)[OP == Op::Moments ? CH : 1], uint32_t my, bool writer,
@@ -284,24 +285,29 @@ __device__ __forceinline__ void chunk_to_lds(uint32_t (&a0)[CH], uint32_t (&ar)[
     const uint32_t t0 = wave_transpose_sum<CH>(a0);
     if (writer && t0) atomicAdd(&m0[my], t0);
     if constexpr (OP == Op::Moments) {
+        // the head levels add at most 8 lanes' terms: below 2^31 for any detector
+        // (up to 1024 per side); only the tail needs 16-bit halves on large ones
+        transpose_head<CH>(ar);
+        transpose_head<CH>(ac);
         unsigned long long tr, tc;
         if (!split) {
-            tr = wave_transpose_sum<CH>(ar);
-            tc = wave_transpose_sum<CH>(ac);
+            tr = transpose_tail<CH>(ar);
+            tc = transpose_tail<CH>(ac);
         } else {
-            uint32_t lo[CH];
+            constexpr int R = CH / 8;
+            uint32_t lo[R], hi[R];
 #pragma unroll
-            for (int i = 0; i < CH; i++) {
+            for (int i = 0; i < R; i++) {
                 lo[i] = ar[i] & 0xFFFFu;
-                ar[i] >>= 16;
+                hi[i] = ar[i] >> 16;
             }
-            tr = ((unsigned long long)wave_transpose_sum<CH>(ar) << 16) + wave_transpose_sum<CH>(lo);
+            tr = ((unsigned long long)transpose_tail<CH>(hi) << 16) + transpose_tail<CH>(lo);
 #pragma unroll
-            for (int i = 0; i < CH; i++) {
+            for (int i = 0; i < R; i++) {
                 lo[i] = ac[i] & 0xFFFFu;
-                ac[i] >>= 16;
+                hi[i] = ac[i] >> 16;
             }
-            tc = ((unsigned long long)wave_transpose_sum<CH>(ac) << 16) + wave_transpose_sum<CH>(lo);
+            tc = ((unsigned long long)transpose_tail<CH>(hi) << 16) + transpose_tail<CH>(lo);
         }
         if (writer && tr) atomicAdd(&mr[my], tr);
         if (writer && tc) atomicAdd(&mc[my], tc);
