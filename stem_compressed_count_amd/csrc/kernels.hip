@@ -383,12 +383,33 @@ constexpr bool is_region(Op op) { return op == Op::Region || is_frames(op); }
 // Value v of pixel p in the output row starting at element `row` (one scan):
 // the row's address is uniform and the pixel's byte offset a 32-bit lane
 // value, so the store needs no 64-bit address arithmetic per lane.
+// The amplitudes of counts 0-255 in LDS, staged once per workgroup by the
+// amplitude kernels (only their instantiations allocate it): frames of counts
+// read their square roots without a global load, whose wait would also hold
+// back the reservoir's refill.
+__device__ __forceinline__ float *amp_cache() {
+    __shared__ float a[256];
+    return a;
+}
+template <int WG>
+__device__ __forceinline__ void amp_stage(const RegionArgs &ra) {
+    float *a = amp_cache();
+    for (uint32_t i = threadIdx.x; i < 256; i += WG) a[i] = ra.amp[i];
+}
+
 template <bool WIDE, bool AMP>
 __device__ __forceinline__ void region_put(const RegionArgs &ra, uint64_t row, uint32_t p, uint32_t v, double scale,
                                            double offset) {
     uint8_t *out = static_cast<uint8_t *>(ra.out);
     if constexpr (AMP) {
-        *reinterpret_cast<float *>(out + 4 * row + 4u * p) = ra.amp[v & 0xFFFFu];  // counts are at most 65535
+        // counts are at most 65535; the rare larger ones in the wave load their
+        // amplitude from the full table and store it over the cached one
+        float *dst = reinterpret_cast<float *>(out + 4 * row + 4u * p);
+        const uint32_t c = v & 0xFFFFu;
+        *dst = amp_cache()[c & 255u];
+        if (__builtin_amdgcn_ballot_w64(c > 255u)) {
+            if (c > 255u) *dst = ra.amp[c];
+        }
     } else if (ra.out_kind == 1) {
         *reinterpret_cast<float *>(out + 4 * row + 4u * p) = (float)__dadd_rn(__dmul_rn((double)v, scale), offset);
     } else if (WIDE) {
@@ -1712,6 +1733,7 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     }
     const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
+    if constexpr (OP == Op::Amp) amp_stage<kRansWG>(ra);  // read after the item loop's first barrier
     uint32_t loaded = 0xFFFFFFFFu;
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = w % n_live;
@@ -1808,6 +1830,7 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     }
     const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
+    if constexpr (OP == Op::Amp) amp_stage<kPairWG>(ra);  // read after the item loop's first barrier
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = w % n_live;
         const uint32_t b = is_region(OP) ? rb.b[vb] : vb * stride;
