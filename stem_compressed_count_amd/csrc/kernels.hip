@@ -400,6 +400,11 @@ __device__ __forceinline__ void amp_stage(const RegionArgs &ra) {
 template <bool WIDE, bool AMP>
 __device__ __forceinline__ void region_put(const RegionArgs &ra, uint64_t row, uint32_t p, uint32_t v, double scale,
                                            double offset) {
+    // the row is the same in every lane: readfirstlane keeps it in scalar
+    // registers, so each lane's address is that base plus its pixel offset
+    const uint32_t row_lo = __builtin_amdgcn_readfirstlane((uint32_t)row);
+    const uint32_t row_hi = __builtin_amdgcn_readfirstlane((uint32_t)(row >> 32));
+    row = ((uint64_t)row_hi << 32) | row_lo;
     uint8_t *out = static_cast<uint8_t *>(ra.out);
     if constexpr (AMP) {
         // counts are at most 65535; the rare larger ones in the wave load their
