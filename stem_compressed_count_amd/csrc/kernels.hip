@@ -852,8 +852,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     // first, so they fill waves of their own): no reservoir and no per-step
     // branch. Each slot's values are read a 16-scan chunk at a time (two
     // 16-byte loads and one dword, 4-byte aligned, shifted into place with a
-    // funnel shift), and the next chunk's loads are issued before the current
-    // chunk is reduced, unconditionally, so the memory wait is one chunk old.
+    // funnel shift), and each chunk's loads are issued two chunks ahead,
+    // unconditionally, so every wait is for a load two chunks old.
     if constexpr ((OP == Op::Sum || OP == Op::Moments) && K == 1) {
         bool rans_live = false;
 #pragma unroll
@@ -875,7 +875,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 vs[k] = s0 & ~3u;
                 sh[k] = (s0 & 3u) * 8u;
             }
-            uint32_t bufA[K][ND + 1], bufB[K][ND + 1];
+            uint32_t bufA[K][ND + 1], bufB[K][ND + 1], bufC[K][ND + 1];
             auto load = [&](uint32_t (&d)[K][ND + 1], uint32_t c) {
 #pragma unroll
                 for (int k = 0; k < K; k++) {
@@ -922,17 +922,22 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + j0 + c * CH, pt.mr + j0 + c * CH,
                                      pt.mc + j0 + c * CH);
             };
-            // two chunks per iteration, so the buffers swap roles without copies;
-            // loads past a stream's end stay inside the block or return zeros
+            // three buffers, each chunk's loads issued two chunks ahead; three
+            // chunks per iteration, so the buffers rotate without copies; loads
+            // past a stream's end stay inside the block or return zeros
             load(bufA, 0);
+            load(bufB, 1);
             uint32_t c = 0;
-            for (; c + 1 < nfull; c += 2) {
-                load(bufB, c + 1);
+            for (; c + 2 < nfull; c += 3) {
+                load(bufC, c + 2);
                 chunk(bufA, c);
-                load(bufA, c + 2);
+                load(bufA, c + 3);
                 chunk(bufB, c + 1);
+                load(bufB, c + 4);
+                chunk(bufC, c + 2);
             }
             if (c < nfull) chunk(bufA, c);
+            if (c + 1 < nfull) chunk(bufB, c + 1);
             // ragged end of a final partial block: one scan at a time
             for (uint32_t j = nfull * CH; j < nsteps; j++) {
                 uint32_t t0 = 0, tr = 0, tc = 0;
