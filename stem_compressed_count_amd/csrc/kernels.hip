@@ -70,6 +70,13 @@ __device__ __forceinline__ uint32_t mad24(uint32_t a, uint32_t b, uint32_t c) {
     return d;
 }
 
+// the same with b uniform over the wave, read from a scalar register
+__device__ __forceinline__ uint32_t mad24u(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+    return d;
+}
+
 // a * b + c on sign-extended 24-bit operands (v_mad_i32_i24, full rate), low 32
 // bits: the modulo-2^32 product of operands in [-2^23, 2^23)
 __device__ __forceinline__ uint32_t mad24s(uint32_t a, uint32_t b, uint32_t c) {
@@ -850,112 +857,223 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
 
     // RAW-only waves of sums and moments (a block's RAW streams are ordered
     // first, so they fill waves of their own): no reservoir and no per-step
-    // branch. Each slot's values are read a 16-scan chunk at a time (two
-    // 16-byte loads and one dword, 4-byte aligned, shifted into place with a
-    // funnel shift), and each chunk's loads are issued two chunks ahead,
-    // unconditionally, so every wait is for a load two chunks old.
+    // branch.
     if constexpr ((OP == Op::Sum || OP == Op::Moments) && K == 1) {
         bool rans_live = false;
 #pragma unroll
         for (int k = 0; k < K; k++) rans_live |= sl[k].live && !sl[k].raw;
         if (raw_block && !__builtin_amdgcn_ballot_w64(rans_live)) {
-            constexpr int CH = 16;
             constexpr uint32_t W = WIDE ? 2u : 1u;  // bytes per value
-            constexpr int ND = CH * (int)W / 4;     // dwords of one chunk's values
-            const uint32_t my = lane_scan<CH>();
-            const bool writer = lane_writes<CH>();
             const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
             const uint32_t j0 = half == 2 ? kSplit : 0u, nsteps = half == 0 ? n : (half == 1 ? kSplit : n - kSplit);
-            const uint32_t nfull = nsteps / CH;
-            uint32_t vs[K], sh[K];
+            if (OP == Op::Sum || !split) {
+                // The wave reads its streams one at a time, all lanes together:
+                // lane l loads the 8 values of scans [8 l, 8 l + 8) of the stream's
+                // range (one 8 W-byte load and the next dword, 4-byte aligned and
+                // shifted into place), so a load covers up to 512 W consecutive
+                // bytes. A lane keeps the totals of its own 8 scans over all the
+                // wave's streams, so no reduction across lanes is needed. Over at most 64
+                // streams, a moment total stays below 2^32 while both detector
+                // dimensions are at most 256. Streams are taken in lane order
+                // (scalar bit scan, offsets read from their lanes), each one's
+                // loads issued two streams ahead; past the last stream the loads
+                // fall outside the buffer and add zeros.
+                constexpr uint32_t E = 8;       // values per lane per stream
+                constexpr int NW = 2 * (int)W;  // their dwords
+                const uint32_t span = nsteps * W;
+                uint32_t km[NW];
 #pragma unroll
-            for (int k = 0; k < K; k++) {
-                // an idle slot reads outside the buffer range: zeros
-                const uint32_t s0 = sl[k].live ? sl[k].org + 2u + j0 * W : 0x80000000u;
-                vs[k] = s0 & ~3u;
-                sh[k] = (s0 & 3u) * 8u;
-            }
-            uint32_t bufA[K][ND + 1], bufB[K][ND + 1], bufC[K][ND + 1];
-            auto load = [&](uint32_t (&d)[K][ND + 1], uint32_t c) {
-#pragma unroll
-                for (int k = 0; k < K; k++) {
-                    const uint32_t o = vs[k] + c * (CH * W);
-#pragma unroll
-                    for (int q = 0; q < ND / 4; q++) {
-                        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 16u * q), 0, 0);
-                        d[k][4 * q] = v[0];
-                        d[k][4 * q + 1] = v[1];
-                        d[k][4 * q + 2] = v[2];
-                        d[k][4 * q + 3] = v[3];
-                    }
-                    d[k][ND] = bload(rs, o + 4u * ND);
+                for (int i = 0; i < NW; i++) {
+                    const int rem = (int)span - (int)(8u * W * lane + 4u * (uint32_t)i);
+                    km[i] = rem >= 4 ? ~0u : (rem <= 0 ? 0u : (1u << (8 * rem)) - 1u);
                 }
-            };
-            auto chunk = [&](const uint32_t (&d)[K][ND + 1], uint32_t c) {
-                uint32_t a0[CH];
-                uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+                uint32_t a0[E], ar[OP == Op::Moments ? E : 1], ac[OP == Op::Moments ? E : 1];
 #pragma unroll
-                for (int i = 0; i < CH; i++) {
-                    a0[i] = 0;
-                    if (OP == Op::Moments) {
-                        ar[i] = 0;
-                        ac[i] = 0;
+                for (uint32_t t = 0; t < E; t++) {
+                    a0[t] = 0;
+                    if constexpr (OP == Op::Moments) {
+                        ar[t] = 0;
+                        ac[t] = 0;
                     }
                 }
+                const uint32_t so = sl[0].live ? sl[0].org + 2u + j0 * W : 0u;  // this lane's stream, first value of the range
+                uint64_t left = __builtin_amdgcn_ballot_w64(sl[0].live);
+                const uint32_t nl = (uint32_t)__builtin_popcountll(left);
+                struct Pick {
+                    uint32_t vs, sh, kr, kc;
+                };
+                auto pick = [&]() {
+                    Pick s{0x80000000u, 0u, 0u, 0u};
+                    if (left) {
+                        const int l = (int)__builtin_ctzll(left);
+                        left &= left - 1;
+                        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)so, l);
+                        s.vs = o & ~3u;
+                        s.sh = (o & 3u) * 8u;
+                        if constexpr (OP == Op::Moments) {
+                            s.kr = (uint32_t)__builtin_amdgcn_readlane((int)kr[0], l);
+                            s.kc = (uint32_t)__builtin_amdgcn_readlane((int)kc[0], l);
+                        }
+                    }
+                    return s;
+                };
+                auto load = [&](uint32_t (&d)[NW + 1], const Pick &s) {
+                    const uint32_t o = s.vs + 8u * W * lane;
+                    if constexpr (WIDE) {
+                        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
+                        d[0] = v[0];
+                        d[1] = v[1];
+                        d[2] = v[2];
+                        d[3] = v[3];
+                    } else {
+                        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)o, 0, 0);
+                        d[0] = v[0];
+                        d[1] = v[1];
+                    }
+                    d[NW] = bload(rs, o + 4u * NW);
+                };
+                auto add = [&](const uint32_t (&d)[NW + 1], const Pick &s) {
 #pragma unroll
-                for (int k = 0; k < K; k++) {
-#pragma unroll
-                    for (int i = 0; i < ND; i++) {
-                        const uint32_t e = __builtin_amdgcn_alignbit(d[k][i + 1], d[k][i], sh[k]);
+                    for (int i = 0; i < NW; i++) {
+                        const uint32_t e = __builtin_amdgcn_alignbit(d[i + 1], d[i], s.sh) & km[i];
 #pragma unroll
                         for (int q = 0; q < (int)(4 / W); q++) {
-                            const int j = i * (int)(4 / W) + q;
+                            const int t = i * (int)(4 / W) + q;
                             const uint32_t v = WIDE ? __builtin_amdgcn_ubfe(e, 16 * q, 16) : __builtin_amdgcn_ubfe(e, 8 * q, 8);
-                            a0[j] += v;
+                            a0[t] += v;
                             if constexpr (OP == Op::Moments) {
-                                ar[j] = mad24(v, kr[k], ar[j]);
-                                ac[j] = mad24(v, kc[k], ac[j]);
+                                ar[t] = mad24u(v, s.kr, ar[t]);
+                                ac[t] = mad24u(v, s.kc, ac[t]);
                             }
                         }
                     }
+                };
+                uint32_t dA[NW + 1], dB[NW + 1], dC[NW + 1];
+                Pick sA = pick(), sB = pick(), sC;
+                load(dA, sA);
+                load(dB, sB);
+                for (uint32_t i = 0; i < nl; i += 3) {
+                    sC = pick();
+                    load(dC, sC);
+                    add(dA, sA);
+                    sA = pick();
+                    load(dA, sA);
+                    add(dB, sB);
+                    sB = pick();
+                    load(dB, sB);
+                    add(dC, sC);
                 }
-                chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + j0 + c * CH, pt.mr + j0 + c * CH,
-                                     pt.mc + j0 + c * CH);
-            };
-            // three buffers, each chunk's loads issued two chunks ahead; three
-            // chunks per iteration, so the buffers rotate without copies; loads
-            // past a stream's end stay inside the block or return zeros
-            load(bufA, 0);
-            load(bufB, 1);
-            uint32_t c = 0;
-            for (; c + 2 < nfull; c += 3) {
-                load(bufC, c + 2);
-                chunk(bufA, c);
-                load(bufA, c + 3);
-                chunk(bufB, c + 1);
-                load(bufB, c + 4);
-                chunk(bufC, c + 2);
-            }
-            if (c < nfull) chunk(bufA, c);
-            if (c + 1 < nfull) chunk(bufB, c + 1);
-            // ragged end of a final partial block: one scan at a time
-            for (uint32_t j = nfull * CH; j < nsteps; j++) {
-                uint32_t t0 = 0, tr = 0, tc = 0;
 #pragma unroll
-                for (int k = 0; k < K; k++) {
-                    const uint32_t s0 = sl[k].live ? sl[k].org + 2u + (j0 + j) * W : 0x80000000u;
-                    const uint32_t e = bload(rs, s0 & ~3u) >> ((s0 & 3u) * 8u);
-                    const uint32_t v = WIDE ? (e & 0xFFFFu) : (e & 0xFFu);
-                    t0 += v;
+                for (uint32_t t = 0; t < E; t++) {
+                    const uint32_t j = lane * E + t;
+                    if (j >= nsteps) continue;
+                    if (a0[t]) atomicAdd(&pt.m0[j0 + j], a0[t]);
                     if constexpr (OP == Op::Moments) {
-                        tr = mad24(v, kr[k], tr);
-                        tc = mad24(v, kc[k], tc);
+                        if (ar[t]) atomicAdd(&pt.mr[j0 + j], (unsigned long long)ar[t]);
+                        if (ac[t]) atomicAdd(&pt.mc[j0 + j], (unsigned long long)ac[t]);
                     }
                 }
-                if (t0) atomicAdd(&pt.m0[j0 + j], t0);
-                if constexpr (OP == Op::Moments) {
-                    if (tr) atomicAdd(&pt.mr[j0 + j], (unsigned long long)tr);
-                    if (tc) atomicAdd(&pt.mc[j0 + j], (unsigned long long)tc);
+            } else {
+                // Moments on larger detectors: each slot's values are read a 16-scan
+                // chunk at a time (two 16-byte loads and one dword, 4-byte aligned,
+                // shifted into place with a funnel shift) and reduced across lanes
+                // per chunk; each chunk's loads are issued two chunks ahead,
+                // unconditionally, so every wait is for a load two chunks old.
+                constexpr int CH = 16;
+                constexpr int ND = CH * (int)W / 4;     // dwords of one chunk's values
+                const uint32_t my = lane_scan<CH>();
+                const bool writer = lane_writes<CH>();
+                const uint32_t nfull = nsteps / CH;
+                uint32_t vs[K], sh[K];
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+                    // an idle slot reads outside the buffer range: zeros
+                    const uint32_t s0 = sl[k].live ? sl[k].org + 2u + j0 * W : 0x80000000u;
+                    vs[k] = s0 & ~3u;
+                    sh[k] = (s0 & 3u) * 8u;
+                }
+                uint32_t bufA[K][ND + 1], bufB[K][ND + 1], bufC[K][ND + 1];
+                auto load = [&](uint32_t (&d)[K][ND + 1], uint32_t c) {
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        const uint32_t o = vs[k] + c * (CH * W);
+#pragma unroll
+                        for (int q = 0; q < ND / 4; q++) {
+                            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 16u * q), 0, 0);
+                            d[k][4 * q] = v[0];
+                            d[k][4 * q + 1] = v[1];
+                            d[k][4 * q + 2] = v[2];
+                            d[k][4 * q + 3] = v[3];
+                        }
+                        d[k][ND] = bload(rs, o + 4u * ND);
+                    }
+                };
+                auto chunk = [&](const uint32_t (&d)[K][ND + 1], uint32_t c) {
+                    uint32_t a0[CH];
+                    uint32_t ar[OP == Op::Moments ? CH : 1], ac[OP == Op::Moments ? CH : 1];
+#pragma unroll
+                    for (int i = 0; i < CH; i++) {
+                        a0[i] = 0;
+                        if (OP == Op::Moments) {
+                            ar[i] = 0;
+                            ac[i] = 0;
+                        }
+                    }
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+#pragma unroll
+                        for (int i = 0; i < ND; i++) {
+                            const uint32_t e = __builtin_amdgcn_alignbit(d[k][i + 1], d[k][i], sh[k]);
+#pragma unroll
+                            for (int q = 0; q < (int)(4 / W); q++) {
+                                const int j = i * (int)(4 / W) + q;
+                                const uint32_t v = WIDE ? __builtin_amdgcn_ubfe(e, 16 * q, 16) : __builtin_amdgcn_ubfe(e, 8 * q, 8);
+                                a0[j] += v;
+                                if constexpr (OP == Op::Moments) {
+                                    ar[j] = mad24(v, kr[k], ar[j]);
+                                    ac[j] = mad24(v, kc[k], ac[j]);
+                                }
+                            }
+                        }
+                    }
+                    chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + j0 + c * CH, pt.mr + j0 + c * CH,
+                                         pt.mc + j0 + c * CH);
+                };
+                // three buffers, each chunk's loads issued two chunks ahead; three
+                // chunks per iteration, so the buffers rotate without copies; loads
+                // past a stream's end stay inside the block or return zeros
+                load(bufA, 0);
+                load(bufB, 1);
+                uint32_t c = 0;
+                for (; c + 2 < nfull; c += 3) {
+                    load(bufC, c + 2);
+                    chunk(bufA, c);
+                    load(bufA, c + 3);
+                    chunk(bufB, c + 1);
+                    load(bufB, c + 4);
+                    chunk(bufC, c + 2);
+                }
+                if (c < nfull) chunk(bufA, c);
+                if (c + 1 < nfull) chunk(bufB, c + 1);
+                // ragged end of a final partial block: one scan at a time
+                for (uint32_t j = nfull * CH; j < nsteps; j++) {
+                    uint32_t t0 = 0, tr = 0, tc = 0;
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        const uint32_t s0 = sl[k].live ? sl[k].org + 2u + (j0 + j) * W : 0x80000000u;
+                        const uint32_t e = bload(rs, s0 & ~3u) >> ((s0 & 3u) * 8u);
+                        const uint32_t v = WIDE ? (e & 0xFFFFu) : (e & 0xFFu);
+                        t0 += v;
+                        if constexpr (OP == Op::Moments) {
+                            tr = mad24(v, kr[k], tr);
+                            tc = mad24(v, kc[k], tc);
+                        }
+                    }
+                    if (t0) atomicAdd(&pt.m0[j0 + j], t0);
+                    if constexpr (OP == Op::Moments) {
+                        if (tr) atomicAdd(&pt.mr[j0 + j], (unsigned long long)tr);
+                        if (tc) atomicAdd(&pt.mc[j0 + j], (unsigned long long)tc);
+                    }
                 }
             }
             asm volatile("" ::"v"(touched));
