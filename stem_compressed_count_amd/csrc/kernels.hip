@@ -70,13 +70,6 @@ __device__ __forceinline__ uint32_t mad24(uint32_t a, uint32_t b, uint32_t c) {
     return d;
 }
 
-// the same with b uniform over the wave, read from a scalar register
-__device__ __forceinline__ uint32_t mad24u(uint32_t a, uint32_t b, uint32_t c) {
-    uint32_t d;
-    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
-    return d;
-}
-
 // a * b + c on sign-extended 24-bit operands (v_mad_i32_i24, full rate), low 32
 // bits: the modulo-2^32 product of operands in [-2^23, 2^23)
 __device__ __forceinline__ uint32_t mad24s(uint32_t a, uint32_t b, uint32_t c) {
@@ -569,16 +562,22 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         }
         z.live = true;
         z.raw = mode == 2;
+        // a RAW stream that a RAW-only wave of a sum (or of moments on a detector
+        // of at most 256 per side) reads with whole-wave loads: no prefetch here,
+        // since the in-order load counter would make the first wait of that form
+        // wait for all of it
+        const bool raw_whole = (OP == Op::Sum || OP == Op::Moments) && K == 1 && raw_block && z.raw &&
+                               (OP == Op::Sum || (r.det_cols <= 256 && r.P / r.det_cols <= 256));
         if (half == 2) {
             // resume where the first half ends: a RAW stream at its value kSplit, a
             // RANS stream at its split point (state, byte offset from the stream start)
             const uint64_t si = 2 * ((uint64_t)b * r.P + z.p);
             const uint32_t off = z.raw ? 2u + kSplit * (WIDE ? 2u : 1u) : r.split[si + 1];
-            touched += touch_stream(rs, z.org + off, z.len > off ? z.len - off : 0u);
+            if (!raw_whole) touched += touch_stream(rs, z.org + off, z.len > off ? z.len - off : 0u);
             bbits_init(z.s, rs, z.org + off);
             if (!z.raw) z.x = r.split[si];
         } else {
-            touched += touch_stream(rs, z.org, z.len);
+            if (!raw_whole) touched += touch_stream(rs, z.org, z.len);
             bbits_init(z.s, rs, z.org);
             pop16(z.s);  // header
             if (mode == 1) {
@@ -867,24 +866,28 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             const bool split = r.det_cols > 256 || r.P / r.det_cols > 256;
             const uint32_t j0 = half == 2 ? kSplit : 0u, nsteps = half == 0 ? n : (half == 1 ? kSplit : n - kSplit);
             if (OP == Op::Sum || !split) {
-                // The wave reads its streams one at a time, all lanes together:
-                // lane l loads the 8 values of scans [8 l, 8 l + 8) of the stream's
-                // range (one 8 W-byte load and the next dword, 4-byte aligned and
-                // shifted into place), so a load covers up to 512 W consecutive
-                // bytes. A lane keeps the totals of its own 8 scans over all the
-                // wave's streams, so no reduction across lanes is needed. Over at most 64
-                // streams, a moment total stays below 2^32 while both detector
-                // dimensions are at most 256. Streams are taken in lane order
-                // (scalar bit scan, offsets read from their lanes), each one's
-                // loads issued two streams ahead; past the last stream the loads
-                // fall outside the buffer and add zeros.
+                // The wave reads its streams together: a stream's range of nsteps
+                // scans takes G = 64, 32 or 16 lanes (8 scans each; enough for
+                // nsteps), so one load instruction covers 64 / G streams. Lane l
+                // loads the 8 values of scans [8 (l mod G), 8 (l mod G) + 8) of its
+                // group's stream (one 8 W-byte load and the next dword, 4-byte
+                // aligned and shifted into place), and keeps the totals of those 8
+                // scans over all the streams of its group: no reduction across
+                // lanes is needed. Over at most 64 streams, a moment total stays
+                // below 2^32 while both detector dimensions are at most 256.
+                // Streams are taken in lane order (a scalar bit scan; offsets,
+                // rows and columns read from their lanes), each one's loads issued
+                // two iterations ahead; past the last stream the loads fall
+                // outside the buffer and add zeros.
                 constexpr uint32_t E = 8;       // values per lane per stream
                 constexpr int NW = 2 * (int)W;  // their dwords
+                const uint32_t G = nsteps > 256 ? 64u : (nsteps > 128 ? 32u : 16u);
+                const uint32_t gl = lane & (G - 1), grp = lane / G, ng = 64u / G;
                 const uint32_t span = nsteps * W;
                 uint32_t km[NW];
 #pragma unroll
                 for (int i = 0; i < NW; i++) {
-                    const int rem = (int)span - (int)(8u * W * lane + 4u * (uint32_t)i);
+                    const int rem = (int)span - (int)(8u * W * gl + 4u * (uint32_t)i);
                     km[i] = rem >= 4 ? ~0u : (rem <= 0 ? 0u : (1u << (8 * rem)) - 1u);
                 }
                 uint32_t a0[E], ar[OP == Op::Moments ? E : 1], ac[OP == Op::Moments ? E : 1];
@@ -902,23 +905,29 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 struct Pick {
                     uint32_t vs, sh, kr, kc;
                 };
+                // the next stream of each group, in this lane's registers
                 auto pick = [&]() {
                     Pick s{0x80000000u, 0u, 0u, 0u};
-                    if (left) {
+#pragma unroll
+                    for (uint32_t g = 0; g < 4; g++) {
+                        if (g >= ng || !left) break;
                         const int l = (int)__builtin_ctzll(left);
                         left &= left - 1;
                         const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)so, l);
-                        s.vs = o & ~3u;
-                        s.sh = (o & 3u) * 8u;
+                        const bool mine = grp == g;
+                        s.vs = mine ? o & ~3u : s.vs;
+                        s.sh = mine ? (o & 3u) * 8u : s.sh;
                         if constexpr (OP == Op::Moments) {
-                            s.kr = (uint32_t)__builtin_amdgcn_readlane((int)kr[0], l);
-                            s.kc = (uint32_t)__builtin_amdgcn_readlane((int)kc[0], l);
+                            const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)kr[0], l);
+                            const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)kc[0], l);
+                            s.kr = mine ? a : s.kr;
+                            s.kc = mine ? c : s.kc;
                         }
                     }
                     return s;
                 };
                 auto load = [&](uint32_t (&d)[NW + 1], const Pick &s) {
-                    const uint32_t o = s.vs + 8u * W * lane;
+                    const uint32_t o = s.vs + 8u * W * gl;
                     if constexpr (WIDE) {
                         const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
                         d[0] = v[0];
@@ -942,8 +951,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                             const uint32_t v = WIDE ? __builtin_amdgcn_ubfe(e, 16 * q, 16) : __builtin_amdgcn_ubfe(e, 8 * q, 8);
                             a0[t] += v;
                             if constexpr (OP == Op::Moments) {
-                                ar[t] = mad24u(v, s.kr, ar[t]);
-                                ac[t] = mad24u(v, s.kc, ac[t]);
+                                ar[t] = mad24(v, s.kr, ar[t]);
+                                ac[t] = mad24(v, s.kc, ac[t]);
                             }
                         }
                     }
@@ -952,7 +961,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 Pick sA = pick(), sB = pick(), sC;
                 load(dA, sA);
                 load(dB, sB);
-                for (uint32_t i = 0; i < nl; i += 3) {
+                for (uint32_t i = 0; i < nl; i += 3 * ng) {
                     sC = pick();
                     load(dC, sC);
                     add(dA, sA);
@@ -965,7 +974,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 }
 #pragma unroll
                 for (uint32_t t = 0; t < E; t++) {
-                    const uint32_t j = lane * E + t;
+                    const uint32_t j = gl * E + t;
                     if (j >= nsteps) continue;
                     if (a0[t]) atomicAdd(&pt.m0[j0 + j], a0[t]);
                     if constexpr (OP == Op::Moments) {
