@@ -277,31 +277,36 @@ __device__ __forceinline__ bool lane_writes() {
 // the 8 lanes of the head levels below 2^31 for any detector (dim <= 1024).
 // Larger detectors split the head's sums into 16-bit halves for the tail
 // levels (8 x 2^16 < 2^32) and recombine them in 64 bits.
-template <int CH, Op OP>
+// ROWU: every pixel of the wave lies in detector row kru, so the row moment of
+// a scan is kru times its total and ar is not used.
+template <int CH, Op OP, bool ROWU = false>
 __device__ __forceinline__ void chunk_to_lds(uint32_t (&a0)[CH], uint32_t (&ar)[OP == Op::Moments ? CH : 1],
                                              uint32_t (&ac)[OP == Op::Moments ? CH : 1], uint32_t my, bool writer,
                                              bool split, uint32_t *m0, unsigned long long *mr,
-                                             unsigned long long *mc) {
+                                             unsigned long long *mc, uint32_t kru = 0) {
     const uint32_t t0 = wave_transpose_sum<CH>(a0);
     if (writer && t0) atomicAdd(&m0[my], t0);
     if constexpr (OP == Op::Moments) {
         // the head levels add at most 8 lanes' terms: below 2^31 for any detector
         // (up to 1024 per side); only the tail needs 16-bit halves on large ones
-        transpose_head<CH>(ar);
+        if constexpr (!ROWU) transpose_head<CH>(ar);
         transpose_head<CH>(ac);
-        unsigned long long tr, tc;
+        unsigned long long tr = 0, tc;
+        if constexpr (ROWU) tr = (unsigned long long)t0 * kru;
         if (!split) {
-            tr = transpose_tail<CH>(ar);
+            if constexpr (!ROWU) tr = transpose_tail<CH>(ar);
             tc = transpose_tail<CH>(ac);
         } else {
             constexpr int R = CH / 8;
             uint32_t lo[R], hi[R];
+            if constexpr (!ROWU) {
 #pragma unroll
-            for (int i = 0; i < R; i++) {
-                lo[i] = ar[i] & 0xFFFFu;
-                hi[i] = ar[i] >> 16;
+                for (int i = 0; i < R; i++) {
+                    lo[i] = ar[i] & 0xFFFFu;
+                    hi[i] = ar[i] >> 16;
+                }
+                tr = ((unsigned long long)transpose_tail<CH>(hi) << 16) + transpose_tail<CH>(lo);
             }
-            tr = ((unsigned long long)transpose_tail<CH>(hi) << 16) + transpose_tail<CH>(lo);
 #pragma unroll
             for (int i = 0; i < R; i++) {
                 lo[i] = ac[i] & 0xFFFFu;
@@ -595,6 +600,21 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             kc[k] = sl[k].p - kr[k] * r.det_cols;
         }
     }
+    // moments of a wave whose pixels share one detector row (a wave of
+    // consecutive pixels that does not cross a row end): the row moment comes
+    // from the per-scan totals, one multiply per scan instead of one per value
+    bool rowu = false;
+    uint32_t kru = 0;
+    if constexpr (OP == Op::Moments) {
+        const uint64_t lv = __builtin_amdgcn_ballot_w64(sl[0].live);
+        if (lv) {
+            kru = (uint32_t)__builtin_amdgcn_readlane((int)kr[0], (int)__builtin_ctzll(lv));
+            bool diff = false;
+#pragma unroll
+            for (int k = 0; k < K; k++) diff |= sl[k].live && kr[k] != kru;
+            rowu = !__builtin_amdgcn_ballot_w64(diff);
+        }
+    }
 
     // byte-rANS decode step (FORMAT 2.3). The block table holds two words per
     // slot, side by side and read by one 64-bit LDS load: f | symbol << 24
@@ -670,7 +690,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         for (int k = 0; k < K; k++) bbits_refill(sl[k].s, rs);
     };
 
-    auto run = [&](auto form) {
+    auto run = [&](auto form, auto rowu) {
+        constexpr bool ROWU = decltype(rowu)::value;  // moments of a wave inside one detector row
         // the escape form refills after every step: a step then starts with at
         // least 33 bits, enough for a renormalisation word and a literal, so an
         // escape reads its literal without a load of its own
@@ -804,14 +825,15 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                                 ar[jj] = mad24(v[k], kr[k], ar[jj]);
                                 ac[jj] = mad24(v[k], kc[k], ac[jj]);
                             } else {
-                                ar[jj] += __umul24(v[k], kr[k]);
+                                if constexpr (!ROWU) ar[jj] += __umul24(v[k], kr[k]);
                                 ac[jj] += __umul24(v[k], kc[k]);
                             }
                         }
                     }
                     // materialise the sums here: deferring them to the chunk end keeps every step's table entry live
                     asm volatile("" : "+v"(a0[jj]));
-                    if constexpr (OP == Op::Moments) asm volatile("" : "+v"(ar[jj]), "+v"(ac[jj]));
+                    if constexpr (OP == Op::Moments && !ROWU) asm volatile("" : "+v"(ar[jj]), "+v"(ac[jj]));
+                    if constexpr (OP == Op::Moments && ROWU) asm volatile("" : "+v"(ac[jj]));
                     if (every || (jj & 1)) refill();
                     // keep the scheduler's interleaving to the K independent slots of one step
                     __builtin_amdgcn_sched_barrier(0);
@@ -821,8 +843,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     const uint32_t t0 = wave_transpose_sum<CH>(a0) + cw;
                     if (writer && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + c * CH + my], t0);
                 } else {
-                    chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + j0 + c * CH, pt.mr + j0 + c * CH,
-                                         pt.mc + j0 + c * CH);
+                    chunk_to_lds<CH, OP, ROWU>(a0, ar, ac, my, writer, split, pt.m0 + j0 + c * CH,
+                                               pt.mr + j0 + c * CH, pt.mc + j0 + c * CH, kru);
                 }
             }
             // ragged end of a final partial block (never split): one scan at a time, reduced per scan
@@ -1113,14 +1135,24 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         idle |= !sl[k].live;
     }
     const bool idle_ok = (tbl[0] >> 24) == 0u;
+    auto run_rows = [&](auto form) {
+        if constexpr (OP == Op::Moments) {
+            if (rowu)
+                run(form, std::true_type{});
+            else
+                run(form, std::false_type{});
+        } else {
+            run(form, std::false_type{});
+        }
+    };
     if (__builtin_amdgcn_ballot_w64(raw || (idle && !idle_ok))) {
-        run(std::integral_constant<int, kMixed>{});
+        run(std::integral_constant<int, kMixed>{}, std::false_type{});
     } else if (WIDE && (tbl[2 * 4095] >> 24) == 255u) {
         // symbols are laid out in increasing order, so the last slot holds the
         // largest coded symbol: 255 there means escapes can occur
-        run(std::integral_constant<int, kEscape>{});
+        run_rows(std::integral_constant<int, kEscape>{});
     } else {
-        run(std::integral_constant<int, kPlain>{});
+        run_rows(std::integral_constant<int, kPlain>{});
     }
     asm volatile("" ::"v"(touched));
     if constexpr (OP == Op::Split) {
