@@ -302,6 +302,32 @@ def test_raw_streams_fill_waves(dtype):
         res.finish()
 
 
+@pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
+@pytest.mark.parametrize("S", [589, 712])
+def test_raw_streams_short_final_block(dtype, S):
+    """A final block of 77 scans (odd: a padded uint8 stream) or 200 scans:
+    RAW-only waves read several streams per load (four for 77 scans, two for
+    200), each stream cut by the per-lane byte mask at the block's end."""
+    rng = np.random.default_rng(S)
+    dr = dc = 16
+    P = dr * dc
+    maxv = 255 if dtype == np.uint8 else 65535
+    c = rng.poisson(0.4, size=(S, P)).astype(dtype)
+    raw = np.sort(rng.choice(P, 150, replace=False))
+    c[:, raw] = rng.integers(0, maxv + 1, size=(S, raw.size)).astype(dtype)
+    blob = q().encode(c, 1, S, dr, dc)
+    w = synth.Workload("raw_short", 1, S, dr, dc, 1 if dtype == np.uint8 else 2, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    masks = {"all": np.ones(P, np.uint8), "disk": synth.disk_mask(dr, dc, 8, 8, 5)}
+    with q().Resident(blob) as res:
+        assert res.info.mode_counts[2] >= 2 * raw.size
+        for name, m in masks.items():
+            for k in (1, 2):
+                got = u(res.masked_sum(m, block_stride=k))
+                assert np.array_equal(got, oracle.masked_sum(c, m, stride=k)), (name, k)
+            check_com(res, c, w, m, None)
+        res.finish()
+
+
 def test_raw_streams_without_a_plan():
     """A 257 x 257 detector (more pixels than a query plan covers): items are
     pixel tiles, and RAW streams (30 %, uniform uint16) are still ordered first
