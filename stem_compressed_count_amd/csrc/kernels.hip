@@ -1343,6 +1343,20 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             kc[k] = sl[k].p - kr[k] * r.det_cols;
         }
     }
+    // moments of a wave whose pixels share one detector row: the row moment
+    // comes from the per-scan totals (as in the byte-rANS tile)
+    bool rowu = false;
+    uint32_t kru = 0;
+    if constexpr (OP == Op::Moments) {
+        const uint64_t lv = __builtin_amdgcn_ballot_w64((sl[0].meta & 7u) != 7u);
+        if (lv) {
+            kru = (uint32_t)__builtin_amdgcn_readlane((int)kr[0], (int)__builtin_ctzll(lv));
+            bool diff = false;
+#pragma unroll
+            for (int k = 0; k < K; k++) diff |= (sl[k].meta & 7u) != 7u && kr[k] != kru;  // mode 7: idle
+            rowu = !__builtin_amdgcn_ballot_w64(diff);
+        }
+    }
 
     // One pair step of every slot: window-relative values for PAIRED slots,
     // absolute values for RAW slots, zeros for idle ones. Two forms, chosen
@@ -1417,7 +1431,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         }
     };
 
-    auto run = [&](auto form) {
+    auto run = [&](auto form, auto rowu) {
+        constexpr bool ROWU = decltype(rowu)::value;  // moments of a wave inside one detector row
         if constexpr (is_region(OP)) {
             auto rw = region_walk<is_frames(OP)>(r, b, ra);
             for (uint32_t t = 0; t < kBlk / 2; t++) {
@@ -1496,24 +1511,27 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                             // window-relative values lie in [-65535, 65535] (an escape below
                             // the window is negative) and pixel coordinates below 1024: signed
                             // 24-bit products give the same sums modulo 2^32 at full rate
-                            ar[2 * tt] = mad24s(v0[k], kr[k], ar[2 * tt]);
-                            ar[2 * tt + 1] = mad24s(v1[k], kr[k], ar[2 * tt + 1]);
+                            if constexpr (!ROWU) {
+                                ar[2 * tt] = mad24s(v0[k], kr[k], ar[2 * tt]);
+                                ar[2 * tt + 1] = mad24s(v1[k], kr[k], ar[2 * tt + 1]);
+                            }
                             ac[2 * tt] = mad24s(v0[k], kc[k], ac[2 * tt]);
                             ac[2 * tt + 1] = mad24s(v1[k], kc[k], ac[2 * tt + 1]);
                         }
                     }
                     // materialise the sums here (see the byte-rANS tile)
                     asm volatile("" : "+v"(a0[2 * tt]), "+v"(a0[2 * tt + 1]));
-                    if constexpr (OP == Op::Moments)
+                    if constexpr (OP == Op::Moments && !ROWU)
                         asm volatile("" : "+v"(ar[2 * tt]), "+v"(ar[2 * tt + 1]), "+v"(ac[2 * tt]), "+v"(ac[2 * tt + 1]));
+                    if constexpr (OP == Op::Moments && ROWU) asm volatile("" : "+v"(ac[2 * tt]), "+v"(ac[2 * tt + 1]));
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (OP == Op::Index) {
                     const uint32_t t0 = wave_transpose_sum<CH>(a0) + cw;
                     if (writer && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + c * CH + my], t0);
                 } else {
-                    chunk_to_lds<CH, OP>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH,
-                                         pt.mc + c * CH);
+                    chunk_to_lds<CH, OP, ROWU>(a0, ar, ac, my, writer, split, pt.m0 + c * CH, pt.mr + c * CH,
+                                               pt.mc + c * CH, kru);
                 }
             }
         }
@@ -1522,10 +1540,20 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     bool raw = false;
 #pragma unroll
     for (int k = 0; k < K; k++) raw |= (sl[k].meta & 7u) == 4u;
+    auto run_rows = [&](auto form) {
+        if constexpr (OP == Op::Moments) {
+            if (rowu)
+                run(form, std::true_type{});
+            else
+                run(form, std::false_type{});
+        } else {
+            run(form, std::false_type{});
+        }
+    };
     if (__builtin_amdgcn_ballot_w64(raw))
-        run(std::integral_constant<int, kPMixed>{});
+        run_rows(std::integral_constant<int, kPMixed>{});
     else
-        run(std::integral_constant<int, kPPlain>{});
+        run_rows(std::integral_constant<int, kPPlain>{});
     asm volatile("" ::"v"(touched));
     // end checks (FORMAT 3.3-3.4)
 #pragma unroll
