@@ -63,6 +63,9 @@ def _load():
         lib.orc_reconstruct.argtypes = [vp, u64, ctypes.c_double, ctypes.c_double, vp]
         lib.orc_reconstruct.restype = None
         lib.orc_pair_models.argtypes = [vp, vp, vp]
+        lib.orc_pair_decode_table.argtypes = [ctypes.c_int, vp, vp, vp]
+        lib.orc_pair_encode_steps.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        lib.orc_paired_size.argtypes = [vp, u32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_uint64)]
         _lib = lib
     return _lib
 
@@ -328,6 +331,41 @@ def pair_models():
     use = np.empty(32, dtype=np.uint32)
     _load().orc_pair_models(n.ctypes.data, a0.ctypes.data, use.ctypes.data)
     return n, a0, use
+
+
+def pair_decode_table(m):
+    """Decode entries of pair model m (FORMAT 3.2): (symbol, nbits, next-state base) per state, 1024 each."""
+    sym = np.empty(1024, dtype=np.uint16)
+    nb = np.empty(1024, dtype=np.uint8)
+    nx = np.empty(1024, dtype=np.uint16)
+    rc = _load().orc_pair_decode_table(m, sym.ctypes.data, nb.ctypes.data, nx.ctypes.data)
+    if rc:
+        raise OracleError(rc, "pair_decode_table")
+    return sym, nb, nx
+
+
+def pair_encode_steps(m, i):
+    """The encoder step of pair symbol i of model m from every state x = 1024..2047:
+    (emitted bit count, emitted bits, new state - 1024), each indexed by x - 1024."""
+    k = np.empty(1024, dtype=np.uint32)
+    bits = np.empty(1024, dtype=np.uint32)
+    st = np.empty(1024, dtype=np.uint32)
+    rc = _load().orc_pair_encode_steps(m, i, k.ctypes.data, bits.ctypes.data, st.ctypes.data)
+    if rc:
+        raise OracleError(rc, "pair_encode_steps")
+    return k, bits, st
+
+
+def paired_size(values, dtype):
+    """(model, bytes) of the PAIRED form of one 512-value stream: the model the static
+    cost picks and the stream size with its header (FORMAT 3.4)."""
+    v = np.ascontiguousarray(values, dtype=np.uint32)
+    assert v.size == BLOCK
+    m, n = ctypes.c_int(), ctypes.c_uint64()
+    rc = _load().orc_paired_size(v.ctypes.data, dtype, ctypes.byref(m), ctypes.byref(n))
+    if rc:
+        raise OracleError(rc, "paired_size")
+    return m.value, n.value
 
 
 # ---------------------------------------------------------------------------

@@ -409,20 +409,28 @@ static int paired_cost(const pair_model *pm, const uint32_t *v, uint32_t dtype, 
     return 1;
 }
 
+/* One encoder step of FORMAT 3.2: pair symbol i from encoder state x in
+ * [1024, 2048). k = the fewest low bits of x whose removal leaves x >> k below
+ * 2*n[i]; those bits are emitted; the new state is 1024 plus the state that
+ * holds occurrence (x >> k) - n[i] of symbol i (occurrences counted in
+ * increasing state order). */
+static uint32_t encode_step(const pair_model *pm, int i, uint32_t x, uint32_t *bits, uint32_t *k_out) {
+    uint32_t ni = pm->n[i];
+    int k = 0;
+    while ((x >> k) >= 2 * ni) k++;
+    *bits = x & ((1u << k) - 1);
+    *k_out = (uint32_t)k;
+    uint32_t y = x >> k;
+    return TL + pm->occ[i][y - ni];
+}
+
 /* PAIRED code section bytes (padded to 16 bits); returns byte count */
 static uint64_t paired_encode(const pair_model *pm, const uint32_t *v, uint32_t dtype, uint8_t **out) {
     uint32_t chunk_val[256], chunk_nb[256];
     uint32_t x = TL;
     for (int t = 255; t >= 0; t--) {
         int a = window_sym(v[2 * t], pm->a0, pm->in_use), b = window_sym(v[2 * t + 1], pm->a0, pm->in_use);
-        int i = 16 * a + b;
-        uint32_t ni = pm->n[i];
-        int k = 0;
-        while ((x >> k) >= 2 * ni) k++;
-        chunk_val[t] = x & ((1u << k) - 1);
-        chunk_nb[t] = (uint32_t)k;
-        uint32_t y = x >> k;
-        x = TL + pm->occ[i][y - ni];
+        x = encode_step(pm, 16 * a + b, x, &chunk_val[t], &chunk_nb[t]);
     }
     bitw w = {0, 0, 0};
     int lit = dtype == 2 ? 16 : 8;
@@ -435,6 +443,58 @@ static uint64_t paired_encode(const pair_model *pm, const uint32_t *v, uint32_t 
     while (w.nbits % 16) bw_put(&w, 0, 1);
     *out = w.bytes;
     return w.nbits / 8;
+}
+
+/* Decode table of pair model m (FORMAT 3.2): for every state X, the pair
+ * symbol, the code length and the next-state base. */
+int orc_pair_decode_table(int m, uint16_t *sym, uint8_t *nbits, uint16_t *newX) {
+    if (m < 0 || m > 31) return ORC_ERR_ARG;
+    pair_model *pm = (pair_model *)malloc(sizeof(pair_model));
+    if (!pm) return ORC_ERR_OOM;
+    build_model(m, pm);
+    decode_entries(pm->n, pm->spread, sym, nbits, newX);
+    free(pm);
+    return ORC_OK;
+}
+
+/* The encoder step of pair symbol i of model m from every state x in
+ * [1024, 2048): emitted bit count, emitted bits and the new state (x - 1024
+ * form, i.e. the decoder's state), index x - 1024. */
+int orc_pair_encode_steps(int m, int i, uint32_t *k, uint32_t *bits, uint32_t *state) {
+    if (m < 0 || m > 31 || i < 0 || i > 255) return ORC_ERR_ARG;
+    pair_model *pm = (pair_model *)malloc(sizeof(pair_model));
+    if (!pm) return ORC_ERR_OOM;
+    build_model(m, pm);
+    if (pm->n[i] == 0) {
+        free(pm);
+        return ORC_ERR_ARG;
+    }
+    for (uint32_t x = TL; x < 2 * TL; x++) state[x - TL] = encode_step(pm, i, x, &bits[x - TL], &k[x - TL]) - TL;
+    free(pm);
+    return ORC_OK;
+}
+
+/* Size of the PAIRED stream (header included) of 512 values with the model
+ * the format's static cost picks (FORMAT 3.4), and that model. */
+int orc_paired_size(const uint32_t *v, uint32_t dtype, int *model, uint64_t *bytes) {
+    pair_model *models = (pair_model *)malloc(sizeof(pair_model) * 32);
+    if (!models) return ORC_ERR_OOM;
+    int best_m = -1;
+    uint64_t best_cost = 0;
+    for (int m = 0; m < 32; m++) {
+        uint64_t cst;
+        build_model(m, &models[m]);
+        if (paired_cost(&models[m], v, dtype, &cst) && (best_m < 0 || cst < best_cost)) {
+            best_m = m;
+            best_cost = cst;
+        }
+    }
+    uint8_t *code = NULL;
+    *model = best_m;
+    *bytes = 2 + paired_encode(&models[best_m], v, dtype, &code);
+    free(code);
+    free(models);
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------------ */

@@ -39,31 +39,38 @@ def read_golden(name):
     return vals, freq, stream, counts, extra
 
 
-def pack_container(scan_rows, scan_cols, det_rows, det_cols, dtype, table, stream_list):
-    """A one-block byte-rANS container laid out by hand from FORMAT 1.1-1.3."""
+def pack_container(scan_rows, scan_cols, det_rows, det_cols, dtype, table, stream_list, layout=0):
+    """A one-block container laid out by hand from FORMAT 1.1-1.3.
+
+    Layout 0 takes the block's frequency table as {symbol: f}; layout 1 takes
+    the 32 x 256 pair-model counts (a uint16 array) for its table section."""
     P = det_rows * det_cols
     G = (P + 31) // 32
     S = scan_rows * scan_cols
-    assert S <= 512
+    assert S <= 512 and (layout == 0 or S == 512)
 
     def up(o):
         return (o + 255) // 256 * 256
 
     dir_off = 256
     table_off = up(dir_off + 16)
-    gbase_off = up(table_off + 512)
+    gbase_off = up(table_off + (512 if layout == 0 else 2 * 32 * 256))
     rel_off = up(gbase_off + 4 * G)
     payload_off = up(rel_off + 64 * G)
     payload = b"".join(stream_list)
     total = payload_off + len(payload)
     blob = bytearray(total)
     blob[0:8] = b"QSCRES01"
-    blob[8:8 + 16] = b"qsc-byte-rans-v1"
-    struct.pack_into("<10I", blob, 40, 1, 0, scan_rows, scan_cols, det_rows, det_cols, dtype, 512, 1, 0)
+    tag = b"qsc-byte-rans-v1" if layout == 0 else b"qsc-paired-v1"
+    blob[8:8 + len(tag)] = tag
+    struct.pack_into("<10I", blob, 40, 1, layout, scan_rows, scan_cols, det_rows, det_cols, dtype, 512, 1, 0)
     struct.pack_into("<8Q", blob, 80, dir_off, table_off, gbase_off, rel_off, payload_off, len(payload), 0, total)
     struct.pack_into("<QII", blob, dir_off, 0, S, len(payload))
-    for s, f in table.items():
-        struct.pack_into("<H", blob, table_off + 2 * s, f)
+    if layout == 0:
+        for s, f in table.items():
+            struct.pack_into("<H", blob, table_off + 2 * s, f)
+    else:
+        blob[table_off:table_off + 2 * 32 * 256] = np.asarray(table, dtype="<u2").tobytes()
     starts = np.cumsum([0] + [len(x) for x in stream_list])
     for g in range(G):
         gb = int(starts[32 * g])
@@ -108,6 +115,171 @@ def test_golden_pair_model0():
     for i, c in counts.items():
         want[i] = c
     assert np.array_equal(n[0], want)
+
+
+def read_runs_golden(name):
+    """A golden of value runs and stream bytes: 'run v n', 'hex b..', 'repeat k b..', '<key> ints'."""
+    vals, stream, extra = [], bytearray(), {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        key, *rest = line.split()
+        if key == "run":
+            vals += [int(rest[0])] * int(rest[1])
+        elif key == "hex":
+            stream += bytes(int(b, 16) for b in rest)
+        elif key == "repeat":
+            stream += bytes(int(b, 16) for b in rest[1:]) * int(rest[0])
+        else:
+            extra[key] = [int(v) for v in rest]
+    return vals, bytes(stream), extra
+
+
+def paired_golden_blob(stream):
+    n, _, _ = oracle.pair_models()
+    return pack_container(1, 512, 1, 1, 2, n, [stream], layout=1)
+
+
+def test_golden_paired_stream_decodes():
+    vals, stream, _ = read_runs_golden("paired_u16_model0.txt")
+    assert len(vals) == 512 and len(stream) == 2 + 326
+    assert oracle.decode(paired_golden_blob(stream)).ravel().tolist() == vals
+
+
+def test_golden_paired_stream_end_checks():
+    """FORMAT 3.3 end check on the hand-worked stream: each change below breaks it."""
+    _, stream, _ = read_runs_golden("paired_u16_model0.txt")
+    cases = {}
+    b = bytearray(stream)
+    b[-1] |= 0x80  # a one in the zero padding
+    cases["pad bit"] = bytes(b)
+    cases["16 spare bits"] = stream + bytes(2)  # a whole spare word after the pad
+    cases["shortened"] = stream[:-2]  # the last literal loses its top bits and the pad
+    b = bytearray(stream)
+    # the last literal (bits 2583-2598 of the section) 2 -> 1: a value in use inside the window
+    bit = 16 + 2583  # 2 header bytes
+    b[bit // 8] ^= 1 << (bit % 8)
+    b[(bit + 1) // 8] ^= 1 << ((bit + 1) % 8)
+    cases["in-window literal"] = bytes(b)
+    b = bytearray(stream)
+    # the final 10 bits read at t = 255 (bits 2573-2582) 0 -> 1: the state does not return to 0
+    bit = 16 + 2573
+    b[bit // 8] ^= 1 << (bit % 8)
+    cases["final state"] = bytes(b)
+    b = bytearray(stream)
+    b[1] |= 0x01  # reserved header bit 8
+    cases["reserved bit"] = bytes(b)
+    for name, bad in cases.items():
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.decode(paired_golden_blob(bad))
+        assert e.value.code == oracle.ERR_MALFORMED, name
+
+
+def test_pair_tables_every_state_decodes_to_a_valid_next_state():
+    """FORMAT 3.2 for all 32 models: each state's entry (symbol, nbits, next-state
+    base) leads into [0, 1024); per symbol the ranges [newX, newX + 2^nbits)
+    tile [0, 1024) exactly (so every encoder state has exactly one decoder
+    predecessor); each symbol holds n[i] states; and the encoder step of every
+    symbol from every state x in [1024, 2048) lands on a state whose entry has
+    that symbol, emits that entry's nbits, and decodes back to x - 1024."""
+    counts, _, _ = oracle.pair_models()
+    for m in range(32):
+        sym, nb, nx = oracle.pair_decode_table(m)
+        n = counts[m]
+        assert np.array_equal(np.bincount(sym, minlength=256), n), m
+        assert nb.max() <= 10
+        assert np.all(nx.astype(np.int64) + (1 << nb.astype(np.int64)) <= 1024), m
+        for i in np.nonzero(n)[0]:
+            st = np.nonzero(sym == i)[0]
+            lo = nx[st].astype(np.int64)
+            hi = lo + (1 << nb[st].astype(np.int64))
+            order = np.argsort(lo)
+            assert lo[order][0] == 0 and hi[order][-1] == 1024, (m, i)
+            assert np.array_equal(lo[order][1:], hi[order][:-1]), (m, i)
+            k, bits, to = oracle.pair_encode_steps(m, int(i))
+            assert np.all(sym[to] == i), (m, i)
+            assert np.array_equal(nb[to].astype(np.uint32), k), (m, i)
+            assert np.all(bits < (1 << k))
+            assert np.array_equal(nx[to].astype(np.int64) + bits, np.arange(1024)), (m, i)
+
+
+def table_golden_cases(name):
+    """Cases of a table golden: (histogram, expected frequencies) per 'case' (one if none)."""
+    cases, h, f = [], {}, {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        key, *rest = line.split()
+        if key == "case":
+            if h:
+                cases.append((h, f))
+            h, f = {}, {}
+            continue
+        r = [int(v) for v in rest]
+        if key == "hist":
+            h[r[0]] = r[1]
+        elif key == "histrange":
+            h.update({s: r[2] for s in range(r[0], r[1] + 1)})
+        elif key == "freq":
+            f[r[0]] = r[1]
+        elif key == "freqrange":
+            f.update({s: r[2] for s in range(r[0], r[1] + 1)})
+    cases.append((h, f))
+    return cases
+
+
+def block_with_histogram(h, seed):
+    """One uint8 block of 9 non-constant streams x 512 scans whose symbols have histogram h."""
+    vals = np.concatenate([np.full(c, s, np.uint8) for s, c in sorted(h.items())])
+    assert vals.size == 9 * 512
+    rng = np.random.default_rng(seed)
+    c = rng.permutation(vals).reshape(512, 9)
+    assert not any((c[:, p] == c[0, p]).all() for p in range(9))
+    return c
+
+
+@pytest.mark.parametrize("name", ["rans_table_excess.txt", "rans_table_deficit.txt"])
+def test_golden_rans_table_rules(name):
+    """FORMAT 2.2 steps 3 and 4 on hand-worked histograms (excess with a tie; deficit
+    to the largest h, not the largest remainder; deficit with a tie)."""
+    for j, (h, f) in enumerate(table_golden_cases(name)):
+        c = block_with_histogram(h, seed=40 + j)
+        blob = oracle.encode(c, 1, 512, 3, 3)
+        hd = oracle.header(blob)
+        got = np.frombuffer(blob[hd["table_off"]:hd["table_off"] + 512], dtype=np.uint16)
+        want = np.zeros(256, np.uint16)
+        for s, v in f.items():
+            want[s] = v
+        assert np.array_equal(got, want), (name, j)
+        assert np.array_equal(oracle.decode(blob), c)
+
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.uint8])
+def test_mode_choice_at_the_sparse_paired_boundary(dtype):
+    """FORMAT 3.4: PAIRED replaces SPARSE only when it is at least 2 bytes smaller.
+    Stream sizes are even, so gaps of 0 and 2 bytes fix the rule. With model 0 a
+    count of 1 is in the window and a count of 2 escapes to a literal; a lone 2
+    codes in 10 + 10 + literal + a few one-bit (0,0) steps, under 48 bits for
+    u16, so PAIRED is 8 bytes, SPARSE's size (a tie); a lone 1 saves the
+    literal and codes in 6 bytes."""
+    lit = 2 if dtype == np.uint16 else 1
+    cases = [([(100, 2)], 2), ([(100, 1)], 3), ([(100, 1), (300, 2)], 3), ([(100, 2), (300, 2)], 2)]
+    for nz, mode in cases:
+        v = np.zeros(512, np.uint32)
+        for pos, val in nz:
+            v[pos] = val
+        nnz = len(nz)
+        sparse = 4 + 2 * nnz + (2 * nnz if lit == 2 else nnz + nnz % 2)
+        model, paired = oracle.paired_size(v, 2 if lit == 2 else 1)
+        assert model == 0
+        assert sparse - paired == (2 if mode == 3 else 0), (nz, sparse, paired)
+        blob = oracle.encode(v.astype(dtype).reshape(512, 1), 1, 512, 1, 1, layout=1)
+        hd = oracle.header(blob)
+        assert stream_modes(blob)[0][0] & 7 == mode, nz
+        assert hd["payload_bytes"] == (paired if mode == 3 else sparse), nz
+        assert np.array_equal(oracle.decode(blob).ravel(), v)
 
 
 def test_pair_model_invariants():
