@@ -273,6 +273,22 @@ class Resident:
             raise ValueError(f"mask must have {self.P} entries")
         return m
 
+    def _on(self, stream, *tensors):
+        """A query queued on a stream other than the current one: that stream first
+        waits for the current one (where the mask copies and new outputs were
+        made), and the tensors are marked as used there, so the caching allocator
+        does not hand their memory to other work before the query is done."""
+        import torch
+        if stream is None:
+            return
+        cur = torch.cuda.current_stream()
+        if stream.cuda_stream == cur.cuda_stream:
+            return
+        stream.wait_stream(cur)
+        for t in tensors:
+            if t is not None:
+                t.record_stream(stream)
+
     def _out(self, out, dtype, n):
         import torch
         if out is None:
@@ -286,6 +302,7 @@ class Resident:
         """Exact per-scan sums over mask & valid (int32 storage of uint32, or int64 of uint64)."""
         m = self._mask(mask)
         o = self._out(out, self.sum_dtype, self.S)
+        self._on(stream, m, o)
         self._check(lib.qsc_masked_sum(self._h, m.data_ptr(), block_stride, o.data_ptr(), _stream_handle(stream),
                                        int(wait)), "masked_sum")
         return o
@@ -296,6 +313,7 @@ class Resident:
         if prev_out.dtype != self.sum_dtype or prev_out.numel() != self.S or not prev_out.is_contiguous():
             raise ValueError(f"prev_out must be a contiguous {self.sum_dtype} tensor of {self.S} elements")
         o = self._out(out, self.sum_dtype, self.S)
+        self._on(stream, pm, m, prev_out, o)
         self._check(lib.qsc_masked_sum_delta(self._h, pm.data_ptr(), prev_out.data_ptr(), m.data_ptr(), block_stride,
                                              o.data_ptr(), _stream_handle(stream), int(wait)), "masked_sum_delta")
         return o
@@ -303,6 +321,7 @@ class Resident:
     def dense_df(self, mask, out=None, stream=None, wait=True):
         m = self._mask(mask)
         o = self._out(out, self.sum_dtype, self.S)
+        self._on(stream, m, o)
         self._check(lib.qsc_dense_df(self._h, m.data_ptr(), o.data_ptr(), _stream_handle(stream), int(wait)),
                     "dense_df")
         return o
@@ -312,6 +331,7 @@ class Resident:
         m = None if mask is None else self._mask(mask)
         row = self._out(out_row, torch.float32, self.S)
         col = self._out(out_col, torch.float32, self.S)
+        self._on(stream, m, row, col)
         self._check(lib.qsc_com(self._h, None if m is None else m.data_ptr(), row.data_ptr(), col.data_ptr(),
                                 _stream_handle(stream), int(wait)), "com")
         return row, col
@@ -324,6 +344,7 @@ class Resident:
         n = (r1 - r0) * (c1 - c0) * self.P
         dt = torch.float32 if calibrated else (torch.uint8 if self.dtype == 1 else torch.int16)
         o = self._out(out, dt, n)
+        self._on(stream, o)
         self._check(lib.qsc_decode_region(self._h, r0, r1, c0, c1, 1 if calibrated else 0, o.data_ptr(),
                                           _stream_handle(stream), int(wait)), "decode_region")
         return o.view((r1 - r0) * (c1 - c0), self.P)
@@ -338,6 +359,7 @@ class Resident:
         n = max(0, min(self.S, (first_block + n_blocks) * 512) - s0) * self.P
         dt = torch.float32 if kinds[kind] else (torch.uint8 if self.dtype == 1 else torch.int16)
         o = self._out(out, dt, n)
+        self._on(stream, o)
         self._check(lib.qsc_decode_blocks(self._h, first_block, n_blocks, kinds[kind], o.data_ptr(),
                                           _stream_handle(stream), int(wait)), "decode_blocks")
         return o.view(-1, self.P)
@@ -352,6 +374,7 @@ class Resident:
                 raise ValueError(f"scan_mask must have {self.S} entries")
         s = self._out(out_sum, torch.int64, self.P)
         mean = self._out(out_mean, torch.float32, self.P)
+        self._on(stream, m, s, mean)
         self._check(lib.qsc_sum_dp(self._h, None if m is None else m.data_ptr(), block_stride, s.data_ptr(),
                                    mean.data_ptr(), _stream_handle(stream), int(wait)), "sum_dp")
         return s, mean

@@ -235,6 +235,9 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
         if ((e = dalloc(res.get(), &res->d_split, 8ull * g.n_blocks() * g.P())) != hipSuccess) return bail(e, "split points");
         if ((e = launch_split_build(d, res->d_split, strm)) != hipSuccess) return bail(e, "split points");
         if ((e = hipStreamSynchronize(strm)) != hipSuccess) return bail(e, "split points");
+        // streams are judged by the queries that decode them: whatever the
+        // build's decode flagged is not carried into the first query
+        if ((e = hipMemset(res->d_err, 0, sizeof(unsigned long long))) != hipSuccess) return bail(e, "error word");
         d.split = res->d_split;
     }
     return QSC_OK;

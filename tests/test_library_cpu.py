@@ -199,3 +199,21 @@ def test_device_encoder_bound_and_argument_errors():
     h = ctypes.c_void_p()
     assert q.lib.qsc_resident_create_device(None, 4096, None, None, ctypes.byref(h)) == q.ERR_INVALID_ARG
     assert q.lib.qsc_resident_create_device_borrow(None, 4096, 8192, None, None, ctypes.byref(h)) == q.ERR_INVALID_ARG
+
+
+def test_stream_split_and_pack_are_inverse():
+    """The tests' container editor (tests/streams.py) rebuilds a container
+    byte for byte from its streams, for both layouts and a partial group."""
+    import streams
+    rng = np.random.default_rng(12)
+    for layout, sr, sc, det in [(0, 3, 301, (7, 9)), (1, 2, 512, (5, 13))]:
+        c = rng.poisson(1.5, size=(sr * sc, det[0] * det[1])).astype(np.uint16)
+        blob = oracle.encode(c, sr, sc, det[0], det[1], layout=layout)
+        _, st = streams.split(blob)
+        assert streams.pack(blob, st) == blob
+        # a stream two bytes longer: the container stays structurally sound, and
+        # the oracle finds exactly that stream malformed
+        st[0][3] = st[0][3] + b"\0\0"
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.decode(streams.pack(blob, st))
+        assert e.value.code == oracle.ERR_MALFORMED and "block 0 pixel 3" in str(e.value)
