@@ -208,6 +208,18 @@ qsc_status qsc_masked_sum(qsc_resident *res, const uint8_t *d_mask, uint32_t blo
 qsc_status qsc_dense_df(qsc_resident *res, const uint8_t *d_mask, void *d_out, void *hip_stream, int wait);
 qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float *d_col, void *hip_stream,
                    int wait);
+/* qsc_com_noalloc: qsc_com for callers that cannot allocate device memory
+ *   (code under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc). Same arguments and results as qsc_com, but its moment
+ *   partials live in a static device buffer of 3 x 1,048,576 uint64 (24 MiB)
+ *   that each GPU holds until the process ends, so the call allocates
+ *   nothing. A resident of more than 1,048,576 scans -> INVALID_ARG. Every
+ *   call on one GPU shares that buffer: calls that overlap on a GPU (other
+ *   streams, other host threads) race and must be ordered by the caller. The
+ *   buffer keeps the last call's contents; each call clears the part it uses
+ *   first. */
+qsc_status qsc_com_noalloc(qsc_resident *res, const uint8_t *d_mask, float *d_row, float *d_col, void *hip_stream,
+                           int wait);
 qsc_status qsc_decode_region(qsc_resident *res, uint32_t r0, uint32_t r1, uint32_t c0, uint32_t c1, int out_kind,
                              void *d_out, void *hip_stream, int wait);
 qsc_status qsc_decode_blocks(qsc_resident *res, uint32_t first_block, uint32_t n_blocks, int out_kind, void *d_out,

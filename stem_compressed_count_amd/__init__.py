@@ -14,6 +14,7 @@ Entry points mirror include/qsc.h:
     Resident.masked_sum(mask, block_stride)  qsc_masked_sum
     Resident.dense_df(mask)                  qsc_dense_df
     Resident.com(mask=None)                  qsc_com
+    Resident.com_noalloc(mask=None)          qsc_com_noalloc
     Resident.decode_region(r0, r1, c0, c1)   qsc_decode_region
     Resident.sum_dp(scan_mask, stride)       qsc_sum_dp
     Resident.decode_blocks(first, n, kind)   qsc_decode_blocks
@@ -88,6 +89,7 @@ _SIGS = {
     "qsc_masked_sum": ([_vp, _vp, _u32, _vp, _vp, ctypes.c_int], _i32),
     "qsc_dense_df": ([_vp, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_com": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int], _i32),
+    "qsc_com_noalloc": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_decode_region": ([_vp, _u32, _u32, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
     "qsc_sum_dp": ([_vp, _vp, _u32, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_decode_blocks": ([_vp, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
@@ -334,6 +336,18 @@ class Resident:
         self._on(stream, m, row, col)
         self._check(lib.qsc_com(self._h, None if m is None else m.data_ptr(), row.data_ptr(), col.data_ptr(),
                                 _stream_handle(stream), int(wait)), "com")
+        return row, col
+
+    def com_noalloc(self, mask=None, out_row=None, out_col=None, stream=None, wait=True):
+        """com with the library's static moment buffer (qsc_com_noalloc): no device allocation
+        inside the call; at most 1,048,576 scans; calls overlapping on one GPU race."""
+        import torch
+        m = None if mask is None else self._mask(mask)
+        row = self._out(out_row, torch.float32, self.S)
+        col = self._out(out_col, torch.float32, self.S)
+        self._on(stream, m, row, col)
+        self._check(lib.qsc_com_noalloc(self._h, None if m is None else m.data_ptr(), row.data_ptr(),
+                                        col.data_ptr(), _stream_handle(stream), int(wait)), "com_noalloc")
         return row, col
 
     def decode_region(self, r0, r1, c0, c1, calibrated=False, out=None, stream=None, wait=True):

@@ -14,6 +14,7 @@
 #include <tuple>
 #include <cmath>
 #include <memory>
+#include <mutex>
 #include <new>
 
 #include "kernels.hpp"
@@ -243,6 +244,33 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
     return QSC_OK;
 }
 
+// Moment partials of qsc_com_noalloc: M0, Mr, Mc per scan, u64, for up to
+// kNoAllocScans scans (24 MiB). Every GPU the library runs on holds one copy
+// until the process ends. Host code never passes the array's name to a kernel:
+// that is a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr uint64_t kNoAllocScans = 1ull << 20;
+static __device__ __align__(256) uint64_t scratch[3 * kNoAllocScans];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's scratch (the current device must be it).
+hipError_t scratch_address(int device, uint64_t **out) {
+    static std::mutex mu;
+    static uint64_t *ptrs[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptrs[device] = static_cast<uint64_t *>(p);
+    }
+    *out = ptrs[device];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -450,6 +478,23 @@ qsc_status qsc_com(qsc_resident *res, const uint8_t *d_mask, float *d_row, float
         return hip_fail(res, e, "moment buffer");
     e = launch_query(res->dev, d_mask, 0, 1, Op::Moments, res->d_moments, 1, 0, nullptr, 3 * res->g.S(), st);
     if (e == hipSuccess) e = launch_com_finalize(res->d_moments, res->g.S(), d_row, d_col, st);
+    return finish_query(res, e, st, wait);
+}
+
+qsc_status qsc_com_noalloc(qsc_resident *res, const uint8_t *d_mask, float *d_row, float *d_col, void *hip_stream,
+                           int wait) {
+    if (!res) return QSC_ERR_INVALID_ARG;
+    if (!d_row || !d_col) return fail(res, QSC_ERR_INVALID_ARG, "com_noalloc: bad argument");
+    if (res->g.S() > kNoAllocScans)
+        return fail(res, QSC_ERR_INVALID_ARG, "com_noalloc: more than 1048576 scans (its static moment buffer)");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    uint64_t *m = nullptr;
+    hipError_t e = scratch_address(res->device, &m);
+    if (e != hipSuccess) return hip_fail(res, e, "static moment buffer address");
+    // the init kernel zeroes the 3 x S moments this call uses before the decode adds into them
+    e = launch_query(res->dev, d_mask, 0, 1, Op::Moments, m, 1, 0, nullptr, 3 * res->g.S(), st);
+    if (e == hipSuccess) e = launch_com_finalize(m, res->g.S(), d_row, d_col, st);
     return finish_query(res, e, st, wait);
 }
 
