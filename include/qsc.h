@@ -127,7 +127,11 @@ qsc_status qsc_encode_device(const qsc_geometry *geom, const void *d_data, void 
  * qsc_resident_destroy: synchronises and frees everything the resident owns.
  *   The caller must destroy every resident it creates (scaled-uint16 page:
  *   the caller closes loaded residents).
- * qsc_resident_info: geometry and sizes (see qsc_info).
+ * qsc_resident_info: geometry and sizes (see qsc_info). A diagnostic helper
+ *   that no passage defines: it reports the uint32/uint64 virtual-image width
+ *   the paired-resident page's "Contract" fixes (row "virtual image"), the
+ *   resident's device footprint (the optimization matrix page's "Memory
+ *   Footprint" concern) and the per-mode stream counts.
  */
 qsc_status qsc_resident_create(const void *host_blob, uint64_t nbytes, const uint8_t *host_valid,
                                void *hip_stream, qsc_resident **out);
@@ -201,7 +205,10 @@ qsc_status qsc_resident_info(const qsc_resident *res, qsc_info *info);
  * qsc_finish: synchronises hip_stream and reports (then clears) the first
  *   malformed stream found by queries enqueued since the last check.
  * qsc_last_error: message of the resident's last failure, naming the first
- *   bad (block, pixel) for MALFORMED; valid until the next call on it.
+ *   bad (block, pixel) for MALFORMED; valid until the next call on it. A
+ *   diagnostic helper: the paired-resident page ("Contract", malformed
+ *   stream) only asks that the query fail without a result; the message says
+ *   which stream failed.
  */
 qsc_status qsc_masked_sum(qsc_resident *res, const uint8_t *d_mask, uint32_t block_stride, void *d_out,
                           void *hip_stream, int wait);
@@ -264,7 +271,9 @@ qsc_status qsc_masked_sum_delta(qsc_resident *res, const uint8_t *d_prev_mask, c
 /* Exact encoded bytes and logical counts a masked_sum with this host mask
  * (P bytes) and stride touches: stream bytes of every selected (block, pixel)
  * plus its offset entries, and n_visited_scans x n_selected counts. This is
- * the numerator of the encoded-byte GB/s a query sustains. */
+ * the numerator of the encoded-byte GB/s a query sustains. A measurement
+ * helper that no passage defines; host-only (it reads the resident's host
+ * copy of the offsets and one device copy of the validity mask). */
 qsc_status qsc_query_bytes(const qsc_resident *res, const uint8_t *host_mask, uint32_t block_stride,
                            uint64_t *bytes, uint64_t *counts);
 
