@@ -168,7 +168,9 @@ void build_pair_tables(uint32_t *out) {
             const uint32_t nb = 10 - (31 - __builtin_clz(y));
             const uint32_t newX = (y << nb) - kTansL;
             const uint32_t a = i >> 4, b = i & 15;
-            out[m * kTansL + X] = a | (b << 8) | (nb << 16) | (newX << 20) | ((a == 15 || b == 15) ? 1u << 31 : 0u);
+            // code length, window values, escape flag, and the next state's table index
+            out[m * kTansL + X] = nb | (a << 6) | (b << 10) | ((a == 15 || b == 15) ? 1u << 15 : 0u) |
+                                  ((m * kTansL + newX) << 16);
         }
     }
 }

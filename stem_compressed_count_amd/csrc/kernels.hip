@@ -1187,32 +1187,81 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
 }
 
 // ------------------------------------------------------------------ paired tile
+// Any lane of the wave whose entry (or OR of entries) flags an escape: one
+// 16-bit signed compare of the entry's low half (bit 15 is its sign).
+__device__ __forceinline__ bool any_escape(uint32_t e) {
+    uint64_t m;
+    asm("v_cmp_gt_i16_e64 %0, 0, %1" : "=s"(m) : "v"(e));
+    return m != 0;
+}
+
+// Bit reservoir of a paired stream: the valid bits sit below a single marker
+// bit, so consuming bits is one 64-bit shift (the marker moves with them) and
+// the count of valid bits is only needed at the refill and at the end.
+struct MBits {
+    uint64_t r;    // valid bits, the marker, zeros
+    uint32_t off;  // block offset of the prefetched dword pf
+    uint32_t pf;
+};
+
+// From a counted reservoir holding fewer than 64 bits.
+__device__ __forceinline__ MBits mbits_from(const BBits &s) { return MBits{s.r | (1ull << s.n), s.off, s.pf}; }
+
+__device__ __forceinline__ uint32_t mbits_count(const MBits &s) { return 63u - (uint32_t)__builtin_clzll(s.r); }
+
+// At most 31 valid bits (the marker in the low word): the prefetched dword
+// goes above them, and the marker 32 bits higher.
+__device__ __forceinline__ void mbits_refill(MBits &s, Rsrc rs) {
+    if ((uint32_t)(s.r >> 32) == 0u) {
+        const uint32_t lo = (uint32_t)s.r;
+        const uint32_t n = 31u - (uint32_t)__builtin_clz(lo);             // the marker's position
+        const uint64_t ins = ((((uint64_t)1) << 32) | s.pf) << n;          // the new bits and marker
+        s.r = ((uint64_t)(uint32_t)(ins >> 32) << 32) | ((lo ^ (1u << n)) | (uint32_t)ins);
+        s.off += 4;
+        s.pf = bload(rs, s.off);
+    }
+}
+
+__device__ __forceinline__ uint32_t mbits_pop(MBits &s, uint32_t nb) {
+    const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)s.r, 0, nb);
+    s.r >>= nb;
+    return v;
+}
+
+// bits consumed since the stream start (block offset start)
+__device__ __forceinline__ uint32_t mbits_used(const MBits &s, uint32_t start) {
+    return 8u * (s.off - (start & ~3u)) - mbits_count(s) - ((start & 2) ? 16u : 0u);
+}
+
+// One tANS step's code bits: the entry's code length of bits from the
+// reservoir; returns the next state's entry index.
+__device__ __forceinline__ uint32_t take_code(MBits &s, uint32_t e) {
+    const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)s.r, 0, e);  // width = e[4:0] = code length
+    s.r >>= (e & 63u);                                                // amount = e[5:0] = code length
+    return (e >> 16) + v;
+}
+
 struct PSlot {
-    uint32_t X;     // tANS state
+    uint32_t idx;   // LDS index of the tANS state's entry: model * 1024 + state (the idle entry unless PAIRED)
+    uint32_t e;     // that entry, read one step ahead
     uint32_t meta;  // mode (3 PAIRED, 4 RAW, 7 idle) | model << 3
-    uint32_t tb;    // LDS index of the slot's decode table (the idle entry unless PAIRED)
     uint32_t a0;    // window base of the slot's model (0 unless PAIRED)
     uint32_t p;
     uint32_t org;  // stream start within the block payload
     uint32_t len;
-    BBits s;
+    MBits s;
 };
 
-// Paired decode-table entry: window values a, b (15 = escape) in bytes 0 and 1,
-// code length in bits 16-19, next-state base in bits 20-29, bit 31 set when
-// either value escapes.
-__device__ __forceinline__ uint32_t pe_a(uint32_t e) { return e & 0xFFu; }
-__device__ __forceinline__ uint32_t pe_b(uint32_t e) { return __builtin_amdgcn_ubfe(e, 8, 8); }
-__device__ __forceinline__ uint32_t pe_nbits(uint32_t e) { return __builtin_amdgcn_ubfe(e, 16, 4); }
-__device__ __forceinline__ uint32_t pe_next(uint32_t e) { return __builtin_amdgcn_ubfe(e, 20, 10); }
+// Paired decode-table entry: code length in bits 0-3 (bits 4-5 zero, so the
+// entry itself is the width operand of a bit-field extract and the amount of
+// a 64-bit shift), window values a, b (15 = escape) in bits 6-9 and 10-13,
+// bit 15 set when either value escapes, and in bits 16-31 the LDS index of
+// the next state's base entry (model * 1024 + next-state base). One shift
+// and one add give the next lookup's index.
+__device__ __forceinline__ uint32_t pe_a(uint32_t e) { return __builtin_amdgcn_ubfe(e, 6, 4); }
+__device__ __forceinline__ uint32_t pe_b(uint32_t e) { return __builtin_amdgcn_ubfe(e, 10, 4); }
+__device__ __forceinline__ bool pe_escape(uint32_t e) { return (int16_t)e < 0; }
 
-// Reads nb (< 32) bits from the reservoir.
-__device__ __forceinline__ uint32_t take_bits(BBits &s, uint32_t nb) {
-    const uint32_t v = __builtin_amdgcn_ubfe((uint32_t)s.r, 0, nb);
-    s.r >>= nb;
-    s.n -= nb;
-    return v;
-}
 
 __device__ __forceinline__ uint32_t window_sym(uint32_t v, uint32_t a0, uint32_t use) {
     const uint32_t d = v - a0;
@@ -1221,9 +1270,9 @@ __device__ __forceinline__ uint32_t window_sym(uint32_t v, uint32_t a0, uint32_t
 
 // An escaped count: its literal, returned relative to the model's window base.
 template <bool WIDE>
-__device__ __forceinline__ uint32_t pair_literal(BBits &s, Rsrc rs, uint32_t info, uint32_t &bad) {
-    bbits_refill(s, rs);
-    const uint32_t lit = popn(s, WIDE ? 16u : 8u);
+__device__ __forceinline__ uint32_t pair_literal(MBits &s, Rsrc rs, uint32_t info, uint32_t &bad) {
+    mbits_refill(s, rs);
+    const uint32_t lit = mbits_pop(s, WIDE ? 16u : 8u);
     const uint32_t a0 = info & 0xFFFFu;
     bad |= window_sym(lit, a0, info >> 16) != 15u;
     return lit - a0;
@@ -1244,13 +1293,11 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     for (int k = 0; k < K; k++) {
         PSlot &z = sl[k];
         z.meta = 7;
-        z.X = 0;
+        z.idx = kPairIdle;  // the idle entry after the 32 model tables: no bits, zero values, itself next
         z.p = 0;
-        z.tb = 32u << 10;  // the idle entry after the 32 model tables
         z.a0 = 0;
         // an idle slot reads outside the buffer range (zeros) and consumes no bits
-        z.s.r = 0;
-        z.s.n = 64;
+        z.s.r = 1ull << 63;
         z.s.off = 0x80000000u;
         z.s.pf = 0;
         const uint32_t i = first + k * 64 + lane;
@@ -1322,19 +1369,23 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             continue;
         }
         z.meta = hdr & 0xFFu;  // mode and model
-        bbits_init(z.s, rs, z.org);
-        pop16(z.s);  // header
+        BBits cs;
+        bbits_init(cs, rs, z.org);
+        pop16(cs);  // header
         if (mode == 3) {
             const uint32_t a0 = tbl[kPairTable + ((hdr >> 3) & 31u)] & 0xFFFFu;
-            z.X = popn(z.s, 10);
-            z.tb = ((hdr >> 3) & 31u) << 10;
+            z.idx = (((hdr >> 3) & 31u) << 10) + popn(cs, 10);
             z.a0 = a0;
             base0 += a0;
             baseR += a0 * kr;
             baseC += a0 * kc;
         }
-        bbits_refill(z.s, rs);
+        z.s = mbits_from(cs);  // at most 48 bits are left after the header
+        mbits_refill(z.s, rs);
     }
+    // the first table entry of every slot (the idle entry for slots without a PAIRED stream)
+#pragma unroll
+    for (int k = 0; k < K; k++) sl[k].e = tbl[sl[k].idx];
     uint32_t kr[OP == Op::Moments ? K : 1], kc[OP == Op::Moments ? K : 1];
     if (OP == Op::Moments) {
 #pragma unroll
@@ -1366,27 +1417,33 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     auto step = [&](auto form, uint32_t t, uint32_t (&v0)[K], uint32_t (&v1)[K]) {
         constexpr int F = decltype(form)::value;
         if constexpr (F == kPPlain) {
+            // the entry read a step ahead gives the code bits and the next
+            // state at once; the next entry's read is issued right away, and
+            // this step's values, escapes and refill run while it is in flight
             uint32_t e[K];
-#pragma unroll
-            for (int k = 0; k < K; k++) e[k] = tbl[sl[k].tb + sl[k].X];
-            bool esc_any = false;
+            uint32_t esc_any = 0;
 #pragma unroll
             for (int k = 0; k < K; k++) {
                 PSlot &z = sl[k];
-                z.X = pe_next(e[k]) + take_bits(z.s, pe_nbits(e[k]));
+                e[k] = z.e;
+                z.idx = take_code(z.s, e[k]);
+                z.e = tbl[z.idx];
+            }
+#pragma unroll
+            for (int k = 0; k < K; k++) {
                 v0[k] = pe_a(e[k]);
                 v1[k] = pe_b(e[k]);
-                esc_any |= (int32_t)e[k] < 0;
+                esc_any |= e[k];
             }
-            if (__builtin_amdgcn_ballot_w64(esc_any)) {  // values outside the model window
+            if (any_escape(esc_any)) {  // values outside the model window
 #pragma unroll
                 for (int k = 0; k < K; k++) {
-                    if ((int32_t)e[k] < 0) {
+                    if (pe_escape(e[k])) {
                         PSlot &z = sl[k];
                         const uint32_t info = tbl[kPairTable + (z.meta >> 3)];
                         if (v0[k] == 15u) v0[k] = pair_literal<WIDE>(z.s, rs, info, bad);
                         if (v1[k] == 15u) v1[k] = pair_literal<WIDE>(z.s, rs, info, bad);
-                        bbits_refill(z.s, rs);  // keep 32+ bits until the next cadence point
+                        mbits_refill(z.s, rs);  // keep 32+ bits until the next cadence point
                     }
                 }
             }
@@ -1394,7 +1451,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             // wave-uniform cadence (the paired-resident page's refill rhythm)
             if (t % 3 == 2) {
 #pragma unroll
-                for (int k = 0; k < K; k++) bbits_refill(sl[k].s, rs);
+                for (int k = 0; k < K; k++) mbits_refill(sl[k].s, rs);
             }
         } else {
 #pragma unroll
@@ -1404,28 +1461,29 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 v0[k] = 0;
                 v1[k] = 0;
                 if (mode == 3) {
-                    const uint32_t e = tbl[z.tb + z.X];
-                    z.X = pe_next(e) + take_bits(z.s, pe_nbits(e));
+                    const uint32_t e = z.e;
+                    z.idx = take_code(z.s, e);
+                    z.e = tbl[z.idx];
                     v0[k] = pe_a(e);
                     v1[k] = pe_b(e);
-                    if ((int32_t)e < 0) {
+                    if (pe_escape(e)) {
                         const uint32_t info = tbl[kPairTable + (z.meta >> 3)];
                         if (v0[k] == 15u) v0[k] = pair_literal<WIDE>(z.s, rs, info, bad);
                         if (v1[k] == 15u) v1[k] = pair_literal<WIDE>(z.s, rs, info, bad);
-                        bbits_refill(z.s, rs);
+                        mbits_refill(z.s, rs);
                     }
-                    if (t % 3 == 2) bbits_refill(z.s, rs);
+                    if (t % 3 == 2) mbits_refill(z.s, rs);
                 } else if (mode == 4) {
                     if (WIDE) {
-                        v0[k] = pop16(z.s);
-                        bbits_refill(z.s, rs);
-                        v1[k] = pop16(z.s);
+                        v0[k] = mbits_pop(z.s, 16);
+                        mbits_refill(z.s, rs);
+                        v1[k] = mbits_pop(z.s, 16);
                     } else {
-                        const uint32_t w = pop16(z.s);
+                        const uint32_t w = mbits_pop(z.s, 16);
                         v0[k] = w & 0xFFu;
                         v1[k] = w >> 8;
                     }
-                    bbits_refill(z.s, rs);
+                    mbits_refill(z.s, rs);
                 }
             }
         }
@@ -1561,15 +1619,15 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         PSlot &z = sl[k];
         const uint32_t mode = z.meta & 7u;
         if (mode != 3 && mode != 4) continue;
-        const uint32_t used = bbits_used(z.s, z.org), total = 8u * z.len;
+        const uint32_t used = mbits_used(z.s, z.org), total = 8u * z.len;
         bool ok;
         if (mode == 4) {
             ok = used == total;
         } else {
-            ok = z.X == 0 && used <= total && total - used < 16;
+            ok = (z.idx & 1023u) == 0 && used <= total && total - used < 16;  // state 0 of the model
             if (ok && total > used) {
-                bbits_refill(z.s, rs);
-                ok = popn(z.s, total - used) == 0;
+                mbits_refill(z.s, rs);
+                ok = mbits_pop(z.s, total - used) == 0;
             }
         }
         if (!ok || bad) report(r, b, z.p);

@@ -9,6 +9,9 @@ namespace qsc {
 // Paired decode tables on the device: 32 models x 1024 states, then one idle
 // entry (values 0, no bits, next state 0) padded to 16 bytes.
 constexpr uint32_t kPairTable = 32 * 1024 + 4;
+// LDS index of the paired layout's idle entry (after the 32 model tables): no
+// code bits, zero values, and itself as the next entry
+constexpr uint32_t kPairIdle = 32 * 1024;
 
 // Query plan: the selected pixels are counted per 64-pixel tile (at most
 // kMaxPlanTiles tiles, so detectors up to 65,536 pixels; larger ones decode

@@ -169,8 +169,9 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
             build_rans_table(f, tables.data() + 2 * kRansM * b);
         }
     } else {
-        tables.assign(kPairTable, 0);  // the idle entry stays 0
+        tables.assign(kPairTable, 0);
         build_pair_tables(tables.data());
+        tables[kPairIdle] = kPairIdle << 16;  // the idle entry: no bits, zero values, itself next
         const PairModels &pm = pair_models();
         for (uint32_t m = 0; m < kModels; m++) info[m] = pm.a0[m] | (pm.in_use[m] << 16);
     }
