@@ -257,6 +257,13 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return v;
 }
 
+// Smallest value over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = min(v, (uint32_t)__shfl_xor(v, off));
+    return v;
+}
+
 // Scan (within the chunk) whose total lane_id() holds after wave_transpose_sum,
 // and whether this lane is the one that writes it.
 template <int CH>
@@ -1408,14 +1415,47 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             rowu = !__builtin_amdgcn_ballot_w64(diff);
         }
     }
+    // Packed moments: in a wave inside one detector row whose live columns span
+    // at most 128, one 32-bit accumulator per scan holds the sum of the values
+    // (low half) and their column moment relative to the wave's first live
+    // column (high half): one 24-bit multiply-add per value with the weight
+    // 1 + (column offset << 16). Window values are at most 15 (escaped counts
+    // beyond that are clamped to 15 and their excess goes to the partials
+    // directly), so over 16 lanes of two slots each both halves stay below
+    // 2^16 (16 x 2 x 15 = 480; 16 x 15 x (127 + 126) < 65536): the first four
+    // reduction levels run on the packed words, the last two on each half.
+    // The window bases enter once per scan as wave totals.
+    bool packed = false;
+    uint32_t kcw = 0, B0 = 0, Bc = 0, wgt[OP == Op::Moments ? K : 1];
+    if constexpr (OP == Op::Moments) {
+        if (rowu) {
+            uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+            for (int k = 0; k < K; k++)
+                if ((sl[k].meta & 7u) != 7u) m = min(m, kc[k]);
+            kcw = wave_min(m);
+            bool far = false;
+#pragma unroll
+            for (int k = 0; k < K; k++) far |= (sl[k].meta & 7u) != 7u && kc[k] - kcw > 127u;
+            packed = !__builtin_amdgcn_ballot_w64(far);
+#pragma unroll
+            for (int k = 0; k < K; k++) wgt[k] = (sl[k].meta & 7u) != 7u ? 1u + ((kc[k] - kcw) << 16) : 0u;
+            if (packed) {
+                B0 = wave_sum(base0);
+                Bc = wave_sum(baseC);
+            }
+        }
+    }
 
     // One pair step of every slot: window-relative values for PAIRED slots,
     // absolute values for RAW slots, zeros for idle ones. Two forms, chosen
     // once per wave: kPMixed when some slot is RAW (per-slot branches), kPPlain
     // otherwise (every slot, idle ones included, runs the same table step).
     constexpr int kPMixed = 0, kPPlain = 1;
-    auto step = [&](auto form, uint32_t t, uint32_t (&v0)[K], uint32_t (&v1)[K]) {
+    // Returns whether some slot of the wave read an escape literal at this step.
+    auto step = [&](auto form, uint32_t t, uint32_t (&v0)[K], uint32_t (&v1)[K]) -> bool {
         constexpr int F = decltype(form)::value;
+        bool escaped = true;
         if constexpr (F == kPPlain) {
             // the entry read a step ahead gives the code bits and the next
             // state at once; the next entry's read is issued right away, and
@@ -1435,7 +1475,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 v1[k] = pe_b(e[k]);
                 esc_any |= e[k];
             }
-            if (any_escape(esc_any)) {  // values outside the model window
+            escaped = any_escape(esc_any);
+            if (escaped) {  // values outside the model window
 #pragma unroll
                 for (int k = 0; k < K; k++) {
                     if (pe_escape(e[k])) {
@@ -1487,10 +1528,12 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 }
             }
         }
+        return escaped;
     };
 
-    auto run = [&](auto form, auto rowu) {
+    auto run = [&](auto form, auto rowu, auto packed_t) {
         constexpr bool ROWU = decltype(rowu)::value;  // moments of a wave inside one detector row
+        constexpr bool PACKED = decltype(packed_t)::value;
         if constexpr (is_region(OP)) {
             auto rw = region_walk<is_frames(OP)>(r, b, ra);
             for (uint32_t t = 0; t < kBlk / 2; t++) {
@@ -1538,6 +1581,61 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             for (int k = 0; k < K; k++) {
                 const uint32_t mode = sl[k].meta & 7u;
                 if (mode == 3 || mode == 4) dt.row[sl[k].p] = acc[k];
+            }
+        } else if constexpr (OP == Op::Moments && PACKED) {
+            constexpr int CH = 8;
+            const uint32_t my = lane_scan<CH>();
+            const bool writer = lane_writes<CH>();
+            for (uint32_t c = 0; c < kBlk / CH; c++) {
+                uint32_t acc[CH];
+#pragma unroll
+                for (int i = 0; i < CH; i++) acc[i] = 0;
+#pragma unroll
+                for (int tt = 0; tt < CH / 2; tt++) {
+                    uint32_t v0[K], v1[K];
+                    if (step(form, c * (CH / 2) + tt, v0, v1)) {
+                        // escaped counts beyond the packed range (window-relative, so a
+                        // count below the window base is negative): 15 stays packed, the
+                        // excess goes to the partials with its moments
+#pragma unroll
+                        for (int k = 0; k < K; k++) {
+#pragma unroll
+                            for (int h = 0; h < 2; h++) {
+                                uint32_t &v = h ? v1[k] : v0[k];
+                                if (v > 15u) {
+                                    const uint32_t s = c * CH + 2 * tt + h;
+                                    const long long x = (int32_t)(v - 15u);
+                                    atomicAdd(&pt.m0[s], v - 15u);
+                                    atomicAdd(&pt.mc[s], (unsigned long long)(x * (long long)kc[k]));
+                                    atomicAdd(&pt.mr[s], (unsigned long long)(x * (long long)kru));
+                                    v = 15u;
+                                }
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        acc[2 * tt] = mad24(v0[k], wgt[k], acc[2 * tt]);
+                        acc[2 * tt + 1] = mad24(v1[k], wgt[k], acc[2 * tt + 1]);
+                    }
+                    asm volatile("" : "+v"(acc[2 * tt]), "+v"(acc[2 * tt + 1]));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                transpose_head<CH>(acc);
+                uint32_t v = acc[0];
+                v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kHalfMirror, 0xF, 0xF, false);  // 16 lanes
+                uint32_t t0 = v & 0xFFFFu, tc = v >> 16;
+                t0 += (uint32_t)__builtin_amdgcn_mov_dpp((int)t0, kQuadXor2, 0xF, 0xF, false);
+                tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor2, 0xF, 0xF, false);
+                t0 += (uint32_t)__builtin_amdgcn_mov_dpp((int)t0, kQuadXor1, 0xF, 0xF, false);
+                tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor1, 0xF, 0xF, false);
+                const uint32_t m0 = t0 + B0;
+                if (writer && m0) {
+                    const uint32_t s = c * CH + my;
+                    atomicAdd(&pt.m0[s], m0);
+                    atomicAdd(&pt.mc[s], (unsigned long long)Bc + (unsigned long long)kcw * t0 + tc);
+                    atomicAdd(&pt.mr[s], (unsigned long long)kru * m0);
+                }
             }
         } else {
             // paired workgroups have 128 VGPRs per lane: moments reduce every 8 scans
@@ -1599,13 +1697,22 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
 #pragma unroll
     for (int k = 0; k < K; k++) raw |= (sl[k].meta & 7u) == 4u;
     auto run_rows = [&](auto form) {
+        constexpr bool PLAIN = decltype(form)::value == kPPlain;
         if constexpr (OP == Op::Moments) {
-            if (rowu)
-                run(form, std::true_type{});
-            else
-                run(form, std::false_type{});
+            if (rowu) {
+                if constexpr (PLAIN) {
+                    if (packed)
+                        run(form, std::true_type{}, std::true_type{});
+                    else
+                        run(form, std::true_type{}, std::false_type{});
+                } else {
+                    run(form, std::true_type{}, std::false_type{});
+                }
+            } else {
+                run(form, std::false_type{}, std::false_type{});
+            }
         } else {
-            run(form, std::false_type{});
+            run(form, std::false_type{}, std::false_type{});
         }
     };
     if (__builtin_amdgcn_ballot_w64(raw))

@@ -191,6 +191,36 @@ def test_paired_generator_byte_rans_too():
     check_all_products(w, counts, valid, blob, {"bf": masks["bf"]}, masks["df"], [(0, 8, 0, 8)], strides=(1, 4))
 
 
+@pytest.mark.parametrize("dtype", [np.uint16, np.uint8])
+def test_paired_moments_of_row_waves_with_escapes(dtype):
+    """Full-detector CoM on a paired resident whose waves each lie inside one
+    192-pixel detector row (the packed moment accumulators): bright columns
+    coded with the lambda = 20 model (window 13..27, so counts below 13 escape
+    below the window base and are negative relative to it), counts far above
+    the window, saturated pixels, and a masked CoM with some waves spanning
+    two rows. Bit-exact against the oracle."""
+    rng = np.random.default_rng(88)
+    R, C, S = 12, 192, 1024
+    P = R * C
+    maxv = np.iinfo(dtype).max
+    c = rng.poisson(0.3, size=(S, P)).astype(np.int64)
+    bright = rng.choice(P, 400, replace=False)
+    c[:, bright] = rng.poisson(20.0, size=(S, 400))
+    c[:, bright[:40]] = rng.integers(0, 40, size=(S, 40))          # wide spread around the window
+    spikes = rng.choice(S * P, 3000, replace=False)
+    c.reshape(-1)[spikes] = rng.choice([300 % (maxv + 1), maxv, 16, 200], size=3000)
+    c[:, 5 * C + 17] = maxv                                         # a saturated pixel
+    c = np.minimum(c, maxv).astype(dtype)
+    blob = q().encode(c, 2, 512, R, C, layout=1)
+    masks = [None, synth.disk_mask(R, C, 6, 96, 5), (rng.random(P) < 0.7).astype(np.uint8)]
+    with q().Resident(blob) as res:
+        for m in masks:
+            check_com(res, c, synth.Workload("rows", 2, 512, R, C, 2, 0, 0, 0, 0, 0, 0, 0, 0, 1), m, None)
+            mm = np.ones(P, np.uint8) if m is None else m
+            assert np.array_equal(u(res.masked_sum(mm)), oracle.masked_sum(c, mm))
+        res.finish()
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_uint64_sums_257_detector(layout):
     # 257 x 257 uint16: a full-detector sum can pass 2^32, so outputs are uint64
