@@ -134,22 +134,6 @@ const PairModels &pair_models() {
 
 // ---------------------------------------------------------------- device tables
 
-void build_rans_table(const uint16_t *freq, uint32_t *out) {
-    // 4096 slots of two words each, side by side so that one 64-bit LDS read
-    // fetches both: f | symbol << 24, then slot - c[symbol]
-    uint32_t c = 0;
-    for (uint32_t s = 0; s < 256; s++) {
-        const uint32_t f = freq[s];
-        // f < 4096 in every table a RANS stream may use (a single 4096 entry is degenerate)
-        for (uint32_t t = 0; t < f && c + t < kRansM; t++) {
-            out[2 * (c + t)] = (f & 0xFFFu) | (s << 24);
-            out[2 * (c + t) + 1] = t;
-        }
-        c += f;
-    }
-    for (; c < kRansM; c++) out[2 * c] = out[2 * c + 1] = 0;  // empty table: never used by a valid RANS stream
-}
-
 void build_pair_tables(uint32_t *out) {
     const PairModels &pm = pair_models();
     for (uint32_t m = 0; m < kModels; m++) {

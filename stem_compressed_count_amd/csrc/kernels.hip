@@ -1929,6 +1929,65 @@ __device__ __forceinline__ uint32_t index_group(const DevResident &r, const uint
     return WG;
 }
 
+// ------------------------------------------------------------------ byte-rANS table in LDS
+// A block's decode table built from its 256 frequencies (FORMAT 2.2-2.3): slot
+// t of symbol s (c[s] <= t < c[s] + f[s]) holds f | s << 24 and t - c[s]. The
+// frequencies' exclusive prefix sums c go to cum (257 words of LDS); then each
+// thread fills 4096 / WG consecutive slots, starting from the symbol that a
+// binary search over c finds for its first one. A table that sums to 0 (no
+// RANS stream may use it) is all zero. f is thread s's frequency, loaded by
+// the caller early (before the item's pixel selection) so that its latency
+// overlaps that work: 512 bytes per build instead of a 32 KB expanded table.
+template <int WG>
+__device__ __forceinline__ void rans_table_build(uint32_t f, uint32_t *tbl, uint32_t *cum, uint32_t *wtot) {
+    static_assert(WG == 256, "one symbol per thread");
+    constexpr uint32_t kSlots = 4096 / WG;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    uint32_t x = f;  // inclusive prefix within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= (uint32_t)off) x += y;
+    }
+    __syncthreads();  // wtot and cum may still be read by the previous user
+    if (lane == 63) wtot[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < WG / 64; w++) {
+        before += w < wave ? wtot[w] : 0u;
+        total += wtot[w];
+    }
+    cum[tid] = before + x - f;
+    if (tid == WG - 1) cum[WG] = before + x;
+    __syncthreads();
+    const uint32_t t0 = tid * kSlots;
+    uint2 *out = reinterpret_cast<uint2 *>(tbl);
+    if (total == 0) {
+#pragma unroll
+        for (uint32_t j = 0; j < kSlots; j++) out[t0 + j] = make_uint2(0u, 0u);
+        return;
+    }
+    // the last symbol whose range starts at or before t0 (its range holds t0)
+    uint32_t lo = 0, hi = WG - 1;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (cum[mid] <= t0) lo = mid; else hi = mid - 1;
+    }
+    uint32_t sym = lo, c = cum[sym], e = cum[sym + 1];
+#pragma unroll
+    for (uint32_t j = 0; j < kSlots; j++) {
+        const uint32_t t = t0 + j;
+        while (t >= e) {
+            sym++;
+            c = e;
+            e = cum[sym + 1];
+        }
+        out[t] = make_uint2(((e - c) & 0xFFFu) | (sym << 24), t - c);
+    }
+}
+
 // ------------------------------------------------------------------ reduce kernels
 template <Op OP>
 struct SharedPartials {
@@ -2065,6 +2124,32 @@ __device__ __forceinline__ void raw_first(const DevResident &r, uint32_t b, uint
     __syncthreads();
 }
 
+// The work items of a query: n_live items of each of n_visited blocks. With
+// at least as many blocks as workgroups, workgroup g takes every item of
+// blocks g, g + grid, ... in turn, so it decodes consecutive items of one block
+// and keeps that block's LDS partials (and decode table) between them;
+// otherwise item w of the grid-strided sequence is item w / n_visited of block
+// w % n_visited (a grid that is a multiple of the blocks still keeps each
+// workgroup on one block). Returns false when the workgroup has no k-th item.
+__device__ __forceinline__ bool work_item(uint32_t k, uint32_t n_live, uint32_t n_visited, uint32_t &vb, uint32_t &t) {
+    if (n_visited >= gridDim.x) {
+        vb = (k / n_live) * gridDim.x + blockIdx.x;
+        t = k % n_live;
+        return vb < n_visited;
+    }
+    const uint32_t w = blockIdx.x + k * gridDim.x;
+    vb = w % n_visited;
+    t = w / n_visited;
+    return w < n_live * n_visited;
+}
+
+// Whether sums and moments may keep a block's LDS partials over several items:
+// a scan's u32 total over every pixel of the detector cannot pass 2^32 - 1
+// (the rule that keeps a virtual image in 32 bits).
+__device__ __forceinline__ bool hold_partials(const DevResident &r) {
+    return (uint64_t)r.P * (r.dtype == 2 ? 65535u : 255u) <= 0xFFFFFFFFull;
+}
+
 template <bool WIDE, Op OP>
 __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
@@ -2093,13 +2178,18 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     } else if constexpr (OP == Op::Region) {
         halves = da.halves && r.split;  // a latency-bound region read: items of half a workgroup
     }
-    const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     if constexpr (OP == Op::Amp) amp_stage<kRansWG>(ra);  // read after the item loop's first barrier
     uint32_t loaded = 0xFFFFFFFFu;
-    for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-        const uint32_t vb = w / n_live, t = w % n_live;
+    // the block (and sign) whose sums the LDS partials hold; flushed when the block changes
+    constexpr bool kAcc = OP == Op::Sum || OP == Op::Moments;
+    const bool hold = hold_partials(r);
+    uint32_t held_b = 0xFFFFFFFFu, held_n = 0;
+    bool held_sub = false;
+    uint32_t vb, t;
+    for (uint32_t k = 0; n_live && work_item(k, n_live, n_visited, vb, t); k++) {
         const uint32_t b = is_region(OP) ? rb.b[vb] : vb * stride;
+        const uint32_t fq = b != loaded ? r.freq[256ull * b + threadIdx.x] : 0u;  // the table build's input
         const bool sub = two && t >= n_first;  // an item of the subtracted mask
         const uint8_t *m = sub ? da.neg_mask : mask;
         uint32_t p0 = OP == Op::Index ? 0 : (sub && !plan ? t - n_first : t) * tile_px;
@@ -2123,19 +2213,30 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
             __syncthreads();
             dt.row = da.part + (uint64_t)vb * r.P;
             dt.n_sel = dp_count(sbits);
-            if (threadIdx.x == 0 && w % n_live == 0) da.nb[vb] = dt.n_sel;  // once per visited block
+            if (threadIdx.x == 0 && t == 0) da.nb[vb] = dt.n_sel;  // once per visited block
         }
         if (n_sel == 0) continue;
+        if (kAcc && held_b != 0xFFFFFFFFu && (held_b != b || held_sub != sub)) {
+            flush_partials<OP>(sp, held_n, (uint64_t)held_b * kBlk, r.S, out, out64, negate ^ (int)held_sub);
+            held_b = 0xFFFFFFFFu;
+            __syncthreads();
+        }
         if (b != loaded) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(r.tables + 8192ull * b);
-            uint4 *dst = reinterpret_cast<uint4 *>(tbl);
-            for (uint32_t i = threadIdx.x; i < 2048; i += kRansWG) dst[i] = src[i];
+            // no partials are held here (they belong to the block), so they lend
+            // the build room for the prefix sums; they are zeroed after it
+            rans_table_build<kRansWG>(fq, tbl, sp.m0, wtot);
             loaded = b;
+            __syncthreads();  // the table is complete, and cum is read before the partials are zeroed
         }
         // a block with RAW streams: put them in waves of their own (an index
         // leaf must stay one wave, and the split-point build does not care)
         if (raw_block) raw_first<kRansWG>(r, b, base, nbytes, p0, n_sel, sel);
-        if (OP == Op::Sum || OP == Op::Moments) zero_partials<OP>(sp, n);
+        if (kAcc && held_b == 0xFFFFFFFFu) {
+            zero_partials<OP>(sp, n);
+            held_b = b;
+            held_n = n;
+            held_sub = sub;
+        }
         __syncthreads();
         // at most two slots per lane: with three decode forms, more do not fit 3 waves per SIMD
         const uint32_t K = (OP == Op::Index || n_sel <= kRansWG) ? 1 : 2;  // an index leaf is one wave
@@ -2152,9 +2253,13 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
                 rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, half, raw_block);
         }
         __syncthreads();
-        if (OP == Op::Sum || OP == Op::Moments)
+        if (kAcc && !hold) {
             flush_partials<OP>(sp, n, (uint64_t)b * kBlk, r.S, out, out64, negate ^ (int)sub);
+            held_b = 0xFFFFFFFFu;
+        }
     }
+    if (kAcc && held_b != 0xFFFFFFFFu)
+        flush_partials<OP>(sp, held_n, (uint64_t)held_b * kBlk, r.S, out, out64, negate ^ (int)held_sub);
 }
 
 template <bool WIDE, Op OP>
@@ -2190,9 +2295,17 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
         end[0] = pv.end[0];
         end[1] = pv.end[1];
     }
-    const uint32_t n_work = n_live * n_visited;
     const Partials<OP> pt{sp.m0, sp.mr, sp.mc, &sp.c0, &sp.cr, &sp.cc};
     if constexpr (OP == Op::Amp) amp_stage<kPairWG>(ra);  // read after the item loop's first barrier
+    // the block (and sign) whose sums the LDS partials hold; flushed when the block changes
+    constexpr bool kAcc = OP == Op::Sum || OP == Op::Moments;
+    const bool hold = hold_partials(r);
+    uint32_t held_b = 0xFFFFFFFFu;
+    bool held_sub = false;
+    // a block's items go to neighbouring workgroups (w / n_live), so a wave of
+    // workgroups reads few blocks at a time: measured faster here than keeping
+    // a workgroup on one block; the partials are held only while the block stays
+    const uint32_t n_work = n_live * n_visited;
     for (uint32_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         const uint32_t vb = w / n_live, t = w % n_live;
         const uint32_t b = is_region(OP) ? rb.b[vb] : vb * stride;
@@ -2214,10 +2327,19 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
             __syncthreads();
             dt.row = da.part + (uint64_t)vb * r.P;
             dt.n_sel = dp_count(sbits);
-            if (threadIdx.x == 0 && w % n_live == 0) da.nb[vb] = dt.n_sel;  // once per visited block
+            if (threadIdx.x == 0 && t == 0) da.nb[vb] = dt.n_sel;  // once per visited block
         }
         if (n_sel == 0) continue;
-        if (OP == Op::Sum || OP == Op::Moments) zero_partials<OP>(sp, kBlk);
+        if (kAcc && held_b != 0xFFFFFFFFu && (held_b != b || held_sub != sub)) {
+            flush_partials<OP>(sp, kBlk, (uint64_t)held_b * kBlk, r.S, out, out64, negate ^ (int)held_sub);
+            held_b = 0xFFFFFFFFu;
+            __syncthreads();
+        }
+        if (kAcc && held_b == 0xFFFFFFFFu) {
+            zero_partials<OP>(sp, kBlk);
+            held_b = b;
+            held_sub = sub;
+        }
         __syncthreads();
         // at most two slots per lane: 1024-thread workgroups have 128 VGPRs per lane
         const uint32_t K = (OP == Op::Index || n_sel <= kPairWG) ? 1 : 2;  // an index leaf is one wave
@@ -2229,9 +2351,13 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
                 paired_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, base, nbytes, tbl, pt, ra, dt);
         }
         __syncthreads();
-        if (OP == Op::Sum || OP == Op::Moments)
+        if (kAcc && !hold) {
             flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate ^ (int)sub);
+            held_b = 0xFFFFFFFFu;
+        }
     }
+    if (kAcc && held_b != 0xFFFFFFFFu)
+        flush_partials<OP>(sp, kBlk, (uint64_t)held_b * kBlk, r.S, out, out64, negate ^ (int)held_sub);
 }
 
 // out[i] = init[i], or 0 without init (u32 or u64 elements); with a plan,

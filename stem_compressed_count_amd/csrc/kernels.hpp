@@ -30,7 +30,8 @@ struct DevResident {
     const uint8_t *dir;      // n_blocks x {u64 base, u32 n_scans, u32 nbytes}
     const uint32_t *gbase;   // n_blocks x G
     const uint16_t *rel;     // n_blocks x G x 32
-    const uint32_t *tables;  // byte-rANS: n_blocks x 2 x 4096 entries; paired: kPairTable entries
+    const uint16_t *freq;    // byte-rANS: n_blocks x 256 frequencies (the container's table section)
+    const uint32_t *tables;  // paired: kPairTable entries (null for byte-rANS)
     const uint32_t *model_info; // paired: per model a0 | in_use << 16
     const uint8_t *valid;    // P bytes, nonzero = valid
     const double *calib;     // scaled: n_blocks x {scale, offset}

@@ -158,26 +158,19 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
             return bail(e, "upload");
     }
     if ((e = hipMemset(res->d_blob + nbytes, 0, kDevicePad)) != hipSuccess) return bail(e, "pad");
-    // decode tables
-    std::vector<uint32_t> tables;
+    // decode tables: the paired layout's 32 model tables; byte-rANS decoders
+    // build each block's table in LDS from its 512-byte frequency table
     std::vector<uint32_t> info(kModels, 0);
-    if (g.layout == 0) {
-        tables.resize(nb * 2 * kRansM);
-        for (uint64_t b = 0; b < nb; b++) {
-            uint16_t f[256];
-            std::memcpy(f, blob + s.table + 512 * b, 512);
-            build_rans_table(f, tables.data() + 2 * kRansM * b);
-        }
-    } else {
-        tables.assign(kPairTable, 0);
+    if (g.layout == 1) {
+        std::vector<uint32_t> tables(kPairTable, 0);
         build_pair_tables(tables.data());
         tables[kPairIdle] = kPairIdle << 16;  // the idle entry: no bits, zero values, itself next
         const PairModels &pm = pair_models();
         for (uint32_t m = 0; m < kModels; m++) info[m] = pm.a0[m] | (pm.in_use[m] << 16);
+        if ((e = dalloc(res.get(), &res->d_tables, 4 * tables.size())) != hipSuccess) return bail(e, "tables");
+        if ((e = hipMemcpy(res->d_tables, tables.data(), 4 * tables.size(), hipMemcpyHostToDevice)) != hipSuccess)
+            return bail(e, "tables upload");
     }
-    if ((e = dalloc(res.get(), &res->d_tables, 4 * tables.size())) != hipSuccess) return bail(e, "tables");
-    if ((e = hipMemcpy(res->d_tables, tables.data(), 4 * tables.size(), hipMemcpyHostToDevice)) != hipSuccess)
-        return bail(e, "tables upload");
     if ((e = dalloc(res.get(), &res->d_model_info, 4 * kModels)) != hipSuccess) return bail(e, "model info");
     if ((e = hipMemcpy(res->d_model_info, info.data(), 4 * kModels, hipMemcpyHostToDevice)) != hipSuccess)
         return bail(e, "model info upload");
@@ -201,6 +194,7 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
     d.gbase = reinterpret_cast<const uint32_t *>(res->d_blob + s.gbase);
     d.rel = reinterpret_cast<const uint16_t *>(res->d_blob + s.rel);
     d.tables = res->d_tables;
+    d.freq = g.layout == 0 ? reinterpret_cast<const uint16_t *>(res->d_blob + s.table) : nullptr;
     d.model_info = res->d_model_info;
     d.valid = res->d_valid;
     d.calib = g.scaled ? reinterpret_cast<const double *>(res->d_blob + s.calib) : nullptr;
