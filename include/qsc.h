@@ -236,6 +236,40 @@ qsc_status qsc_sum_dp(qsc_resident *res, const uint8_t *d_scan_mask, uint32_t bl
 qsc_status qsc_finish(qsc_resident *res, void *hip_stream);
 const char *qsc_last_error(const qsc_resident *res);
 
+/* ---------------------------------------------------------------- block feed
+ * The reconstruction feed of the paired-resident page ("Operation pipeline"
+ * item 6: PairedFeed decodes whole blocks to frames for the consumer, depth
+ * buffers ahead, with events both ways): blocks first_block ..
+ * first_block + n_blocks - 1, blocks_per_item at a time, each item decoded as
+ * by qsc_decode_blocks (out_kind, layout and invalid pixels likewise) into
+ * one of the caller's depth device buffers d_bufs[0 .. depth-1] (each at
+ * least blocks_per_item x 512 x P x element bytes: dtype bytes for native,
+ * 4 for the float kinds) on a stream the feed creates (default priority).
+ * The caller owns the buffers and must keep them until qsc_feed_destroy.
+ *
+ * qsc_feed_create: validates (range, item size, 1 <= depth <= 64, kind,
+ *   buffers -> INVALID_ARG), orders the feed after the work already queued on
+ *   consumer_stream, and queues the first depth items.
+ * qsc_feed_next: the next item: consumer_stream waits for its decode (no
+ *   host wait); *buf_index is its buffer, *first_scan its first scan and
+ *   *n_scans its scan count, 0 after the last item. The item is the
+ *   consumer's until qsc_feed_release; calling next again first ->
+ *   INVALID_ARG.
+ * qsc_feed_release: the consumer is done with the item as of the work queued
+ *   on consumer_stream so far; its buffer then takes the item depth ahead.
+ * qsc_feed_destroy: waits for the feed's decodes and frees its stream and
+ *   events; MALFORMED if a decoded stream was malformed (those items' buffers
+ *   hold no result). The feed's decodes use only the resident's error word
+ *   and read-only tables, so queries on consumer_stream may run meanwhile.
+ */
+typedef struct qsc_feed qsc_feed;
+qsc_status qsc_feed_create(qsc_resident *res, uint32_t first_block, uint32_t n_blocks, uint32_t blocks_per_item,
+                           int out_kind, uint32_t depth, void *const *d_bufs, uint64_t buf_bytes,
+                           void *consumer_stream, qsc_feed **out);
+qsc_status qsc_feed_next(qsc_feed *feed, uint32_t *buf_index, uint64_t *first_scan, uint32_t *n_scans);
+qsc_status qsc_feed_release(qsc_feed *feed);
+qsc_status qsc_feed_destroy(qsc_feed *feed);
+
 /* ---------------------------------------------------------------- polar interaction index
  * qsc_index_build: builds the resident's interaction index (paired-resident
  *   page, "Operation pipeline" items 3-4): the valid pixels ordered by squared

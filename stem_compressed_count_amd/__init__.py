@@ -18,6 +18,7 @@ Entry points mirror include/qsc.h:
     Resident.decode_region(r0, r1, c0, c1)   qsc_decode_region
     Resident.sum_dp(scan_mask, stride)       qsc_sum_dp
     Resident.decode_blocks(first, n, kind)   qsc_decode_blocks
+    Resident.feed(first, n, per, kind, depth) qsc_feed_create / _next / _release / _destroy
     Resident.index_build(center)             qsc_index_build
     Resident.masked_sum_delta(prev, ...)     qsc_masked_sum_delta
     Resident.finish()                        qsc_finish
@@ -94,6 +95,11 @@ _SIGS = {
     "qsc_sum_dp": ([_vp, _vp, _u32, _vp, _vp, _vp, ctypes.c_int], _i32),
     "qsc_decode_blocks": ([_vp, _u32, _u32, ctypes.c_int, _vp, _vp, ctypes.c_int], _i32),
     "qsc_finish": ([_vp, _vp], _i32),
+    "qsc_feed_create": ([_vp, _u32, _u32, _u32, ctypes.c_int, _u32, ctypes.POINTER(_vp), _u64, _vp,
+                         ctypes.POINTER(_vp)], _i32),
+    "qsc_feed_next": ([_vp, ctypes.POINTER(_u32), ctypes.POINTER(_u64), ctypes.POINTER(_u32)], _i32),
+    "qsc_feed_release": ([_vp], _i32),
+    "qsc_feed_destroy": ([_vp], _i32),
     "qsc_index_build": ([_vp, ctypes.c_int32, ctypes.c_int32, _vp], _i32),
     "qsc_masked_sum_delta": ([_vp, _vp, _vp, _vp, _u32, _vp, _vp, ctypes.c_int], _i32),
     "qsc_last_error": ([_vp], ctypes.c_char_p),
@@ -378,6 +384,15 @@ class Resident:
                                           _stream_handle(stream), int(wait)), "decode_blocks")
         return o.view(-1, self.P)
 
+    def feed(self, first_block=0, n_blocks=None, blocks_per_item=1, kind="native", depth=2, stream=None):
+        """Iterator over whole-block frames decoded depth items ahead on a stream of the
+        library's (qsc_feed_*): yields (frames (scans, P) tensor, first scan). A yielded
+        tensor is a view of one of the feed's buffers and is reused once the iteration
+        moves on: copy it to keep it. Work queued on the consumer stream (the current one,
+        or stream) while an item is held is ordered before its buffer is reused."""
+        return Feed(self, first_block, self.info.n_blocks - first_block if n_blocks is None else n_blocks,
+                    blocks_per_item, kind, depth, stream)
+
     def sum_dp(self, scan_mask=None, block_stride=1, out_sum=None, out_mean=None, stream=None, wait=True):
         """Sum (int64 storage of uint64) and mean (float32) diffraction pattern over the selected scans."""
         import torch
@@ -425,6 +440,59 @@ class Resident:
 
     def __del__(self):
         self.close()
+
+
+class Feed:
+    """Whole-block frames of a resident, decoded ahead on the library's own stream (qsc_feed_*)."""
+
+    def __init__(self, res, first_block, n_blocks, blocks_per_item, kind, depth, stream):
+        import torch
+        kinds = {"native": 0, "calibrated": 1, "amplitude": 2}
+        if kind not in kinds:
+            raise ValueError(f"kind must be one of {sorted(kinds)}")
+        self.res, self.P = res, res.P
+        self._h = _vp()
+        self._held = False
+        dt = torch.float32 if kinds[kind] else (torch.uint8 if res.dtype == 1 else torch.int16)
+        n = blocks_per_item * 512 * res.P
+        self.bufs = [torch.empty(n, dtype=dt, device=res.device) for _ in range(max(0, depth))]
+        self.stream = stream
+        ptrs = (_vp * max(1, depth))(*[b.data_ptr() for b in self.bufs])
+        res._check(lib.qsc_feed_create(res._h, first_block, n_blocks, blocks_per_item, kinds[kind], depth, ptrs,
+                                       n * self.bufs[0].element_size() if self.bufs else 0,
+                                       _stream_handle(stream), ctypes.byref(self._h)), "feed_create")
+
+    def __iter__(self):
+        return self
+
+    def __next__(self):
+        if not self._h:
+            raise StopIteration
+        if self._held:
+            self.res._check(lib.qsc_feed_release(self._h), "feed_release")
+            self._held = False
+        i, s0, n = _u32(), _u64(), _u32()
+        self.res._check(lib.qsc_feed_next(self._h, ctypes.byref(i), ctypes.byref(s0), ctypes.byref(n)), "feed_next")
+        if n.value == 0:
+            self.close()
+            raise StopIteration
+        self._held = True
+        return self.bufs[i.value][:n.value * self.P].view(n.value, self.P), s0.value
+
+    def close(self):
+        """Waits for the feed's decodes; raises if a decoded stream was malformed."""
+        if self._h:
+            if self._held:
+                lib.qsc_feed_release(self._h)
+                self._held = False
+            h, self._h = self._h, _vp()
+            self.res._check(lib.qsc_feed_destroy(h), "feed")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def as_unsigned(t):

@@ -574,6 +574,133 @@ qsc_status qsc_decode_blocks(qsc_resident *res, uint32_t first_block, uint32_t n
     return finish_query(res, e, st, wait);
 }
 
+// ---------------------------------------------------------------- block feed
+struct qsc_feed {
+    qsc_resident *res = nullptr;
+    hipStream_t prod = nullptr;  // the feed's own stream (default priority)
+    hipStream_t cons = nullptr;  // the caller's stream
+    std::vector<void *> bufs;
+    std::vector<hipEvent_t> ready, freed;  // per buffer: decode done (producer), consumer done with it
+    uint32_t first = 0, n_blocks = 0, per = 1, depth = 1, n_items = 0, issued = 0, consumed = 0;
+    int kind = 0;
+    bool holding = false;
+};
+
+static void feed_free(qsc_feed *f) {
+    if (f->prod) (void)hipStreamSynchronize(f->prod);
+    for (hipEvent_t e : f->ready)
+        if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : f->freed)
+        if (e) (void)hipEventDestroy(e);
+    if (f->prod) (void)hipStreamDestroy(f->prod);
+    delete f;
+}
+
+// Decodes item f->issued into buffer issued % depth on the feed's stream, once
+// the consumer has released that buffer's previous item.
+static qsc_status feed_issue(qsc_feed *f) {
+    const uint32_t j = f->issued, i = j % f->depth;
+    if (j >= f->depth && hipStreamWaitEvent(f->prod, f->freed[i], 0) != hipSuccess)
+        return fail(f->res, QSC_ERR_HIP, "feed: wait for a released buffer");
+    const uint32_t b0 = f->first + j * f->per;
+    const uint32_t nb = std::min(f->per, f->first + f->n_blocks - b0);
+    const qsc_status st = qsc_decode_blocks(f->res, b0, nb, f->kind, f->bufs[i], f->prod, 0);
+    if (st != QSC_OK) return st;
+    if (hipEventRecord(f->ready[i], f->prod) != hipSuccess) return fail(f->res, QSC_ERR_HIP, "feed: record a decode");
+    f->issued++;
+    return QSC_OK;
+}
+
+qsc_status qsc_feed_create(qsc_resident *res, uint32_t first_block, uint32_t n_blocks, uint32_t blocks_per_item,
+                           int out_kind, uint32_t depth, void *const *d_bufs, uint64_t buf_bytes,
+                           void *consumer_stream, qsc_feed **out) {
+    if (!res || !out) return QSC_ERR_INVALID_ARG;
+    *out = nullptr;
+    const Geometry &g = res->g;
+    const uint64_t elem = out_kind ? 4 : g.dtype;
+    if (n_blocks < 1 || first_block >= g.n_blocks() || n_blocks > g.n_blocks() - first_block ||
+        blocks_per_item < 1 || depth < 1 || depth > 64 || out_kind < 0 || out_kind > 2 || (out_kind == 1 && !g.scaled) ||
+        !d_bufs || buf_bytes < uint64_t(blocks_per_item) * kBlock * g.P() * elem)
+        return fail(res, QSC_ERR_INVALID_ARG, "feed_create: bad block range, item size, depth, kind or buffers");
+    for (uint32_t i = 0; i < depth; i++)
+        if (!d_bufs[i]) return fail(res, QSC_ERR_INVALID_ARG, "feed_create: null buffer");
+    if (!on_device(res)) return fail(res, QSC_ERR_HIP, "cannot select the resident's device");
+    qsc_feed *f = new (std::nothrow) qsc_feed;
+    if (!f) return QSC_ERR_OOM;
+    f->res = res;
+    f->cons = static_cast<hipStream_t>(consumer_stream);
+    f->bufs.assign(d_bufs, d_bufs + depth);
+    f->first = first_block;
+    f->n_blocks = n_blocks;
+    f->per = blocks_per_item;
+    f->depth = depth;
+    f->n_items = (n_blocks + blocks_per_item - 1) / blocks_per_item;
+    f->kind = out_kind;
+    f->ready.assign(depth, nullptr);
+    f->freed.assign(depth, nullptr);
+    hipError_t e = hipStreamCreateWithFlags(&f->prod, hipStreamNonBlocking);
+    for (uint32_t i = 0; i < depth && e == hipSuccess; i++) {
+        e = hipEventCreateWithFlags(&f->ready[i], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f->freed[i], hipEventDisableTiming);
+    }
+    // the buffers may still be in use by work the caller queued before
+    hipEvent_t start = nullptr;
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&start, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(start, f->cons);
+    if (e == hipSuccess) e = hipStreamWaitEvent(f->prod, start, 0);
+    if (start) (void)hipEventDestroy(start);
+    if (e != hipSuccess) {
+        feed_free(f);
+        return hip_fail(res, e, "feed: stream and events");
+    }
+    qsc_status st = QSC_OK;
+    while (st == QSC_OK && f->issued < std::min(f->depth, f->n_items)) st = feed_issue(f);
+    if (st != QSC_OK) {
+        feed_free(f);
+        return st;
+    }
+    *out = f;
+    return QSC_OK;
+}
+
+qsc_status qsc_feed_next(qsc_feed *f, uint32_t *buf_index, uint64_t *first_scan, uint32_t *n_scans) {
+    if (!f || !buf_index || !first_scan || !n_scans) return QSC_ERR_INVALID_ARG;
+    if (f->holding) return fail(f->res, QSC_ERR_INVALID_ARG, "feed_next: release the current item first");
+    *buf_index = 0;
+    *first_scan = 0;
+    *n_scans = 0;
+    if (f->consumed == f->n_items) return QSC_OK;
+    const uint32_t i = f->consumed % f->depth;
+    if (hipStreamWaitEvent(f->cons, f->ready[i], 0) != hipSuccess)
+        return fail(f->res, QSC_ERR_HIP, "feed_next: wait for a decode");
+    const uint64_t b0 = f->first + uint64_t(f->consumed) * f->per;
+    const uint64_t s0 = b0 * kBlock;
+    const uint64_t s1 = std::min<uint64_t>(f->res->g.S(), std::min<uint64_t>(b0 + f->per, f->first + f->n_blocks) * kBlock);
+    *buf_index = i;
+    *first_scan = s0;
+    *n_scans = uint32_t(s1 - s0);
+    f->holding = true;
+    return QSC_OK;
+}
+
+qsc_status qsc_feed_release(qsc_feed *f) {
+    if (!f) return QSC_ERR_INVALID_ARG;
+    if (!f->holding) return fail(f->res, QSC_ERR_INVALID_ARG, "feed_release: no item is held");
+    const uint32_t i = f->consumed % f->depth;
+    if (hipEventRecord(f->freed[i], f->cons) != hipSuccess) return fail(f->res, QSC_ERR_HIP, "feed_release");
+    f->consumed++;
+    f->holding = false;
+    return f->issued < f->n_items ? feed_issue(f) : QSC_OK;
+}
+
+qsc_status qsc_feed_destroy(qsc_feed *f) {
+    if (!f) return QSC_ERR_INVALID_ARG;
+    qsc_resident *res = f->res;
+    const qsc_status st = on_device(res) ? check_done(res, f->prod) : QSC_ERR_HIP;
+    feed_free(f);
+    return st;
+}
+
 static void drop_index(qsc_resident *res) {
     for (void **p : {(void **)&res->d_ix_perm, (void **)&res->d_ix_leaf_valid, (void **)&res->d_ix_packed,
                      (void **)&res->d_ix_offset, (void **)&res->d_ix_fields, (void **)&res->d_ix_width,
