@@ -501,6 +501,67 @@ __device__ __forceinline__ void region_fill(const DevResident &r, uint32_t b, ui
         if (rw.inside()) region_put<WIDE, AMP>(ra, rw.index(r.P), p, v, rw.scale, rw.offset);
 }
 
+// ------------------------------------------------------------------ staged stream window
+// A uint16 byte-rANS stream whose symbol 255 (escape) is frequent spends up to
+// 32 bits a step: a renormalisation word and a 16-bit literal. Refilled one
+// dword at a time from a lane's own stream, it sends one cache-line request
+// per 4 bytes, and with thousands of streams in flight per CU each line has
+// left the L1 before its next dword is read: the L1 then misses on nearly
+// every access and its queue of misses bounds the decode.
+//
+// The staged form moves each stream in 32-byte chunks instead. Every kStageC
+// steps (a cadence the whole wave shares) a lane whose older ring half has
+// been consumed requests the next chunk with two 16-byte loads, and at the
+// next cadence writes it into its ring in LDS. Every lane issues the loads at
+// every cadence, and a lane with no request addresses past the buffer range
+// (the hardware returns zero and reads no memory), so the compiler's wait
+// before the write counts them exactly. A step reads its two candidate words
+// (renormalisation, literal) as one word pair from the ring. A step consumes
+// at most two words, and a cadence of 4 steps with a two-chunk ring keeps a
+// lane's next two words written before it reads them.
+constexpr uint32_t kStageC = 4;    // steps between cadence points
+constexpr uint32_t kStageDw = 17;  // ring dwords per stream: two chunks of 8 and a copy of dword 0
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+__device__ __forceinline__ u32x4 bload4(Rsrc rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+}
+
+// Slot s of a block's decode table as fe = f | symbol << 24 (v_mad_u32_u24
+// reads only f) and bias = s - c[symbol]: two words per slot, read together, or
+// (T32) one word f | bias << 12 | symbol << 24.
+template <bool T32>
+__device__ __forceinline__ void tbl_read(const uint32_t *tbl, uint32_t s, uint32_t &fe, uint32_t &bias) {
+    if constexpr (T32) {
+        const uint32_t w = tbl[s];
+        fe = w & 0xFF000FFFu;
+        bias = __builtin_amdgcn_ubfe(w, 12, 12);
+    } else {
+        const uint2 w = reinterpret_cast<const uint2 *>(tbl)[s];
+        fe = w.x;
+        bias = w.y;
+    }
+}
+
+struct Stage {
+    uint32_t wi;    // next word of the stream, counted from the start of chunk 0
+    uint32_t fl;    // chunks requested (the latest is written at the next cadence)
+    uint32_t c0;    // chunk 0's offset in the staging range (a 32-byte boundary)
+    uint32_t endc;  // the stream's end in that range: no chunk starts at or past it
+    bool pend;      // a chunk is in flight
+    u32x4 q0, q1;   // its two halves
+};
+
+// Dword i of a lane's ring, stored lane-major (dword i of the 64 lanes side by
+// side) so the lanes of a wave fall in distinct banks whatever their i.
+__device__ __forceinline__ void ring_put8(uint32_t *q, const u32x4 &a, const u32x4 &b) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        q[64 * i] = a[i];
+        q[64 * (4 + i)] = b[i];
+    }
+}
+
 // ------------------------------------------------------------------ byte-rANS tile
 // Per-slot state kept in registers across the 512 steps (kept small: the tile
 // holds up to two slots per lane).
@@ -523,10 +584,15 @@ struct RSlot {
 // half: 0 decodes whole streams; 1 the first kSplit scans of each stream
 // (checked against its split point); 2 the rest, resumed from the split point
 // (a complete block's streams then take two lanes, one per half).
-template <int K, bool WIDE, Op OP>
+//
+// STG: escape-heavy waves take the staged form, with `ring` the workgroup's
+// stream rings (kStageDw x 64 dwords per wave), and the block table has one
+// word per slot.
+template <int K, bool WIDE, Op OP, bool STG = false>
 __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
                           uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt,
-                          const RegionArgs &ra, const DpTile &dt, uint32_t half = 0, bool raw_block = false) {
+                          const RegionArgs &ra, const DpTile &dt, uint32_t half = 0, bool raw_block = false,
+                          uint32_t *ring = nullptr) {
     const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
@@ -626,7 +692,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     // byte-rANS decode step (FORMAT 2.3). The block table holds two words per
     // slot, side by side and read by one 64-bit LDS load: f | symbol << 24
     // (v_mad_u32_u24 reads only the low 24 bits, so the symbol rides along) and
-    // slot - c[symbol]. A renormalisation appends the next 16-bit word with one
+    // slot - c[symbol] (one word per slot under STG: see tbl_read). A renormalisation appends the next 16-bit word with one
     // byte permute; an escape (symbol 255 of a uint16 stream) reads its literal.
     //
     // One step of every slot: values in v[], escapes resolved. Three forms of
@@ -634,17 +700,42 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     //  kMixed   some slot is RAW or idle: every slot runs the unified step;
     //  kEscape  all slots are rANS and the block's table codes symbol 255;
     //  kPlain   all slots are rANS and no escape can occur.
-    constexpr int kMixed = 0, kEscape = 1, kPlain = 2;
+    //  kStaged  (STG) as kEscape, with the stream words read from LDS rings.
+    constexpr int kMixed = 0, kEscape = 1, kPlain = 2, kStaged = 3;
+    static_assert(!STG || K == 1, "the staged form decodes one stream per lane");
+    Stage sg[STG ? K : 1];
+    uint32_t *rk[STG ? K : 1];
+    if constexpr (STG) rk[0] = ring + (threadIdx.x >> 6) * kStageDw * 64 + lane;
     auto step = [&](auto form, bool even, uint32_t (&v)[K]) {
         constexpr int F = decltype(form)::value;
+        if constexpr (F == kStaged) {
+            // the step of the escape form, its two candidate words taken from
+            // the ring as one pair (words wi and wi + 1)
+            uint32_t e[K], bias[K], w2[K];
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                tbl_read<STG>(tbl, sl[k].x & 4095u, e[k], bias[k]);
+                const uint32_t *q = rk[k] + ((sg[k].wi >> 1) & 15u) * 64u;
+                w2[k] = __builtin_amdgcn_alignbit(q[64], q[0], sg[k].wi << 4);
+            }
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                RSlot &z = sl[k];
+                const uint32_t xn = __umul24(e[k], z.x >> 12) + bias[k];
+                const bool need = xn < 65536u;
+                z.x = need ? __builtin_amdgcn_perm(xn, w2[k], 0x05040100u) : xn;
+                const uint32_t lit = need ? w2[k] >> 16 : w2[k] & 0xFFFFu;
+                const uint32_t sym = e[k] >> 24;
+                const bool esc = sym == 255u;
+                v[k] = esc ? lit : sym;
+                bad |= (uint32_t)(esc && lit < 255u);
+                sg[k].wi += (uint32_t)need + (uint32_t)esc;
+            }
+            return;
+        }
         uint32_t e[K], bias[K];
 #pragma unroll
-        for (int k = 0; k < K; k++) {
-            const uint32_t slot = sl[k].x & 4095u;
-            const uint2 eb = reinterpret_cast<const uint2 *>(tbl)[slot];
-            e[k] = eb.x;
-            bias[k] = eb.y;
-        }
+        for (int k = 0; k < K; k++) tbl_read<STG>(tbl, sl[k].x & 4095u, e[k], bias[k]);
         bool esc_any = false;
         bool esc[K];
 #pragma unroll
@@ -696,6 +787,53 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
 #pragma unroll
         for (int k = 0; k < K; k++) bbits_refill(sl[k].s, rs);
     };
+    // The staged form's range: the block from the 32-byte boundary at or
+    // below its start, so chunk loads are aligned.
+    const uint32_t delta = STG ? (uint32_t)reinterpret_cast<uint64_t>(r.payload + base) & 31u : 0u;
+    const Rsrc rs2 = STG ? block_rsrc(r.payload + base - delta, nbytes + delta) : rs;
+    // its cadence: write the chunk that landed, then request the next where
+    // the ring half it goes to has been consumed (see the staged window above)
+    auto cadence = [&]() {
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            const Stage &g = sg[k];
+            if (g.pend) {
+                const uint32_t half_i = (g.fl - 1u) & 1u;
+                ring_put8(rk[k] + half_i * 8u * 64u, g.q0, g.q1);
+                if (half_i == 0) rk[k][16 * 64] = g.q0[0];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            Stage &g = sg[k];
+            const bool req = sl[k].live && g.wi >= 16u * (g.fl - 1u) && g.c0 + 32u * g.fl < g.endc;
+            const uint32_t o = req ? g.c0 + 32u * g.fl : 0x80000000u;
+            g.q0 = bload4(rs2, o);
+            g.q1 = bload4(rs2, o + 16u);
+            g.pend = req;
+            g.fl += req ? 1u : 0u;
+        }
+    };
+    // the staged form's start: the words after those the reservoir has taken
+    // (header and state, or the split point), chunks 0 and 1 in the ring
+    auto stage_init = [&]() {
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            Stage &g = sg[k];
+            const RSlot &z = sl[k];
+            const uint32_t rel = z.org + bbits_used(z.s, z.org) / 8u + delta;
+            g.c0 = rel & ~31u;
+            g.wi = (rel - g.c0) >> 1;
+            g.endc = z.live ? z.org + z.len + delta : 0u;
+            g.fl = 2;
+            g.pend = false;
+            const uint32_t o = z.live ? g.c0 : 0x80000000u;
+            const u32x4 a = bload4(rs2, o), bq = bload4(rs2, o + 16u), c = bload4(rs2, o + 32u), d = bload4(rs2, o + 48u);
+            ring_put8(rk[k], a, bq);
+            ring_put8(rk[k] + 8u * 64u, c, d);
+            rk[k][16 * 64] = a[0];
+        }
+    };
 
     auto run = [&](auto form, auto rowu) {
         constexpr bool ROWU = decltype(rowu)::value;  // moments of a wave inside one detector row
@@ -703,6 +841,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         // least 33 bits, enough for a renormalisation word and a literal, so an
         // escape reads its literal without a load of its own
         constexpr bool every = decltype(form)::value == kEscape;
+        constexpr bool staged = decltype(form)::value == kStaged;  // sums and moments only
         if constexpr (is_region(OP)) {
             // values of scans inside the rectangle go straight to the output;
             // frames store every step, and a shorter unroll keeps their
@@ -841,7 +980,11 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     asm volatile("" : "+v"(a0[jj]));
                     if constexpr (OP == Op::Moments && !ROWU) asm volatile("" : "+v"(ar[jj]), "+v"(ac[jj]));
                     if constexpr (OP == Op::Moments && ROWU) asm volatile("" : "+v"(ac[jj]));
-                    if (every || (jj & 1)) refill();
+                    if constexpr (staged) {
+                        if (jj % kStageC == kStageC - 1) cadence();
+                    } else if (every || (jj & 1)) {
+                        refill();
+                    }
                     // keep the scheduler's interleaving to the K independent slots of one step
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -878,7 +1021,11 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     if (tr) atomicAdd(&pt.mr[j], (unsigned long long)tr);
                     if (tc) atomicAdd(&pt.mc[j], (unsigned long long)tc);
                 }
-                if (every || (j & 1) || j + 1 == n) refill();
+                if constexpr (staged) {
+                    if (j % kStageC == kStageC - 1) cadence();
+                } else if (every || (j & 1) || j + 1 == n) {
+                    refill();
+                }
             }
         }
     };
@@ -1154,10 +1301,21 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     };
     if (__builtin_amdgcn_ballot_w64(raw || (idle && !idle_ok))) {
         run(std::integral_constant<int, kMixed>{}, std::false_type{});
-    } else if (WIDE && (tbl[2 * 4095] >> 24) == 255u) {
+    } else if (WIDE && (tbl[(STG ? 1 : 2) * 4095] >> 24) == 255u) {
         // symbols are laid out in increasing order, so the last slot holds the
         // largest coded symbol: 255 there means escapes can occur
-        run_rows(std::integral_constant<int, kEscape>{});
+        if constexpr (STG) {
+            stage_init();
+            run_rows(std::integral_constant<int, kStaged>{});
+            // hand the end position to the reservoir, where the end checks read it
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                sl[k].s.off = sg[k].c0 + 2u * sg[k].wi - delta;
+                sl[k].s.n = 0;
+            }
+        } else {
+            run_rows(std::integral_constant<int, kEscape>{});
+        }
     } else {
         run_rows(std::integral_constant<int, kPlain>{});
     }
@@ -1785,13 +1943,15 @@ constexpr uint32_t kMaxItems = 2 * kMaxPlanTiles * kPlanFine / (WG / 2);
 // items (whose values the query subtracts) start after the first mask's:
 // its pixel numbering starts at the first multiple of cap past the first's.
 //
+// one_slot: items of at most one stream per lane.
+//
 // can_split: the streams have split points. When every item of half-workgroup
 // size fits one round of the resident workgroups, the query is latency-bound:
 // each item then takes half a workgroup of streams and the other half of the
 // lanes decodes their second halves, so the chain of dependent steps halves.
 template <int WG>
 __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P, uint32_t n_visited, bool two,
-                                             bool can_split, uint16_t *desc, uint32_t *wtot) {
+                                             bool can_split, uint16_t *desc, uint32_t *wtot, bool one_slot = false) {
     constexpr uint32_t kPer = 2 * kMaxPlanTiles / WG;
     constexpr uint32_t kWaves = WG / 64;
     __shared__ uint32_t wpart[5][kWaves];  // per wave: the second mask's sum, each mask's last tile, bytes
@@ -1856,7 +2016,7 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
     // make them about twice as slow. 1024-lane workgroups fill a
     // compute unit alone and pay only when most pixels are selected.
     const bool dim = total_bytes * 10 <= (uint64_t)total * kBlk * 4;
-    if ((WG < 1024 ? dim : 2 * total >= P) && cost(2 * WG) < cost(cap)) cap = 2 * WG;
+    if (!one_slot && (WG < 1024 ? dim : 2 * total >= P) && cost(2 * WG) < cost(cap)) cap = 2 * WG;
     const bool halves = can_split && cap == WG / 2 && cost(WG / 2) <= 1.0f;
     const uint32_t n_first = (total1 + cap - 1) / cap, pad = n_first * cap - total1;
     // tile t starts item k when it holds the pixel numbered k * cap
@@ -1938,7 +2098,8 @@ __device__ __forceinline__ uint32_t index_group(const DevResident &r, const uint
 // RANS stream may use it) is all zero. f is thread s's frequency, loaded by
 // the caller early (before the item's pixel selection) so that its latency
 // overlaps that work: 512 bytes per build instead of a 32 KB expanded table.
-template <int WG>
+// T32: one word per slot, f | (t - c[s]) << 12 | s << 24 (a 16 KB table).
+template <int WG, bool T32 = false>
 __device__ __forceinline__ void rans_table_build(uint32_t f, uint32_t *tbl, uint32_t *cum, uint32_t *wtot) {
     static_assert(WG == 256, "one symbol per thread");
     constexpr uint32_t kSlots = 4096 / WG;
@@ -1965,7 +2126,12 @@ __device__ __forceinline__ void rans_table_build(uint32_t f, uint32_t *tbl, uint
     uint2 *out = reinterpret_cast<uint2 *>(tbl);
     if (total == 0) {
 #pragma unroll
-        for (uint32_t j = 0; j < kSlots; j++) out[t0 + j] = make_uint2(0u, 0u);
+        for (uint32_t j = 0; j < kSlots; j++) {
+            if constexpr (T32)
+                tbl[t0 + j] = 0u;
+            else
+                out[t0 + j] = make_uint2(0u, 0u);
+        }
         return;
     }
     // the last symbol whose range starts at or before t0 (its range holds t0)
@@ -1984,7 +2150,10 @@ __device__ __forceinline__ void rans_table_build(uint32_t f, uint32_t *tbl, uint
             c = e;
             e = cum[sym + 1];
         }
-        out[t] = make_uint2(((e - c) & 0xFFFu) | (sym << 24), t - c);
+        if constexpr (T32)
+            tbl[t] = ((e - c) & 0xFFFu) | ((t - c) << 12) | (sym << 24);
+        else
+            out[t] = make_uint2(((e - c) & 0xFFFu) | (sym << 24), t - c);
     }
 }
 
@@ -2150,17 +2319,21 @@ __device__ __forceinline__ bool hold_partials(const DevResident &r) {
     return (uint64_t)r.P * (r.dtype == 2 ? 65535u : 255u) <= 0xFFFFFFFFull;
 }
 
-template <bool WIDE, Op OP>
+// STG: sums and moments of residents whose blocks are mostly escape-heavy: one
+// stream per lane, 17 KB of stream rings and a table of one word per slot, so
+// the LDS allows as many workgroups per CU as without.
+template <bool WIDE, Op OP, bool STG = false>
 __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_rans(DevResident r, const uint8_t *mask, int complement,
                                                          uint32_t stride, uint32_t n_visited, uint32_t tile_px,
                                                          const uint32_t *plan, void *out, int out64, int negate,
                                                          RegionBlocks rb, RegionArgs ra, AuxArgs da) {
-    __shared__ __align__(16) uint32_t tbl[2 * 4096];  // per slot: f | symbol << 24, slot - c[symbol]
+    __shared__ __align__(16) uint32_t tbl[STG ? 4096 : 2 * 4096];  // per slot: f | symbol << 24, slot - c[symbol]
     __shared__ SharedPartials<OP> sp;
     __shared__ uint16_t sel[2 * kRansWG];
     __shared__ uint32_t wtot[kRansWG / 64];
     __shared__ uint32_t sbits[OP == Op::Dp ? 16 : 1];
     __shared__ uint16_t desc[kMaxItems<kRansWG>];
+    __shared__ uint32_t ring[STG ? (kRansWG / 64) * kStageDw * 64 : 1];
     // planned: items of `cap` selected pixels; else every pixel tile of
     // tile_px. With a subtracted mask, its items follow those of mask.
     const bool two = da.neg_mask != nullptr;
@@ -2168,7 +2341,7 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     bool halves = false;
     if (plan) {
         const PlanView pv =
-            plan_cut<kRansWG>(plan, r.P, n_visited, two, (OP == Op::Sum || OP == Op::Moments) && r.split, desc, wtot);
+            plan_cut<kRansWG>(plan, r.P, n_visited, two, (OP == Op::Sum || OP == Op::Moments) && r.split, desc, wtot, STG);
         n_live = pv.n_items;
         n_first = pv.n_first;
         cap = pv.cap;
@@ -2224,7 +2397,7 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         if (b != loaded) {
             // no partials are held here (they belong to the block), so they lend
             // the build room for the prefix sums; they are zeroed after it
-            rans_table_build<kRansWG>(fq, tbl, sp.m0, wtot);
+            rans_table_build<kRansWG, STG>(fq, tbl, sp.m0, wtot);
             loaded = b;
             __syncthreads();  // the table is complete, and cum is read before the partials are zeroed
         }
@@ -2239,7 +2412,7 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         }
         __syncthreads();
         // at most two slots per lane: with three decode forms, more do not fit 3 waves per SIMD
-        const uint32_t K = (OP == Op::Index || n_sel <= kRansWG) ? 1 : 2;  // an index leaf is one wave
+        const uint32_t K = (STG || OP == Op::Index || n_sel <= kRansWG) ? 1 : 2;  // an index leaf is one wave
         // split items (at most half a workgroup of streams): waves 0-1 decode the
         // first halves of the streams, waves 2-3 the second halves
         const uint32_t wave = threadIdx.x >> 6;
@@ -2247,10 +2420,12 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
         const uint32_t half = split_item ? 1u + (wave >> 1) : 0u;
         const uint32_t first = split_item ? (wave & 1u) * 64u : wave * 64 * K;
         if (first < n_sel) {  // whole waves without a stream skip the decode
-            if (K == 2)
-                rans_tile<2, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, 0, raw_block);
+            if (!STG && K == 2)
+                rans_tile<STG ? 1 : 2, WIDE, OP, STG>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, 0,
+                                                      raw_block, ring);
             else
-                rans_tile<1, WIDE, OP>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, half, raw_block);
+                rans_tile<1, WIDE, OP, STG>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, half, raw_block,
+                                            ring);
         }
         __syncthreads();
         if (kAcc && !hold) {
@@ -2749,6 +2924,13 @@ static void launch_layout(const DevResident &r, const uint8_t *mask, int complem
                           const RegionBlocks &rb, const RegionArgs &ra, hipStream_t st, const AuxArgs &da = AuxArgs{}) {
     if (r.layout == 0) {
         const uint32_t cands[2] = {2 * kRansWG, kRansWG};
+        if constexpr (W && (O == Op::Sum || O == Op::Moments)) {
+            if (r.esc_heavy) {  // one stream per lane
+                launch_items(k_reduce_rans<W, O, true>, kRansWG, cands + 1, 1, st, r, mask, complement, stride,
+                             n_visited, out, out64, negate, init, n_init, rb, ra, da);
+                return;
+            }
+        }
         launch_items(k_reduce_rans<W, O>, kRansWG, cands, 2, st, r, mask, complement, stride, n_visited, out, out64,
                      negate, init, n_init, rb, ra, da);
     } else {

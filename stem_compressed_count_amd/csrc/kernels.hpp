@@ -40,6 +40,7 @@ struct DevResident {
     const uint32_t *split;   // byte-rANS: per (block, pixel), the state and byte offset of the stream after
                              // its first kSplit scans (two words), or null when not built
     const uint8_t *raw_blk;  // byte-rANS: per block, nonzero when it holds a RAW stream (null: none does)
+    uint32_t esc_heavy;      // byte-rANS uint16: most blocks give the escape symbol at least 1/4 of the table
     uint64_t S;
     uint32_t P, G, det_cols, scan_cols, n_blocks, dtype, layout;
 };

@@ -224,6 +224,18 @@ qsc_status build_resident(const Parsed &ps, const uint8_t *blob, const uint8_t *
         for (uint8_t f : flags)
             if (f) d.raw_blk = res->d_raw_blk;
     }
+    // uint16 blocks whose tables give the escape symbol (255) at least a
+    // quarter of the 4096 slots: when most blocks are such, sums and moments
+    // take the staged decode, which reads each stream in 32-byte chunks
+    d.esc_heavy = 0;
+    if (g.layout == 0 && g.dtype == 2) {
+        std::vector<uint16_t> fq(256ull * g.n_blocks());
+        if ((e = hipMemcpy(fq.data(), d.freq, 2 * fq.size(), hipMemcpyDeviceToHost)) != hipSuccess)
+            return bail(e, "frequency tables");
+        uint64_t heavy = 0;
+        for (uint32_t b = 0; b < g.n_blocks(); b++) heavy += fq[256ull * b + 255] >= 1024;
+        d.esc_heavy = 2 * heavy >= g.n_blocks() ? 1u : 0u;
+    }
     // split points of the byte-rANS streams of complete blocks: one decode of
     // their first halves, so that latency-bound queries decode both halves of
     // a stream side by side
