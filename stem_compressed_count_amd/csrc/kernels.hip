@@ -592,7 +592,7 @@ template <int K, bool WIDE, Op OP, bool STG = false>
 __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *sel, uint32_t p0, uint32_t n_sel, uint32_t first, uint32_t b,
                           uint32_t n, uint64_t base, uint32_t nbytes, const uint32_t *tbl, const Partials<OP> &pt,
                           const RegionArgs &ra, const DpTile &dt, uint32_t half = 0, bool raw_block = false,
-                          uint32_t *ring = nullptr) {
+                          uint32_t *ring = nullptr, bool touch = true) {
     const Rsrc rs = block_rsrc(r.payload + base, nbytes);
     const uint32_t lane = lane_id();
     const uint32_t maxv = WIDE ? 65535u : 255u;
@@ -651,11 +651,11 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             // RANS stream at its split point (state, byte offset from the stream start)
             const uint64_t si = 2 * ((uint64_t)b * r.P + z.p);
             const uint32_t off = z.raw ? 2u + kSplit * (WIDE ? 2u : 1u) : r.split[si + 1];
-            if (!raw_whole) touched += touch_stream(rs, z.org + off, z.len > off ? z.len - off : 0u);
+            if (!raw_whole && touch) touched += touch_stream(rs, z.org + off, z.len > off ? z.len - off : 0u);
             bbits_init(z.s, rs, z.org + off);
             if (!z.raw) z.x = r.split[si];
         } else {
-            if (!raw_whole) touched += touch_stream(rs, z.org, z.len);
+            if (!raw_whole && touch) touched += touch_stream(rs, z.org, z.len);
             bbits_init(z.s, rs, z.org);
             pop16(z.s);  // header
             if (mode == 1) {
@@ -1933,6 +1933,7 @@ struct PlanView {
     uint32_t cap;               // selected pixels per item
     uint32_t end[2];            // per mask, the end of its last non-empty tile (pixels)
     bool halves;                // decode each stream's two halves side by side (split points)
+    bool sparse;                // at most a quarter of the pixels are selected (per mask)
 };
 
 // Most items a plan can hold: two masks of kMaxPlanTiles tiles cut in halves of a workgroup.
@@ -2034,7 +2035,7 @@ __device__ __forceinline__ PlanView plan_cut(const uint32_t *counts, uint32_t P,
     }
     __syncthreads();
     return PlanView{n_first + (total2 + cap - 1) / cap, n_first, cap,
-                    {min(end0 * kPlanFine, P), min(end1 * kPlanFine, P)}, halves};
+                    {min(end0 * kPlanFine, P), min(end1 * kPlanFine, P)}, halves, 4ull * total <= (two ? 2ull : 1ull) * P};
 }
 
 // The pixels of one planned item: from tile (desc >> 6) on, skipping that
@@ -2339,9 +2340,14 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
     const bool two = da.neg_mask != nullptr;
     uint32_t n_first = (r.P + tile_px - 1) / tile_px, n_live = two ? 2 * n_first : n_first, cap = 0, end[2] = {0, 0};
     bool halves = false;
+    // the staged form prefetches streams only for sparse selections: over most
+    // of the detector the prefetched lines leave the L2 before their chunks
+    // are read
+    bool touch = true;
     if (plan) {
         const PlanView pv =
             plan_cut<kRansWG>(plan, r.P, n_visited, two, (OP == Op::Sum || OP == Op::Moments) && r.split, desc, wtot, STG);
+        touch = !STG || pv.sparse;
         n_live = pv.n_items;
         n_first = pv.n_first;
         cap = pv.cap;
@@ -2425,7 +2431,7 @@ __global__ __launch_bounds__(kRansWG, OP == Op::Moments ? 3 : 4) void k_reduce_r
                                                       raw_block, ring);
             else
                 rans_tile<1, WIDE, OP, STG>(r, sel, p0, n_sel, first, b, n, base, nbytes, tbl, pt, ra, dt, half, raw_block,
-                                            ring);
+                                            ring, touch);
         }
         __syncthreads();
         if (kAcc && !hold) {
