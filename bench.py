@@ -23,12 +23,22 @@ source (null otherwise).
 
 --all-workloads instead prints one JSON line per workload with every query
 timed alone (the per-workload table of the design notes), the 64-position
-sweep and the device encoder.
+sweep and the device encoder; the scaled (float32) variant of the sentinel
+workload, whose uint16 codes are escape-heavy, has a line of its own.
+
+--only-query times one query alone (--scaled: on the float32 variant) for
+profiling runs, and --summarize turns rocprofv3 output directories of
+--only-step or --only-query runs into the markdown tables kept under profiles/.
 """
 import argparse
+import collections
+import csv
+import glob
 import hashlib
 import json
 import os
+import re
+import statistics
 import sys
 import time
 
@@ -75,6 +85,16 @@ def parse():
                     help="one JSON line per workload: every query timed alone, the sweep and the device encoder")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (the FETCH_SIZE/WRITE_SIZE calibration kernel)")
+    ap.add_argument("--scaled", action="store_true",
+                    help="with --only-query: the workload's float32 intensities (a scaled resident)")
+    ap.add_argument("--only-query", choices=QUERY_NAMES, default=None,
+                    help="time one query alone, warm, --steps times after --warmup (profiling runs)")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR", default=None,
+                    help="print markdown tables of rocprofv3 output directories (kernel trace or counters)")
+    ap.add_argument("--label", default="step",
+                    help="with --summarize: 'step' for --only-step runs, else the query of an --only-query run")
+    ap.add_argument("--calibration", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="with --summarize: FETCH_SIZE and WRITE_SIZE runs of --copy-probe")
     return ap.parse_args()
 
 
@@ -221,8 +241,16 @@ def cpu_baseline(w, bf, df_mask, valid):
     return line
 
 
-def build_blob(qsc, synth, w, cache=None):
-    """The workload's container, from the host encoder (generated and added 16 blocks at a time)."""
+def build_blob(qsc, synth, w, cache=None, scaled=False):
+    """The workload's container, from the host encoder (generated and added 16 blocks at a time);
+    scaled: from the float32 intensities (no cache)."""
+    if scaled:
+        enc = qsc.Encoder(w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, dtype=2, layout=0, scaled=True)
+        for s0 in range(0, w.S, BLOCK * 16):
+            enc.add(synth.scaled(w, s0, min(BLOCK * 16, w.S - s0)))
+        blob = enc.blob()
+        enc.close()
+        return blob
     if cache and os.path.exists(cache):
         blob = np.fromfile(cache, dtype=np.uint8)
         h = blob[:256]
@@ -262,27 +290,38 @@ def timed(torch, stream, fn, reps, flush=None):
     return float(np.median(ms)), float(np.percentile(ms, 95))
 
 
-def query_table(torch, res, w, d_bf, d_df, valid, reps=20, flushed=True, full_sum=False):
-    """Each query of the step alone: median and p95 of reps runs, warm, and with a
-    1 GiB scratch write before every run so the 256 MB MALL and the L2s hold nothing
-    of the resident (flushed)."""
+QUERY_NAMES = ["masked_sum_bf_k1", "masked_sum_bf_k4", "dense_df_warm", "com_full", "com_bf", "decode_region_8x8",
+               "masked_sum_full"]
+
+
+def query_fns(torch, res, w, d_bf, d_df, valid):
+    """The queries of the step, plus the full-detector sum, as calls queued without waiting."""
     dev = d_bf.device
-    stream = torch.cuda.current_stream()
     out = torch.empty(w.S, dtype=res.sum_dtype, device=dev)
     row, col = torch.empty(w.S, dtype=torch.float32, device=dev), torch.empty(w.S, dtype=torch.float32, device=dev)
     reg = torch.empty(64 * w.P, dtype=torch.int16 if w.dtype == 2 else torch.uint8, device=dev)
     rr, rc = min(8, w.scan_rows), min(8, w.scan_cols)
     full = torch.as_tensor(np.ones(w.P, np.uint8) if valid is None else valid, device=dev)
-    queries = {
+    return {
         "masked_sum_bf_k1": lambda: res.masked_sum(d_bf, 1, out=out, wait=False),
         "masked_sum_bf_k4": lambda: res.masked_sum(d_bf, 4, out=out, wait=False),
         "dense_df_warm": lambda: res.dense_df(d_df, out=out, wait=False),
         "com_full": lambda: res.com(None, out_row=row, out_col=col, wait=False),
         "com_bf": lambda: res.com(d_bf, out_row=row, out_col=col, wait=False),
         "decode_region_8x8": lambda: res.decode_region(0, rr, 0, rc, out=reg[:rr * rc * w.P], wait=False),
+        "masked_sum_full": lambda: res.masked_sum(full, 1, out=out, wait=False),
     }
-    if full_sum:
-        queries["masked_sum_full"] = lambda: res.masked_sum(full, 1, out=out, wait=False)
+
+
+def query_table(torch, res, w, d_bf, d_df, valid, reps=20, flushed=True, full_sum=False):
+    """Each query of the step alone: median and p95 of reps runs, warm, and with a
+    1 GiB scratch write before every run so the 256 MB MALL and the L2s hold nothing
+    of the resident (flushed)."""
+    dev = d_bf.device
+    stream = torch.cuda.current_stream()
+    queries = query_fns(torch, res, w, d_bf, d_df, valid)
+    if not full_sum:
+        del queries["masked_sum_full"]
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flushed else None
     table = {}
     for name, q in queries.items():
@@ -442,10 +481,188 @@ def all_workloads(torch, qsc, synth):
         del blob
         torch.cuda.empty_cache()
         print(json.dumps(line), flush=True)
+    # the scaled variant: calibrated float32 intensities held as uint16 codes, most
+    # of them above 254 (escape-heavy byte-rANS streams, RAW ones in the BF disk)
+    w = synth.WORKLOADS["scan256_u16_sentinel"]
+    t0 = time.perf_counter()
+    blob = build_blob(qsc, synth, w, scaled=True)
+    setup = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    res = qsc.Resident(blob)
+    masks = synth.query_masks(w)
+    d_bf = torch.as_tensor(masks["bf"], device=dev)
+    d_df = torch.as_tensor(masks.get("df", (1 - masks["bf"]).astype(np.uint8)), device=dev)
+    line = {"workload": w.name + " (scaled float32)", "resident_bytes": int(res.info.resident_bytes),
+            "counts": w.S * w.P, "setup_s": round(setup, 1),
+            "queries": query_table(torch, res, w, d_bf, d_df, None, flushed=False, full_sum=True)}
+    res.close()
+    del blob
+    torch.cuda.empty_cache()
+    print(json.dumps(line), flush=True)
+
+
+def only_query(torch, qsc, synth, args):
+    """One query alone, warm: --warmup untimed runs, then --steps runs each bracketed by HIP events."""
+    w = synth.WORKLOADS[args.workload]
+    if args.scaled and w.dtype != 2:
+        raise SystemExit("--scaled needs a uint16 workload")
+    t0 = time.perf_counter()
+    blob = build_blob(qsc, synth, w, None if args.scaled else args.blob_cache, scaled=args.scaled)
+    log(f"container {w.name}{' (scaled)' if args.scaled else ''}: {blob.size} bytes, {time.perf_counter() - t0:.1f} s")
+    valid = None if args.scaled else synth.valid_pixels(w)
+    dev = torch.device("cuda:0")
+    res = qsc.Resident(blob, valid=valid)
+    masks = synth.query_masks(w)
+    bf = masks["bf"]
+    df_mask = masks.get("df", (1 - bf).astype(np.uint8))
+    q = query_fns(torch, res, w, torch.as_tensor(bf, device=dev), torch.as_tensor(df_mask, device=dev), valid)
+    fn = q[args.only_query]
+    for _ in range(args.warmup):
+        fn()
+    res.finish()
+    torch.cuda.synchronize()
+    m, p = timed(torch, torch.cuda.current_stream(), fn, args.steps)
+    res.finish()
+    full = np.ones(w.P, np.uint8) if valid is None else valid
+    sel = {"masked_sum_bf_k1": (bf, 1), "masked_sum_bf_k4": (bf, 4), "com_full": (full, 1), "com_bf": (bf, 1),
+           "dense_df_warm": ((1 - df_mask).astype(np.uint8), 1), "masked_sum_full": (full, 1)}.get(args.only_query)
+    line = {"workload": w.name + (" (scaled float32)" if args.scaled else ""), "query": args.only_query,
+            "steps": args.steps, "warmup": args.warmup, "warm_median_ms": round(m, 4), "warm_p95_ms": round(p, 4)}
+    if sel is not None:
+        nbytes, ncounts = res.query_bytes(*sel)
+        line.update({"encoded_bytes_per_launch": int(nbytes), "counts_per_launch": int(ncounts),
+                     "counts_per_s": round(ncounts / (m * 1e-3), 1), "encoded_GBps": round(nbytes / (m * 1e-3) / 1e9, 2)})
+    res.close()
+    print(json.dumps(line), flush=True)
+
+
+# ------------------------------------------------------------------ rocprofv3 summaries
+STEP_QUERIES = ["masked_sum BF k=1", "masked_sum BF k=4", "dense_df warm", "com full detector", "com BF",
+                "decode_region 8x8"]
+COLD_QUERIES = ["dense_df cold (total)", "dense_df cold (complement)"]
+
+
+OP_NAMES = ["Sum", "Moments", "Region", "Dp", "Index", "Amp", "Frames", "Split"]
+
+
+def short_kernel(name):
+    name = re.sub(r"\(qsc::Op\)(\d)", lambda m: OP_NAMES[int(m.group(1))], name)
+    m = re.search(r"(k_\w+)(<[^()]*>)?", name)
+    return name[:60] if not m else m.group(1) + (m.group(2) or "")
+
+
+def dispatch_labels(kernel_by_dispatch, label):
+    """Query of each decode dispatch (k_reduce_*): an --only-step run issues the cold
+    dense DF (two), then six per step; an --only-query run issues its one query."""
+    split = {d for d, k in kernel_by_dispatch.items() if "k_reduce" in k and "(qsc::Op)7" in k}
+    red = [d for d in sorted(kernel_by_dispatch) if "k_reduce" in kernel_by_dispatch[d] and d not in split]
+    seq = COLD_QUERIES + STEP_QUERIES * (len(red) // len(STEP_QUERIES) + 1) if label == "step" else [label] * len(red)
+    labels = dict(zip(red, seq))
+    labels.update({d: "split points (resident creation)" for d in split})
+    return labels
+
+
+def read_csv(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        return None
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def copy_scale(d, counter):
+    """Bytes per KiB that a counter reads on the 1 GiB copy probe (1 GiB read, 1 GiB written)."""
+    rows = read_csv(d, "counter_collection.csv")
+    per = collections.defaultdict(float)
+    for r in rows:
+        if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]:
+            per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    kib = statistics.median(per.values())
+    return (1 << 30) / kib, kib
+
+
+def summarize(dirs, label, calibration):
+    """Markdown tables of rocprofv3 runs, and the fields bench.py reads back from them."""
+    main_query = "com full detector" if label == "step" else label
+    fields = {}
+    for d in dirs:
+        trace = read_csv(d, "kernel_trace.csv")
+        if trace:
+            kernels = {int(r["Dispatch_Id"]): r["Kernel_Name"] for r in trace}
+            labels = dispatch_labels(kernels, label)
+            groups = collections.defaultdict(list)
+            for r in trace:
+                k = int(r["Dispatch_Id"])
+                groups[(short_kernel(r["Kernel_Name"]), labels.get(k, "-"))].append(
+                    ((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3, r))
+            print(f"Kernel trace ({d}):\n")
+            print("| kernel | query | dispatches | average us | median us | VGPR | SGPR | LDS B | scratch | WG | grid |")
+            print("|---|---|---|---|---|---|---|---|---|---|---|")
+            for (k, lab), v in sorted(groups.items(), key=lambda kv: -sum(x[0] for x in kv[1])):
+                ds = [x[0] for x in v]
+                r = v[0][1]
+                print(f"| {k} | {lab} | {len(ds)} | {statistics.mean(ds):.1f} | {statistics.median(ds):.1f} | "
+                      f"{r.get('VGPR_Count', '')} | {r.get('SGPR_Count', '')} | {r.get('LDS_Block_Size', '')} | "
+                      f"{r.get('Scratch_Size', '')} | {r.get('Workgroup_Size_X', '')} | {r.get('Grid_Size_X', '')} |")
+            print()
+            continue
+        rows = read_csv(d, "counter_collection.csv")
+        if not rows:
+            raise SystemExit(f"no kernel trace or counter collection under {d}")
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        kernels = {}
+        for r in rows:
+            k = int(r["Dispatch_Id"])
+            per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            kernels[k] = r["Kernel_Name"]
+        labels = dispatch_labels(kernels, label)
+        names = sorted({c for k in per for c in per[k]})
+        scale = {}
+        if calibration:
+            for c, cd in zip(("FETCH_SIZE", "WRITE_SIZE"), calibration):
+                if c in names:
+                    scale[c] = copy_scale(cd, c)
+        groups = collections.defaultdict(list)
+        for k in sorted(per):
+            if "k_reduce" in kernels[k]:
+                groups[(short_kernel(kernels[k]), labels.get(k, "-"))].append(per[k])
+        cols = names + (["SQ_WAIT_ANY / SQ_WAVE_CYCLES"] if {"SQ_WAIT_ANY", "SQ_WAVE_CYCLES"} <= set(names) else [])
+        cols += [f"{c} scaled MB" for c in names if c in scale]
+        print(f"Counters ({d}), median per dispatch:\n")
+        for c, (f, kib) in scale.items():
+            print(f"- {c}: the copy probe reads {kib:.1f} KiB per 1 GiB copy, so 1 KiB counts as {f / 1024:.4f} KiB")
+        print("\n| kernel | query | dispatches | " + " | ".join(cols) + " |")
+        print("|---|---|---|" + "---|" * len(cols))
+        for (k, lab), v in groups.items():
+            med = {n: statistics.median(x.get(n, 0.0) for x in v) for n in names}
+            vals = [f"{med[n]:.4g}" for n in names]
+            if "SQ_WAIT_ANY / SQ_WAVE_CYCLES" in cols:
+                vals.append(f"{med['SQ_WAIT_ANY'] / med['SQ_WAVE_CYCLES']:.3f}")
+            vals += [f"{med[c] * scale[c][0] / 1e6:.2f}" for c in names if c in scale]
+            print(f"| {k} | {lab} | {len(v)} | " + " | ".join(vals) + " |")
+            if lab == main_query:
+                if "SQ_INSTS_VALU" in med:
+                    fields["valu_insts_per_launch"] = int(round(med["SQ_INSTS_VALU"]))
+                for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                    if c in scale:
+                        fields[c] = med[c] * scale[c][0]
+        print()
+    print(f"Fields for the {main_query} launch, read back by bench.py:\n")
+    print(f"source_sha256: {kernel_source_hash()}")
+    if "valu_insts_per_launch" in fields:
+        print(f"valu_insts_per_launch: {fields['valu_insts_per_launch']}")
+    if "FETCH_SIZE" in fields and "WRITE_SIZE" in fields:
+        print(f"traffic_bytes: {int(round(fields['FETCH_SIZE'] + fields['WRITE_SIZE']))}")
 
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.label, args.calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every query runs on a single device's resident "
               "(the sharded design is described, not built); run with --gpus 1", file=sys.stderr)
@@ -463,6 +680,9 @@ def main():
         return
     if args.all_workloads:
         all_workloads(torch, qsc, synth)
+        return
+    if args.only_query:
+        only_query(torch, qsc, synth, args)
         return
     copy_gbps = copy_ceiling(torch)
     w = synth.WORKLOADS[args.workload]

@@ -221,11 +221,18 @@ def test_scaled_u16_256x256_full_size():
                     want_f.append(oracle.reconstruct(code, sc, off))
             assert np.array_equal(got_c, np.stack(want_c)), (r0, r1, c0, c1)
             assert np.array_equal(got_f, np.stack(want_f)), (r0, r1, c0, c1)
-        # integer products of a scaled resident are exact sums of its codes
+        # integer products of a scaled resident are exact sums of its codes; the
+        # whole detector (mostly escape-heavy streams) takes the staged decode
+        full = np.ones(w.P, np.uint8)
+        fsum = u(res.masked_sum(full))
+        frow, fcol = (t.cpu().numpy() for t in res.com())
         for b in sorted(region_cache)[:4]:
             codes = region_cache[b][2].reshape(-1, w.P)
-            s0 = b * BLOCK
-            assert np.array_equal(sums[s0:s0 + codes.shape[0]], oracle.masked_sum(codes, bf))
+            s0, n = b * BLOCK, codes.shape[0]
+            assert np.array_equal(sums[s0:s0 + n], oracle.masked_sum(codes, bf))
+            assert np.array_equal(fsum[s0:s0 + n], oracle.masked_sum(codes, full))
+            orow, ocol, _ = oracle.com(codes, w.det_rows, w.det_cols)
+            assert np.array_equal(frow[s0:s0 + n], orow) and np.array_equal(fcol[s0:s0 + n], ocol), b
         res.finish()
 
 
@@ -281,6 +288,7 @@ def test_paired_u16_1024x1024_full_size():
         total = u(res.masked_sum(np.ones(w.P, np.uint8)))
         assert np.array_equal(d + s1, total)
         check_com_rows(res, w, bf, None, scans, sampled)
+        check_com_rows(res, w, None, None, scans, sampled)  # the whole detector
         check_rects(res, w, None, rects_for(w, 52)[:3])
         check_frames_ends(res, w, None)
         res.finish()
