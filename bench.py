@@ -626,8 +626,9 @@ def summarize(dirs, label, calibration):
                 if c in names:
                     scale[c] = copy_scale(cd, c)
         groups = collections.defaultdict(list)
+        decode = any("k_reduce" in n for n in kernels.values())  # else a copy probe: list every kernel
         for k in sorted(per):
-            if "k_reduce" in kernels[k]:
+            if "k_reduce" in kernels[k] or not decode:
                 groups[(short_kernel(kernels[k]), labels.get(k, "-"))].append(per[k])
         cols = names + (["SQ_WAIT_ANY / SQ_WAVE_CYCLES"] if {"SQ_WAIT_ANY", "SQ_WAVE_CYCLES"} <= set(names) else [])
         cols += [f"{c} scaled MB" for c in names if c in scale]
