@@ -1585,6 +1585,37 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     // The window bases enter once per scan as wave totals.
     bool packed = false;
     uint32_t kcw = 0, B0 = 0, Bc = 0, wgt[OP == Op::Moments ? K : 1];
+    // Packed per slot: in a two-slot wave that crosses a row end, each slot's
+    // 64 pixels may still lie in one row (64-pixel runs of a full detector
+    // whose width is a multiple of 64). Then each slot keeps its own packed
+    // accumulator, relative to that slot's first live column; with spans of
+    // at most 63 columns both halves stay below 2^16 over all 64 lanes
+    // (64 x 15 x 63 = 60480), so the whole reduction runs packed. The row
+    // moment is each slot's row times its total.
+    bool pack2 = false;
+    uint32_t krs[K], kcs[K], Br = 0;
+    if constexpr (OP == Op::Moments && K == 2) {
+        if (!rowu) {
+            bool diff = false, far = false;
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                const bool live = (sl[k].meta & 7u) != 7u;
+                const uint64_t lv = __builtin_amdgcn_ballot_w64(live);
+                krs[k] = lv ? (uint32_t)__builtin_amdgcn_readlane((int)kr[k], (int)__builtin_ctzll(lv)) : 0u;
+                kcs[k] = wave_min(live ? kc[k] : 0xFFFFFFFFu);
+                diff |= live && kr[k] != krs[k];
+                far |= live && kc[k] - kcs[k] > 63u;
+            }
+            pack2 = !__builtin_amdgcn_ballot_w64(diff || far);
+            if (pack2) {
+#pragma unroll
+                for (int k = 0; k < K; k++) wgt[k] = (sl[k].meta & 7u) != 7u ? 1u + ((kc[k] - kcs[k]) << 16) : 0u;
+                B0 = wave_sum(base0);
+                Bc = wave_sum(baseC);
+                Br = wave_sum(baseR);
+            }
+        }
+    }
     if constexpr (OP == Op::Moments) {
         if (rowu) {
             uint32_t m = 0xFFFFFFFFu;
@@ -1691,7 +1722,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
 
     auto run = [&](auto form, auto rowu, auto packed_t) {
         constexpr bool ROWU = decltype(rowu)::value;  // moments of a wave inside one detector row
-        constexpr bool PACKED = decltype(packed_t)::value;
+        constexpr bool PACKED = decltype(packed_t)::value == 1;  // one packed accumulator (a row-uniform wave)
+        constexpr bool PACK2 = decltype(packed_t)::value == 2;   // one per slot (each slot's pixels in one row)
         if constexpr (is_region(OP)) {
             auto rw = region_walk<is_frames(OP)>(r, b, ra);
             for (uint32_t t = 0; t < kBlk / 2; t++) {
@@ -1739,6 +1771,63 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             for (int k = 0; k < K; k++) {
                 const uint32_t mode = sl[k].meta & 7u;
                 if (mode == 3 || mode == 4) dt.row[sl[k].p] = acc[k];
+            }
+        } else if constexpr (OP == Op::Moments && PACK2) {
+            constexpr int CH = 8;
+            const uint32_t my = lane_scan<CH>();
+            const bool writer = lane_writes<CH>();
+            for (uint32_t c = 0; c < kBlk / CH; c++) {
+                uint32_t acc[K][CH];
+#pragma unroll
+                for (int k = 0; k < K; k++)
+#pragma unroll
+                    for (int i = 0; i < CH; i++) acc[k][i] = 0;
+#pragma unroll
+                for (int tt = 0; tt < CH / 2; tt++) {
+                    uint32_t v0[K], v1[K];
+                    if (step(form, c * (CH / 2) + tt, v0, v1)) {
+                        // counts beyond the packed range: 15 stays packed, the excess
+                        // (negative below the window) goes to the partials with its moments
+#pragma unroll
+                        for (int k = 0; k < K; k++) {
+#pragma unroll
+                            for (int h = 0; h < 2; h++) {
+                                uint32_t &v = h ? v1[k] : v0[k];
+                                if (v > 15u) {
+                                    const uint32_t s = c * CH + 2 * tt + h;
+                                    const long long x = (int32_t)(v - 15u);
+                                    atomicAdd(&pt.m0[s], v - 15u);
+                                    atomicAdd(&pt.mc[s], (unsigned long long)(x * (long long)kc[k]));
+                                    atomicAdd(&pt.mr[s], (unsigned long long)(x * (long long)kr[k]));
+                                    v = 15u;
+                                }
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        acc[k][2 * tt] = mad24(v0[k], wgt[k], acc[k][2 * tt]);
+                        acc[k][2 * tt + 1] = mad24(v1[k], wgt[k], acc[k][2 * tt + 1]);
+                        asm volatile("" : "+v"(acc[k][2 * tt]), "+v"(acc[k][2 * tt + 1]));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                uint32_t t0[K], tc[K];
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+                    const uint32_t v = wave_transpose_sum<CH>(acc[k]);  // packed to the end
+                    t0[k] = v & 0xFFFFu;
+                    tc[k] = v >> 16;
+                }
+                const uint32_t m0 = t0[0] + t0[1] + B0;
+                if (writer && m0) {
+                    const uint32_t s = c * CH + my;
+                    atomicAdd(&pt.m0[s], m0);
+                    atomicAdd(&pt.mc[s], (unsigned long long)Bc + (unsigned long long)kcs[0] * t0[0] + tc[0] +
+                                             (unsigned long long)kcs[1] * t0[1] + tc[1]);
+                    atomicAdd(&pt.mr[s], (unsigned long long)Br + (unsigned long long)krs[0] * t0[0] +
+                                             (unsigned long long)krs[1] * t0[1]);
+                }
             }
         } else if constexpr (OP == Op::Moments && PACKED) {
             constexpr int CH = 8;
@@ -1856,21 +1945,27 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     for (int k = 0; k < K; k++) raw |= (sl[k].meta & 7u) == 4u;
     auto run_rows = [&](auto form) {
         constexpr bool PLAIN = decltype(form)::value == kPPlain;
+        using none = std::integral_constant<int, 0>;
         if constexpr (OP == Op::Moments) {
             if (rowu) {
                 if constexpr (PLAIN) {
                     if (packed)
-                        run(form, std::true_type{}, std::true_type{});
+                        run(form, std::true_type{}, std::integral_constant<int, 1>{});
                     else
-                        run(form, std::true_type{}, std::false_type{});
+                        run(form, std::true_type{}, none{});
                 } else {
-                    run(form, std::true_type{}, std::false_type{});
+                    run(form, std::true_type{}, none{});
                 }
+            } else if constexpr (PLAIN && K == 2) {
+                if (pack2)
+                    run(form, std::false_type{}, std::integral_constant<int, 2>{});
+                else
+                    run(form, std::false_type{}, none{});
             } else {
-                run(form, std::false_type{}, std::false_type{});
+                run(form, std::false_type{}, none{});
             }
         } else {
-            run(form, std::false_type{}, std::false_type{});
+            run(form, std::false_type{}, none{});
         }
     };
     if (__builtin_amdgcn_ballot_w64(raw))
