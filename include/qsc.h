@@ -66,7 +66,7 @@ typedef struct {
     uint64_t index_bytes;   /* device bytes of the polar interaction index, 0 when none is built */
 } qsc_info;
 
-/* ABI strings of the stream layouts this build reads:
+/* ABI strings of the stream layouts this library reads:
  * "qsc-byte-rans-v1;qsc-paired-v1". A container carrying another tag is
  * refused (paired-resident page, "Contract": reopen refuses another ABI). */
 const char *qsc_abi(void);

@@ -221,6 +221,32 @@ def test_paired_moments_of_row_waves_with_escapes(dtype):
         res.finish()
 
 
+@pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
+def test_paired_moments_packed_per_slot_at_the_bound(dtype):
+    """Full-detector CoM on an 8 x 192 paired resident (1536 pixels: two streams
+    per lane, so every second wave's two 64-pixel slots lie in different rows
+    and keep one packed word each). Every count is uniform in 10..40, so the
+    chosen model's window (15 values) holds many counts at 13-14 and the rest
+    escape and are clamped to 15 in the packed word: each slot's word reaches
+    its bound of 64 lanes x 15 x 63 columns. Bit-exact against the oracle, with
+    a mask that shifts the slots off the 64-pixel grid as well."""
+    rng = np.random.default_rng(4242)
+    R, C, S = 8, 192, 1024
+    P = R * C
+    c = rng.integers(10, 41, size=(S, P)).astype(dtype)
+    c[:, 3 * C + 64: 3 * C + 128] = 14  # a whole slot at one value: CONST streams beside PAIRED ones
+    blob = q().encode(c, 2, 512, R, C, layout=1)
+    shifted = np.ones(P, np.uint8)
+    shifted[0] = 0
+    w = synth.Workload("bound", 2, 512, R, C, 2, 0, 0, 0, 0, 0, 0, 0, 0, 1)
+    with q().Resident(blob) as res:
+        for m in (None, shifted):
+            check_com(res, c, w, m, None)
+            mm = np.ones(P, np.uint8) if m is None else m
+            assert np.array_equal(u(res.masked_sum(mm)), oracle.masked_sum(c, mm))
+        res.finish()
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_uint64_sums_257_detector(layout):
     # 257 x 257 uint16: a full-detector sum can pass 2^32, so outputs are uint64
