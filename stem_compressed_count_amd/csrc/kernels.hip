@@ -1668,7 +1668,11 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             if (escaped) {  // values outside the model window
 #pragma unroll
                 for (int k = 0; k < K; k++) {
-                    if (pe_escape(e[k])) {
+                    // the per-lane test stays inside the wave's branch (the compiler
+                    // would otherwise compute it at every step, escapes or not)
+                    uint32_t ek = e[k];
+                    asm volatile("" : "+v"(ek));
+                    if (pe_escape(ek)) {
                         PSlot &z = sl[k];
                         const uint32_t info = tbl[kPairTable + (z.meta >> 3)];
                         if (v0[k] == 15u) v0[k] = pair_literal<WIDE>(z.s, rs, info, bad);
@@ -1681,7 +1685,14 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             // wave-uniform cadence (the paired-resident page's refill rhythm)
             if (t % 3 == 2) {
 #pragma unroll
-                for (int k = 0; k < K; k++) mbits_refill(sl[k].s, rs);
+                for (int k = 0; k < K; k++) {
+                    // keep the reservoir test inside the cadence branch (else it
+                    // runs at every step)
+                    uint32_t hi = (uint32_t)(sl[k].s.r >> 32);
+                    asm volatile("" : "+v"(hi));
+                    sl[k].s.r = ((uint64_t)hi << 32) | (uint32_t)sl[k].s.r;
+                    mbits_refill(sl[k].s, rs);
+                }
             }
         } else {
 #pragma unroll
