@@ -430,21 +430,22 @@ def feed_rows(torch, res, w, max_blocks=64):
         res.finish()
         feed[kind] = {"ms": round(m, 4), "counts_per_s": round(counts / (m * 1e-3), 1),
                       "out_GBps": round(fbuf.numel() * fbuf.element_size() / (m * 1e-3) / 1e9, 1)}
-        # the same blocks through the block feed: one block per item, two
-        # buffers, decoded ahead on the library's stream while the consumer
-        # stream waits for each item in turn
-        def iterate():
-            for _frames, _s0 in res.feed(0, nb, 1, kind, 2):
-                pass
-        iterate()
-        torch.cuda.synchronize()
-        m, _ = timed(torch, stream, iterate, 3)
-        feed[kind]["feed_ms"] = round(m, 4)
-        feed[kind]["feed_counts_per_s"] = round(counts / (m * 1e-3), 1)
+        # the same blocks through the block feed: items of one and of eight
+        # blocks, two buffers, decoded ahead on the library's stream while the
+        # consumer stream waits for each item in turn
+        for per, key in ((1, "feed"), (8, "feed8")):
+            def iterate():
+                for _frames, _s0 in res.feed(0, nb, per, kind, 2):
+                    pass
+            iterate()
+            torch.cuda.synchronize()
+            m, _ = timed(torch, stream, iterate, 3)
+            feed[kind][key + "_ms"] = round(m, 4)
+            feed[kind][key + "_counts_per_s"] = round(counts / (m * 1e-3), 1)
         del fbuf
         torch.cuda.empty_cache()
     feed["what"] = (f"the first {nb} blocks decoded to frames (not in the step): one decode_blocks call, "
-                    f"and the block feed (one block per item, depth 2)")
+                    f"and the block feed (items of one and of eight blocks, depth 2)")
     return feed
 
 
