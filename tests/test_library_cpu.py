@@ -217,3 +217,56 @@ def test_stream_split_and_pack_are_inverse():
         with pytest.raises(oracle.OracleError) as e:
             oracle.decode(streams.pack(blob, st))
         assert e.value.code == oracle.ERR_MALFORMED and "block 0 pixel 3" in str(e.value)
+
+
+def staged_lane(demand, start_word, n_steps=512, chunk_words=16, cadence=4):
+    """One lane of the staged escape-heavy decode, as the kernel runs it: a ring
+    of two chunks of `chunk_words` 16-bit words, both filled before the first
+    step; at every `cadence` steps the chunk requested at the previous cadence
+    is written, then the next chunk is requested if the ring half it goes to
+    has been consumed. A step reads the word pair (wi, wi + 1) and consumes
+    0-2 words. Returns the smallest number of written words ahead of wi seen
+    at any step that consumed words (each such step needs that many)."""
+    wi = start_word          # next word, counted from chunk 0
+    fl = 2                   # chunks requested (and written: chunks 0 and 1)
+    written = 2 * chunk_words
+    pend = False
+    worst = None
+    for t in range(n_steps):
+        if t and t % cadence == 0:
+            if pend:
+                written += chunk_words
+                assert written - wi <= 2 * chunk_words, (t, wi, written)  # no unconsumed word is overwritten
+            req = wi >= chunk_words * (fl - 1)   # the older half is free
+            pend = req
+            fl += req
+        d = demand(t)
+        if d:
+            ahead = written - wi
+            assert ahead >= d, (t, wi, written, d)
+            worst = ahead if worst is None else min(worst, ahead)
+        wi += d
+    return worst
+
+
+def test_staged_ring_never_reads_an_unwritten_word():
+    """The staged decode's ring protocol (32-byte chunks, two per ring, a
+    cadence of four steps, a chunk written one cadence after its request)
+    keeps a lane's next two words written whatever the stream's rate: at most
+    two words a step (a renormalisation word and an escape literal), checked
+    for the worst case, idle stretches followed by bursts, and random rates,
+    from every starting word of chunk 0; and a chunk is written only over
+    words already consumed."""
+    rng = np.random.default_rng(5)
+    for start in range(16):
+        assert staged_lane(lambda t: 2, start) >= 2
+        for period in (3, 5, 13, 37, 61):
+            staged_lane(lambda t: 0 if (t // period) % 2 else 2, start)
+        for _ in range(20):
+            p = rng.random()
+            draws = (rng.random((512, 2)) < p).sum(axis=1)
+            staged_lane(lambda t: int(draws[t]), start)
+    # a cadence of eight steps with the same ring runs dry
+    with pytest.raises(AssertionError):
+        for start in range(16):
+            staged_lane(lambda t: 2, start, cadence=8)
