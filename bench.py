@@ -24,9 +24,12 @@ source (null otherwise).
 --all-workloads instead prints one JSON line per workload with every query
 timed alone (the per-workload table of the design notes), the 64-position
 sweep and the device encoder; the scaled (float32) variant of the sentinel
-workload, whose uint16 codes are escape-heavy, has a line of its own.
+workload, whose uint16 codes are escape-heavy, has a line of its own, and so
+has that workload's geometry filled with uniform 16-bit values (every stream
+stored RAW: the queries there are bound by HBM, not by the decode).
 
---only-query times one query alone (--scaled: on the float32 variant) for
+--only-query times one query alone (--scaled: on the float32 variant; --raw:
+on the uniform 16-bit values) for
 profiling runs, and --summarize turns rocprofv3 output directories of
 --only-step or --only-query runs into the markdown tables kept under profiles/.
 """
@@ -87,6 +90,8 @@ def parse():
                     help="only run a plain 1 GiB device copy (the FETCH_SIZE/WRITE_SIZE calibration kernel)")
     ap.add_argument("--scaled", action="store_true",
                     help="with --only-query: the workload's float32 intensities (a scaled resident)")
+    ap.add_argument("--raw", action="store_true",
+                    help="with --only-query: uniform 16-bit values on the workload's geometry (every stream RAW)")
     ap.add_argument("--only-query", choices=QUERY_NAMES, default=None,
                     help="time one query alone, warm, --steps times after --warmup (profiling runs)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR", default=None,
@@ -241,9 +246,22 @@ def cpu_baseline(w, bf, df_mask, valid):
     return line
 
 
-def build_blob(qsc, synth, w, cache=None, scaled=False):
+def raw_values(w, s0, n):
+    """Uniform 16-bit values for scans [s0, s0 + n) of w's geometry (seeded per chunk start): incompressible
+    data that the encoder stores as RAW streams, the path bound by HBM."""
+    return np.random.default_rng([w.seed, s0]).integers(0, 65536, size=(n, w.P), dtype=np.uint16)
+
+
+def build_blob(qsc, synth, w, cache=None, scaled=False, raw=False):
     """The workload's container, from the host encoder (generated and added 16 blocks at a time);
-    scaled: from the float32 intensities (no cache)."""
+    scaled: from the float32 intensities; raw: from uniform 16-bit values (neither cached)."""
+    if raw:
+        enc = qsc.Encoder(w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, dtype=2, layout=0)
+        for s0 in range(0, w.S, BLOCK * 16):
+            enc.add(raw_values(w, s0, min(BLOCK * 16, w.S - s0)))
+        blob = enc.blob()
+        enc.close()
+        return blob
     if scaled:
         enc = qsc.Encoder(w.scan_rows, w.scan_cols, w.det_rows, w.det_cols, dtype=2, layout=0, scaled=True)
         for s0 in range(0, w.S, BLOCK * 16):
@@ -500,17 +518,36 @@ def all_workloads(torch, qsc, synth):
     del blob
     torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
+    # uniform 16-bit values on the same geometry: every stream RAW, 2 bytes per
+    # count, the one case where HBM rather than the decode bounds the queries
+    t0 = time.perf_counter()
+    blob = build_blob(qsc, synth, w, raw=True)
+    setup = time.perf_counter() - t0
+    res = qsc.Resident(blob)
+    line = {"workload": w.name + " geometry, uniform 16-bit values (RAW)", "resident_bytes": int(res.info.resident_bytes),
+            "counts": w.S * w.P, "setup_s": round(setup, 1),
+            "queries": query_table(torch, res, w, d_bf, d_df, None, flushed=False, full_sum=True)}
+    nbytes, _ = res.query_bytes(np.ones(w.P, np.uint8), 1)
+    ms = line["queries"]["masked_sum_full"]["warm_median_ms"]
+    line["full_sum_encoded_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    line["full_sum_hbm_frac"] = round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    res.close()
+    del blob
+    torch.cuda.empty_cache()
+    print(json.dumps(line), flush=True)
 
 
 def only_query(torch, qsc, synth, args):
     """One query alone, warm: --warmup untimed runs, then --steps runs each bracketed by HIP events."""
     w = synth.WORKLOADS[args.workload]
-    if args.scaled and w.dtype != 2:
-        raise SystemExit("--scaled needs a uint16 workload")
+    if (args.scaled or args.raw) and w.dtype != 2:
+        raise SystemExit("--scaled and --raw need a uint16 workload")
     t0 = time.perf_counter()
-    blob = build_blob(qsc, synth, w, None if args.scaled else args.blob_cache, scaled=args.scaled)
-    log(f"container {w.name}{' (scaled)' if args.scaled else ''}: {blob.size} bytes, {time.perf_counter() - t0:.1f} s")
-    valid = None if args.scaled else synth.valid_pixels(w)
+    blob = build_blob(qsc, synth, w, None if (args.scaled or args.raw) else args.blob_cache, scaled=args.scaled,
+                      raw=args.raw)
+    kind = " (scaled)" if args.scaled else (" (uniform, RAW)" if args.raw else "")
+    log(f"container {w.name}{kind}: {blob.size} bytes, {time.perf_counter() - t0:.1f} s")
+    valid = None if (args.scaled or args.raw) else synth.valid_pixels(w)
     dev = torch.device("cuda:0")
     res = qsc.Resident(blob, valid=valid)
     masks = synth.query_masks(w)
@@ -527,12 +564,14 @@ def only_query(torch, qsc, synth, args):
     full = np.ones(w.P, np.uint8) if valid is None else valid
     sel = {"masked_sum_bf_k1": (bf, 1), "masked_sum_bf_k4": (bf, 4), "com_full": (full, 1), "com_bf": (bf, 1),
            "dense_df_warm": ((1 - df_mask).astype(np.uint8), 1), "masked_sum_full": (full, 1)}.get(args.only_query)
-    line = {"workload": w.name + (" (scaled float32)" if args.scaled else ""), "query": args.only_query,
+    line = {"workload": w.name + (" (scaled float32)" if args.scaled else (" (uniform 16-bit, RAW)" if args.raw else "")),
+            "query": args.only_query,
             "steps": args.steps, "warmup": args.warmup, "warm_median_ms": round(m, 4), "warm_p95_ms": round(p, 4)}
     if sel is not None:
         nbytes, ncounts = res.query_bytes(*sel)
         line.update({"encoded_bytes_per_launch": int(nbytes), "counts_per_launch": int(ncounts),
-                     "counts_per_s": round(ncounts / (m * 1e-3), 1), "encoded_GBps": round(nbytes / (m * 1e-3) / 1e9, 2)})
+                     "counts_per_s": round(ncounts / (m * 1e-3), 1), "encoded_GBps": round(nbytes / (m * 1e-3) / 1e9, 2),
+                     "encoded_hbm_frac": round(nbytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
     res.close()
     print(json.dumps(line), flush=True)
 
