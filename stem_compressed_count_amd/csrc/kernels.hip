@@ -1591,7 +1591,9 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     // accumulator, relative to that slot's first live column; with spans of
     // at most 63 columns both halves stay below 2^16 over all 64 lanes
     // (64 x 15 x 63 = 60480), so the whole reduction runs packed. The row
-    // moment is each slot's row times its total.
+    // moment is each slot's row times its total. These waves reduce every 16
+    // scans (two sets of 16 accumulators), halving the per-scan share of the
+    // reduction's fixed levels and of the partials' atomics.
     bool pack2 = false;
     uint32_t krs[K], kcs[K], Br = 0;
     if constexpr (OP == Op::Moments && K == 2) {
@@ -1784,7 +1786,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 if (mode == 3 || mode == 4) dt.row[sl[k].p] = acc[k];
             }
         } else if constexpr (OP == Op::Moments && PACK2) {
-            constexpr int CH = 8;
+            constexpr int CH = 16;
             const uint32_t my = lane_scan<CH>();
             const bool writer = lane_writes<CH>();
             for (uint32_t c = 0; c < kBlk / CH; c++) {
@@ -1832,12 +1834,13 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 }
                 const uint32_t m0 = t0[0] + t0[1] + B0;
                 if (writer && m0) {
+                    // one wave's moments of one scan fit 32 bits: slot totals at most
+                    // 64 x 15, packed column moments below 2^16, window-base sums at most
+                    // 128 x 13 x 1023 (model bases are at most 13, detector sides at most 1024)
                     const uint32_t s = c * CH + my;
                     atomicAdd(&pt.m0[s], m0);
-                    atomicAdd(&pt.mc[s], (unsigned long long)Bc + (unsigned long long)kcs[0] * t0[0] + tc[0] +
-                                             (unsigned long long)kcs[1] * t0[1] + tc[1]);
-                    atomicAdd(&pt.mr[s], (unsigned long long)Br + (unsigned long long)krs[0] * t0[0] +
-                                             (unsigned long long)krs[1] * t0[1]);
+                    atomicAdd(&pt.mc[s], (unsigned long long)mad24(kcs[0], t0[0], mad24(kcs[1], t0[1], Bc + tc[0] + tc[1])));
+                    atomicAdd(&pt.mr[s], (unsigned long long)mad24(krs[0], t0[0], mad24(krs[1], t0[1], Br)));
                 }
             }
         } else if constexpr (OP == Op::Moments && PACKED) {
@@ -1891,8 +1894,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                 if (writer && m0) {
                     const uint32_t s = c * CH + my;
                     atomicAdd(&pt.m0[s], m0);
-                    atomicAdd(&pt.mc[s], (unsigned long long)Bc + (unsigned long long)kcw * t0 + tc);
-                    atomicAdd(&pt.mr[s], (unsigned long long)kru * m0);
+                    atomicAdd(&pt.mc[s], (unsigned long long)mad24(kcw, t0, Bc + tc));
+                    atomicAdd(&pt.mr[s], (unsigned long long)mad24(kru, m0, 0u));
                 }
             }
         } else {
