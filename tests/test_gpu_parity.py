@@ -247,6 +247,31 @@ def test_paired_moments_packed_per_slot_at_the_bound(dtype):
         res.finish()
 
 
+@pytest.mark.parametrize("R,C", [(1024, 64), (64, 1024)])
+def test_paired_moments_packed_at_the_largest_coordinates(R, C):
+    """Full-detector CoM on 65,536-pixel paired residents at the detector-side
+    limit of 1024. With 1024 rows of 64 pixels every two-slot wave keeps one
+    packed word per slot with rows up to 1023; with 64 rows of 1024 pixels
+    every wave lies in one row and keeps one packed word with columns up to
+    1023. Counts are uniform in 10..40, so the streams take the highest-mean
+    models (window bases up to 13) and most counts escape: each wave's
+    per-scan moments, formed in 32 bits before the 64-bit partials, are at
+    their largest. Bit-exact against the oracle, also with a mask that moves
+    every slot off the 64-pixel grid."""
+    rng = np.random.default_rng(9090)
+    S = 1024
+    P = R * C
+    c = rng.integers(10, 41, size=(S, P), dtype=np.uint16)
+    blob = q().encode(c, 2, 512, R, C, layout=1)
+    shifted = np.ones(P, np.uint8)
+    shifted[0] = 0
+    w = synth.Workload("largest", 2, 512, R, C, 2, 0, 0, 0, 0, 0, 0, 0, 0, 1)
+    with q().Resident(blob) as res:
+        for m in (None, shifted):
+            check_com(res, c, w, m, None)
+        res.finish()
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_uint64_sums_257_detector(layout):
     # 257 x 257 uint16: a full-detector sum can pass 2^32, so outputs are uint64
