@@ -1587,13 +1587,15 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
     uint32_t kcw = 0, B0 = 0, Bc = 0, wgt[OP == Op::Moments ? K : 1];
     // Packed per slot: in a two-slot wave that crosses a row end, each slot's
     // 64 pixels may still lie in one row (64-pixel runs of a full detector
-    // whose width is a multiple of 64). Then each slot keeps its own packed
-    // accumulator, relative to that slot's first live column; with spans of
-    // at most 63 columns both halves stay below 2^16 over all 64 lanes
-    // (64 x 15 x 63 = 60480), so the whole reduction runs packed. The row
-    // moment is each slot's row times its total. These waves reduce every 16
-    // scans (two sets of 16 accumulators), halving the per-scan share of the
-    // reduction's fixed levels and of the partials' atomics.
+    // whose width is a multiple of 64). Both slots then share one accumulator
+    // per scan with three fields: bits 0-8 the sum of the values, bits 9-16
+    // the second slot's sum, bits 17-31 the column moment relative to each
+    // slot's own first live column (a span of at most 63). The weight of a
+    // value is 1 (+ 2^9 in the second slot) + (column offset << 17). Over 16
+    // lanes of two slots the fields stay below their widths (480 < 2^9,
+    // 240 < 2^8, 16 x 2 x 15 x 63 = 30240 < 2^15), so the first four
+    // reduction levels run on the packed words and the last two per field.
+    // The row moment is each slot's row times its total.
     bool pack2 = false;
     uint32_t krs[K], kcs[K], Br = 0;
     if constexpr (OP == Op::Moments && K == 2) {
@@ -1611,7 +1613,8 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             pack2 = !__builtin_amdgcn_ballot_w64(diff || far);
             if (pack2) {
 #pragma unroll
-                for (int k = 0; k < K; k++) wgt[k] = (sl[k].meta & 7u) != 7u ? 1u + ((kc[k] - kcs[k]) << 16) : 0u;
+                for (int k = 0; k < K; k++)
+                    wgt[k] = (sl[k].meta & 7u) != 7u ? 1u + (k ? 1u << 9 : 0u) + ((kc[k] - kcs[k]) << 17) : 0u;
                 B0 = wave_sum(base0);
                 Bc = wave_sum(baseC);
                 Br = wave_sum(baseR);
@@ -1790,11 +1793,9 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             const uint32_t my = lane_scan<CH>();
             const bool writer = lane_writes<CH>();
             for (uint32_t c = 0; c < kBlk / CH; c++) {
-                uint32_t acc[K][CH];
+                uint32_t acc[CH];
 #pragma unroll
-                for (int k = 0; k < K; k++)
-#pragma unroll
-                    for (int i = 0; i < CH; i++) acc[k][i] = 0;
+                for (int i = 0; i < CH; i++) acc[i] = 0;
 #pragma unroll
                 for (int tt = 0; tt < CH / 2; tt++) {
                     uint32_t v0[K], v1[K];
@@ -1819,32 +1820,34 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     }
 #pragma unroll
                     for (int k = 0; k < K; k++) {
-                        acc[k][2 * tt] = mad24(v0[k], wgt[k], acc[k][2 * tt]);
-                        acc[k][2 * tt + 1] = mad24(v1[k], wgt[k], acc[k][2 * tt + 1]);
-                        asm volatile("" : "+v"(acc[k][2 * tt]), "+v"(acc[k][2 * tt + 1]));
+                        acc[2 * tt] = mad24(v0[k], wgt[k], acc[2 * tt]);
+                        acc[2 * tt + 1] = mad24(v1[k], wgt[k], acc[2 * tt + 1]);
                     }
+                    asm volatile("" : "+v"(acc[2 * tt]), "+v"(acc[2 * tt + 1]));
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                uint32_t t0[K], tc[K];
-#pragma unroll
-                for (int k = 0; k < K; k++) {
-                    const uint32_t v = wave_transpose_sum<CH>(acc[k]);  // packed to the end
-                    t0[k] = v & 0xFFFFu;
-                    tc[k] = v >> 16;
-                }
-                const uint32_t m0 = t0[0] + t0[1] + B0;
+                transpose_head<CH>(acc);
+                const uint32_t v = bfdpp<kHalfMirror, 4>(acc[0], acc[1]);  // 16 lanes
+                uint32_t ts = v & 0x1FFu, t1 = __builtin_amdgcn_ubfe(v, 9, 8), tc = v >> 17;
+                ts += (uint32_t)__builtin_amdgcn_mov_dpp((int)ts, kQuadXor2, 0xF, 0xF, false);
+                t1 += (uint32_t)__builtin_amdgcn_mov_dpp((int)t1, kQuadXor2, 0xF, 0xF, false);
+                tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor2, 0xF, 0xF, false);
+                ts += (uint32_t)__builtin_amdgcn_mov_dpp((int)ts, kQuadXor1, 0xF, 0xF, false);
+                t1 += (uint32_t)__builtin_amdgcn_mov_dpp((int)t1, kQuadXor1, 0xF, 0xF, false);
+                tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor1, 0xF, 0xF, false);
+                const uint32_t m0 = ts + B0;
                 if (writer && m0) {
                     // one wave's moments of one scan fit 32 bits: slot totals at most
-                    // 64 x 15, packed column moments below 2^16, window-base sums at most
+                    // 64 x 15, column moments below 2^16, window-base sums at most
                     // 128 x 13 x 1023 (model bases are at most 13, detector sides at most 1024)
-                    const uint32_t s = c * CH + my;
+                    const uint32_t s = c * CH + my, t0 = ts - t1;
                     atomicAdd(&pt.m0[s], m0);
-                    atomicAdd(&pt.mc[s], (unsigned long long)mad24(kcs[0], t0[0], mad24(kcs[1], t0[1], Bc + tc[0] + tc[1])));
-                    atomicAdd(&pt.mr[s], (unsigned long long)mad24(krs[0], t0[0], mad24(krs[1], t0[1], Br)));
+                    atomicAdd(&pt.mc[s], (unsigned long long)mad24(kcs[0], t0, mad24(kcs[1], t1, Bc + tc)));
+                    atomicAdd(&pt.mr[s], (unsigned long long)mad24(krs[0], t0, mad24(krs[1], t1, Br)));
                 }
             }
         } else if constexpr (OP == Op::Moments && PACKED) {
-            constexpr int CH = 8;
+            constexpr int CH = 16;
             const uint32_t my = lane_scan<CH>();
             const bool writer = lane_writes<CH>();
             for (uint32_t c = 0; c < kBlk / CH; c++) {
@@ -1883,8 +1886,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 transpose_head<CH>(acc);
-                uint32_t v = acc[0];
-                v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kHalfMirror, 0xF, 0xF, false);  // 16 lanes
+                const uint32_t v = bfdpp<kHalfMirror, 4>(acc[0], acc[1]);  // 16 lanes
                 uint32_t t0 = v & 0xFFFFu, tc = v >> 16;
                 t0 += (uint32_t)__builtin_amdgcn_mov_dpp((int)t0, kQuadXor2, 0xF, 0xF, false);
                 tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor2, 0xF, 0xF, false);
