@@ -1621,6 +1621,31 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             }
         }
     }
+    // Packed over rows: a one-stream-per-lane wave that spans up to four
+    // detector rows and 64 columns (a row or two of a disk mask) keeps one
+    // accumulator per scan with three fields relative to the wave's first live
+    // row and column: bits 0-7 the sum of the values, bits 8-17 the row moment,
+    // bits 18-31 the column moment (weight 1 + (row offset << 8) + (column
+    // offset << 18), below 2^24). Over 16 lanes the fields stay below their
+    // widths (240 < 2^8, 16 x 15 x 3 = 720 < 2^10, 16 x 15 x 63 = 15120 < 2^14),
+    // so the first four reduction levels run packed and the last two per field.
+    bool pack3 = false;
+    uint32_t kr0 = 0, kc0 = 0;
+    if constexpr (OP == Op::Moments && K == 1) {
+        if (!rowu) {
+            const bool live = (sl[0].meta & 7u) != 7u;
+            kr0 = wave_min(live ? kr[0] : 0xFFFFFFFFu);
+            kc0 = wave_min(live ? kc[0] : 0xFFFFFFFFu);
+            const bool far = live && (kr[0] - kr0 > 3u || kc[0] - kc0 > 63u);
+            pack3 = __builtin_amdgcn_ballot_w64(live) && !__builtin_amdgcn_ballot_w64(far);
+            if (pack3) {
+                wgt[0] = live ? 1u + ((kr[0] - kr0) << 8) + ((kc[0] - kc0) << 18) : 0u;
+                B0 = wave_sum(base0);
+                Bc = wave_sum(baseC);
+                Br = wave_sum(baseR);
+            }
+        }
+    }
     if constexpr (OP == Op::Moments) {
         if (rowu) {
             uint32_t m = 0xFFFFFFFFu;
@@ -1740,6 +1765,7 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
         constexpr bool ROWU = decltype(rowu)::value;  // moments of a wave inside one detector row
         constexpr bool PACKED = decltype(packed_t)::value == 1;  // one packed accumulator (a row-uniform wave)
         constexpr bool PACK2 = decltype(packed_t)::value == 2;   // one per slot (each slot's pixels in one row)
+        constexpr bool PACK3 = decltype(packed_t)::value == 3;   // one over up to four rows (one slot per lane)
         if constexpr (is_region(OP)) {
             auto rw = region_walk<is_frames(OP)>(r, b, ra);
             for (uint32_t t = 0; t < kBlk / 2; t++) {
@@ -1844,6 +1870,57 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     atomicAdd(&pt.m0[s], m0);
                     atomicAdd(&pt.mc[s], (unsigned long long)mad24(kcs[0], t0, mad24(kcs[1], t1, Bc + tc)));
                     atomicAdd(&pt.mr[s], (unsigned long long)mad24(krs[0], t0, mad24(krs[1], t1, Br)));
+                }
+            }
+        } else if constexpr (OP == Op::Moments && PACK3) {
+            constexpr int CH = 16;
+            const uint32_t my = lane_scan<CH>();
+            const bool writer = lane_writes<CH>();
+            for (uint32_t c = 0; c < kBlk / CH; c++) {
+                uint32_t acc[CH];
+#pragma unroll
+                for (int i = 0; i < CH; i++) acc[i] = 0;
+#pragma unroll
+                for (int tt = 0; tt < CH / 2; tt++) {
+                    uint32_t v0[K], v1[K];
+                    if (step(form, c * (CH / 2) + tt, v0, v1)) {
+                        // counts beyond the packed range: 15 stays packed, the excess
+                        // (negative below the window) goes to the partials with its moments
+#pragma unroll
+                        for (int h = 0; h < 2; h++) {
+                            uint32_t &v = h ? v1[0] : v0[0];
+                            if (v > 15u) {
+                                const uint32_t s = c * CH + 2 * tt + h;
+                                const long long x = (int32_t)(v - 15u);
+                                atomicAdd(&pt.m0[s], v - 15u);
+                                atomicAdd(&pt.mc[s], (unsigned long long)(x * (long long)kc[0]));
+                                atomicAdd(&pt.mr[s], (unsigned long long)(x * (long long)kr[0]));
+                                v = 15u;
+                            }
+                        }
+                    }
+                    acc[2 * tt] = mad24(v0[0], wgt[0], acc[2 * tt]);
+                    acc[2 * tt + 1] = mad24(v1[0], wgt[0], acc[2 * tt + 1]);
+                    asm volatile("" : "+v"(acc[2 * tt]), "+v"(acc[2 * tt + 1]));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                transpose_head<CH>(acc);
+                const uint32_t v = bfdpp<kHalfMirror, 4>(acc[0], acc[1]);  // 16 lanes
+                uint32_t ts = v & 0xFFu, tr = __builtin_amdgcn_ubfe(v, 8, 10), tc = v >> 18;
+                ts += (uint32_t)__builtin_amdgcn_mov_dpp((int)ts, kQuadXor2, 0xF, 0xF, false);
+                tr += (uint32_t)__builtin_amdgcn_mov_dpp((int)tr, kQuadXor2, 0xF, 0xF, false);
+                tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor2, 0xF, 0xF, false);
+                ts += (uint32_t)__builtin_amdgcn_mov_dpp((int)ts, kQuadXor1, 0xF, 0xF, false);
+                tr += (uint32_t)__builtin_amdgcn_mov_dpp((int)tr, kQuadXor1, 0xF, 0xF, false);
+                tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor1, 0xF, 0xF, false);
+                const uint32_t m0 = ts + B0;
+                if (writer && m0) {
+                    // 32 bits suffice: totals at most 64 x 15, relative moments below
+                    // 64 x 15 x 63, window-base sums at most 64 x 13 x 1023
+                    const uint32_t s = c * CH + my;
+                    atomicAdd(&pt.m0[s], m0);
+                    atomicAdd(&pt.mc[s], (unsigned long long)mad24(kc0, ts, Bc + tc));
+                    atomicAdd(&pt.mr[s], (unsigned long long)mad24(kr0, ts, Br + tr));
                 }
             }
         } else if constexpr (OP == Op::Moments && PACKED) {
@@ -1975,6 +2052,11 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
             } else if constexpr (PLAIN && K == 2) {
                 if (pack2)
                     run(form, std::false_type{}, std::integral_constant<int, 2>{});
+                else
+                    run(form, std::false_type{}, none{});
+            } else if constexpr (PLAIN && K == 1) {
+                if (pack3)
+                    run(form, std::false_type{}, std::integral_constant<int, 3>{});
                 else
                     run(form, std::false_type{}, none{});
             } else {

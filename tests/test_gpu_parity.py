@@ -272,6 +272,37 @@ def test_paired_moments_packed_at_the_largest_coordinates(R, C):
         res.finish()
 
 
+@pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
+def test_paired_moments_packed_over_rows_at_the_bound(dtype):
+    """Masked CoM on a 16 x 192 paired resident whose one-stream-per-lane waves
+    span four detector rows and 64 columns: the mask keeps columns 0-7 and
+    56-63 of every row (16 pixels a row), so each wave's 64 pixels have row
+    offsets 0-3 and column offsets 0-63 and share one packed word per scan
+    with three fields. Counts are uniform in 10..40, so most escape the chosen
+    model's window and are clamped to 15 in the packed word (the excess goes
+    to the partials): the fields reach their bounds. Two more masks fall just
+    outside the packed range and take the unpacked form: one adds column 64
+    (a column offset of 64), one keeps 12 pixels a row (waves over five rows).
+    Bit-exact against the oracle."""
+    rng = np.random.default_rng(5151)
+    R, C, S = 16, 192, 1024
+    P = R * C
+    c = rng.integers(10, 41, size=(S, P)).astype(dtype)
+    c[:, 2 * C: 2 * C + 8] = 0  # EMPTY streams inside a packed wave
+    blob = q().encode(c, 2, 512, R, C, layout=1)
+    w = synth.Workload("over_rows", 2, 512, R, C, 2, 0, 0, 0, 0, 0, 0, 0, 0, 1)
+    masks = []
+    for keep in ([*range(0, 8), *range(56, 64)], [*range(0, 8), *range(56, 65)], [*range(0, 6), *range(58, 64)]):
+        row = np.zeros(C, np.uint8)
+        row[keep] = 1
+        masks.append(np.tile(row, R))
+    with q().Resident(blob) as res:
+        for m in masks:
+            check_com(res, c, w, m, None)
+            assert np.array_equal(u(res.masked_sum(m)), oracle.masked_sum(c, m))
+        res.finish()
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_uint64_sums_257_detector(layout):
     # 257 x 257 uint16: a full-detector sum can pass 2^32, so outputs are uint64
