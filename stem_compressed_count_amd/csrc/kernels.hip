@@ -1711,12 +1711,19 @@ __device__ __forceinline__ void paired_tile(const DevResident &r, const uint16_t
                     }
                 }
             }
-            // codes are at most 10 bits: one 32-bit refill per three pairs, on a
-            // wave-uniform cadence (the paired-resident page's refill rhythm)
-            if (t % 3 == 2) {
+            // Codes are at most 10 bits. The wave refills when some lane holds
+            // fewer than 10 bits (the marker below bit 10), and then every lane
+            // with room for a dword takes one: the refills of a wave's lanes fall
+            // together, so a wave of dim streams refills every ten or more pairs
+            // instead of at every cadence point, and each refill's load has had
+            // that long to arrive.
+            bool low = false;
+#pragma unroll
+            for (int k = 0; k < K; k++) low |= sl[k].s.r < 1024u;
+            if (__builtin_amdgcn_ballot_w64(low)) {
 #pragma unroll
                 for (int k = 0; k < K; k++) {
-                    // keep the reservoir test inside the cadence branch (else it
+                    // keep the reservoir test inside the wave's branch (else it
                     // runs at every step)
                     uint32_t hi = (uint32_t)(sl[k].s.r >> 32);
                     asm volatile("" : "+v"(hi));
