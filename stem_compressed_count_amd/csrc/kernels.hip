@@ -787,6 +787,23 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
 #pragma unroll
         for (int k = 0; k < K; k++) bbits_refill(sl[k].s, rs);
     };
+    // The plain form's sums and moments refill on demand in waves of dim
+    // streams: a step takes at most one 16-bit word, so the wave refills when
+    // some lane holds fewer than 16 bits, and then every lane with room for a
+    // dword takes one. The lanes' refills fall together, every several steps
+    // instead of every second one. A wave holding a stream of more than 5
+    // coded bits per value (renormalising in a third of its steps or more)
+    // would refill about every step that way, so it keeps the cadence.
+    bool dim = true;
+#pragma unroll
+    for (int k = 0; k < K; k++) dim &= !sl[k].live || sl[k].raw || 8u * sl[k].len <= 5u * n;
+    const bool ondemand = !__builtin_amdgcn_ballot_w64(!dim);
+    auto refill_low = [&]() {
+        bool low = false;
+#pragma unroll
+        for (int k = 0; k < K; k++) low |= sl[k].s.n < 16u;
+        if (__builtin_amdgcn_ballot_w64(low)) refill();
+    };
     // The staged form's range: the block from the 32-byte boundary at or
     // below its start, so chunk loads are aligned.
     const uint32_t delta = STG ? (uint32_t)reinterpret_cast<uint64_t>(r.payload + base) & 31u : 0u;
@@ -835,8 +852,9 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         }
     };
 
-    auto run = [&](auto form, auto rowu) {
+    auto run = [&](auto form, auto rowu, auto od) {
         constexpr bool ROWU = decltype(rowu)::value;  // moments of a wave inside one detector row
+        constexpr bool OD = decltype(od)::value;      // sums and moments refill on demand (plain form, dim wave)
         // the escape form refills after every step: a step then starts with at
         // least 33 bits, enough for a renormalisation word and a literal, so an
         // escape reads its literal without a load of its own
@@ -982,6 +1000,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     if constexpr (OP == Op::Moments && ROWU) asm volatile("" : "+v"(ac[jj]));
                     if constexpr (staged) {
                         if (jj % kStageC == kStageC - 1) cadence();
+                    } else if constexpr (OD) {
+                        refill_low();
                     } else if (every || (jj & 1)) {
                         refill();
                     }
@@ -1013,7 +1033,10 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 if constexpr (OP == Op::Index) {
                     t0 = wave_sum(t0) + cw;
                     if (lane == 0 && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + j], t0);
-                    if (every || (j & 1) || j + 1 == n) refill();
+                    if constexpr (OD)
+                        refill_low();
+                    else if (every || (j & 1) || j + 1 == n)
+                        refill();
                     continue;
                 }
                 if (t0) atomicAdd(&pt.m0[j], t0);
@@ -1023,6 +1046,8 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 }
                 if constexpr (staged) {
                     if (j % kStageC == kStageC - 1) cadence();
+                } else if constexpr (OD) {
+                    refill_low();
                 } else if (every || (j & 1) || j + 1 == n) {
                     refill();
                 }
@@ -1289,24 +1314,24 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
         idle |= !sl[k].live;
     }
     const bool idle_ok = (tbl[0] >> 24) == 0u;
-    auto run_rows = [&](auto form) {
+    auto run_rows = [&](auto form, auto od) {
         if constexpr (OP == Op::Moments) {
             if (rowu)
-                run(form, std::true_type{});
+                run(form, std::true_type{}, od);
             else
-                run(form, std::false_type{});
+                run(form, std::false_type{}, od);
         } else {
-            run(form, std::false_type{});
+            run(form, std::false_type{}, od);
         }
     };
     if (__builtin_amdgcn_ballot_w64(raw || (idle && !idle_ok))) {
-        run(std::integral_constant<int, kMixed>{}, std::false_type{});
+        run(std::integral_constant<int, kMixed>{}, std::false_type{}, std::false_type{});
     } else if (WIDE && (tbl[(STG ? 1 : 2) * 4095] >> 24) == 255u) {
         // symbols are laid out in increasing order, so the last slot holds the
         // largest coded symbol: 255 there means escapes can occur
         if constexpr (STG) {
             stage_init();
-            run_rows(std::integral_constant<int, kStaged>{});
+            run_rows(std::integral_constant<int, kStaged>{}, std::false_type{});
             // hand the end position to the reservoir, where the end checks read it
 #pragma unroll
             for (int k = 0; k < K; k++) {
@@ -1314,10 +1339,15 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                 sl[k].s.n = 0;
             }
         } else {
-            run_rows(std::integral_constant<int, kEscape>{});
+            run_rows(std::integral_constant<int, kEscape>{}, std::false_type{});
         }
+    } else if constexpr (OP == Op::Sum || OP == Op::Moments || OP == Op::Index) {
+        if (ondemand)
+            run_rows(std::integral_constant<int, kPlain>{}, std::true_type{});
+        else
+            run_rows(std::integral_constant<int, kPlain>{}, std::false_type{});
     } else {
-        run_rows(std::integral_constant<int, kPlain>{});
+        run_rows(std::integral_constant<int, kPlain>{}, std::false_type{});
     }
     asm volatile("" ::"v"(touched));
     if constexpr (OP == Op::Split) {
