@@ -688,6 +688,31 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
             rowu = !__builtin_amdgcn_ballot_w64(diff);
         }
     }
+    // Packed row moments: in such a wave, when the block codes no symbol above
+    // 127 and the live columns span at most 128, one accumulator per scan holds
+    // the sum of the values (bits 0-11) and their column moment relative to the
+    // wave's first live column (bits 12-31): one 24-bit multiply-add per value
+    // with the weight 1 + (column offset << 12). Over 16 lanes of two slots both
+    // fields stay below their widths (16 x 2 x 127 = 4064 < 2^12, 4064 x 127 <
+    // 2^20), so the first four reduction levels run packed and the last two per
+    // field. Only the plain form (no escapes, no RAW slots) takes it.
+    bool rowp = false;
+    uint32_t kcw = 0, wgt[OP == Op::Moments ? K : 1];
+    if constexpr (OP == Op::Moments && !STG) {
+        if (rowu && (tbl[2 * 4095] >> 24) <= 127u) {
+            uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+            for (int k = 0; k < K; k++)
+                if (sl[k].live) m = min(m, kc[k]);
+            kcw = wave_min(m);
+            bool far = false;
+#pragma unroll
+            for (int k = 0; k < K; k++) far |= sl[k].live && kc[k] - kcw > 127u;
+            rowp = !__builtin_amdgcn_ballot_w64(far);
+#pragma unroll
+            for (int k = 0; k < K; k++) wgt[k] = sl[k].live ? 1u + ((kc[k] - kcw) << 12) : 0u;
+        }
+    }
 
     // byte-rANS decode step (FORMAT 2.3). The block table holds two words per
     // slot, side by side and read by one 64-bit LDS load: f | symbol << 24
@@ -853,8 +878,9 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     };
 
     auto run = [&](auto form, auto rowu, auto od) {
-        constexpr bool ROWU = decltype(rowu)::value;  // moments of a wave inside one detector row
-        constexpr bool OD = decltype(od)::value;      // sums and moments refill on demand (plain form, dim wave)
+        constexpr bool ROWU = decltype(rowu)::value != 0;  // moments of a wave inside one detector row
+        constexpr bool ROWP = decltype(rowu)::value == 2;  // packed row moments
+        constexpr bool OD = decltype(od)::value;           // sums and moments refill on demand (plain form, dim wave)
         // the escape form refills after every step: a step then starts with at
         // least 33 bits, enough for a renormalisation word and a literal, so an
         // escape reads its literal without a load of its own
@@ -982,6 +1008,10 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     step(form, (jj & 1) == 0, v);  // chunks start at even scans
 #pragma unroll
                     for (int k = 0; k < K; k++) {
+                        if constexpr (ROWP) {
+                            a0[jj] = mad24(v[k], wgt[k], a0[jj]);
+                            continue;
+                        }
                         a0[jj] += v[k];
                         if (OP == Op::Moments) {
                             // 24-bit multiplies run at full rate
@@ -997,7 +1027,7 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     // materialise the sums here: deferring them to the chunk end keeps every step's table entry live
                     asm volatile("" : "+v"(a0[jj]));
                     if constexpr (OP == Op::Moments && !ROWU) asm volatile("" : "+v"(ar[jj]), "+v"(ac[jj]));
-                    if constexpr (OP == Op::Moments && ROWU) asm volatile("" : "+v"(ac[jj]));
+                    if constexpr (OP == Op::Moments && ROWU && !ROWP) asm volatile("" : "+v"(ac[jj]));
                     if constexpr (staged) {
                         if (jj % kStageC == kStageC - 1) cadence();
                     } else if constexpr (OD) {
@@ -1012,6 +1042,21 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
                     // one leaf per wave: its per-scan totals go to the leaf's index row
                     const uint32_t t0 = wave_transpose_sum<CH>(a0) + cw;
                     if (writer && t0) atomicAdd(&dt.row[(first >> 6) * kBlk + c * CH + my], t0);
+                } else if constexpr (ROWP) {
+                    transpose_head<CH>(a0);
+                    const uint32_t pv = bfdpp<kHalfMirror, 4>(a0[0], a0[1]);  // 16 lanes
+                    uint32_t t0 = pv & 0xFFFu, tc = pv >> 12;
+                    t0 += (uint32_t)__builtin_amdgcn_mov_dpp((int)t0, kQuadXor2, 0xF, 0xF, false);
+                    tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor2, 0xF, 0xF, false);
+                    t0 += (uint32_t)__builtin_amdgcn_mov_dpp((int)t0, kQuadXor1, 0xF, 0xF, false);
+                    tc += (uint32_t)__builtin_amdgcn_mov_dpp((int)tc, kQuadXor1, 0xF, 0xF, false);
+                    if (writer && t0) {
+                        // totals at most 64 x 2 x 127, column moments below 2^21 + 2^24
+                        const uint32_t j = j0 + c * CH + my;
+                        atomicAdd(&pt.m0[j], t0);
+                        atomicAdd(&pt.mc[j], (unsigned long long)mad24(kcw, t0, tc));
+                        atomicAdd(&pt.mr[j], (unsigned long long)mad24(kru, t0, 0u));
+                    }
                 } else {
                     chunk_to_lds<CH, OP, ROWU>(a0, ar, ac, my, writer, split, pt.m0 + j0 + c * CH,
                                                pt.mr + j0 + c * CH, pt.mc + j0 + c * CH, kru);
@@ -1315,13 +1360,23 @@ __device__ __forceinline__ void rans_tile(const DevResident &r, const uint16_t *
     }
     const bool idle_ok = (tbl[0] >> 24) == 0u;
     auto run_rows = [&](auto form, auto od) {
+        using rows0 = std::integral_constant<int, 0>;
         if constexpr (OP == Op::Moments) {
-            if (rowu)
-                run(form, std::true_type{}, od);
-            else
-                run(form, std::false_type{}, od);
+            if constexpr (decltype(form)::value == kPlain) {
+                if (rowp)
+                    run(form, std::integral_constant<int, 2>{}, od);
+                else if (rowu)
+                    run(form, std::integral_constant<int, 1>{}, od);
+                else
+                    run(form, rows0{}, od);
+            } else {
+                if (rowu)
+                    run(form, std::integral_constant<int, 1>{}, od);
+                else
+                    run(form, rows0{}, od);
+            }
         } else {
-            run(form, std::false_type{}, od);
+            run(form, rows0{}, od);
         }
     };
     if (__builtin_amdgcn_ballot_w64(raw || (idle && !idle_ok))) {

@@ -303,6 +303,37 @@ def test_paired_moments_packed_over_rows_at_the_bound(dtype):
         res.finish()
 
 
+@pytest.mark.parametrize("dtype", [np.uint8, np.uint16])
+@pytest.mark.parametrize("top", [127, 128])
+def test_rans_moments_packed_rows_at_the_bound(dtype, top):
+    """Full-detector CoM on a 4 x 256 byte-rANS resident: every two-stream wave
+    lies in one detector row and spans 128 columns. Counts are mostly small with
+    a sprinkle at `top` and two whole frames at `top`. With top = 127 the block
+    codes no symbol above 127, so those waves keep one packed word per scan, and
+    the full frames take both of its fields to their bounds (16 lanes x 2 x 127
+    values, column offsets up to 127). With top = 128 they take the unpacked
+    form. Bit-exact against the oracle, also with a mask that moves the slots
+    off the 64-pixel grid."""
+    rng = np.random.default_rng(777 + top)
+    R, C, S = 4, 256, 1024
+    P = R * C
+    c = np.minimum(rng.geometric(0.25, size=(S, P)) - 1, top)
+    c[rng.random((S, P)) < 0.02] = top
+    c[7] = top
+    c[600] = top
+    c = c.astype(dtype)
+    blob = q().encode(c, 2, 512, R, C, layout=0)
+    shifted = np.ones(P, np.uint8)
+    shifted[0] = 0
+    w = synth.Workload("rows_rans", 2, 512, R, C, 2, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    with q().Resident(blob) as res:
+        for m in (None, shifted):
+            check_com(res, c, w, m, None)
+            mm = np.ones(P, np.uint8) if m is None else m
+            assert np.array_equal(u(res.masked_sum(mm)), oracle.masked_sum(c, mm))
+        res.finish()
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_uint64_sums_257_detector(layout):
     # 257 x 257 uint16: a full-detector sum can pass 2^32, so outputs are uint64
