@@ -170,6 +170,29 @@ def test_u8_low_dose():
                        strides=(1, 4))
 
 
+@pytest.mark.parametrize("name", ["scan512_u8_lowdose", "scan128_u16"])
+def test_dim_waves_on_a_ragged_final_block(name):
+    """1147 scans (37 x 31): two complete blocks and a final one of 123 scans,
+    seven 16-scan chunks and a tail of 11 scans decoded one at a time. Most
+    waves hold dim streams (mean 0.02 or 0.1 outside the disk), which refill
+    on demand, and the disk's waves keep the two-step cadence; the switch
+    between the chunks and the tail must keep every lane supplied. Every
+    product against the oracle at strides 1 and 3, and the polar index's sums
+    (the index build decodes the same way)."""
+    w, counts, valid, blob = case(name, 37, 31)
+    assert w.S % 512 == 123
+    masks = synth.query_masks(w)
+    check_all_products(w, counts, valid, blob, masks, masks["df"] if "df" in masks else masks["bf"],
+                       [(0, 8, 0, 8), (33, 37, 20, 31)] + random_rects(w, 3, 11), strides=(1, 3))
+    full = np.ones(w.P, np.uint8)
+    with q().Resident(blob, valid=valid) as res:
+        res.index_build()
+        for m in (full, masks["bf"]):
+            for k in (1, 3):
+                assert np.array_equal(u(res.masked_sum(m, block_stride=k)), oracle.masked_sum(counts, m, valid, stride=k))
+        res.finish()
+
+
 def test_u8_moving_mask_sweep():
     w, counts, valid, blob = case("scan512_u8_lowdose", 16, 512)
     sweep = synth.sweep_masks(w)
