@@ -2357,6 +2357,78 @@ __device__ __forceinline__ uint32_t select_range(const DevResident &r, const uin
     return seen > skip ? min(seen, want) - skip : 0u;
 }
 
+// Units of `unit` selected pixels (one mask): tile t starts unit k when it
+// holds the pixel numbered k * unit; udesc[k] is that tile and the selected
+// pixels of it before the unit's first, as for the items above. Returns the
+// number of units.
+template <int WG>
+__device__ __forceinline__ uint32_t plan_units(const uint32_t *counts, uint32_t P, uint32_t unit, uint16_t *udesc,
+                                               uint32_t *wtot) {
+    constexpr uint32_t kPer = 2 * kMaxPlanTiles / WG;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    const uint32_t n_tiles = (P + kPlanFine - 1) / kPlanFine;
+    uint32_t c[kPer], s = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kPer; j++) {
+        const uint32_t t = tid * kPer + j;
+        c[j] = t < n_tiles ? counts[t] : 0u;
+        s += c[j];
+    }
+    uint32_t x = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= (uint32_t)off) x += y;
+    }
+    __syncthreads();  // wtot may still be read by the previous user
+    if (lane == 63) wtot[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < WG / 64; w++) {
+        before += w < wave ? wtot[w] : 0u;
+        total += wtot[w];
+    }
+    uint32_t e = before + x - s;
+#pragma unroll
+    for (uint32_t j = 0; j < kPer; j++) {
+        const uint32_t t = tid * kPer + j;
+        if (c[j]) {
+            const uint32_t k = (e + unit - 1) / unit;
+            if (k * unit < e + c[j]) udesc[k] = (uint16_t)((t << 6) | (k * unit - e));
+        }
+        e += c[j];
+    }
+    __syncthreads();
+    return (total + unit - 1) / unit;
+}
+
+// The pixels of one unit, gathered by one wave alone into its own slice of
+// the list (offsets from the unit's first tile), 64 pixels per ballot.
+__device__ __forceinline__ uint32_t select_unit(const DevResident &r, const uint8_t *mask, int complement,
+                                                uint32_t desc, uint32_t unit, uint32_t end, uint32_t &p0,
+                                                uint16_t *wsel) {
+    const uint32_t lane = lane_id();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const uint32_t skip = desc & 63u, want = skip + unit;
+    p0 = (desc >> 6) * kPlanFine;
+    uint32_t seen = 0;  // selected pixels from p0 on, skipped ones included
+    for (uint32_t base = p0; base < end && seen < want; base += 64) {
+        const uint32_t p = base + lane;
+        bool f = false;
+        if (p < end) f = r.valid[p] != 0 && (mask ? ((mask[p] != 0) != (complement != 0)) : true);
+        const unsigned long long bal = __ballot(f);
+        const uint32_t ord = seen + (uint32_t)__popcll(bal & below);
+        if (f && ord >= skip && ord < want) wsel[ord - skip] = (uint16_t)(p - p0);
+        seen += (uint32_t)__popcll(bal);
+    }
+    // the wave's own list: its writes are read by other lanes of the same wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return seen > skip ? min(seen, want) - skip : 0u;
+}
+
 // ------------------------------------------------------------------ index groups
 // One work item of the index build: WG consecutive polar positions, lane l of
 // wave w at position (group * WG / 64 + w) * 64 + l, so every wave decodes one
@@ -2749,6 +2821,7 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
         if (threadIdx.x < 32) tbl[kPairTable + threadIdx.x] = r.model_info[threadIdx.x];
     }
     __shared__ uint16_t desc[kMaxItems<kPairWG>];
+    __shared__ uint16_t udesc[(OP == Op::Sum || OP == Op::Moments) ? kMaxPlanTiles : 1];
     // planned: items of `cap` selected pixels; else every pixel tile of
     // tile_px. With a subtracted mask, its items follow those of mask.
     const bool two = da.neg_mask != nullptr;
@@ -2768,6 +2841,46 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     const bool hold = hold_partials(r);
     uint32_t held_b = 0xFFFFFFFFu;
     bool held_sub = false;
+    // Sums and moments of one mask: a workgroup takes whole blocks (or, with
+    // fewer visited blocks than workgroups, an equal share of one block's
+    // units), and each of its waves takes units of 64 or 128 selected pixels
+    // (one or two streams per lane) one after another, selecting each unit's
+    // pixels itself. The waves meet only at the end of the block or share,
+    // where the partials are flushed: with a barrier after every work item,
+    // waves spent a quarter of their time waiting for the slowest wave of the
+    // item.
+    if constexpr (kAcc) {
+        if (plan && !two && hold) {
+            const uint32_t unit = cap > kPairWG ? 128u : 64u;
+            const uint32_t n_units = plan_units<kPairWG>(plan, r.P, unit, udesc, wtot);
+            const uint32_t shares = n_visited >= gridDim.x ? 1u : gridDim.x / n_visited;
+            const uint32_t wave = threadIdx.x >> 6;
+            uint16_t *wsel = sel + wave * 128u;
+            const DpTile dt{nullptr, sbits, 0};
+            for (uint32_t w = blockIdx.x; w < n_visited * shares; w += gridDim.x) {
+                const uint32_t vb = w / shares, part = w % shares;
+                const uint32_t b = vb * stride;
+                const uint8_t *d = r.dir + 16ull * b;
+                const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
+                const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
+                zero_partials<OP>(sp, kBlk);
+                __syncthreads();
+                for (uint32_t u = part * (kPairWG / 64) + wave; u < n_units; u += shares * (kPairWG / 64)) {
+                    uint32_t p0 = 0;
+                    const uint32_t n_sel = select_unit(r, mask, complement, udesc[u], unit, end[0], p0, wsel);
+                    if (n_sel == 0) continue;
+                    if (unit == 128u)
+                        paired_tile<2, WIDE, OP>(r, wsel, p0, n_sel, 0, b, base, nbytes, tbl, pt, ra, dt);
+                    else
+                        paired_tile<1, WIDE, OP>(r, wsel, p0, n_sel, 0, b, base, nbytes, tbl, pt, ra, dt);
+                }
+                __syncthreads();
+                flush_partials<OP>(sp, kBlk, (uint64_t)b * kBlk, r.S, out, out64, negate);
+                __syncthreads();
+            }
+            return;
+        }
+    }
     // a block's items go to neighbouring workgroups (w / n_live), so a wave of
     // workgroups reads few blocks at a time: measured faster here than keeping
     // a workgroup on one block; the partials are held only while the block stays
