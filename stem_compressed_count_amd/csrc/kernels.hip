@@ -2822,6 +2822,7 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     }
     __shared__ uint16_t desc[kMaxItems<kPairWG>];
     __shared__ uint16_t udesc[(OP == Op::Sum || OP == Op::Moments) ? kMaxPlanTiles : 1];
+    __shared__ uint32_t next_unit;
     // planned: items of `cap` selected pixels; else every pixel tile of
     // tile_px. With a subtracted mask, its items follow those of mask.
     const bool two = da.neg_mask != nullptr;
@@ -2848,7 +2849,8 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
     // pixels itself. The waves meet only at the end of the block or share,
     // where the partials are flushed: with a barrier after every work item,
     // waves spent a quarter of their time waiting for the slowest wave of the
-    // item.
+    // item. Running apart, the waves fetch more stream lines again from past
+    // the L2, but those reads stay far below the HBM rate.
     if constexpr (kAcc) {
         if (plan && !two && hold) {
             const uint32_t unit = cap > kPairWG ? 128u : 64u;
@@ -2864,8 +2866,20 @@ __global__ __launch_bounds__(kPairWG) void k_reduce_paired(DevResident r, const 
                 const uint64_t base = *reinterpret_cast<const uint64_t *>(d);
                 const uint32_t nbytes = *reinterpret_cast<const uint32_t *>(d + 12);
                 zero_partials<OP>(sp, kBlk);
+                if (threadIdx.x == 0) next_unit = 0;
                 __syncthreads();
-                for (uint32_t u = part * (kPairWG / 64) + wave; u < n_units; u += shares * (kPairWG / 64)) {
+                // the c-th unit of this share: two-stream units go to whichever wave
+                // asks next (dim full-detector waves run far ahead of bright ones);
+                // one-stream units (a disk's) in a fixed interleave, measured faster
+                for (uint32_t k = 0;; k++) {
+                    uint32_t c = k * (kPairWG / 64) + wave;
+                    if (unit == 128u) {
+                        if ((threadIdx.x & 63u) == 0) c = atomicAdd(&next_unit, 1u);
+                        c = (uint32_t)__builtin_amdgcn_readfirstlane((int)c);
+                    }
+                    const uint32_t u = (c / (kPairWG / 64)) * shares * (kPairWG / 64) + part * (kPairWG / 64) +
+                                       c % (kPairWG / 64);
+                    if (u >= n_units) break;
                     uint32_t p0 = 0;
                     const uint32_t n_sel = select_unit(r, mask, complement, udesc[u], unit, end[0], p0, wsel);
                     if (n_sel == 0) continue;
